@@ -1,0 +1,324 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each check takes an ``oracle.Oracle`` handle so that the same checks can run
+against builds of the oracle with a planted mistake (see
+test_oracle_mutations.py): every plausible mistake must trip at least one.
+
+Sources of truth used here, none of them the oracle's own code:
+  * scipy's normal survival function (a different routine from libm's erfc)
+    for the exponent probabilities of N(0, sigma^2)  [pages, section 2.A];
+  * float64 Monte-Carlo draws classified with numpy.frexp, which fixes the
+    octave -> BF16 exponent-field mapping independently;
+  * a brute-force exponent histogram of quantile-stratified inputs, whose
+    top-7 must agree with the closed-form plan away from near-ties
+    [section 2.A: the table replaces an online histogram];
+  * the pages' stated facts: top-7 cover more than 97 % of near-Gaussian values,
+    an exponent among the seven takes a 3-bit code 001..111, any other takes
+    000 and goes whole to a separate zero-point array, 16 -> 11 bits, lossless
+    [sections 2.A and 2.B];
+  * the invariant that scaling sigma by 2^k shifts every probability by k
+    exponents exactly (powers of two scale without rounding);
+  * exhaustive enumeration of all 65,536 BF16 bit patterns.
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy import special, stats
+
+from lossless_bf16_exponent_amd import workloads
+
+MAGIC = b"ZCC1"
+GROUP = 4096
+HAND_PLAN = (0, 1, 2, 127, 128, 253, 255)  # non-contiguous, touches both ends
+
+
+# --------------------------------------------------------------------------
+# helpers that read a stream by the layout reading (no oracle code involved)
+# --------------------------------------------------------------------------
+
+def exponent_field(x: np.ndarray) -> np.ndarray:
+    return ((x.astype(np.uint32) >> 7) & 0xFF).astype(np.int64)
+
+
+def scipy_probabilities(sigma: float) -> np.ndarray:
+    """P(exponent field == e) for N(0, sigma^2), from scipy's normal tail."""
+    e = np.arange(1, 255)
+    lo = np.ldexp(1.0, e - 127) / sigma
+    hi = np.ldexp(1.0, e - 126) / sigma
+    p = np.zeros(256)
+    p[1:255] = 2.0 * (stats.norm.sf(lo) - stats.norm.sf(hi))
+    p[0] = 1.0 - 2.0 * stats.norm.sf(np.ldexp(1.0, -126) / sigma)
+    return p
+
+
+def top7(p_or_counts: np.ndarray) -> tuple:
+    """Seven largest entries, ties to the smaller index, returned ascending."""
+    order = sorted(range(len(p_or_counts)), key=lambda e: (-p_or_counts[e], e))
+    return tuple(sorted(order[:7]))
+
+
+def parse_stream(s: np.ndarray, n: int, lay: dict) -> dict:
+    b = s.tobytes()
+    hdr = {
+        "magic": b[0:4],
+        "version": int.from_bytes(b[4:6], "little"),
+        "header_bytes": int.from_bytes(b[6:8], "little"),
+        "n": int.from_bytes(b[8:16], "little"),
+        "group": int.from_bytes(b[16:20], "little"),
+        "groups": int.from_bytes(b[20:24], "little"),
+        "exps": tuple(b[24:31]),
+        "pad31": b[31],
+        "E": int.from_bytes(b[32:40], "little"),
+        "total": int.from_bytes(b[40:48], "little"),
+        "tail": b[48:128],
+    }
+    sm = s[lay["off_sm"]:lay["off_sm"] + n]
+    planes = [np.unpackbits(s[lay[k]:lay[k] + (n + 7) // 8], bitorder="little")[:n]
+              for k in ("off_p0", "off_p1", "off_p2")]
+    code = planes[0].astype(np.int64) | (planes[1].astype(np.int64) << 1) | (planes[2].astype(np.int64) << 2)
+    ng = lay["groups"]
+    tab = s[lay["off_tab"]:lay["off_tab"] + 4 * (ng + 1)].view("<u4").astype(np.int64)
+    zp = s[lay["off_zp"]:lay["off_zp"] + hdr["E"]]
+    return {"hdr": hdr, "sm": sm, "code": code, "tab": tab, "zp": zp}
+
+
+def check_stream(orc, x: np.ndarray, exps, s: np.ndarray) -> None:
+    """Every field of the stream against the definition of the method."""
+    n = x.size
+    lay = orc.layout(n)
+    # every section starts on a 128-byte boundary (section 2.C pads blocks to 128 B)
+    assert all(lay[k] % 128 == 0 for k in ("off_sm", "off_p0", "off_p1", "off_p2", "off_tab", "off_zp"))
+    assert lay["off_p0"] >= lay["off_sm"] + n and lay["off_tab"] - lay["off_p2"] >= (n + 7) // 8
+    st = parse_stream(s, n, lay)
+    h = st["hdr"]
+    assert h["magic"] == MAGIC and h["version"] == 1 and h["header_bytes"] == 128
+    assert h["n"] == n and h["group"] == GROUP and h["groups"] == (n + GROUP - 1) // GROUP
+    assert h["exps"] == tuple(exps) and h["pad31"] == 0 and h["tail"] == bytes(80)
+    e = exponent_field(x)
+    in_plan = np.isin(e, np.array(exps))
+    # sign+mantissa byte: sign in bit 7, the 7 mantissa bits below it
+    assert np.array_equal(st["sm"] & 0x7F, (x & 0x7F).astype(np.uint8))
+    assert np.array_equal(st["sm"] >> 7, (x >> 15).astype(np.uint8))
+    # remap: code k (1..7) <-> k-th smallest exponent of the seven, 000 otherwise
+    code = st["code"]
+    assert np.array_equal(code == 0, ~in_plan)
+    sorted_exps = np.array(sorted(exps))
+    assert np.array_equal(sorted_exps[code[in_plan] - 1], e[in_plan])
+    # zero-point array: the full exponent of every value coded 000, in order
+    assert h["E"] == int((~in_plan).sum())
+    assert np.array_equal(st["zp"], e[~in_plan].astype(np.uint8))
+    # table: zero-point values before the first element of every group
+    before = np.concatenate([[0], np.cumsum(~in_plan)])
+    ng = h["groups"]
+    assert np.array_equal(st["tab"], before[np.minimum(np.arange(ng + 1) * GROUP, n)])
+    # size
+    assert h["total"] == lay["off_zp"] + h["E"] == s.size
+    # every byte outside the fields is zero
+    mask = np.zeros(s.size, dtype=bool)
+    mask[0:48] = True
+    mask[lay["off_sm"]:lay["off_sm"] + n] = True
+    for k in ("off_p0", "off_p1", "off_p2"):
+        mask[lay[k]:lay[k] + (n + 7) // 8] = True
+    mask[lay["off_tab"]:lay["off_tab"] + 4 * (ng + 1)] = True
+    mask[lay["off_zp"]:] = True
+    assert not s[~mask].any()
+    if n % 8:
+        for k in ("off_p0", "off_p1", "off_p2"):
+            assert s[lay[k] + n // 8] >> (n % 8) == 0
+
+
+def all_patterns(seed: int = 7) -> np.ndarray:
+    return np.random.default_rng(seed).permutation(65536).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# plan pins (section 2.A)
+# --------------------------------------------------------------------------
+
+PLAN_SIGMAS = (1e-5, 3e-4, 0.01, 0.02, 0.16, 1.0, 7.5)
+
+
+def pin_probabilities_vs_scipy(orc) -> None:
+    for sigma in PLAN_SIGMAS:
+        p = orc.exponent_probabilities(sigma)
+        ref = scipy_probabilities(sigma)
+        assert p[255] == 0.0
+        assert np.allclose(p[:255], ref[:255], rtol=1e-9, atol=1e-14), sigma
+        assert abs(p.sum() - 1.0) < 1e-12
+
+
+def pin_probabilities_monte_carlo(orc) -> None:
+    """Octave bounds and exponent bias: float64 draws classified with frexp."""
+    sigma = 0.02
+    z = np.random.default_rng(11).standard_normal(2_000_000) * sigma
+    _, k = np.frexp(np.abs(z))  # |z| = m * 2^k, m in [0.5, 1) -> field = k - 1 + 127
+    freq = np.bincount(k + 126, minlength=256)[:256] / z.size
+    p = orc.exponent_probabilities(sigma)
+    tol = 6.0 * np.sqrt(p * (1 - p) / z.size) + 2e-6
+    assert np.all(np.abs(freq - p) <= tol)
+
+
+def pin_plan_values(orc) -> None:
+    """Top-7 of scipy's probabilities, and hand-checkable cases."""
+    for sigma in PLAN_SIGMAS:
+        assert orc.plan_from_sigma(sigma) == top7(scipy_probabilities(sigma)), sigma
+    assert orc.plan_from_sigma(0.02) == tuple(range(116, 123))
+    assert orc.plan_from_sigma(1.0) == tuple(range(122, 129))
+    # all mass below 2^-126: the zero/subnormal field first, then ties broken low
+    assert orc.plan_from_sigma(2.0 ** -130) == tuple(range(0, 7))
+    # mass near the top of the range: field 255 (Inf/NaN) is never chosen
+    assert orc.plan_from_sigma(1e38) == tuple(range(248, 255))
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        try:
+            orc.plan_from_sigma(bad)
+        except ValueError:
+            continue
+        raise AssertionError("sigma %r accepted" % bad)
+
+
+def pin_scale_covariance(orc) -> None:
+    for sigma in (0.02, 0.3):
+        p = orc.exponent_probabilities(sigma)
+        for k in (1, 3):
+            q = orc.exponent_probabilities(sigma * 2.0 ** k)
+            assert np.array_equal(q[1 + k:255], p[1:255 - k]), (sigma, k)
+    assert orc.plan_from_sigma(0.16) == tuple(e + 3 for e in orc.plan_from_sigma(0.02))
+
+
+def pin_coverage(orc) -> None:
+    """Top-7 coverage: above 97 % at the pages' operating points, and within the
+    closed-form band [0.96972, 0.97875] at every sigma (it depends only on
+    log2(sigma) mod 1)."""
+    for f in np.arange(-12.0, 2.0, 1.0 / 32):
+        p = orc.exponent_probabilities(2.0 ** f)
+        cov = p[list(orc.plan_from_sigma(2.0 ** f))].sum()
+        assert 0.96972 <= cov <= 0.97875, (f, cov)
+    for sigma in (0.02, 1.0):
+        p = orc.exponent_probabilities(sigma)
+        assert p[list(orc.plan_from_sigma(sigma))].sum() > 0.97
+
+
+def pin_histogram_top7(orc) -> None:
+    """Closed-form plan == brute-force histogram top-7 of quantile-stratified
+    BF16 samples, except where the 7th and 8th probabilities nearly tie."""
+    checked = 0
+    for n in (4096, 16384, 65536):
+        q = special.ndtri((np.arange(n) + 0.5) / n)
+        for f in np.arange(0.0, 1.0, 1.0 / 64):
+            sigma = 2.0 ** (-6.0 + f)
+            ref = np.sort(scipy_probabilities(sigma))[::-1]
+            if ref[6] - ref[7] < 1e-3 + 4.0 / n:
+                continue
+            x = workloads.bf16_bits_from_f32((q * sigma).astype(np.float32))
+            counts = np.bincount(exponent_field(x), minlength=256)
+            assert top7(counts) == orc.plan_from_sigma(sigma), (n, f)
+            checked += 1
+    assert checked > 150
+
+
+def pin_contiguity_exception(orc) -> None:
+    """Where the zero/subnormal bucket outweighs field 1 the plan has a gap."""
+    sigma = 2.0 ** -120.7
+    assert orc.plan_from_sigma(sigma) == top7(scipy_probabilities(sigma)) == (0, 2, 3, 4, 5, 6, 7)
+    for f in (-122.0, -119.5, -60.0):
+        plan = orc.plan_from_sigma(2.0 ** f)
+        assert plan == tuple(range(plan[0], plan[0] + 7)), f
+
+
+# --------------------------------------------------------------------------
+# codec pins (section 2.B)
+# --------------------------------------------------------------------------
+
+CODEC_PLANS = ((116, 117, 118, 119, 120, 121, 122), (122, 123, 124, 125, 126, 127, 128),
+               (105, 106, 107, 108, 109, 110, 111), (248, 249, 250, 251, 252, 253, 254), HAND_PLAN)
+
+
+def pin_roundtrip_exhaustive(orc) -> None:
+    """Lossless on every BF16 bit pattern (NaN payloads, -0, subnormals, Inf)."""
+    x = all_patterns()
+    for exps in CODEC_PLANS:
+        s = orc.encode(x, exps)
+        status, y = orc.decode(s, x.size)
+        assert status == 0 and np.array_equal(x, y), exps
+        check_stream(orc, x, exps, s)
+
+
+def pin_edge_sizes(orc) -> None:
+    g = np.random.default_rng(3)
+    for n in (0, 1, 7, 8, 9, 63, 64, 65, 511, 512, 513, 4095, 4096, 4097, 8191, 8192, 8193, 20011):
+        x = workloads.bf16_bits_from_f32((g.standard_normal(n) * 0.02).astype(np.float32))
+        for exps in (CODEC_PLANS[0], HAND_PLAN):
+            s = orc.encode(x, exps)
+            status, y = orc.decode(s, n)
+            assert status == 0 and np.array_equal(x, y), (n, exps)
+            check_stream(orc, x, exps, s)
+
+
+def pin_eleven_bits(orc) -> None:
+    """No zero-point values: sign+mantissa (8) + three code planes (3) = 11 bits
+    per element, a 31.25 % reduction of the payload."""
+    n = 1 << 16
+    exps = CODEC_PLANS[0]
+    g = np.random.default_rng(5)
+    e = g.choice(np.array(exps), n).astype(np.uint16)
+    x = (g.integers(0, 2, n).astype(np.uint16) << 15) | (e << 7) | g.integers(0, 128, n).astype(np.uint16)
+    s = orc.encode(x, exps)
+    lay = orc.layout(n)
+    st = parse_stream(s, n, lay)
+    assert st["hdr"]["E"] == 0
+    payload = (lay["off_p0"] - lay["off_sm"]) + (lay["off_tab"] - lay["off_p0"])
+    assert payload * 8 == 11 * n
+    assert 1 - payload / (2 * n) == 0.3125
+    # the only other bytes: the 128-byte header and the 128-byte-padded table
+    assert s.size == payload + 128 + 128
+
+
+def pin_offsets_example(orc) -> None:
+    """n = 2^20: 128 + 2^20 -> 1,048,704; three planes of 131,072; a table of
+    257 u32 padded to 1,152 -> zero-point array at 1,443,072."""
+    lay = orc.layout(1 << 20)
+    assert (lay["off_p0"], lay["off_tab"], lay["off_zp"]) == (1_048_704, 1_441_920, 1_443_072)
+    assert orc.max_bytes(1 << 30) == 2_551_185_664
+
+
+def pin_config1_zero_points(orc) -> None:
+    """1,048,576 draws of N(0, 0.02^2) under the sigma = 0.02 plan: the zero-point
+    count agrees with the closed-form rate 1 - coverage within 6 binomial sd;
+    22,181 is the count this seeded recipe yields."""
+    w = workloads.config1()
+    exps = orc.plan_from_sigma(0.02)
+    s = orc.encode(w.buffer, exps)
+    E = int.from_bytes(s[32:40].tobytes(), "little")
+    rate = 1.0 - scipy_probabilities(0.02)[list(exps)].sum()
+    n = w.n
+    assert abs(E - n * rate) < 6 * np.sqrt(n * rate * (1 - rate))
+    assert E == 22_181
+    check_stream(orc, w.buffer, exps, s)
+
+
+def pin_strict_decoder(orc) -> None:
+    """Every header field, pad and table entry is checked before decoding."""
+    g = np.random.default_rng(9)
+    n = 10_000
+    x = workloads.bf16_bits_from_f32((g.standard_normal(n) * 0.02).astype(np.float32))
+    exps = CODEC_PLANS[0]
+    s = orc.encode(x, exps)
+    lay = orc.layout(n)
+    assert orc.decode(s, n)[0] == 0
+    assert orc.decode(s, n + 1)[0] != 0
+    assert orc.decode(s[:-1], n)[0] != 0
+    positions = [0, 3, 4, 6, 8, 15, 16, 20, 25, 30, 31, 32, 40, 47, 60, 127,
+                 lay["off_sm"] + n,                       # SM pad
+                 lay["off_p1"] - 1, lay["off_p0"] + n // 8,  # plane pad, bits past n
+                 lay["off_tab"], lay["off_tab"] + 4,       # table entries
+                 lay["off_zp"] - 1]                        # table pad
+    for pos in positions:
+        bad = s.copy()
+        bad[pos] ^= 0x40
+        assert orc.decode(bad, n)[0] != 0, pos
+
+
+ALL_PINS = [pin_probabilities_vs_scipy, pin_probabilities_monte_carlo, pin_plan_values,
+            pin_scale_covariance, pin_coverage, pin_histogram_top7, pin_contiguity_exception,
+            pin_roundtrip_exhaustive, pin_edge_sizes, pin_eleven_bits, pin_offsets_example,
+            pin_config1_zero_points, pin_strict_decoder]

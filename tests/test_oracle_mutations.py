@@ -1,0 +1,70 @@
+"""Planted mistakes in the CPU oracle must each trip at least one pin.
+
+Each case copies the oracle's C source, plants one plausible mistake with a
+textual substitution (in the encoder and decoder alike where a symmetric
+mistake would survive a round trip), builds it with gcc into a temporary
+directory, and runs the pins against that build.  Nothing here touches the
+HIP library or a GPU.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTATIONS = {
+    "planes_swapped_both_sides": [
+        ("{out + L.off_p0, out + L.off_p1, out + L.off_p2}", "{out + L.off_p1, out + L.off_p0, out + L.off_p2}"),
+        ("{in + L.off_p0, in + L.off_p1, in + L.off_p2}", "{in + L.off_p1, in + L.off_p0, in + L.off_p2}"),
+    ],
+    "plane_bit_order_reversed_both_sides": [
+        ("(uint8_t)(1u << (i % 8))", "(uint8_t)(1u << (7 - i % 8))"),
+        ("(plane[b][i / 8] >> (i % 8))", "(plane[b][i / 8] >> (7 - i % 8))"),
+    ],
+    "sign_bit_misplaced": [("sm[i] = (uint8_t)((sign << 7) | mantissa);",
+                            "sm[i] = (uint8_t)((sign << 6) | mantissa);")],
+    "code_zero_based": [("if (exps[k] == exponent) code = k + 1;", "if (exps[k] == exponent) code = k;")],
+    "codes_descending_both_sides": [
+        ("if (exps[k] == exponent) code = k + 1;", "if (exps[k] == exponent) code = 7 - k;"),
+        ("unsigned exponent = c ? exps[c - 1] : zp[k++];", "unsigned exponent = c ? exps[7 - c] : zp[k++];"),
+    ],
+    "tie_break_to_larger_exponent": [("if (best < 0 || p[e] > p[best]) best = e;",
+                                      "if (best < 0 || p[e] >= p[best]) best = e;")],
+    "missing_sqrt2": [("const double s = sigma * sqrt(2.0);", "const double s = sigma;")],
+    "octave_off_by_one": [("double lo = ldexp(1.0, e - 127);", "double lo = ldexp(1.0, e - 128);"),
+                          ("double hi = ldexp(1.0, e - 126);", "double hi = ldexp(1.0, e - 127);")],
+    "dropped_upper_tail_term": [("p[e] = erfc(lo / s) - erfc(hi / s);", "p[e] = erfc(lo / s);")],
+    "no_zero_subnormal_bucket": [("p[0] = erf(ldexp(1.0, -126) / s);", "p[0] = 0.0;")],
+    "table_counts_after_append": [
+        ("        if (i % ZCO_GROUP == 0) put_u32(tab + 4 * (i / ZCO_GROUP), (uint32_t)zp_count);\n", ""),
+        ("        if (code == 0) zp[zp_count++] = (uint8_t)exponent;\n",
+         "        if (code == 0) zp[zp_count++] = (uint8_t)exponent;\n"
+         "        if (i % ZCO_GROUP == 0) put_u32(tab + 4 * (i / ZCO_GROUP), (uint32_t)zp_count);\n"),
+    ],
+    "zero_point_byte_altered": [("if (code == 0) zp[zp_count++] = (uint8_t)exponent;",
+                                 "if (code == 0) zp[zp_count++] = (uint8_t)(exponent ^ 1u);")],
+    "mantissa_mask_short": [("unsigned mantissa = v & 0x7Fu;", "unsigned mantissa = v & 0x3Fu;")],
+    "sm_section_unaligned": [("L.off_p0 = round_up_128(L.off_sm + n);", "L.off_p0 = L.off_sm + n;")],
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    src = open(oracle.SOURCE).read()
+    for old, new in MUTATIONS[name]:
+        assert src.count(old) == 1, "mutation anchor not found: %r" % old
+        src = src.replace(old, new)
+    path = tmp_path / ("mut_%s.c" % name)
+    path.write_text(src)
+    lib = oracle.compile_source(str(path), str(tmp_path / ("libmut_%s.so" % name)))
+    mutant = oracle.Oracle(lib)
+    failures = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except Exception as exc:  # an assertion, or the mutant rejecting its own output
+            failures.append((pin.__name__, type(exc).__name__))
+            break
+    assert failures, "planted mistake %r passed every pin" % name
+    os.remove(lib)
