@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Throughput of the BF16 exponent codec on one MI355X.
+
+One step = compress every segment of the workload in one batched launch, then
+decompress every stream in one batched launch (the whole hot path on the GPU).
+The exponent tables are computed once per sigma on the host before timing, as
+the pages precompute the table from sigma; their cost is reported as plan_us.
+
+Default workload: the 256 Mi-element gradient bucket (32 layer segments, per-
+segment sigma log-uniform in [1e-5, 1e-2], 1 % exact zeros), the 256M-element
+buffer the throughput target is set on.  Inputs are resident in HBM before the
+timed region starts.
+
+Printed: one JSON line.  value = uncompressed BF16 bytes per second through
+compress + decompress (2n / step time); compress and decompress rates, the
+compression ratio, a roofline object for the slower kernel (algorithmic bytes
+/ its average event-timed duration vs the 8 TB/s HBM peak) and the CPU oracle
+timed on the host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["lossless_bf16_exponent_amd/csrc/zc_codec.hip", "lossless_bf16_exponent_amd/csrc/zc_lane.h",
+                  "lossless_bf16_exponent_amd/csrc/zc_format.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per dispatch from the committed rocprofv3 counter summary, or
+    None when the kernel sources changed since the counters were taken."""
+    path = os.path.join(PROFILES, "traffic_%s_%s.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_sha") != kernel_source_hash():
+        return None
+    try:
+        return int(float(vals["fetch_bytes"]) + float(vals["write_bytes"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, plans, max_segments: int):
+    """The oracle as it stands (plain C, one thread) on the first segments."""
+    import numpy as np
+    import oracle
+
+    segs = list(zip(w.segments, plans))[:max_segments]
+    n = sum(s.x.size for s, _ in segs)
+    t_enc = t_dec = 0.0
+    for seg, plan in segs:
+        out = np.empty(oracle.max_bytes(seg.x.size), dtype=np.uint8)
+        t0 = time.perf_counter()
+        total = oracle.encode_into(seg.x, plan, out)
+        t1 = time.perf_counter()
+        dec = np.empty(seg.x.size, dtype=np.uint16)
+        rc = oracle.decode_into(out[:total], seg.x.size, dec)
+        t2 = time.perf_counter()
+        if rc != 0 or not np.array_equal(dec, seg.x):
+            raise RuntimeError("oracle round trip failed on the CPU sample")
+        t_enc += t1 - t0
+        t_dec += t2 - t1
+    gb = 2.0 * n / 1e9
+    return {"value": round(gb / (t_enc + t_dec), 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "first %d of %d segments (%d BF16 values), one compress + one decompress, "
+                      "single-threaded plain C -O2" % (len(segs), len(w.segments), n),
+            "compress_gbps": round(gb / t_enc, 4), "decompress_gbps": round(gb / t_dec, 4),
+            "seconds": round(t_enc + t_dec, 3)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="3", help="workload id (1, 2, 3, 4, 5a, 5b); default 3")
+    ap.add_argument("--cpu-segments", type=int, default=32, help="segments in the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the codec on one GPU; multi-GPU runs are not part of this build "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from lossless_bf16_exponent_amd import workloads, zc
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    dev_name = torch.cuda.get_device_name(0)
+
+    t_gen = time.perf_counter()
+    w = workloads.get(args.workload)
+    print("# workload %s: %d values in %d segments, generated in %.1f s"
+          % (w.name, w.n, len(w.segments), time.perf_counter() - t_gen), file=sys.stderr, flush=True)
+
+    t0 = time.perf_counter()
+    plans = [zc.zc_plan_from_sigma(seg.sigma) for seg in w.segments]
+    plan_us = (time.perf_counter() - t0) * 1e6 / len(plans)
+
+    x = torch.from_numpy(w.buffer.view(np.int16)).cuda()
+    ns = [seg.x.size for seg in w.segments]
+    offs = np.concatenate([[0], np.cumsum(ns)]).astype(np.int64)
+    caps = [zc.zc_max_compressed_bytes(n) for n in ns]
+    slots = [(c + 255) // 256 * 256 for c in caps]
+    soff = np.concatenate([[0], np.cumsum(slots)]).astype(np.int64)
+    out = torch.empty(int(soff[-1]), dtype=torch.uint8, device="cuda")
+    sizes = torch.zeros(len(ns), dtype=torch.int64, device="cuda")
+    dec = torch.empty_like(x)
+    status = torch.zeros(len(ns), dtype=torch.int32, device="cuda")
+    xb, ob, db = x.data_ptr(), out.data_ptr(), dec.data_ptr()
+    enc_segs = zc.make_enc_segs([(xb + 2 * int(offs[i]) if ns[i] else 0, ns[i], plans[i], ob + int(soff[i]),
+                                  caps[i], sizes.data_ptr() + 8 * i) for i in range(len(ns))])
+    dec_segs = zc.make_dec_segs([(ob + int(soff[i]), caps[i], ns[i], db + 2 * int(offs[i]) if ns[i] else 0, 0)
+                                 for i in range(len(ns))])
+    chk_segs = zc.make_dec_segs([(ob + int(soff[i]), caps[i], ns[i], db + 2 * int(offs[i]) if ns[i] else 0,
+                                  status.data_ptr() + 4 * i) for i in range(len(ns))])
+    stream = torch.cuda.current_stream()
+
+    # correctness of what is timed: one checked round trip first
+    zc.zc_compress_batch(enc_segs, stream)
+    zc.zc_decompress_batch(chk_segs, stream)
+    torch.cuda.synchronize()
+    if status.any() or not torch.equal(dec, x):
+        print("bench.py: GPU round trip is not lossless", file=sys.stderr)
+        return 1
+    totals = sizes.cpu().numpy()
+    stream_bytes = int(totals.sum())
+    zero_points = 0
+    for i in range(len(ns)):
+        o = int(soff[i])
+        zero_points += int.from_bytes(out[o + 32:o + 40].cpu().numpy().tobytes(), "little")
+
+    n = w.n
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        zc.zc_compress_batch(enc_segs, stream)
+        zc.zc_decompress_batch(dec_segs, stream)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        e = ev[k]
+        e[0].record(stream)
+        zc.zc_compress_batch(enc_segs, stream)
+        e[1].record(stream)
+        e[2].record(stream)
+        zc.zc_decompress_batch(dec_segs, stream)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    if not torch.equal(dec, x):
+        print("bench.py: decoded buffer differs after timing", file=sys.stderr)
+        return 1
+
+    # practical ceiling: a device-to-device copy of the input
+    cp = torch.empty_like(x)
+    for _ in range(3):
+        cp.copy_(x)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        cp.copy_(x)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / 10
+    del cp
+
+    ms_per_step = t_total * 1e3 / args.steps
+    gb = 2.0 * n / 1e9
+    enc_alg = 2.0 * n + stream_bytes
+    dec_alg = stream_bytes + 2.0 * n
+    kernels = {"encode_kernel": (enc_ms, enc_alg), "decode_kernel": (dec_ms, dec_alg)}
+    dom = max(kernels, key=lambda k: kernels[k][0])
+    dom_ms, dom_bytes = kernels[dom]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = load_traffic(dom, w.name)
+
+    rec = {
+        "metric": "compress/decompress GB/s (uncompressed BF16) + % HBM roofline; compression ratio",
+        "value": round(gb / (ms_per_step * 1e-3), 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "values": n, "segments": len(ns), "input": "bf16",
+                   "description": w.description, "launches_per_step": "1 batched compress + 1 batched decompress"},
+        "compress_gbps": round(gb / (enc_ms * 1e-3), 2),
+        "decompress_gbps": round(gb / (dec_ms * 1e-3), 2),
+        "compress_us": round(enc_ms * 1e3, 2),
+        "decompress_us": round(dec_ms * 1e3, 2),
+        "compress_hbm_frac": round(enc_alg / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "decompress_hbm_frac": round(dec_alg / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "compression_ratio": round(stream_bytes / (2.0 * n), 5),
+        "bits_per_value": round(8.0 * stream_bytes / n, 4),
+        "zero_point_rate": round(zero_points / n, 6),
+        "copy_ceiling_gbps": round(4.0 * n / (copy_ms * 1e-3) / 1e9, 1),
+        "plan_us": round(plan_us, 2),
+        "device": dev_name,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": dom, "algorithmic_bytes": int(dom_bytes),
+                     "avg_launch_us": round(dom_ms * 1e3, 2)},
+        "kernel_sha": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, plans, args.cpu_segments)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

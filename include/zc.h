@@ -1,0 +1,174 @@
+/*
+ * zc.h -- C ABI of the MI355X (gfx950) BF16 exponent-coding codec.
+ *
+ * The method is the exponent coding described on the explainer pages of
+ *   "ZipCCL: Efficient Lossless Data Compression of Communication Collectives
+ *    for Accelerating LLM Training" (gist.science; fr / ja / ko pages),
+ * technical summary, section 2 ("Methodology"):
+ *   2.A  near-Gaussian training tensors concentrate their BF16 exponents; the
+ *        7 most frequent cover more than 97 % of the values, and the table of
+ *        those 7 is derived from the standard deviation sigma instead of an
+ *        online histogram or sort;
+ *   2.B  each value is split into sign+mantissa bits and exponent bits; an
+ *        exponent among the 7 becomes a 3-bit code 001..111, any other gets the
+ *        "zero-point" code 000 and its full 8 bits go to a separate zero-point
+ *        array; 16 bits become 11 when no value takes the zero-point path;
+ *   2.C  data blocks are padded to 128-byte boundaries and the 3-bit codes are
+ *        kept as three 1-bit arrays.
+ * Section 1 (problem statement) motivates the shape of the interface: general
+ * GPU compressors lose on launch overhead, so a whole set of messages is coded
+ * in one launch (the *_batch calls), and section 3 (contributions) describes a
+ * drop-in library, so every stream is self-describing.
+ *
+ * Compressed stream (little-endian; every section starts on a 128-byte
+ * boundary of the stream; every pad byte is zero):
+ *   offset 0        header, 128 B:
+ *                     u32 magic 0x3143435A ("ZCC1") | u16 version 1 | u16 128
+ *                     u64 n | u32 group elements 4096 | u32 NG = ceil(n/4096)
+ *                     u8 exps[7] | u8 0 | u64 E (zero-point count)
+ *                     u64 total_bytes | 80 zero bytes
+ *   128             SM: n bytes, byte i = sign(x_i) << 7 | mantissa(x_i)
+ *   off_p0          plane 0: ceil(n/64) little-endian u64 words; bit (i mod 64)
+ *                   of word i/64 is bit 0 of the code of element i
+ *   off_p1, off_p2  planes 1 and 2, same shape, bits 1 and 2 of the codes
+ *   off_tab         NG+1 u32: entry g = zero-point values before element 4096 g
+ *   off_zp          E bytes: the exponent of every element coded 000, in order
+ *   with  A(x) = x rounded up to 128, W = ceil(n/64),
+ *         off_p0 = A(128+n), off_p1 = off_p0 + A(8W), off_p2 = off_p1 + A(8W),
+ *         off_tab = off_p2 + A(8W), off_zp = off_tab + A(4(NG+1)),
+ *         total_bytes = off_zp + E.
+ * Code k (1..7) stands for exps[k-1]; exps is strictly ascending.  The stream
+ * is a pure function of (input bits, plan): it does not depend on launch
+ * geometry, device, stream or batching.
+ *
+ * Conventions for every call:
+ *   - all buffers belong to the caller; the library never allocates, frees or
+ *     synchronizes, and keeps no state between calls;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); device
+ *     work is enqueued on it and the call returns without waiting;
+ *   - "device" pointers are HIP device memory of the current device;
+ *   - inputs and outputs must not overlap;
+ *   - host-detectable errors return a status before anything is enqueued and
+ *     nothing is written; ZC_ERR_HIP reports a failed launch.
+ */
+#ifndef ZC_H
+#define ZC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum zc_status {
+    ZC_OK = 0,
+    ZC_ERR_INVALID_ARG = 1, /* NULL pointer, bad plan, bad sigma, n > 2^32-1, k out of range */
+    ZC_ERR_CAPACITY = 2,    /* out_capacity below zc_max_compressed_bytes(n) */
+    ZC_ERR_MISALIGNED = 3,  /* BF16 buffers need 16-byte, stream buffers 128-byte alignment */
+    ZC_ERR_CORRUPT = 4,     /* a stream failed validation (device-side, via the status word) */
+    ZC_ERR_HIP = 5          /* the HIP runtime refused a launch */
+} zc_status;
+
+/* The exponent table ("codebook" of section 2.A): code k <-> exps[k-1].
+ * exps must be strictly ascending (7 distinct values, any of 0..255);
+ * reserved must be 0. */
+typedef struct zc_plan {
+    uint8_t exps[7];
+    uint8_t reserved;
+} zc_plan;
+
+/* Section 2.A: the table from sigma alone.  For X ~ N(0, sigma^2) the
+ * probability of exponent field e is P(2^(e-127) <= |X| < 2^(e-126)) for
+ * e = 1..254, P(|X| < 2^-126) for e = 0 (zero and subnormals) and 0 for
+ * e = 255; the 7 largest (ties to the smaller e) are returned ascending.
+ * Host only, pure, thread-safe.  sigma must be finite and > 0, out non-NULL,
+ * else ZC_ERR_INVALID_ARG. */
+zc_status zc_plan_from_sigma(double sigma, zc_plan *out);
+
+/* Capacity a compressed output buffer must have for n elements: the largest
+ * stream (every element on the zero-point path, section 2.B) plus the scratch
+ * the encoder keeps behind it.  Returns 0 for n > 2^32-1. */
+uint64_t zc_max_compressed_bytes(uint64_t n);
+
+/* Section 2.B, compress one BF16 tensor.
+ *   d_in          device, n BF16 values (raw 16-bit patterns), 16-byte aligned
+ *   n             element count, 0 .. 2^32-1
+ *   plan          host pointer to the exponent table
+ *   d_out         device, 128-byte aligned, out_capacity bytes; receives the
+ *                 stream in [0, total_bytes); [total_bytes, out_capacity) is
+ *                 encoder scratch with unspecified contents afterwards
+ *   out_capacity  must be >= zc_max_compressed_bytes(n)
+ *   d_out_bytes   device u64 (nullable): receives total_bytes
+ *   stream        hipStream_t
+ * Errors: ZC_ERR_INVALID_ARG, ZC_ERR_MISALIGNED, ZC_ERR_CAPACITY, ZC_ERR_HIP.
+ * The stream size is also in header bytes 40..47 once the work completes. */
+zc_status zc_compress(const void *d_in, uint64_t n, const zc_plan *plan, void *d_out,
+                      uint64_t out_capacity, uint64_t *d_out_bytes, void *stream);
+
+/* Inverse of zc_compress.
+ *   d_in      device, 128-byte aligned, the stream (in_bytes readable bytes)
+ *   in_bytes  bytes available at d_in (>= total_bytes of the stream)
+ *   n         the element count the caller expects
+ *   d_out     device, 16-byte aligned, n BF16 values
+ *   d_status  device int32 (nullable): set to 0 on success or ZC_ERR_CORRUPT.
+ *             A bad header (magic, version, n, group size, exps not ascending,
+ *             E > n, total_bytes inconsistent with n and E or > in_bytes) is
+ *             seen by every workgroup and leaves d_out untouched.  A table or
+ *             plane inconsistency is caught per 8192-element tile: the status
+ *             is set, reads stay inside the stream and the affected tile's
+ *             output is unspecified.
+ * Errors returned: ZC_ERR_INVALID_ARG, ZC_ERR_MISALIGNED, ZC_ERR_HIP. */
+zc_status zc_decompress(const void *d_in, uint64_t in_bytes, uint64_t n, void *d_out,
+                        int32_t *d_status, void *stream);
+
+/* One message of a batched call.  Field meanings as in zc_compress. */
+typedef struct zc_enc_seg {
+    const void *in;
+    uint64_t n;
+    zc_plan plan;
+    void *out;
+    uint64_t out_capacity;
+    uint64_t *out_bytes; /* device, nullable */
+} zc_enc_seg;
+
+/* Field meanings as in zc_decompress. */
+typedef struct zc_dec_seg {
+    const void *in;
+    uint64_t in_bytes;
+    uint64_t n;
+    void *out;
+    int32_t *status; /* device, nullable */
+} zc_dec_seg;
+
+#define ZC_MAX_BATCH 64
+
+/* Compress k (1..ZC_MAX_BATCH) independent tensors in one launch, each with its
+ * own plan and output buffer (per-layer gradient segments, per-destination
+ * all-to-all segments).  Each output equals what zc_compress gives for that
+ * segment alone.  segs is a host array read before the call returns. */
+zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void *stream);
+
+/* Decompress k (1..ZC_MAX_BATCH) streams in one launch. */
+zc_status zc_decompress_batch(const zc_dec_seg *segs, uint32_t k, void *stream);
+
+/* Host-side view of a stream header (first 128 bytes copied to the host). */
+typedef struct zc_stream_info {
+    uint64_t n;
+    uint64_t zero_points; /* E */
+    uint64_t total_bytes;
+    uint32_t groups;
+    zc_plan plan;
+} zc_stream_info;
+
+/* Validate and unpack a header held in host memory (len >= 128).
+ * Returns ZC_ERR_CORRUPT for a header the decoder would reject. */
+zc_status zc_read_header(const void *host_header, uint64_t len, zc_stream_info *out);
+
+/* Static, human-readable name of a status code. */
+const char *zc_status_string(zc_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZC_H */

@@ -1,0 +1,51 @@
+"""Compile the HIP codec library in-tree for gfx950 (hipcc cross-compiles without a GPU)."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libzc.so")
+SOURCES = [os.path.join(CSRC, "zc_codec.hip"), os.path.join(CSRC, "zc_plan.cpp")]
+ARCH = "gfx950"
+
+# Packed-FP32 instructions stay disabled for every HIP translation unit.
+HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; the HIP codec library cannot be built")
+
+
+def compile_command(out: str, extra=()) -> list:
+    return [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+            *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", out, *extra]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = compile_command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def assembly(out_path: str) -> str:
+    """Device assembly of the kernels (for inspection of the generated gfx950 code)."""
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC,
+           "--cuda-device-only", "-S", SOURCES[0], "-o", out_path]
+    subprocess.run(cmd, check=True)
+    return out_path
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,76 @@
+// Stream format constants and section offsets of the BF16 exponent codec.
+//
+// Format of one stream (see include/zc.h for the full table): a 128-byte
+// header, the sign+mantissa bytes, three 1-bit code planes, a table of
+// zero-point counts per 4096-element group and the zero-point exponent bytes.
+// Every section starts on a 128-byte boundary: the ZipCCL explainer pages
+// ("ZipCCL: Efficient Lossless Data Compression of Communication Collectives
+// for Accelerating LLM Training", section 2.C) pad data blocks to 128-byte
+// boundaries so that every global access is a whole, coalesced 128-byte
+// transaction.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define ZC_HD __host__ __device__ __forceinline__
+#else
+#define ZC_HD static inline
+#endif
+
+namespace zc {
+
+constexpr uint32_t kMagic = 0x3143435Au;  // "ZCC1"
+constexpr uint16_t kVersion = 1;
+constexpr uint32_t kHeaderBytes = 128;
+constexpr uint32_t kGroup = 4096;  // elements per zero-point table entry
+constexpr uint64_t kMaxElems = 0xFFFFFFFFull;
+
+// Encoder / decoder tiling (not part of the format; the stream does not depend
+// on it).  A lane owns 8 consecutive elements (one 16-byte load) per step; a
+// wave64 step covers 512 elements; a 256-thread block makes kSteps steps.
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWave * kWaves;
+constexpr int kSteps = 4;
+constexpr uint32_t kTile = kThreads * 8 * kSteps;  // 8192 elements
+constexpr uint32_t kGroupsPerTile = kTile / kGroup;
+static_assert(kTile % kGroup == 0, "a tile holds whole groups");
+
+ZC_HD uint64_t align128(uint64_t x) { return (x + 127u) & ~uint64_t(127u); }
+
+struct Layout {
+    uint64_t n;
+    uint64_t plane_bytes;  // 8 * ceil(n / 64), the section padded to 128
+    uint64_t groups;       // NG
+    uint64_t off_p0, off_p1, off_p2, off_tab, off_zp;
+    uint64_t off_scratch;  // encoder scratch behind the largest stream
+    uint64_t tiles;        // encoder tiles (at least one, so n = 0 still writes a header)
+};
+
+ZC_HD Layout layout_for(uint64_t n) {
+    Layout L;
+    L.n = n;
+    L.plane_bytes = align128(8 * ((n + 63) / 64));
+    L.groups = (n + kGroup - 1) / kGroup;
+    L.off_p0 = align128(kHeaderBytes + n);
+    L.off_p1 = L.off_p0 + L.plane_bytes;
+    L.off_p2 = L.off_p1 + L.plane_bytes;
+    L.off_tab = L.off_p2 + L.plane_bytes;
+    L.off_zp = L.off_tab + align128(4 * (L.groups + 1));
+    L.off_scratch = align128(L.off_zp + n);
+    uint64_t t = (n + kTile - 1) / kTile;
+    L.tiles = t ? t : 1;
+    return L;
+}
+
+// Encoder scratch, at off_scratch: a 128-byte control block (tile ticket,
+// error word) followed by one 64-bit look-back word per tile.  Sized for
+// per-group tiles so that a smaller tile never outgrows it.
+constexpr uint64_t kScratchCtrl = 128;
+ZC_HD uint64_t scratch_bytes(uint64_t n) {
+    uint64_t g = (n + kGroup - 1) / kGroup;
+    return kScratchCtrl + 8 * (g ? g : 1);
+}
+
+}  // namespace zc

@@ -1,0 +1,176 @@
+"""Python binding of the C ABI in include/zc.h (argument marshalling only).
+
+Every function has the name of the C entry point it calls.  Pointer arguments
+accept an integer device address or anything with ``data_ptr()`` (a torch
+tensor); ``stream`` accepts a raw hipStream_t integer, a ``torch.cuda.Stream``
+or None for torch's current stream.  All compression work runs in the HIP
+kernels of libzc.so; nothing here touches the data.
+
+Importing this module fails loudly when libzc.so has not been built: there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libzc.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libzc.so is not built (run __graft_entry__.build() or "
+                      "python -m lossless_bf16_exponent_amd._build); the codec has no fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+ZC_OK, ZC_ERR_INVALID_ARG, ZC_ERR_CAPACITY, ZC_ERR_MISALIGNED, ZC_ERR_CORRUPT, ZC_ERR_HIP = range(6)
+ZC_MAX_BATCH = 64
+
+
+class zc_plan(ctypes.Structure):
+    _fields_ = [("exps", ctypes.c_uint8 * 7), ("reserved", ctypes.c_uint8)]
+
+
+class zc_enc_seg(ctypes.Structure):
+    _fields_ = [("in_", ctypes.c_void_p), ("n", ctypes.c_uint64), ("plan", zc_plan),
+                ("out", ctypes.c_void_p), ("out_capacity", ctypes.c_uint64), ("out_bytes", ctypes.c_void_p)]
+
+
+class zc_dec_seg(ctypes.Structure):
+    _fields_ = [("in_", ctypes.c_void_p), ("in_bytes", ctypes.c_uint64), ("n", ctypes.c_uint64),
+                ("out", ctypes.c_void_p), ("status", ctypes.c_void_p)]
+
+
+class zc_stream_info(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_uint64), ("zero_points", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64),
+                ("groups", ctypes.c_uint32), ("plan", zc_plan)]
+
+
+_lib.zc_plan_from_sigma.argtypes = [ctypes.c_double, ctypes.POINTER(zc_plan)]
+_lib.zc_plan_from_sigma.restype = ctypes.c_int
+_lib.zc_max_compressed_bytes.argtypes = [ctypes.c_uint64]
+_lib.zc_max_compressed_bytes.restype = ctypes.c_uint64
+_lib.zc_compress.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(zc_plan), ctypes.c_void_p,
+                             ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+_lib.zc_compress.restype = ctypes.c_int
+_lib.zc_decompress.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.c_void_p]
+_lib.zc_decompress.restype = ctypes.c_int
+_lib.zc_compress_batch.argtypes = [ctypes.POINTER(zc_enc_seg), ctypes.c_uint32, ctypes.c_void_p]
+_lib.zc_compress_batch.restype = ctypes.c_int
+_lib.zc_decompress_batch.argtypes = [ctypes.POINTER(zc_dec_seg), ctypes.c_uint32, ctypes.c_void_p]
+_lib.zc_decompress_batch.restype = ctypes.c_int
+_lib.zc_read_header.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(zc_stream_info)]
+_lib.zc_read_header.restype = ctypes.c_int
+_lib.zc_status_string.argtypes = [ctypes.c_int]
+_lib.zc_status_string.restype = ctypes.c_char_p
+
+EXPORTED = ("zc_plan_from_sigma", "zc_max_compressed_bytes", "zc_compress", "zc_decompress",
+            "zc_compress_batch", "zc_decompress_batch", "zc_read_header", "zc_status_string")
+
+
+class ZcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__("%s: %s (status %d)" % (where, zc_status_string(status), status))
+        self.status = status
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(s) -> int:
+    if s is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(s, int):
+        return s
+    return int(s.cuda_stream)
+
+
+def _plan(exps) -> zc_plan:
+    if isinstance(exps, zc_plan):
+        return exps
+    exps = tuple(int(e) for e in exps)
+    if len(exps) != 7:
+        raise ValueError("a plan has exactly seven exponents")
+    return zc_plan((ctypes.c_uint8 * 7)(*exps), 0)
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != ZC_OK:
+        raise ZcError(rc, where)
+
+
+def zc_status_string(status: int) -> str:
+    return _lib.zc_status_string(int(status)).decode()
+
+
+def zc_plan_from_sigma(sigma: float) -> tuple:
+    p = zc_plan()
+    _check(_lib.zc_plan_from_sigma(float(sigma), ctypes.byref(p)), "zc_plan_from_sigma")
+    return tuple(int(v) for v in p.exps)
+
+
+def zc_max_compressed_bytes(n: int) -> int:
+    return int(_lib.zc_max_compressed_bytes(int(n)))
+
+
+def zc_compress(d_in, n, plan, d_out, out_capacity, d_out_bytes=None, stream=None) -> None:
+    p = _plan(plan)
+    _check(_lib.zc_compress(_ptr(d_in), int(n), ctypes.byref(p), _ptr(d_out), int(out_capacity),
+                            _ptr(d_out_bytes), _stream(stream)), "zc_compress")
+
+
+def zc_decompress(d_in, in_bytes, n, d_out, d_status=None, stream=None) -> None:
+    _check(_lib.zc_decompress(_ptr(d_in), int(in_bytes), int(n), _ptr(d_out), _ptr(d_status),
+                              _stream(stream)), "zc_decompress")
+
+
+def make_enc_segs(segs) -> ctypes.Array:
+    """segs: iterable of (in, n, plan, out, out_capacity, out_bytes) tuples."""
+    segs = list(segs)
+    arr = (zc_enc_seg * max(1, len(segs)))()
+    for i, (d_in, n, plan, d_out, cap, d_bytes) in enumerate(segs):
+        arr[i] = zc_enc_seg(_ptr(d_in), int(n), _plan(plan), _ptr(d_out), int(cap), _ptr(d_bytes))
+    return arr, len(segs)
+
+
+def make_dec_segs(segs) -> ctypes.Array:
+    """segs: iterable of (in, in_bytes, n, out, status) tuples."""
+    segs = list(segs)
+    arr = (zc_dec_seg * max(1, len(segs)))()
+    for i, (d_in, in_bytes, n, d_out, d_status) in enumerate(segs):
+        arr[i] = zc_dec_seg(_ptr(d_in), int(in_bytes), int(n), _ptr(d_out), _ptr(d_status))
+    return arr, len(segs)
+
+
+def zc_compress_batch(segs, stream=None) -> None:
+    """segs: a (ctypes array, count) pair from make_enc_segs, or tuples for it."""
+    arr, k = segs if isinstance(segs, tuple) and len(segs) == 2 and isinstance(segs[0], ctypes.Array) \
+        else make_enc_segs(segs)
+    _check(_lib.zc_compress_batch(arr, k, _stream(stream)), "zc_compress_batch")
+
+
+def zc_decompress_batch(segs, stream=None) -> None:
+    arr, k = segs if isinstance(segs, tuple) and len(segs) == 2 and isinstance(segs[0], ctypes.Array) \
+        else make_dec_segs(segs)
+    _check(_lib.zc_decompress_batch(arr, k, _stream(stream)), "zc_decompress_batch")
+
+
+def zc_read_header(header: bytes) -> dict:
+    buf = ctypes.create_string_buffer(bytes(header), len(header))
+    info = zc_stream_info()
+    _check(_lib.zc_read_header(buf, len(header), ctypes.byref(info)), "zc_read_header")
+    return {"n": int(info.n), "zero_points": int(info.zero_points), "total_bytes": int(info.total_bytes),
+            "groups": int(info.groups), "plan": tuple(int(v) for v in info.plan.exps)}
+
+
+def raw_status(fn: str, *args) -> int:
+    """Call a C entry point and return its status code without raising (for tests
+    of the host-side argument checks)."""
+    return int(getattr(_lib, fn)(*args))

@@ -1,0 +1,174 @@
+"""Host-side checks of the HIP library that need no GPU: it loads and exports
+every entry point of include/zc.h, its sigma plan equals the oracle's, every
+host-detectable error returns its status before anything is enqueued, the
+header parser agrees with oracle streams, and the per-lane bit helpers pass
+their CPU self-test."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins
+from lossless_bf16_exponent_amd import _build, workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def zc():
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    from lossless_bf16_exponent_amd import zc as mod
+    return mod
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "zc.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(zc_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_entry_point(zc):
+    names = declared_functions()
+    assert len(names) >= 8
+    out = subprocess.run(["nm", "-D", "--defined-only", _build.LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (zc_\w+)", out))
+    for name in names:
+        assert name in exported, name
+        assert hasattr(zc._lib, name)
+    assert set(zc.EXPORTED) == set(names)
+
+
+def test_lane_helpers_selftest(tmp_path):
+    exe = str(tmp_path / "lane_selftest")
+    subprocess.run([_build.hipcc(), "-O2", "-std=c++17", "-x", "c++", "-I", _build.CSRC,
+                    os.path.join(ROOT, "tests", "lane_selftest.cpp"), "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
+def _near_tie(sigma):
+    p = np.sort(oracle.exponent_probabilities(sigma))[::-1]
+    return p[6] - p[7] < 1e-12
+
+
+def test_library_plan_equals_oracle_plan(zc):
+    sigmas = [0.02, 1.0, 0.16, 0.01, 1e-5, 1e38, 2.0 ** -130, 2.0 ** -120.7]
+    sigmas += list(workloads.config3_sigmas())
+    sigmas += [2.0 ** f for f in np.arange(-20.0, 20.0, 0.01)]
+    checked = 0
+    for s in sigmas:
+        if _near_tie(s):
+            continue
+        assert zc.zc_plan_from_sigma(s) == oracle.plan_from_sigma(s), s
+        checked += 1
+    assert checked > 3900
+
+
+def test_plan_rejects_bad_sigma(zc):
+    for bad in (0.0, -0.5, float("nan"), float("inf"), -float("inf")):
+        with pytest.raises(zc.ZcError) as e:
+            zc.zc_plan_from_sigma(bad)
+        assert e.value.status == zc.ZC_ERR_INVALID_ARG
+    assert zc.raw_status("zc_plan_from_sigma", 0.02, None) == zc.ZC_ERR_INVALID_ARG
+
+
+def test_max_compressed_bytes_covers_worst_stream(zc):
+    for n in (0, 1, 63, 64, 4095, 4096, 4097, 8193, 1 << 20, 58_720_256, (1 << 30), (1 << 32) - 1):
+        cap = zc.zc_max_compressed_bytes(n)
+        assert cap >= oracle.max_bytes(n) + 128 + 8, n
+        assert cap % 8 == 0
+    assert zc.zc_max_compressed_bytes(1 << 32) == 0
+
+
+FAKE_IN = 0x7F0000000000  # never dereferenced: every call below fails validation first
+FAKE_OUT = 0x7F1000000000
+PLAN = (116, 117, 118, 119, 120, 121, 122)
+
+
+def _compress_status(zc, d_in=FAKE_IN, n=1000, plan=PLAN, reserved=0, d_out=FAKE_OUT, cap=None, d_bytes=0):
+    p = zc._plan(plan)
+    p.reserved = reserved
+    if cap is None:
+        cap = zc.zc_max_compressed_bytes(n) - 1  # one byte short: every other check must fire first
+    return zc.raw_status("zc_compress", d_in, n, ctypes.byref(p), d_out, cap, d_bytes, 0)
+
+
+def test_compress_host_errors(zc):
+    assert _compress_status(zc) == zc.ZC_ERR_CAPACITY
+    assert _compress_status(zc, d_out=0) == zc.ZC_ERR_INVALID_ARG
+    assert _compress_status(zc, d_in=0) == zc.ZC_ERR_INVALID_ARG
+    assert _compress_status(zc, n=1 << 32, cap=1 << 40) == zc.ZC_ERR_INVALID_ARG
+    assert _compress_status(zc, plan=(116, 116, 118, 119, 120, 121, 122)) == zc.ZC_ERR_INVALID_ARG
+    assert _compress_status(zc, plan=(122, 121, 120, 119, 118, 117, 116)) == zc.ZC_ERR_INVALID_ARG
+    assert _compress_status(zc, reserved=1) == zc.ZC_ERR_INVALID_ARG
+    assert _compress_status(zc, d_in=FAKE_IN + 2) == zc.ZC_ERR_MISALIGNED
+    assert _compress_status(zc, d_out=FAKE_OUT + 64) == zc.ZC_ERR_MISALIGNED
+    assert _compress_status(zc, d_bytes=FAKE_OUT + 4) == zc.ZC_ERR_MISALIGNED
+    assert zc.raw_status("zc_compress", FAKE_IN, 10, None, FAKE_OUT, 1 << 20, 0, 0) == zc.ZC_ERR_INVALID_ARG
+
+
+def test_batch_host_errors(zc):
+    arr, _ = zc.make_enc_segs([(FAKE_IN, 10, PLAN, FAKE_OUT, 1, 0)])
+    assert zc.raw_status("zc_compress_batch", arr, 0, 0) == zc.ZC_ERR_INVALID_ARG
+    assert zc.raw_status("zc_compress_batch", None, 1, 0) == zc.ZC_ERR_INVALID_ARG
+    big, _ = zc.make_enc_segs([(FAKE_IN, 10, PLAN, FAKE_OUT, 1, 0)] * 65)
+    assert zc.raw_status("zc_compress_batch", big, 65, 0) == zc.ZC_ERR_INVALID_ARG
+    # one bad segment among good ones rejects the whole batch before any launch
+    cap = zc.zc_max_compressed_bytes(10)
+    arr, k = zc.make_enc_segs([(FAKE_IN, 10, PLAN, FAKE_OUT, cap, 0),
+                               (FAKE_IN, 10, PLAN, FAKE_OUT + (1 << 20), cap - 8, 0)])
+    assert zc.raw_status("zc_compress_batch", arr, k, 0) == zc.ZC_ERR_CAPACITY
+    darr, _ = zc.make_dec_segs([(FAKE_OUT, 1 << 20, 10, FAKE_IN, 0)])
+    assert zc.raw_status("zc_decompress_batch", darr, 0, 0) == zc.ZC_ERR_INVALID_ARG
+    dbig, _ = zc.make_dec_segs([(FAKE_OUT, 1 << 20, 10, FAKE_IN, 0)] * 65)
+    assert zc.raw_status("zc_decompress_batch", dbig, 65, 0) == zc.ZC_ERR_INVALID_ARG
+
+
+def test_decompress_host_errors(zc):
+    n = 1000
+    smallest = oracle.layout(n)["off_zp"]
+    st = lambda *a: zc.raw_status("zc_decompress", *a)
+    assert st(FAKE_OUT, smallest - 1, n, FAKE_IN, 0, 0) == zc.ZC_ERR_CORRUPT
+    assert st(0, 1 << 20, n, FAKE_IN, 0, 0) == zc.ZC_ERR_INVALID_ARG
+    assert st(FAKE_OUT, 1 << 20, n, 0, 0, 0) == zc.ZC_ERR_INVALID_ARG
+    assert st(FAKE_OUT, 1 << 20, 1 << 32, FAKE_IN, 0, 0) == zc.ZC_ERR_INVALID_ARG
+    assert st(FAKE_OUT + 16, 1 << 20, n, FAKE_IN, 0, 0) == zc.ZC_ERR_MISALIGNED
+    assert st(FAKE_OUT, 1 << 20, n, FAKE_IN + 8, 0, 0) == zc.ZC_ERR_MISALIGNED
+    assert st(FAKE_OUT, 1 << 20, n, FAKE_IN, FAKE_IN + 2, 0) == zc.ZC_ERR_MISALIGNED
+
+
+def test_read_header_of_oracle_streams(zc):
+    g = np.random.default_rng(1)
+    for n in (0, 5, 4096, 10_001):
+        x = workloads.bf16_bits_from_f32((g.standard_normal(n) * 0.3).astype(np.float32))
+        exps = oracle.plan_from_sigma(0.3)
+        s = oracle.encode(x, exps)
+        info = zc.zc_read_header(s[:128].tobytes())
+        E = int(np.isin(oracle_pins.exponent_field(x), exps, invert=True).sum())
+        assert info == {"n": n, "zero_points": E, "total_bytes": s.size,
+                        "groups": (n + 4095) // 4096, "plan": exps}
+        for pos in (0, 4, 16, 20, 25, 31, 33, 41, 100):
+            bad = s[:128].copy()
+            bad[pos] ^= 0x40
+            with pytest.raises(zc.ZcError):
+                zc.zc_read_header(bad.tobytes())
+        # a changed n may still describe a self-consistent stream; the decoder
+        # compares it with the caller's n, the parser reports it
+        bad = s[:128].copy()
+        bad[8] ^= 0x40
+        try:
+            assert zc.zc_read_header(bad.tobytes())["n"] != n
+        except zc.ZcError:
+            pass
+    with pytest.raises(zc.ZcError):
+        zc.zc_read_header(bytes(64))
+
+
+def test_status_strings(zc):
+    for code in range(6):
+        assert zc.zc_status_string(code)
+    assert zc.zc_status_string(99) == "unknown status"
