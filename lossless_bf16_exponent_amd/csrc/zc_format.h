@@ -37,6 +37,19 @@ constexpr uint32_t kTile = kThreads * 8 * kSteps;  // 8192 elements
 constexpr uint32_t kGroupsPerTile = kTile / kGroup;
 static_assert(kTile % kGroup == 0, "a tile holds whole groups");
 
+// The encoder gives each block a span of kEncSubTiles consecutive tiles.
+#ifndef ZC_ENC_SUBTILES
+#define ZC_ENC_SUBTILES 4
+#endif
+constexpr int kEncSubTiles = ZC_ENC_SUBTILES;
+constexpr uint32_t kEncSpan = kTile * kEncSubTiles;
+constexpr int kEncGroups = (int)(kEncSpan / kGroup);
+
+ZC_HD uint64_t enc_blocks(uint64_t n) {
+    const uint64_t b = (n + kEncSpan - 1) / kEncSpan;
+    return b ? b : 1;
+}
+
 ZC_HD uint64_t align128(uint64_t x) { return (x + 127u) & ~uint64_t(127u); }
 
 struct Layout {
@@ -64,9 +77,9 @@ ZC_HD Layout layout_for(uint64_t n) {
     return L;
 }
 
-// Encoder scratch, at off_scratch: a 128-byte control block (tile ticket,
-// error word) followed by one 64-bit look-back word per tile.  Sized for
-// per-group tiles so that a smaller tile never outgrows it.
+// Encoder scratch, at off_scratch: a 128-byte control block (error word at
+// byte 8) followed by one 64-bit look-back word per encoder block.  Sized per
+// 4096-value group so that any span size fits.
 constexpr uint64_t kScratchCtrl = 128;
 ZC_HD uint64_t scratch_bytes(uint64_t n) {
     uint64_t g = (n + kGroup - 1) / kGroup;
