@@ -15,11 +15,14 @@
 //   * codes and bit planes come from dword-wide byte shuffles (zc_lane.h), and
 //     the per-lane plane bytes are regrouped through LDS into whole dwords per
 //     plane before they are stored;
-//   * zero-point bytes are placed by an exclusive scan: lane (packed 16-bit
-//     wave scan) -> wave (LDS) -> sub-tile -> block span (single-pass
-//     decoupled look-back over 64-bit flag+count words, one per block of
-//     kEncSubTiles tiles, so its latency is paid once per 32768 values and
-//     overlaps the next blocks' streaming);
+//   * zero-point bytes are placed by an exclusive scan in two passes: inside
+//     a block (lane DPP scan -> wave -> sub-tile) while it codes its 32768-
+//     value span, which it leaves with its zero-point count and its staged
+//     zero-point bytes in the output's scratch tail; then a small finalize
+//     pass scans the span counts, fills the table and moves the staged bytes
+//     to their place.  No block ever waits for another one: under a saturated
+//     memory system every cross-block handshake costs a full round trip per
+//     block, which measured slower than the extra 2 bytes per zero-point;
 //   * the decoder needs no scan across tiles: the table of zero-point counts
 //     per 4096-element group gives every tile its slice of the zero-point
 //     array, which is staged in LDS and gathered by rank.
@@ -43,11 +46,12 @@ struct EncSeg {
     uint8_t *out;
     unsigned long long *out_bytes;
     uint32_t n;
-    uint32_t tile_begin;  // first flat block of this segment
+    uint32_t tile_begin;  // first flat encode block of this segment
+    uint32_t fin_begin;   // first flat finalize block of this segment
     uint8_t exps[7];
     uint8_t mode;  // kModeWindow or kModeTable
 };
-static_assert(sizeof(EncSeg) == 40, "compact kernel arguments");
+static_assert(sizeof(EncSeg) == 48, "compact kernel arguments");
 
 struct EncArgs {
     uint32_t k;
@@ -61,7 +65,7 @@ struct DecSeg {
     int32_t *status;
     uint64_t in_bytes;
     uint32_t n;
-    uint32_t tile_begin;
+    uint32_t tile_begin;  // first flat block of this segment
 };
 static_assert(sizeof(DecSeg) == 40, "compact kernel arguments");
 
@@ -84,10 +88,6 @@ struct ZeroArgs {
 constexpr uint8_t kModeWindow = 0;  // exps = w+1 .. w+7 with w >= 0: codes by saturating arithmetic
 constexpr uint8_t kModeTable = 1;   // any other ascending set: codes from a 256-byte LDS table
 
-// look-back word: flag in the high 32 bits, zero-point count in the low 32
-constexpr uint64_t kFlagAggregate = 1ull << 32;
-constexpr uint64_t kFlagPrefix = 2ull << 32;
-constexpr uint32_t kSpinLimit = 1u << 20;
 
 // ---------------------------------------------------------------------------
 // streaming memory access: every codec byte is read once and written once,
@@ -125,25 +125,35 @@ __device__ __forceinline__ void store_stream4(void *p, uint32_t a) {
 // wave helpers
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        uint32_t o = __shfl_up(v, d, kWave);
-        if (lane >= d) v += o;
-    }
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS):
+// shifts of 1, 2, 4 and 8 lanes inside each 16-lane row, then the last lane
+// of row 0 / row 2 is broadcast into rows 1 / 3 and lane 31 into rows 2 and 3.
+// A lane whose source lies outside its row keeps the 0 passed as `old`.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
     return v;
 }
 
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-    for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
-    return v;
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(v), kWave - 1);
 }
 
 __device__ __forceinline__ uint32_t find_segment_enc(const EncArgs &a, uint32_t flat) {
     uint32_t s = 0;
     for (uint32_t i = 1; i < a.k; ++i)
         if (a.seg[i].tile_begin <= flat) s = i;
+    return s;
+}
+
+__device__ __forceinline__ uint32_t find_segment_fin(const EncArgs &a, uint32_t flat) {
+    uint32_t s = 0;
+    for (uint32_t i = 1; i < a.k; ++i)
+        if (a.seg[i].fin_begin <= flat) s = i;
     return s;
 }
 
@@ -170,8 +180,9 @@ __device__ __forceinline__ TileCounts count_tile(const uint32_t (&zmask)[kSteps]
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) c[u] = __builtin_popcount(zmask[u]);
     const uint32_t a = c[0] | (c[1] << 16), b = c[2] | (c[3] << 16);
-    const uint32_t ai = wave_inclusive_scan(a, lane), bi = wave_inclusive_scan(b, lane);
-    const uint32_t at = __shfl(ai, kWave - 1, kWave), bt = __shfl(bi, kWave - 1, kWave);
+    const uint32_t ai = wave_inclusive_scan(a), bi = wave_inclusive_scan(b);
+    const uint32_t at = (uint32_t)__builtin_amdgcn_readlane((int)ai, kWave - 1);
+    const uint32_t bt = (uint32_t)__builtin_amdgcn_readlane((int)bi, kWave - 1);
     const uint32_t ae = ai - a, be = bi - b;
     const uint32_t tot[kSteps] = {at & 0xFFFFu, at >> 16, bt & 0xFFFFu, bt >> 16};
     const uint32_t ex[kSteps] = {ae & 0xFFFFu, ae >> 16, be & 0xFFFFu, be >> 16};
@@ -244,20 +255,16 @@ __device__ __forceinline__ Step load_step(const uint16_t *in, uint64_t base, uin
 
 // A block codes kEncSubTiles consecutive 8192-value sub-tiles (its span).
 // All loads of the span are issued up front.  Phase A turns every step into
-// sign+mantissa bytes (stored at once), exponent bytes and plane bytes, and
-// counts the span's zero-point values; the count is published right away so
-// that later blocks' look-backs never wait for this block's stores.  Phase B
-// then ranks, regroups and stages, while wave 0's look-back is in flight.
-// Blocks are ordered by blockIdx: workgroups are dispatched in index order,
-// so a block only ever waits for blocks that are already running or done; the
-// wait is bounded regardless.
+// sign+mantissa bytes (stored at once), exponent bytes and plane bytes;
+// phase B ranks the zero-point values, regroups and stores the planes and
+// stages the zero-point bytes in LDS; the span then leaves its counts and its
+// zero-point bytes in the scratch tail for finalize_kernel.
 __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs args) {
     __shared__ uint32_t s_planes[kTile / 8];     // per 8-value group: plane bytes 0, 1, 2
-    __shared__ uint8_t s_zp[kEncSpan];           // the span's zero-point bytes, in order
+    __shared__ __align__(16) uint8_t s_zp[kEncSpan + 16];  // the span's zero-point bytes, in order
     __shared__ uint8_t s_code[256];              // table mode: exponent -> code
     __shared__ uint32_t s_wave_total[2][kWaves];
     __shared__ uint32_t s_group[kEncGroups];     // zero-points per 4096-value group of the span
-    __shared__ uint32_t s_prefix;
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const uint32_t flat = blockIdx.x;
@@ -271,7 +278,6 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs args) {
     const uint64_t span0 = (uint64_t)b * kEncSpan;
     uint8_t *const out = sg.out;
     uint8_t *const scratch = out + L.off_scratch;
-    unsigned long long *const state = reinterpret_cast<unsigned long long *>(scratch + kScratchCtrl);
 
     if (mode == kModeTable) {
         uint32_t c = 0;
@@ -294,7 +300,6 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs args) {
 
     // ---- phase A: split, code, planes; count the span's zero-points
     uint32_t ex[kEncSubTiles][kSteps][2], pl[kEncSubTiles][kSteps], zm[kEncSubTiles][kSteps];
-    uint32_t lane_zeros = 0;
 #pragma unroll
     for (int sub = 0; sub < kEncSubTiles; ++sub) {
 #pragma unroll
@@ -324,28 +329,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs args) {
             const uint32_t vm = in[sub][u].vmask;
             pl[sub][u] = codes_to_planes(c_lo, c_hi) & (vm * 0x010101u);
             zm[sub][u] = zero_point_mask(pl[sub][u]) & vm;
-            lane_zeros += __builtin_popcount(zm[sub][u]);
             if (vm) store_stream8(out + kHeaderBytes + base, sm0, sm1);
         }
     }
-    {
-        const uint32_t wz = wave_sum(lane_zeros);
-        if (lane == 0) s_wave_total[1][wave] = wz;
-    }
-    __syncthreads();
-    const uint32_t T = s_wave_total[1][0] + s_wave_total[1][1] + s_wave_total[1][2] + s_wave_total[1][3];
-
-    // ---- publish the span's count, and start looking back
-    unsigned long long lb_value = kFlagPrefix;
-    int64_t lb_idx = (int64_t)b - 1;
-    if (wave == 0) {
-        if (lane == 0)
-            __hip_atomic_store(&state[b], (b == 0 ? kFlagPrefix : kFlagAggregate) | T, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        const int64_t j = lb_idx - lane;
-        if (b > 0 && j >= 0) lb_value = __hip_atomic_load(&state[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-
     // ---- phase B: ranks, plane regrouping, zero-point staging
     uint32_t running = 0;  // zero-points of the span so far (uniform)
 #pragma unroll
@@ -384,86 +370,26 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs args) {
         __syncthreads();  // s_planes is rewritten by the next sub-tile
     }
 
-    // ---- span prefix: finish the decoupled look-back (wave 0)
-    if (wave == 0) {
-        uint32_t prefix = 0;
-        if (b > 0) {
-            unsigned long long v = lb_value;
-            uint32_t spins = 0;
-            for (;;) {
-                const uint32_t flag = (uint32_t)(v >> 32);
-                const unsigned long long pmask = __ballot(flag == 2u);
-                const unsigned long long zmask_lb = __ballot(flag == 0u);
-                const unsigned long long upto = pmask ? (pmask & (0ull - pmask)) * 2ull - 1ull : ~0ull;
-                if (zmask_lb & upto) {
-                    if (++spins > kSpinLimit) {
-                        if (lane == 0) atomicOr(reinterpret_cast<uint32_t *>(scratch + 8), 1u);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                } else {
-                    prefix += wave_sum(((upto >> lane) & 1ull) ? (uint32_t)v : 0u);
-                    if (pmask) break;
-                    lb_idx -= kWave;
-                }
-                const int64_t j = lb_idx - lane;
-                v = j >= 0 ? __hip_atomic_load(&state[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kFlagPrefix;
-            }
-            if (lane == 0)
-                __hip_atomic_store(&state[b], kFlagPrefix | (uint64_t)(prefix + T), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (lane == 0) s_prefix = prefix;
-    }
-    __syncthreads();
-    const uint32_t prefix = s_prefix;
+    // ---- hand the span to the finalize pass: its zero-point count, the count
+    // of each of its 4096-value groups (in the groups' table slots) and its
+    // zero-point bytes (in the span's staging slot)
+    const uint32_t T = running;
     const bool last = (b == blocks - 1);
-
-    // ---- zero-point table entries of the span's groups (the last span also
-    // writes the closing entry, E)
-    if (tid <= kEncGroups) {
+    if (tid == 0) reinterpret_cast<uint32_t *>(scratch)[b] = T;
+    if (tid < kEncGroups) {
         const uint64_t g = (uint64_t)b * kEncGroups + tid;
-        if (g <= L.groups && (tid < kEncGroups || last)) {
-            uint32_t before = prefix;
-            for (int j = 0; j < tid; ++j) before += s_group[j];
-            reinterpret_cast<uint32_t *>(out + L.off_tab)[g] = before;
+        if (g < L.groups) reinterpret_cast<uint32_t *>(out + L.off_tab)[g] = s_group[tid];
+    }
+    {
+        uint8_t *const slot = scratch + scratch_counts_bytes(n) + (uint64_t)b * kEncSpan;
+        for (uint32_t i = tid; 16 * i < T; i += kThreads) {
+            const uint4 v = reinterpret_cast<const uint4 *>(s_zp)[i];
+            store_stream16(slot + 16 * i, v.x, v.y, v.z, v.w);
         }
     }
 
-    // ---- zero-point bytes (a prefix past n can only follow a look-back
-    // timeout, which has already marked the stream invalid; never write past
-    // the zero-point section then)
-    if ((uint64_t)prefix + T <= n) {
-        uint8_t *zp = out + L.off_zp + prefix;
-        for (uint32_t i = tid; i < T; i += kThreads) zp[i] = s_zp[i];
-    }
-
-    // ---- the last span writes the header, the pads and the size
+    // ---- pads the data stores never touch (the last span of the segment)
     if (last) {
-        const uint64_t E = (uint64_t)prefix + T;
-        const uint64_t total = L.off_zp + E;
-        const uint32_t err = __hip_atomic_load(reinterpret_cast<uint32_t *>(scratch + 8), __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-        if (tid < 32) {
-            uint32_t w = 0;
-            switch (tid) {
-                case 0: w = err ? 0u : kMagic; break;
-                case 1: w = (uint32_t)kVersion | (kHeaderBytes << 16); break;
-                case 2: w = (uint32_t)n; break;
-                case 3: w = (uint32_t)(n >> 32); break;
-                case 4: w = kGroup; break;
-                case 5: w = (uint32_t)L.groups; break;
-                case 6: w = sg.exps[0] | (sg.exps[1] << 8) | (sg.exps[2] << 16) | ((uint32_t)sg.exps[3] << 24); break;
-                case 7: w = sg.exps[4] | (sg.exps[5] << 8) | (sg.exps[6] << 16); break;
-                case 8: w = (uint32_t)E; break;
-                case 9: w = (uint32_t)(E >> 32); break;
-                case 10: w = (uint32_t)total; break;
-                case 11: w = (uint32_t)(total >> 32); break;
-                default: break;
-            }
-            reinterpret_cast<uint32_t *>(out)[tid] = w;
-        }
-        // pads the data stores above never touch
         const uint64_t sm_end = kHeaderBytes + 8 * ((n + 7) / 8);
         for (uint64_t i = sm_end + tid; i < L.off_p0; i += kThreads) out[i] = 0;
         const uint64_t pl_end = 4 * ((n + 31) / 32);
@@ -473,6 +399,214 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs args) {
             out[L.off_p2 + i] = 0;
         }
         for (uint64_t i = L.off_tab + 4 * (L.groups + 1) + tid; i < L.off_zp; i += kThreads) out[i] = 0;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// finalize: exclusive scan of the span counts, the zero-point table, the
+// compacted zero-point array and the header
+// ---------------------------------------------------------------------------
+
+// One block per run of consecutive encoder spans: at least kFinRunMin, more
+// when a segment would otherwise need over kFinMaxBlocks blocks, which keeps
+// the redundant count sums below kFinMaxBlocks * spans reads per segment.
+constexpr uint32_t kFinRunMin = 32;
+constexpr uint32_t kFinMaxBlocks = 1024;
+constexpr uint32_t kFinRunMax = (uint32_t)((((kMaxElems + kEncSpan - 1) / kEncSpan) + kFinMaxBlocks - 1) / kFinMaxBlocks);
+ZC_HD uint32_t fin_run(uint64_t nb) {
+    const uint64_t r = (nb + kFinMaxBlocks - 1) / kFinMaxBlocks;
+    return (uint32_t)(r > kFinRunMin ? r : kFinRunMin);
+}
+ZC_HD uint64_t fin_block_count(uint64_t nb) {
+    const uint32_t r = fin_run(nb);
+    return (nb + r - 1) / r;
+}
+static_assert(kFinRunMax <= 2 * kThreads, "two span counts per thread");
+static_assert(kEncGroups * kFinRunMax <= 4 * kThreads || kEncGroups * kFinRunMin <= kThreads, "group counts");
+
+__device__ __forceinline__ uint32_t ld32_plain(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
+
+// Every block sums the counts of all spans before its run (cached), so blocks
+// never wait for each other; encode_kernel has completed.
+__global__ __launch_bounds__(kThreads) void finalize_kernel(EncArgs args) {
+    __shared__ uint32_t s_pre[kFinRunMax + 1];
+    __shared__ uint32_t s_gc[kEncGroups * kFinRunMax];
+    __shared__ uint32_t s_red[kWaves];
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const uint32_t flat = blockIdx.x;
+    const uint32_t s = find_segment_fin(args, flat);
+    const EncSeg &sg = args.seg[s];
+    const uint64_t n = sg.n;
+    const Layout L = layout_for(n);
+    const uint64_t nb = enc_blocks(n);
+    const uint32_t run = fin_run(nb);
+    const uint32_t first = (flat - sg.fin_begin) * run;
+    const uint32_t count = (uint32_t)min((uint64_t)run, nb - first);
+    const bool last = (first + count == nb);
+    uint8_t *const out = sg.out;
+    const uint8_t *const scratch = out + L.off_scratch;
+    const uint8_t *const slots = scratch + scratch_counts_bytes(n);
+    const uint32_t *const counts = reinterpret_cast<const uint32_t *>(scratch);
+    uint32_t *const tab = reinterpret_cast<uint32_t *>(out + L.off_tab);
+
+    // ---- first round of loads: counts before the run, the run's counts and
+    // its groups' counts
+    uint32_t acc = 0;
+    {
+        const uint4 *c4 = reinterpret_cast<const uint4 *>(counts);
+        for (uint32_t i = tid; 4 * i + 4 <= first; i += kThreads) {
+            const uint4 w = c4[i];
+            acc += w.x + w.y + w.z + w.w;
+        }
+        if ((uint32_t)tid < (first & 3u)) acc += counts[(first & ~3u) + tid];
+    }
+    const uint32_t own0 = (uint32_t)(2 * tid) < count ? counts[first + 2 * tid] : 0u;
+    const uint32_t own1 = (uint32_t)(2 * tid + 1) < count ? counts[first + 2 * tid + 1] : 0u;
+    const uint32_t ngr = count * kEncGroups;
+    for (uint32_t q = tid; q < ngr; q += kThreads) {
+        const uint64_t g = (uint64_t)first * kEncGroups + q;
+        s_gc[q] = g < L.groups ? tab[g] : 0u;
+    }
+
+    // ---- exclusive prefixes of the run's spans (block reduce + block scan)
+    {
+        const uint32_t pair = own0 + own1;
+        const uint32_t inc = wave_inclusive_scan(pair);
+        const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
+        const uint32_t wacc = wave_sum(acc);
+        if (lane == 0) s_red[wave] = wacc;
+        __syncthreads();
+        uint32_t base = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+        __syncthreads();
+        if (lane == 0) s_red[wave] = wtot;
+        __syncthreads();
+        for (int w = 0; w < wave; ++w) base += s_red[w];
+        const uint32_t ex = base + inc - pair;
+        if ((uint32_t)(2 * tid) < count) s_pre[2 * tid] = ex;
+        if ((uint32_t)(2 * tid + 1) < count) s_pre[2 * tid + 1] = ex + own0;
+        if ((uint32_t)(2 * tid) < count && (uint32_t)(2 * tid + 2) >= count)
+            s_pre[count] = ex + own0 + ((uint32_t)(2 * tid + 1) < count ? own1 : 0u);
+    }
+    __syncthreads();
+
+    // ---- table: group counts -> zero-points before each group
+    for (uint32_t q = tid; q < ngr; q += kThreads) {
+        const uint64_t g = (uint64_t)first * kEncGroups + q;
+        const uint32_t j = q / kEncGroups;
+        uint32_t before = s_pre[j];
+        for (uint32_t k = j * kEncGroups; k < q; ++k) before += s_gc[k];
+        if (g < L.groups) tab[g] = before;
+    }
+
+    // ---- the run's staged bytes -> the stream.  Wave w copies spans w, w+4,
+    // ...: per span the head bytes up to a 4-byte boundary of the stream, the
+    // whole dwords (two aligned staged words and a funnel shift) and the tail
+    // bytes.  One round of loads covers the first kFinFirstDw dwords, the head
+    // and the tail of every span of the wave; longer spans loop for the rest.
+    uint8_t *const zp = out + L.off_zp;
+    constexpr int kMaxSpansPerWave = kFinRunMin / kWaves;
+    constexpr uint32_t kFinFirstDw = 2 * kWave;
+    const uint32_t my_spans = count > (uint32_t)wave ? (count - wave + kWaves - 1) / kWaves : 0u;
+    uint32_t extra = 0;  // dwords past the first round, longest span of the wave
+    for (uint32_t t0 = 0; t0 < my_spans; t0 += kMaxSpansPerWave) {
+        uint32_t hb[kMaxSpansPerWave], tb[kMaxSpansPerWave], w0[kMaxSpansPerWave], w1[kMaxSpansPerWave];
+#pragma unroll
+        for (int u = 0; u < kMaxSpansPerWave; ++u) {
+            const uint32_t t = t0 + u, j = wave + kWaves * t;
+            hb[u] = tb[u] = w0[u] = w1[u] = 0;
+            if (t < my_spans) {
+                const uint32_t p = s_pre[j], T = s_pre[j + 1] - p;
+                const uint32_t head = min((4u - (p & 3u)) & 3u, T);
+                const uint32_t body = (T - head) / 4, tail0 = head + 4 * body;
+                extra = max(extra, body > kFinFirstDw ? body - kFinFirstDw : 0u);
+                const uint8_t *const src = slots + (uint64_t)(first + j) * kEncSpan;
+                if ((uint32_t)lane < head) hb[u] = src[lane];
+                if ((uint32_t)lane < T - tail0) tb[u] = src[tail0 + lane];
+                const uint32_t sh = head;  // staged offset of dword i is head + 4 i
+                if ((uint32_t)lane < body) {
+                    const uint32_t a = 4u * lane, lo = ld32_plain(src + a);
+                    w0[u] = sh ? __builtin_amdgcn_alignbyte(ld32_plain(src + a + 4), lo, sh) : lo;
+                }
+                if ((uint32_t)lane + kWave < body) {
+                    const uint32_t a = 4u * (lane + kWave), lo = ld32_plain(src + a);
+                    w1[u] = sh ? __builtin_amdgcn_alignbyte(ld32_plain(src + a + 4), lo, sh) : lo;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kMaxSpansPerWave; ++u) {
+            const uint32_t t = t0 + u, j = wave + kWaves * t;
+            if (t < my_spans) {
+                const uint32_t p = s_pre[j], T = s_pre[j + 1] - p;
+                const uint32_t head = min((4u - (p & 3u)) & 3u, T);
+                const uint32_t body = (T - head) / 4, tail0 = head + 4 * body;
+                uint8_t *const d = zp + p;
+                if ((uint32_t)lane < head) d[lane] = (uint8_t)hb[u];
+                if ((uint32_t)lane < T - tail0) d[tail0 + lane] = (uint8_t)tb[u];
+                if ((uint32_t)lane < body) *reinterpret_cast<uint32_t *>(d + head + 4u * lane) = w0[u];
+                if ((uint32_t)lane + kWave < body) *reinterpret_cast<uint32_t *>(d + head + 4u * (lane + kWave)) = w1[u];
+            }
+        }
+    }
+    for (uint32_t r = 0; r * kWave < extra; ++r) {
+        for (uint32_t t0 = 0; t0 < my_spans; t0 += kMaxSpansPerWave) {
+            uint32_t word[kMaxSpansPerWave];
+#pragma unroll
+            for (int u = 0; u < kMaxSpansPerWave; ++u) {
+                const uint32_t t = t0 + u;
+                word[u] = 0;
+                if (t < my_spans) {
+                    const uint32_t j = wave + kWaves * t;
+                    const uint32_t p = s_pre[j], T = s_pre[j + 1] - p;
+                    const uint32_t head = min((4u - (p & 3u)) & 3u, T);
+                    const uint32_t body = (T - head) / 4;
+                    const uint32_t i = kFinFirstDw + r * kWave + lane;
+                    if (i < body) {
+                        const uint8_t *const src = slots + (uint64_t)(first + j) * kEncSpan;
+                        const uint32_t a = 4 * i, lo = ld32_plain(src + a);
+                        word[u] = head ? __builtin_amdgcn_alignbyte(ld32_plain(src + a + 4), lo, head) : lo;
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kMaxSpansPerWave; ++u) {
+                const uint32_t t = t0 + u;
+                if (t < my_spans) {
+                    const uint32_t j = wave + kWaves * t;
+                    const uint32_t p = s_pre[j], T = s_pre[j + 1] - p;
+                    const uint32_t head = min((4u - (p & 3u)) & 3u, T);
+                    const uint32_t body = (T - head) / 4;
+                    const uint32_t i = kFinFirstDw + r * kWave + lane;
+                    if (i < body) *reinterpret_cast<uint32_t *>(zp + (uint64_t)p + head + 4 * i) = word[u];
+                }
+            }
+        }
+    }
+    const uint32_t P1 = s_pre[count];
+    if (last && tid == 0) tab[L.groups] = P1;
+
+    // ---- the last block of the segment writes the header and the size
+    if (last) {
+        const uint64_t total = L.off_zp + P1;
+        if (tid < 32) {
+            uint32_t w = 0;
+            switch (tid) {
+                case 0: w = kMagic; break;
+                case 1: w = (uint32_t)kVersion | (kHeaderBytes << 16); break;
+                case 2: w = (uint32_t)n; break;
+                case 3: w = (uint32_t)(n >> 32); break;
+                case 4: w = kGroup; break;
+                case 5: w = (uint32_t)L.groups; break;
+                case 6: w = sg.exps[0] | (sg.exps[1] << 8) | (sg.exps[2] << 16) | ((uint32_t)sg.exps[3] << 24); break;
+                case 7: w = sg.exps[4] | (sg.exps[5] << 8) | (sg.exps[6] << 16); break;
+                case 8: w = P1; break;
+                case 10: w = (uint32_t)total; break;
+                case 11: w = (uint32_t)(total >> 32); break;
+                default: break;
+            }
+            reinterpret_cast<uint32_t *>(out)[tid] = w;
+        }
         if (tid == 0 && sg.out_bytes) *sg.out_bytes = total;
     }
 }
@@ -483,19 +617,61 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs args) {
 
 __device__ __forceinline__ uint32_t ld_u32(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
 
+// A block decodes kDecSubTiles consecutive tiles (its span).  Every plane and
+// sign+mantissa load of the span, and the span's zero-point table entries,
+// are issued before the header is checked (all of them lie inside the n-value
+// layout, which the host has checked against in_bytes); the zero-point slice
+// is then staged in LDS with dword loads and gathered by rank.
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
     __shared__ uint32_t s_planes[kTile / 8];
-    __shared__ uint8_t s_zp[kTile];
-    __shared__ uint32_t s_wave_total[kWaves];
+    __shared__ uint32_t s_zp32[kDecSpan / 4 + 2];  // the span's zero-point bytes from a dword-aligned start
+    __shared__ uint32_t s_wave_total[2][kWaves];
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const uint32_t flat = blockIdx.x;
     const uint32_t s = find_segment_dec(args, flat);
     const DecSeg &sg = args.seg[s];
-    const uint32_t t = flat - sg.tile_begin;
+    const uint32_t b = flat - sg.tile_begin;
     const uint64_t n = sg.n;
     const Layout L = layout_for(n);
     const uint8_t *const in = sg.in;
+    const uint64_t span0 = (uint64_t)b * kDecSpan;
+
+    // ---- data loads of the whole span
+    uint32_t pw[kDecSubTiles][3];
+    uint32_t sm[kDecSubTiles][kSteps][2], vmask[kDecSubTiles][kSteps];
+#pragma unroll
+    for (int sub = 0; sub < kDecSubTiles; ++sub) {
+        const uint64_t tile0 = span0 + (uint64_t)sub * kTile;
+        pw[sub][0] = pw[sub][1] = pw[sub][2] = 0;
+        if (tile0 + 32u * (uint32_t)tid < n) {
+            const uint64_t off = tile0 / 8 + 4u * (uint32_t)tid;
+            pw[sub][0] = load_stream4(in + L.off_p0 + off);
+            pw[sub][1] = load_stream4(in + L.off_p1 + off);
+            pw[sub][2] = load_stream4(in + L.off_p2 + off);
+        }
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            const uint64_t base = tile0 + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
+            sm[sub][u][0] = sm[sub][u][1] = 0;
+            vmask[sub][u] = 0;
+            if (base < n) {
+                const uint2 v = load_stream8(in + kHeaderBytes + base);
+                sm[sub][u][0] = v.x;
+                sm[sub][u][1] = v.y;
+                vmask[sub][u] = base + 8 <= n ? 0xFFu : (1u << (uint32_t)(n - base)) - 1u;
+            }
+        }
+    }
+
+    // ---- the span's zero-point table entries
+    const uint32_t *tab = reinterpret_cast<const uint32_t *>(in + L.off_tab);
+    uint32_t z[kDecGroups + 1];
+#pragma unroll
+    for (int j = 0; j <= kDecGroups; ++j) {
+        const uint64_t g = (uint64_t)b * kDecGroups + j;
+        z[j] = tab[g <= L.groups ? g : L.groups];
+    }
 
     // ---- header: every block checks it, so a bad header stops all of them
     const uint32_t h6 = ld_u32(in + 24), h7 = ld_u32(in + 28);
@@ -520,94 +696,89 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
     // code -> exponent table for v_perm: byte 0 (code 000) is a placeholder
     const uint32_t tbl_lo = h6 << 8, tbl_hi = (h6 >> 24) | (h7 << 8);
 
-    // ---- this tile's slice of the zero-point array
-    const uint32_t *tab = reinterpret_cast<const uint32_t *>(in + L.off_tab);
-    const uint64_t g = 2ull * t;
-    uint32_t z0 = tab[g];
-    uint32_t z1 = tab[g + 1 <= L.groups ? g + 1 : L.groups];
-    uint32_t z2 = tab[g + 2 <= L.groups ? g + 2 : L.groups];
-    const bool last = (t == L.tiles - 1);
-    bool bad = !(z0 <= z1 && z1 <= z2 && z2 <= E) || (t == 0 && z0 != 0) || (last && z2 != E) || z2 - z0 > kTile;
-    if (bad) {  // keep every read inside the stream and inside s_zp
-        z0 = z0 < E ? z0 : (uint32_t)E;
-        z1 = z1 < z0 ? z0 : (z1 > E ? (uint32_t)E : z1);
-        z2 = z2 < z1 ? z1 : (z2 > E ? (uint32_t)E : z2);
-        if (z2 - z0 > kTile) z2 = z0 + kTile;
-    }
-    const uint32_t zcount = z2 - z0;
-    for (uint32_t i = tid; i < zcount; i += kThreads) s_zp[i] = in[L.off_zp + z0 + i];
-
-    // ---- planes: one dword of each plane per thread, interleaved into LDS
-    {
-        uint32_t p0 = 0, p1 = 0, p2 = 0;
-        const uint64_t tile0 = (uint64_t)t * kTile;
-        if (tile0 + 32u * (uint32_t)tid < n) {
-            const uint64_t off = tile0 / 8 + 4u * (uint32_t)tid;
-            p0 = load_stream4(in + L.off_p0 + off);
-            p1 = load_stream4(in + L.off_p1 + off);
-            p2 = load_stream4(in + L.off_p2 + off);
-        }
-        const uint32_t lo = perm(p1, p0, 0x05010400u), hi = perm(p1, p0, 0x07030602u);
-        uint4 q;
-        q.x = perm(p2, lo, 0x0C040100u);
-        q.y = perm(p2, lo, 0x0C050302u);
-        q.z = perm(p2, hi, 0x0C060100u);
-        q.w = perm(p2, hi, 0x0C070302u);
-        reinterpret_cast<uint4 *>(s_planes)[tid] = q;
-    }
-
-    // ---- sign+mantissa bytes
-    const uint64_t tile0 = (uint64_t)t * kTile;
-    uint32_t sm[kSteps][2], vmask[kSteps];
+    // ---- table consistency; clamp so that every read stays inside the stream
+    const bool last = (b == dec_blocks(n) - 1);
+    bool bad = (b == 0 && z[0] != 0) || (last && z[kDecGroups] != E);
 #pragma unroll
-    for (int u = 0; u < kSteps; ++u) {
-        const uint64_t base = tile0 + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
-        sm[u][0] = sm[u][1] = 0;
-        vmask[u] = 0;
-        if (base < n) {
-            const uint2 v = load_stream8(in + kHeaderBytes + base);
-            sm[u][0] = v.x;
-            sm[u][1] = v.y;
-            vmask[u] = base + 8 <= n ? 0xFFu : (1u << (uint32_t)(n - base)) - 1u;
-        }
+    for (int j = 0; j <= kDecGroups; ++j) {
+        const uint32_t lo = j ? z[j - 1] : 0u;
+        if (z[j] < lo || z[j] > E) bad = true;
+        z[j] = z[j] < lo ? lo : (z[j] > E ? (uint32_t)E : z[j]);
     }
-    __syncthreads();  // s_planes, s_zp
-
-    uint32_t e[kSteps][2], zmask[kSteps];
+    if (z[kDecGroups] - z[0] > kDecSpan) {
+        bad = true;
 #pragma unroll
-    for (int u = 0; u < kSteps; ++u) {
-        const uint32_t planes = s_planes[(wave * kSteps + u) * kWave + lane] & 0x00FFFFFFu;
-        uint32_t c_lo, c_hi;
-        planes_to_codes(planes, c_lo, c_hi);
-        e[u][0] = perm(tbl_hi, tbl_lo, c_lo);
-        e[u][1] = perm(tbl_hi, tbl_lo, c_hi);
-        zmask[u] = zero_point_mask(planes) & vmask[u];
+        for (int j = 0; j <= kDecGroups; ++j) z[j] = z[j] - z[0] > kDecSpan ? z[0] + kDecSpan : z[j];
     }
-    const TileCounts tc = count_tile(zmask, lane, wave, s_wave_total);
-    if (tc.tile_total != zcount || (uint64_t)z0 + tc.first_group != z1) bad = true;
+
+    // ---- stage the span's zero-point bytes: stream bytes [A0, A1)
+    const uint64_t A0 = L.off_zp + z[0], A1 = L.off_zp + z[kDecGroups];
+    const uint64_t a0 = A0 & ~uint64_t(3), a1 = A1 & ~uint64_t(3);
+    const uint32_t shift = (uint32_t)(A0 & 3u);
+    const uint32_t ndw = (uint32_t)((a1 - a0) / 4);
+    for (uint32_t i = tid; i < ndw; i += kThreads) s_zp32[i] = ld_u32(in + a0 + 4u * i);
+    if (tid == 0 && A1 > a1) {
+        uint32_t w = 0;
+        for (uint32_t i = 0; i < (uint32_t)(A1 - a1); ++i) w |= (uint32_t)in[a1 + i] << (8 * i);
+        s_zp32[ndw] = w;
+    }
+    const uint8_t *const s_zp = reinterpret_cast<const uint8_t *>(s_zp32) + shift;
+    const uint32_t zspan = z[kDecGroups] - z[0];
+
+#pragma unroll
+    for (int sub = 0; sub < kDecSubTiles; ++sub) {
+        const uint64_t tile0 = span0 + (uint64_t)sub * kTile;
+        {
+            const uint32_t p0 = pw[sub][0], p1 = pw[sub][1], p2 = pw[sub][2];
+            const uint32_t lo = perm(p1, p0, 0x05010400u), hi = perm(p1, p0, 0x07030602u);
+            uint4 q;
+            q.x = perm(p2, lo, 0x0C040100u);
+            q.y = perm(p2, lo, 0x0C050302u);
+            q.z = perm(p2, hi, 0x0C060100u);
+            q.w = perm(p2, hi, 0x0C070302u);
+            reinterpret_cast<uint4 *>(s_planes)[tid] = q;
+        }
+        __syncthreads();  // s_planes (and, for the first sub-tile, s_zp32)
+
+        uint32_t e[kSteps][2], zmask[kSteps];
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            const uint32_t planes = s_planes[(wave * kSteps + u) * kWave + lane] & 0x00FFFFFFu;
+            uint32_t c_lo, c_hi;
+            planes_to_codes(planes, c_lo, c_hi);
+            e[u][0] = perm(tbl_hi, tbl_lo, c_lo);
+            e[u][1] = perm(tbl_hi, tbl_lo, c_hi);
+            zmask[u] = zero_point_mask(planes) & vmask[sub][u];
+        }
+        const TileCounts tc = count_tile(zmask, lane, wave, s_wave_total[sub & 1]);
+        const uint32_t zb = z[2 * sub], zm = z[2 * sub + 1], ze = z[2 * sub + 2];
+        if (tc.tile_total != ze - zb || tc.first_group != zm - zb) bad = true;
+
+        const uint32_t rank0 = zb - z[0];
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            uint32_t m = zmask[u], r = rank0 + tc.rank[u];
+            while (m) {
+                const uint32_t k = __builtin_ctz(m);
+                m &= m - 1;
+                const uint32_t v = r < zspan ? (uint32_t)s_zp[r] : 0u;
+                ++r;
+                put_byte8(e[u][0], e[u][1], k, v);
+            }
+            const uint64_t base = tile0 + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
+            uint32_t o0, o1, o2, o3;
+            rebuild4(sm[sub][u][0], e[u][0], o0, o1);
+            rebuild4(sm[sub][u][1], e[u][1], o2, o3);
+            if (vmask[sub][u] == 0xFFu) {
+                store_stream16(sg.out + base, o0, o1, o2, o3);
+            } else if (vmask[sub][u]) {
+                const uint32_t w4[4] = {o0, o1, o2, o3};
+                for (uint32_t i = 0; base + i < n; ++i) sg.out[base + i] = (uint16_t)(w4[i / 2] >> (16 * (i % 2)));
+            }
+        }
+        if (sub + 1 < kDecSubTiles) __syncthreads();  // s_planes is rewritten by the next sub-tile
+    }
     if (bad && tid == 0 && sg.status) atomicMax(sg.status, (int32_t)ZC_ERR_CORRUPT);
-
-#pragma unroll
-    for (int u = 0; u < kSteps; ++u) {
-        uint32_t m = zmask[u], r = tc.rank[u];
-        while (m) {
-            const uint32_t k = __builtin_ctz(m);
-            m &= m - 1;
-            const uint32_t b = r < zcount ? s_zp[r] : 0u;
-            ++r;
-            put_byte8(e[u][0], e[u][1], k, b);
-        }
-        const uint64_t base = tile0 + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
-        uint32_t o0, o1, o2, o3;
-        rebuild4(sm[u][0], e[u][0], o0, o1);
-        rebuild4(sm[u][1], e[u][1], o2, o3);
-        if (vmask[u] == 0xFFu) {
-            store_stream16(sg.out + base, o0, o1, o2, o3);
-        } else if (vmask[u]) {
-            const uint32_t w4[4] = {o0, o1, o2, o3};
-            for (uint32_t i = 0; base + i < n; ++i) sg.out[base + i] = (uint16_t)(w4[i / 2] >> (16 * (i % 2)));
-        }
-    }
 }
 
 }  // namespace zc
@@ -644,38 +815,34 @@ extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void 
     if (!segs || k == 0 || k > ZC_MAX_BATCH) return ZC_ERR_INVALID_ARG;
     EncArgs a;
     std::memset(&a, 0, sizeof(a));
-    ZeroArgs z;
-    std::memset(&z, 0, sizeof(z));
-    uint64_t tiles = 0;
+    uint64_t blocks = 0, fin_blocks = 0;
     for (uint32_t i = 0; i < k; ++i) {
         const zc_enc_seg &g = segs[i];
         if (!g.out || g.n > kMaxElems || (g.n && !g.in) || !plan_ok(g.plan)) return ZC_ERR_INVALID_ARG;
         if (((uintptr_t)g.in & 15u) || ((uintptr_t)g.out & 127u) || ((uintptr_t)g.out_bytes & 7u))
             return ZC_ERR_MISALIGNED;
         if (g.out_capacity < zc_max_compressed_bytes(g.n)) return ZC_ERR_CAPACITY;
-        const Layout L = layout_for(g.n);
         EncSeg &e = a.seg[i];
         e.in = static_cast<const uint16_t *>(g.in);
         e.out = static_cast<uint8_t *>(g.out);
         e.out_bytes = reinterpret_cast<unsigned long long *>(g.out_bytes);
         e.n = (uint32_t)g.n;
-        e.tile_begin = (uint32_t)tiles;
+        e.tile_begin = (uint32_t)blocks;
+        e.fin_begin = (uint32_t)fin_blocks;
         std::memcpy(e.exps, g.plan.exps, 7);
         e.mode = (g.plan.exps[0] >= 1 && g.plan.exps[6] - g.plan.exps[0] == 6) ? kModeWindow : kModeTable;
-        const uint64_t blocks = enc_blocks(g.n);
-        tiles += blocks;
-        if (tiles > 0xFFFFFFFFull) return ZC_ERR_INVALID_ARG;
-        z.r[i].ptr = reinterpret_cast<uint32_t *>(e.out + L.off_scratch);
-        z.r[i].words = (kScratchCtrl + 8 * blocks) / 4;
+        const uint64_t nb = enc_blocks(g.n);
+        blocks += nb;
+        fin_blocks += fin_block_count(nb);
+        if (blocks > 0xFFFFFFFFull) return ZC_ERR_INVALID_ARG;
     }
     a.k = k;
-    a.total_blocks = (uint32_t)tiles;
-    z.count = k;
+    a.total_blocks = (uint32_t)blocks;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    zc_status rc = launch_zero(z, st);
-    if (rc != ZC_OK) return rc;
-    hipLaunchKernelGGL(encode_kernel, dim3(a.total_blocks), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(encode_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, st, a);
+    if (hipGetLastError() != hipSuccess) return ZC_ERR_HIP;
+    hipLaunchKernelGGL(finalize_kernel, dim3((uint32_t)fin_blocks), dim3(kThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
 }
 
@@ -713,7 +880,7 @@ extern "C" zc_status zc_decompress_batch(const zc_dec_seg *segs, uint32_t k, voi
         d.in_bytes = g.in_bytes;
         d.n = (uint32_t)g.n;
         d.tile_begin = (uint32_t)tiles;
-        tiles += L.tiles;
+        tiles += dec_blocks(g.n);
         if (tiles > 0xFFFFFFFFull) return ZC_ERR_INVALID_ARG;
         if (g.status) {
             z.r[z.count].ptr = reinterpret_cast<uint32_t *>(g.status);

@@ -39,7 +39,7 @@ static_assert(kTile % kGroup == 0, "a tile holds whole groups");
 
 // The encoder gives each block a span of kEncSubTiles consecutive tiles.
 #ifndef ZC_ENC_SUBTILES
-#define ZC_ENC_SUBTILES 4
+#define ZC_ENC_SUBTILES 1
 #endif
 constexpr int kEncSubTiles = ZC_ENC_SUBTILES;
 constexpr uint32_t kEncSpan = kTile * kEncSubTiles;
@@ -47,6 +47,19 @@ constexpr int kEncGroups = (int)(kEncSpan / kGroup);
 
 ZC_HD uint64_t enc_blocks(uint64_t n) {
     const uint64_t b = (n + kEncSpan - 1) / kEncSpan;
+    return b ? b : 1;
+}
+
+// The decoder gives each block a span of kDecSubTiles consecutive tiles.
+#ifndef ZC_DEC_SUBTILES
+#define ZC_DEC_SUBTILES 1
+#endif
+constexpr int kDecSubTiles = ZC_DEC_SUBTILES;
+constexpr uint32_t kDecSpan = kTile * kDecSubTiles;
+constexpr int kDecGroups = (int)(kDecSpan / kGroup);
+
+ZC_HD uint64_t dec_blocks(uint64_t n) {
+    const uint64_t b = (n + kDecSpan - 1) / kDecSpan;
     return b ? b : 1;
 }
 
@@ -77,13 +90,12 @@ ZC_HD Layout layout_for(uint64_t n) {
     return L;
 }
 
-// Encoder scratch, at off_scratch: a 128-byte control block (error word at
-// byte 8) followed by one 64-bit look-back word per encoder block.  Sized per
-// 4096-value group so that any span size fits.
-constexpr uint64_t kScratchCtrl = 128;
-ZC_HD uint64_t scratch_bytes(uint64_t n) {
-    uint64_t g = (n + kGroup - 1) / kGroup;
-    return kScratchCtrl + 8 * (g ? g : 1);
-}
+// Encoder scratch, at off_scratch (behind the largest possible stream):
+//   [0, 4 NB)                          zero-point count of every encoder span
+//   [A(4 NB), A(4 NB) + NB kEncSpan)   one kEncSpan-byte staging slot per span
+//                                      for its zero-point bytes
+// where NB = enc_blocks(n).  The finalize pass reads both.
+ZC_HD uint64_t scratch_counts_bytes(uint64_t n) { return align128(4 * enc_blocks(n)); }
+ZC_HD uint64_t scratch_bytes(uint64_t n) { return scratch_counts_bytes(n) + enc_blocks(n) * (uint64_t)kEncSpan; }
 
 }  // namespace zc
