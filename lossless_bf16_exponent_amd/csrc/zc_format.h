@@ -52,7 +52,7 @@ ZC_HD uint64_t enc_blocks(uint64_t n) {
 
 // The decoder gives each block a span of kDecSubTiles consecutive tiles.
 #ifndef ZC_DEC_SUBTILES
-#define ZC_DEC_SUBTILES 1
+#define ZC_DEC_SUBTILES 2
 #endif
 constexpr int kDecSubTiles = ZC_DEC_SUBTILES;
 constexpr uint32_t kDecSpan = kTile * kDecSubTiles;
