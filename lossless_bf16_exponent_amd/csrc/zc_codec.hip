@@ -28,8 +28,11 @@
 //     array, which is staged in LDS and gathered by rank.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstring>
+#include <random>
 
 #include "zc.h"
 #include "zc_format.h"
@@ -47,7 +50,7 @@ struct EncSeg {
     unsigned long long *out_bytes;
     uint32_t n;
     uint32_t tile_begin;  // first flat encode block of this segment
-    uint32_t fin_begin;   // first flat finalize block of this segment
+    uint32_t fin_begin;   // first finalize block of this segment (counted from the first finalize block)
     uint8_t exps[7];
     uint8_t mode;  // kModeWindow or kModeTable
 };
@@ -55,7 +58,8 @@ static_assert(sizeof(EncSeg) == 48, "compact kernel arguments");
 
 struct EncArgs {
     uint32_t k;
-    uint32_t total_blocks;
+    uint32_t enc_blocks;  // encoder blocks of all segments; finalize blocks follow them in the grid
+    uint32_t tok_lo, tok_hi;  // the call's token (scratch words of other calls never match it)
     EncSeg seg[ZC_MAX_BATCH];
 };
 
@@ -222,7 +226,82 @@ __global__ __launch_bounds__(256) void zero_kernel(ZeroArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// encoder
+// scratch words shared between the blocks of one compress launch
+// ---------------------------------------------------------------------------
+
+// Each word is 16 bytes: two u64 halves, each holding half of the call's
+// 64-bit token in bits 63..32 and the same 32-bit payload in bits 31..0.  A
+// reader accepts a word only when both token halves match and both payloads
+// agree, so old contents pass for fresh with probability about 2^-64.
+// Stores and loads are agent-scope atomics (`sc1`), which go through to the
+// device's coherence point: the writer and the reader may sit on different
+// XCDs, whose L2 caches are not coherent with each other.
+struct Token {
+    uint32_t lo, hi;
+};
+
+__device__ __forceinline__ void put_word(uint8_t *w, Token t, uint32_t payload) {
+    uint64_t *p = reinterpret_cast<uint64_t *>(w);
+    __hip_atomic_store(p, ((uint64_t)t.lo << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p + 1, ((uint64_t)t.hi << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool get_word(const uint8_t *w, Token t, uint32_t &payload) {
+    uint64_t *p = reinterpret_cast<uint64_t *>(const_cast<uint8_t *>(w));
+    const uint64_t a = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t b = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    payload = (uint32_t)a;
+    return (uint32_t)(a >> 32) == t.lo && (uint32_t)(b >> 32) == t.hi && (uint32_t)a == (uint32_t)b;
+}
+
+// Staged zero-point bytes move between blocks the same way (agent-scope
+// stores and loads), 8 and 4 bytes at a time.
+__device__ __forceinline__ void put_staged8(uint8_t *p, uint32_t lo, uint32_t hi) {
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), (uint64_t)lo | ((uint64_t)hi << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t get_staged4(const uint8_t *p) {
+    return __hip_atomic_load(reinterpret_cast<uint32_t *>(const_cast<uint8_t *>(p)), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits of finalize blocks poll at most this often before the call is given
+// up (with s_sleep between polls this is well over a second, far beyond the
+// longest encode).  Only a dispatch that did not follow workgroup order could
+// reach it; the kernel then still ends and the stream is marked invalid.
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+// Thread tid polls words idx(q) = tid * Q + q (q < Q) of a word array while
+// idx < count, until every one carries the token.  Payloads of valid words
+// land in pay[q] (0 for indices at or past count).  Returns false on timeout.
+template <int Q>
+__device__ __forceinline__ bool poll_words(const uint8_t *base, uint32_t count, Token t, uint32_t (&pay)[Q]) {
+    const uint32_t i0 = (uint32_t)threadIdx.x * Q;
+    uint32_t pend = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        pay[q] = 0;
+        if (i0 + q < count) pend |= 1u << q;
+    }
+    for (uint32_t it = 0; pend; ++it) {
+        if (it == kSpinLimit) return false;
+        if (it) __builtin_amdgcn_s_sleep(2);
+        bool got[Q];
+        uint32_t v[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) got[q] = (pend >> q & 1u) && get_word(base + (uint64_t)kWordBytes * (i0 + q), t, v[q]);
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+            if (got[q]) {
+                pay[q] = v[q];
+                pend &= ~(1u << q);
+            }
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// compress: one launch, encoder blocks first, then finalize blocks
 // ---------------------------------------------------------------------------
 
 // One step of one lane: 8 consecutive values (16 bytes) starting at `base`.
@@ -253,21 +332,33 @@ __device__ __forceinline__ Step load_step(const uint16_t *in, uint64_t base, uin
     return st;
 }
 
-// A block codes kEncSubTiles consecutive 8192-value sub-tiles (its span).
-// All loads of the span are issued up front.  Phase A turns every step into
-// sign+mantissa bytes (stored at once), exponent bytes and plane bytes;
-// phase B ranks the zero-point values, regroups and stores the planes and
-// stages the zero-point bytes in LDS; the span then leaves its counts and its
-// zero-point bytes in the scratch tail for finalize_kernel.
-__global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs args) {
-    __shared__ uint32_t s_planes[kTile / 8];     // per 8-value group: plane bytes 0, 1, 2
-    __shared__ __align__(16) uint8_t s_zp[kEncSpan + 16];  // the span's zero-point bytes, in order
-    __shared__ uint8_t s_code[256];              // table mode: exponent -> code
-    __shared__ uint32_t s_wave_total[2][kWaves];
-    __shared__ uint32_t s_group[kEncGroups];     // zero-points per 4096-value group of the span
+// LDS of a compress block; the encoder and finalize roles share it.
+struct EncShared {
+    uint32_t planes[kTile / 8];              // per 8-value group: plane bytes 0, 1, 2
+    __align__(16) uint8_t zp[kEncSpan + 16];  // the span's zero-point bytes, in order
+    uint8_t code[256];                        // table mode: exponent -> code
+    uint32_t wave_total[2][kWaves];
+    uint32_t group[kEncGroups];               // zero-points per 4096-value group of the span
+};
+struct FinShared {
+    uint32_t pre[kFinRunMax + 1];  // zero-points of the run before each of its spans
+    uint32_t red[kWaves];
+};
+union CompressShared {
+    EncShared e;
+    FinShared f;
+};
+static_assert(kEncGroups == 2, "a span word holds the counts of two groups");
 
+// Encoder role.  A block codes kEncSubTiles consecutive 8192-value sub-tiles
+// (its span).  All loads of the span are issued up front.  Phase A turns every
+// step into sign+mantissa bytes (stored at once), exponent bytes and plane
+// bytes; phase B ranks the zero-point values, regroups and stores the planes
+// and stages the zero-point bytes in LDS.  The span then stores its zero-point
+// bytes to its staging slot, waits until every store of the block has
+// completed and publishes its span word for the finalize blocks.
+__device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t flat, EncShared &sh) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const uint32_t flat = blockIdx.x;
     const uint32_t s = find_segment_enc(args, flat);
     const EncSeg &sg = args.seg[s];
     const uint32_t b = flat - sg.tile_begin;  // block (span) index inside the segment
@@ -278,12 +369,13 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs args) {
     const uint64_t span0 = (uint64_t)b * kEncSpan;
     uint8_t *const out = sg.out;
     uint8_t *const scratch = out + L.off_scratch;
+    const Scratch S = scratch_for(n);
 
     if (mode == kModeTable) {
         uint32_t c = 0;
 #pragma unroll
         for (int k = 0; k < 7; ++k) c = (sg.exps[k] == (uint32_t)tid) ? (uint32_t)(k + 1) : c;
-        s_code[tid] = (uint8_t)c;
+        sh.code[tid] = (uint8_t)c;
     }
     const uint32_t wbase = (uint32_t)sg.exps[0] - 1u;  // window mode only (exps[0] >= 1)
     const uint32_t base_hi = (wbase << 8) | (wbase << 24);
@@ -296,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs args) {
         for (int u = 0; u < kSteps; ++u)
             in[sub][u] = load_step(sg.in, span0 + (uint64_t)sub * kTile + 512u * (uint32_t)(wave * kSteps + u) +
                                               8u * (uint32_t)lane, n);
-    if (mode == kModeTable) __syncthreads();  // s_code ready
+    if (mode == kModeTable) __syncthreads();  // sh.code ready
 
     // ---- phase A: split, code, planes; count the span's zero-points
     uint32_t ex[kEncSubTiles][kSteps][2], pl[kEncSubTiles][kSteps], zm[kEncSubTiles][kSteps];
@@ -321,8 +413,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs args) {
                 c_lo = c_hi = 0;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    c_lo |= (uint32_t)s_code[(ex[sub][u][0] >> (8 * k)) & 0xFFu] << (8 * k);
-                    c_hi |= (uint32_t)s_code[(ex[sub][u][1] >> (8 * k)) & 0xFFu] << (8 * k);
+                    c_lo |= (uint32_t)sh.code[(ex[sub][u][0] >> (8 * k)) & 0xFFu] << (8 * k);
+                    c_hi |= (uint32_t)sh.code[(ex[sub][u][1] >> (8 * k)) & 0xFFu] << (8 * k);
                 }
             }
             // values at or past n carry no code bits and are no zero-points
@@ -338,10 +430,10 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs args) {
     for (int sub = 0; sub < kEncSubTiles; ++sub) {
         const uint64_t tile0 = span0 + (uint64_t)sub * kTile;
 #pragma unroll
-        for (int u = 0; u < kSteps; ++u) s_planes[(wave * kSteps + u) * kWave + lane] = pl[sub][u];
-        const TileCounts tc = count_tile(zm[sub], lane, wave, s_wave_total[sub & 1]);
+        for (int u = 0; u < kSteps; ++u) sh.planes[(wave * kSteps + u) * kWave + lane] = pl[sub][u];
+        const TileCounts tc = count_tile(zm[sub], lane, wave, sh.wave_total[sub & 1]);
         {
-            const uint4 q = reinterpret_cast<const uint4 *>(s_planes)[tid];
+            const uint4 q = reinterpret_cast<const uint4 *>(sh.planes)[tid];
             const uint32_t lo01 = perm(q.y, q.x, 0x05010400u), hi23 = perm(q.w, q.z, 0x05010400u);
             const uint32_t p0 = perm(hi23, lo01, 0x05040100u);
             const uint32_t p1 = perm(hi23, lo01, 0x07060302u);
@@ -359,37 +451,30 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs args) {
             while (m) {
                 const uint32_t k = __builtin_ctz(m);
                 m &= m - 1;
-                s_zp[r++] = (uint8_t)get_byte8(ex[sub][u][0], ex[sub][u][1], k);
+                sh.zp[r++] = (uint8_t)get_byte8(ex[sub][u][0], ex[sub][u][1], k);
             }
         }
         if (tid == 0) {
-            s_group[2 * sub] = tc.first_group;
-            s_group[2 * sub + 1] = tc.tile_total - tc.first_group;
+            sh.group[2 * sub] = tc.first_group;
+            sh.group[2 * sub + 1] = tc.tile_total - tc.first_group;
         }
         running += tc.tile_total;
-        __syncthreads();  // s_planes is rewritten by the next sub-tile
+        __syncthreads();  // sh.planes is rewritten by the next sub-tile; sh.zp and sh.group are complete
     }
 
-    // ---- hand the span to the finalize pass: its zero-point count, the count
-    // of each of its 4096-value groups (in the groups' table slots) and its
-    // zero-point bytes (in the span's staging slot)
+    // ---- the span's zero-point bytes -> its staging slot
     const uint32_t T = running;
-    const bool last = (b == blocks - 1);
-    if (tid == 0) reinterpret_cast<uint32_t *>(scratch)[b] = T;
-    if (tid < kEncGroups) {
-        const uint64_t g = (uint64_t)b * kEncGroups + tid;
-        if (g < L.groups) reinterpret_cast<uint32_t *>(out + L.off_tab)[g] = s_group[tid];
-    }
     {
-        uint8_t *const slot = scratch + scratch_counts_bytes(n) + (uint64_t)b * kEncSpan;
+        uint8_t *const slot = scratch + S.staging + (uint64_t)b * kEncSpan;
         for (uint32_t i = tid; 16 * i < T; i += kThreads) {
-            const uint4 v = reinterpret_cast<const uint4 *>(s_zp)[i];
-            store_stream16(slot + 16 * i, v.x, v.y, v.z, v.w);
+            const uint4 v = reinterpret_cast<const uint4 *>(sh.zp)[i];
+            put_staged8(slot + 16 * i, v.x, v.y);
+            put_staged8(slot + 16 * i + 8, v.z, v.w);
         }
     }
 
     // ---- pads the data stores never touch (the last span of the segment)
-    if (last) {
+    if (b == blocks - 1) {
         const uint64_t sm_end = kHeaderBytes + 8 * ((n + 7) / 8);
         for (uint64_t i = sm_end + tid; i < L.off_p0; i += kThreads) out[i] = 0;
         const uint64_t pl_end = 4 * ((n + 31) / 32);
@@ -400,215 +485,180 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs args) {
         }
         for (uint64_t i = L.off_tab + 4 * (L.groups + 1) + tid; i < L.off_zp; i += kThreads) out[i] = 0;
     }
+
+    // ---- publish: every store of every thread has completed (the staged
+    // bytes at the coherence point) before the span word is written
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+        put_word(scratch + S.span_words + (uint64_t)kWordBytes * b, Token{args.tok_lo, args.tok_hi},
+                 sh.group[0] | (sh.group[1] << 16));
 }
 
-// ---------------------------------------------------------------------------
-// finalize: exclusive scan of the span counts, the zero-point table, the
-// compacted zero-point array and the header
-// ---------------------------------------------------------------------------
-
-// One block per run of consecutive encoder spans: at least kFinRunMin, more
-// when a segment would otherwise need over kFinMaxBlocks blocks, which keeps
-// the redundant count sums below kFinMaxBlocks * spans reads per segment.
-constexpr uint32_t kFinRunMin = 32;
-constexpr uint32_t kFinMaxBlocks = 1024;
-constexpr uint32_t kFinRunMax = (uint32_t)((((kMaxElems + kEncSpan - 1) / kEncSpan) + kFinMaxBlocks - 1) / kFinMaxBlocks);
-ZC_HD uint32_t fin_run(uint64_t nb) {
-    const uint64_t r = (nb + kFinMaxBlocks - 1) / kFinMaxBlocks;
-    return (uint32_t)(r > kFinRunMin ? r : kFinRunMin);
+// Copy of one span's staged zero-point bytes (T bytes, 4-aligned source) to
+// stream offset dst_off (any alignment) by one wave.  Lane l writes
+// destination dwords k and k+1 (k = k0 + 2 l) of the run of dwords that holds
+// the bytes; a destination dword takes source bytes 4k - r .. 4k - r + 3 with
+// r = dst_off mod 4, i.e. a byte-aligned window over source dwords k-1 and k.
+// Dwords shared with the neighbouring spans get byte stores.
+__device__ __forceinline__ void copy_span(uint8_t *zp, uint64_t dst_off, const uint8_t *src, uint32_t T, int lane) {
+    if (T == 0) return;
+    const uint32_t r = (uint32_t)(dst_off & 3u);
+    uint8_t *const dst = zp + (dst_off - r);
+    const uint32_t ndw = (r + T + 3) / 4, srcdw = (T + 3) / 4;
+    uint32_t carry = 0;  // source dword k0 - 1
+    for (uint32_t k0 = 0; k0 < ndw; k0 += 2 * kWave) {
+        const uint32_t k = k0 + 2u * (uint32_t)lane;
+        const uint32_t s0 = k < srcdw ? get_staged4(src + 4u * k) : 0u;
+        const uint32_t s1 = k + 1 < srcdw ? get_staged4(src + 4u * (k + 1)) : 0u;
+        // source dword k-1: lane l-1's s1 (wave_shr:1); lane 0 keeps `carry`
+        const uint32_t sm1 = (uint32_t)__builtin_amdgcn_update_dpp((int)carry, (int)s1, 0x138, 0xF, 0xF, false);
+        carry = (uint32_t)__builtin_amdgcn_readlane((int)s1, kWave - 1);
+        const uint32_t d0 = r ? __builtin_amdgcn_alignbyte(s0, sm1, 4 - r) : s0;
+        const uint32_t d1 = r ? __builtin_amdgcn_alignbyte(s1, s0, 4 - r) : s1;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t m = k + h, d = h ? d1 : d0;
+            if (m >= ndw) continue;
+            const int64_t b0 = (int64_t)4 * m - r;  // source index of the dword's byte 0
+            if (b0 >= 0 && b0 + 4 <= (int64_t)T) {
+                *reinterpret_cast<uint32_t *>(dst + 4u * m) = d;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (b0 + j >= 0 && b0 + j < (int64_t)T) dst[4u * m + j] = (uint8_t)(d >> (8 * j));
+            }
+        }
+    }
 }
-ZC_HD uint64_t fin_block_count(uint64_t nb) {
-    const uint32_t r = fin_run(nb);
-    return (nb + r - 1) / r;
-}
-static_assert(kFinRunMax <= 2 * kThreads, "two span counts per thread");
-static_assert(kEncGroups * kFinRunMax <= 4 * kThreads || kEncGroups * kFinRunMin <= kThreads, "group counts");
 
-__device__ __forceinline__ uint32_t ld32_plain(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
-
-// Every block sums the counts of all spans before its run (cached), so blocks
-// never wait for each other; encode_kernel has completed.
-__global__ __launch_bounds__(kThreads) void finalize_kernel(EncArgs args) {
-    __shared__ uint32_t s_pre[kFinRunMax + 1];
-    __shared__ uint32_t s_gc[kEncGroups * kFinRunMax];
-    __shared__ uint32_t s_red[kWaves];
-
+// Finalize role: block jb of a segment completes the run of encoder spans
+// [first, first + count).  It waits for the run's span words, publishes the
+// run total, waits for the totals of every earlier run of the segment (their
+// sum places the run in the zero-point array), writes the run's table entries
+// and moves the staged zero-point bytes to their place.  The last block of
+// the segment also waits until every other block has passed its waits, then
+// writes the header, the final table entry and the stream size.
+__device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t fflat, FinShared &sh) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const uint32_t flat = blockIdx.x;
-    const uint32_t s = find_segment_fin(args, flat);
+    const uint32_t s = find_segment_fin(args, fflat);
     const EncSeg &sg = args.seg[s];
     const uint64_t n = sg.n;
     const Layout L = layout_for(n);
+    const Scratch S = scratch_for(n);
     const uint64_t nb = enc_blocks(n);
+    const uint32_t nf = (uint32_t)fin_blocks(n);
     const uint32_t run = fin_run(nb);
-    const uint32_t first = (flat - sg.fin_begin) * run;
+    const uint32_t jb = fflat - sg.fin_begin;
+    const uint32_t first = jb * run;
     const uint32_t count = (uint32_t)min((uint64_t)run, nb - first);
-    const bool last = (first + count == nb);
+    const bool last = (jb == nf - 1);
+    const Token tok{args.tok_lo, args.tok_hi};
     uint8_t *const out = sg.out;
-    const uint8_t *const scratch = out + L.off_scratch;
-    const uint8_t *const slots = scratch + scratch_counts_bytes(n);
-    const uint32_t *const counts = reinterpret_cast<const uint32_t *>(scratch);
+    uint8_t *const scratch = out + L.off_scratch;
     uint32_t *const tab = reinterpret_cast<uint32_t *>(out + L.off_tab);
+    static_assert(kFinRunMax <= 2 * kThreads, "two spans per thread");
+    static_assert(kFinMaxBlocks <= 4 * kThreads, "four earlier runs per thread");
 
-    // ---- first round of loads: counts before the run, the run's counts and
-    // its groups' counts
-    uint32_t acc = 0;
-    {
-        const uint4 *c4 = reinterpret_cast<const uint4 *>(counts);
-        for (uint32_t i = tid; 4 * i + 4 <= first; i += kThreads) {
-            const uint4 w = c4[i];
-            acc += w.x + w.y + w.z + w.w;
-        }
-        if ((uint32_t)tid < (first & 3u)) acc += counts[(first & ~3u) + tid];
-    }
-    const uint32_t own0 = (uint32_t)(2 * tid) < count ? counts[first + 2 * tid] : 0u;
-    const uint32_t own1 = (uint32_t)(2 * tid + 1) < count ? counts[first + 2 * tid + 1] : 0u;
-    const uint32_t ngr = count * kEncGroups;
-    for (uint32_t q = tid; q < ngr; q += kThreads) {
-        const uint64_t g = (uint64_t)first * kEncGroups + q;
-        s_gc[q] = g < L.groups ? tab[g] : 0u;
-    }
-
-    // ---- exclusive prefixes of the run's spans (block reduce + block scan)
-    {
-        const uint32_t pair = own0 + own1;
+    bool ok = true;
+    // ---- the run's span words (thread tid: spans 2 tid, 2 tid + 1 of the run)
+    uint32_t sp[2];
+    ok = poll_words<2>(scratch + S.span_words + (uint64_t)kWordBytes * first, count, tok, sp);
+    ok = __syncthreads_and(ok);
+    const uint32_t g00 = sp[0] & 0xFFFFu, g01 = sp[0] >> 16, g10 = sp[1] & 0xFFFFu, g11 = sp[1] >> 16;
+    const uint32_t T0 = g00 + g01, T1 = g10 + g11, pair = T0 + T1;
+    uint32_t ex = 0, A = 0;  // exclusive prefix of the thread's pair inside the run; run total
+    if (ok) {
         const uint32_t inc = wave_inclusive_scan(pair);
-        const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
+        if (lane == kWave - 1) sh.red[wave] = inc;
+        __syncthreads();
+        uint32_t base = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            base += w < wave ? sh.red[w] : 0u;
+            A += sh.red[w];
+        }
+        ex = base + inc - pair;
+        if (tid == 0) put_word(scratch + S.run_words + (uint64_t)kWordBytes * jb, tok, A);
+        if ((uint32_t)(2 * tid) < count) sh.pre[2 * tid] = ex;
+        if ((uint32_t)(2 * tid + 1) < count) sh.pre[2 * tid + 1] = ex + T0;
+        if (tid == 0) sh.pre[count] = A;
+    }
+
+    // ---- totals of the earlier runs (thread tid: runs 4 tid .. 4 tid + 3)
+    uint32_t P = 0;
+    if (ok) {
+        uint32_t rp[4];
+        ok = poll_words<4>(scratch + S.run_words, jb, tok, rp);
+        const uint32_t acc = rp[0] + rp[1] + rp[2] + rp[3];
         const uint32_t wacc = wave_sum(acc);
-        if (lane == 0) s_red[wave] = wacc;
-        __syncthreads();
-        uint32_t base = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-        __syncthreads();
-        if (lane == 0) s_red[wave] = wtot;
-        __syncthreads();
-        for (int w = 0; w < wave; ++w) base += s_red[w];
-        const uint32_t ex = base + inc - pair;
-        if ((uint32_t)(2 * tid) < count) s_pre[2 * tid] = ex;
-        if ((uint32_t)(2 * tid + 1) < count) s_pre[2 * tid + 1] = ex + own0;
-        if ((uint32_t)(2 * tid) < count && (uint32_t)(2 * tid + 2) >= count)
-            s_pre[count] = ex + own0 + ((uint32_t)(2 * tid + 1) < count ? own1 : 0u);
-    }
-    __syncthreads();
-
-    // ---- table: group counts -> zero-points before each group
-    for (uint32_t q = tid; q < ngr; q += kThreads) {
-        const uint64_t g = (uint64_t)first * kEncGroups + q;
-        const uint32_t j = q / kEncGroups;
-        uint32_t before = s_pre[j];
-        for (uint32_t k = j * kEncGroups; k < q; ++k) before += s_gc[k];
-        if (g < L.groups) tab[g] = before;
+        __syncthreads();  // sh.red is reused
+        if (lane == 0) sh.red[wave] = wacc;
+        ok = __syncthreads_and(ok);
+        P = sh.red[0] + sh.red[1] + sh.red[2] + sh.red[3];
     }
 
-    // ---- the run's staged bytes -> the stream.  Wave w copies spans w, w+4,
-    // ...: per span the head bytes up to a 4-byte boundary of the stream, the
-    // whole dwords (two aligned staged words and a funnel shift) and the tail
-    // bytes.  One round of loads covers the first kFinFirstDw dwords, the head
-    // and the tail of every span of the wave; longer spans loop for the rest.
-    uint8_t *const zp = out + L.off_zp;
-    constexpr int kMaxSpansPerWave = kFinRunMin / kWaves;
-    constexpr uint32_t kFinFirstDw = 2 * kWave;
-    const uint32_t my_spans = count > (uint32_t)wave ? (count - wave + kWaves - 1) / kWaves : 0u;
-    uint32_t extra = 0;  // dwords past the first round, longest span of the wave
-    for (uint32_t t0 = 0; t0 < my_spans; t0 += kMaxSpansPerWave) {
-        uint32_t hb[kMaxSpansPerWave], tb[kMaxSpansPerWave], w0[kMaxSpansPerWave], w1[kMaxSpansPerWave];
-#pragma unroll
-        for (int u = 0; u < kMaxSpansPerWave; ++u) {
-            const uint32_t t = t0 + u, j = wave + kWaves * t;
-            hb[u] = tb[u] = w0[u] = w1[u] = 0;
-            if (t < my_spans) {
-                const uint32_t p = s_pre[j], T = s_pre[j + 1] - p;
-                const uint32_t head = min((4u - (p & 3u)) & 3u, T);
-                const uint32_t body = (T - head) / 4, tail0 = head + 4 * body;
-                extra = max(extra, body > kFinFirstDw ? body - kFinFirstDw : 0u);
-                const uint8_t *const src = slots + (uint64_t)(first + j) * kEncSpan;
-                if ((uint32_t)lane < head) hb[u] = src[lane];
-                if ((uint32_t)lane < T - tail0) tb[u] = src[tail0 + lane];
-                const uint32_t sh = head;  // staged offset of dword i is head + 4 i
-                if ((uint32_t)lane < body) {
-                    const uint32_t a = 4u * lane, lo = ld32_plain(src + a);
-                    w0[u] = sh ? __builtin_amdgcn_alignbyte(ld32_plain(src + a + 4), lo, sh) : lo;
-                }
-                if ((uint32_t)lane + kWave < body) {
-                    const uint32_t a = 4u * (lane + kWave), lo = ld32_plain(src + a);
-                    w1[u] = sh ? __builtin_amdgcn_alignbyte(ld32_plain(src + a + 4), lo, sh) : lo;
-                }
-            }
+    if (ok) {
+        // ---- table entries of the run's groups
+        const uint64_t g0 = ((uint64_t)first + 2u * (uint32_t)tid) * kEncGroups;
+        if ((uint32_t)(2 * tid) < count) {
+            if (g0 < L.groups) tab[g0] = P + ex;
+            if (g0 + 1 < L.groups) tab[g0 + 1] = P + ex + g00;
         }
-#pragma unroll
-        for (int u = 0; u < kMaxSpansPerWave; ++u) {
-            const uint32_t t = t0 + u, j = wave + kWaves * t;
-            if (t < my_spans) {
-                const uint32_t p = s_pre[j], T = s_pre[j + 1] - p;
-                const uint32_t head = min((4u - (p & 3u)) & 3u, T);
-                const uint32_t body = (T - head) / 4, tail0 = head + 4 * body;
-                uint8_t *const d = zp + p;
-                if ((uint32_t)lane < head) d[lane] = (uint8_t)hb[u];
-                if ((uint32_t)lane < T - tail0) d[tail0 + lane] = (uint8_t)tb[u];
-                if ((uint32_t)lane < body) *reinterpret_cast<uint32_t *>(d + head + 4u * lane) = w0[u];
-                if ((uint32_t)lane + kWave < body) *reinterpret_cast<uint32_t *>(d + head + 4u * (lane + kWave)) = w1[u];
-            }
+        if ((uint32_t)(2 * tid + 1) < count) {
+            if (g0 + 2 < L.groups) tab[g0 + 2] = P + ex + T0;
+            if (g0 + 3 < L.groups) tab[g0 + 3] = P + ex + T0 + g10;
+        }
+        // ---- staged bytes -> the zero-point array: wave w moves spans w, w + 4, ...
+        uint8_t *const zp = out + L.off_zp;
+        const uint8_t *const slots = scratch + S.staging;
+        for (uint32_t j = wave; j < count; j += kWaves) {
+            const uint32_t p = sh.pre[j], T = sh.pre[j + 1] - p;
+            copy_span(zp, (uint64_t)P + p, slots + (uint64_t)(first + j) * kEncSpan, T, lane);
         }
     }
-    for (uint32_t r = 0; r * kWave < extra; ++r) {
-        for (uint32_t t0 = 0; t0 < my_spans; t0 += kMaxSpansPerWave) {
-            uint32_t word[kMaxSpansPerWave];
-#pragma unroll
-            for (int u = 0; u < kMaxSpansPerWave; ++u) {
-                const uint32_t t = t0 + u;
-                word[u] = 0;
-                if (t < my_spans) {
-                    const uint32_t j = wave + kWaves * t;
-                    const uint32_t p = s_pre[j], T = s_pre[j + 1] - p;
-                    const uint32_t head = min((4u - (p & 3u)) & 3u, T);
-                    const uint32_t body = (T - head) / 4;
-                    const uint32_t i = kFinFirstDw + r * kWave + lane;
-                    if (i < body) {
-                        const uint8_t *const src = slots + (uint64_t)(first + j) * kEncSpan;
-                        const uint32_t a = 4 * i, lo = ld32_plain(src + a);
-                        word[u] = head ? __builtin_amdgcn_alignbyte(ld32_plain(src + a + 4), lo, head) : lo;
-                    }
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kMaxSpansPerWave; ++u) {
-                const uint32_t t = t0 + u;
-                if (t < my_spans) {
-                    const uint32_t j = wave + kWaves * t;
-                    const uint32_t p = s_pre[j], T = s_pre[j + 1] - p;
-                    const uint32_t head = min((4u - (p & 3u)) & 3u, T);
-                    const uint32_t body = (T - head) / 4;
-                    const uint32_t i = kFinFirstDw + r * kWave + lane;
-                    if (i < body) *reinterpret_cast<uint32_t *>(zp + (uint64_t)p + head + 4 * i) = word[u];
-                }
-            }
-        }
-    }
-    const uint32_t P1 = s_pre[count];
-    if (last && tid == 0) tab[L.groups] = P1;
 
-    // ---- the last block of the segment writes the header and the size
-    if (last) {
-        const uint64_t total = L.off_zp + P1;
-        if (tid < 32) {
-            uint32_t w = 0;
-            switch (tid) {
-                case 0: w = kMagic; break;
-                case 1: w = (uint32_t)kVersion | (kHeaderBytes << 16); break;
-                case 2: w = (uint32_t)n; break;
-                case 3: w = (uint32_t)(n >> 32); break;
-                case 4: w = kGroup; break;
-                case 5: w = (uint32_t)L.groups; break;
-                case 6: w = sg.exps[0] | (sg.exps[1] << 8) | (sg.exps[2] << 16) | ((uint32_t)sg.exps[3] << 24); break;
-                case 7: w = sg.exps[4] | (sg.exps[5] << 8) | (sg.exps[6] << 16); break;
-                case 8: w = P1; break;
-                case 10: w = (uint32_t)total; break;
-                case 11: w = (uint32_t)(total >> 32); break;
-                default: break;
-            }
-            reinterpret_cast<uint32_t *>(out)[tid] = w;
-        }
-        if (tid == 0 && sg.out_bytes) *sg.out_bytes = total;
+    if (!last) {
+        if (ok && tid == 0) put_word(scratch + S.done_words + (uint64_t)kWordBytes * jb, tok, 1u);
+        return;
     }
+    // ---- last block of the segment: every other block has passed its waits
+    if (ok) {
+        uint32_t dn[4];
+        ok = poll_words<4>(scratch + S.done_words, nf - 1, tok, dn);
+        ok = __syncthreads_and(ok);
+    }
+    const uint32_t E = P + A;
+    const uint64_t total = L.off_zp + E;
+    if (ok && tid == 0) tab[L.groups] = E;
+    if (tid < 32) {
+        uint32_t w = 0;
+        switch (tid) {
+            case 0: w = ok ? kMagic : 0u; break;  // a given-up call leaves a stream every decoder rejects
+            case 1: w = (uint32_t)kVersion | (kHeaderBytes << 16); break;
+            case 2: w = (uint32_t)n; break;
+            case 3: w = (uint32_t)(n >> 32); break;
+            case 4: w = kGroup; break;
+            case 5: w = (uint32_t)L.groups; break;
+            case 6: w = sg.exps[0] | (sg.exps[1] << 8) | (sg.exps[2] << 16) | ((uint32_t)sg.exps[3] << 24); break;
+            case 7: w = sg.exps[4] | (sg.exps[5] << 8) | (sg.exps[6] << 16); break;
+            case 8: w = E; break;
+            case 10: w = (uint32_t)total; break;
+            case 11: w = (uint32_t)(total >> 32); break;
+            default: break;
+        }
+        reinterpret_cast<uint32_t *>(out)[tid] = w;
+    }
+    if (tid == 0 && sg.out_bytes) *sg.out_bytes = ok ? total : 0ull;
+}
+
+__global__ __launch_bounds__(kThreads) void compress_kernel(EncArgs args) {
+    __shared__ CompressShared sh;
+    const uint32_t flat = blockIdx.x;
+    if (flat < args.enc_blocks)
+        encode_span(args, flat, sh.e);
+    else
+        finalize_run(args, flat - args.enc_blocks, sh.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -808,14 +858,34 @@ static zc_status launch_zero(ZeroArgs &z, hipStream_t st) {
 
 extern "C" uint64_t zc_max_compressed_bytes(uint64_t n) {
     if (n > kMaxElems) return 0;
-    return layout_for(n).off_scratch + scratch_bytes(n);
+    return layout_for(n).off_scratch + scratch_for(n).bytes;
+}
+
+// Per-call tokens: splitmix64 (Steele, Lea, Flood, "Fast splittable
+// pseudorandom number generators", 2014) of a process-wide counter whose
+// start is drawn once from the OS entropy source and the clock.  splitmix64 is
+// a bijection, so no two calls of a process share a token.
+static uint64_t splitmix64(uint64_t x) {
+    x += 0x9E3779B97F4A7C15ull;
+    x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+    x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+    return x ^ (x >> 31);
+}
+
+static uint64_t next_token() {
+    static std::atomic<uint64_t> counter{[] {
+        std::random_device rd;
+        const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+        return ((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ splitmix64(t);
+    }()};
+    return splitmix64(counter.fetch_add(1, std::memory_order_relaxed));
 }
 
 extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void *stream) {
     if (!segs || k == 0 || k > ZC_MAX_BATCH) return ZC_ERR_INVALID_ARG;
     EncArgs a;
     std::memset(&a, 0, sizeof(a));
-    uint64_t blocks = 0, fin_blocks = 0;
+    uint64_t blocks = 0, fblocks = 0;
     for (uint32_t i = 0; i < k; ++i) {
         const zc_enc_seg &g = segs[i];
         if (!g.out || g.n > kMaxElems || (g.n && !g.in) || !plan_ok(g.plan)) return ZC_ERR_INVALID_ARG;
@@ -828,21 +898,23 @@ extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void 
         e.out_bytes = reinterpret_cast<unsigned long long *>(g.out_bytes);
         e.n = (uint32_t)g.n;
         e.tile_begin = (uint32_t)blocks;
-        e.fin_begin = (uint32_t)fin_blocks;
+        e.fin_begin = (uint32_t)fblocks;
         std::memcpy(e.exps, g.plan.exps, 7);
         e.mode = (g.plan.exps[0] >= 1 && g.plan.exps[6] - g.plan.exps[0] == 6) ? kModeWindow : kModeTable;
-        const uint64_t nb = enc_blocks(g.n);
-        blocks += nb;
-        fin_blocks += fin_block_count(nb);
-        if (blocks > 0xFFFFFFFFull) return ZC_ERR_INVALID_ARG;
+        blocks += enc_blocks(g.n);
+        fblocks += fin_blocks(g.n);
+        if (blocks + fblocks > 0xFFFFFFFFull) return ZC_ERR_INVALID_ARG;
     }
     a.k = k;
-    a.total_blocks = (uint32_t)blocks;
+    a.enc_blocks = (uint32_t)blocks;
+    const uint64_t tok = next_token();
+    a.tok_lo = (uint32_t)tok;
+    a.tok_hi = (uint32_t)(tok >> 32);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    hipLaunchKernelGGL(encode_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, st, a);
-    if (hipGetLastError() != hipSuccess) return ZC_ERR_HIP;
-    hipLaunchKernelGGL(finalize_kernel, dim3((uint32_t)fin_blocks), dim3(kThreads), 0, st, a);
+    // finalize blocks follow every encoder block: workgroups are dispatched in
+    // index order, so each one they wait for has been dispatched before them
+    hipLaunchKernelGGL(compress_kernel, dim3((uint32_t)(blocks + fblocks)), dim3(kThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
 }
 

@@ -90,12 +90,42 @@ ZC_HD Layout layout_for(uint64_t n) {
     return L;
 }
 
+// Finalize blocks: each one completes a run of consecutive encoder spans.  A
+// run has at least kFinRunMin spans, more when a segment would otherwise need
+// over kFinMaxBlocks finalize blocks.
+constexpr uint32_t kFinRunMin = 32;
+constexpr uint32_t kFinMaxBlocks = 1024;
+ZC_HD uint32_t fin_run(uint64_t nb) {
+    const uint64_t r = (nb + kFinMaxBlocks - 1) / kFinMaxBlocks;
+    return (uint32_t)(r > kFinRunMin ? r : kFinRunMin);
+}
+ZC_HD uint64_t fin_blocks(uint64_t n) {
+    const uint64_t nb = enc_blocks(n);
+    const uint32_t r = fin_run(nb);
+    return (nb + r - 1) / r;
+}
+constexpr uint32_t kFinRunMax = (uint32_t)((((kMaxElems + kEncSpan - 1) / kEncSpan) + kFinMaxBlocks - 1) / kFinMaxBlocks);
+
 // Encoder scratch, at off_scratch (behind the largest possible stream):
-//   [0, 4 NB)                          zero-point count of every encoder span
-//   [A(4 NB), A(4 NB) + NB kEncSpan)   one kEncSpan-byte staging slot per span
-//                                      for its zero-point bytes
-// where NB = enc_blocks(n).  The finalize pass reads both.
-ZC_HD uint64_t scratch_counts_bytes(uint64_t n) { return align128(4 * enc_blocks(n)); }
-ZC_HD uint64_t scratch_bytes(uint64_t n) { return scratch_counts_bytes(n) + enc_blocks(n) * (uint64_t)kEncSpan; }
+//   span words  16 B per encoder span: zero-point counts of its two groups
+//   run words   16 B per finalize block: zero-point total of its run
+//   done words  16 B per finalize block: the block has finished its waits
+//   staging     kEncSpan B per encoder span: its zero-point bytes, in order
+// Every word carries the 64-bit token of the call that wrote it, so words
+// left by an earlier call (or any other old contents) never pass for fresh.
+constexpr uint32_t kWordBytes = 16;
+struct Scratch {
+    uint64_t span_words, run_words, done_words, staging, bytes;  // offsets from off_scratch, total size
+};
+ZC_HD Scratch scratch_for(uint64_t n) {
+    const uint64_t nb = enc_blocks(n), nf = fin_blocks(n);
+    Scratch S;
+    S.span_words = 0;
+    S.run_words = align128(kWordBytes * nb);
+    S.done_words = S.run_words + align128(kWordBytes * nf);
+    S.staging = S.done_words + align128(kWordBytes * nf);
+    S.bytes = S.staging + nb * (uint64_t)kEncSpan;
+    return S;
+}
 
 }  // namespace zc

@@ -112,6 +112,26 @@ def test_batch_equals_single_and_is_deterministic(zc):
             assert np.array_equal(to_host_u16(o[:x.size]), x)
 
 
+def test_output_buffer_reuse_and_old_contents(zc):
+    """Calls in a row into one output buffer that starts with random bytes: the
+    scratch words left behind by earlier calls (or by anything else) must never
+    be taken for the current call's.  Sizes give several finalize blocks."""
+    from gpu_util import slot
+    for n in (300_007, 1_000_003):
+        cap = zc.zc_max_compressed_bytes(n)
+        g = torch.Generator(device="cuda").manual_seed(n)
+        buf = torch.randint(0, 256, (slot(cap),), dtype=torch.uint8, device="cuda", generator=g)
+        size = torch.zeros(1, dtype=torch.int64, device="cuda")
+        for i, (sigma, plan) in enumerate(((0.02, WINDOW_PLAN), (0.16, WINDOW_PLAN), (0.16, WINDOW_PLAN),
+                                           (1e-3, oracle.plan_from_sigma(1e-3)), (0.05, oracle_pins.HAND_PLAN))):
+            x = gaussian(n, sigma, 100 + i)
+            zc.zc_compress(to_device(x), n, plan, buf, cap, size)
+            torch.cuda.synchronize()
+            ref = oracle.encode(x, plan)
+            assert int(size.item()) == ref.size, (n, i)
+            assert np.array_equal(buf[:ref.size].cpu().numpy(), ref), (n, i)
+
+
 def test_decoder_reads_oracle_streams(zc):
     """The GPU decoder on streams written by the oracle (not by the GPU encoder)."""
     for n, plan in ((1_000_003, WINDOW_PLAN), (9000, oracle_pins.HAND_PLAN), (0, WINDOW_PLAN)):
