@@ -49,18 +49,26 @@ struct EncSeg {
     uint8_t *out;
     unsigned long long *out_bytes;
     uint32_t n;
-    uint32_t tile_begin;  // first flat encode block of this segment
-    uint32_t fin_begin;   // first finalize block of this segment (counted from the first finalize block)
     uint8_t exps[7];
     uint8_t mode;  // kModeWindow or kModeTable
 };
-static_assert(sizeof(EncSeg) == 48, "compact kernel arguments");
+static_assert(sizeof(EncSeg) == 40, "compact kernel arguments");
+
+// The compress grid is a sequence of pieces: the encoder blocks of a segment,
+// or its finalize blocks.  A segment's finalize piece always comes after its
+// encoder piece (its blocks wait for those); it is placed once enough later
+// encoder blocks follow that the segment has most likely finished, so that
+// finalize work overlaps the encoding of later segments.
+constexpr uint32_t kMaxPieces = 2 * ZC_MAX_BATCH;
+constexpr uint8_t kPieceFinalize = 0x80;  // piece_info: this bit, plus the segment in bits 0..6
 
 struct EncArgs {
     uint32_t k;
-    uint32_t enc_blocks;  // encoder blocks of all segments; finalize blocks follow them in the grid
+    uint32_t pieces;
     uint32_t tok_lo, tok_hi;  // the call's token (scratch words of other calls never match it)
     EncSeg seg[ZC_MAX_BATCH];
+    uint32_t piece_start[kMaxPieces + 1];  // first grid block of each piece; the last entry is the grid size
+    uint8_t piece_info[kMaxPieces];
 };
 
 struct DecSeg {
@@ -147,18 +155,17 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(v), kWave - 1);
 }
 
-__device__ __forceinline__ uint32_t find_segment_enc(const EncArgs &a, uint32_t flat) {
-    uint32_t s = 0;
-    for (uint32_t i = 1; i < a.k; ++i)
-        if (a.seg[i].tile_begin <= flat) s = i;
-    return s;
-}
-
-__device__ __forceinline__ uint32_t find_segment_fin(const EncArgs &a, uint32_t flat) {
-    uint32_t s = 0;
-    for (uint32_t i = 1; i < a.k; ++i)
-        if (a.seg[i].fin_begin <= flat) s = i;
-    return s;
+// The piece holding grid block `flat` (binary search over the piece starts).
+__device__ __forceinline__ uint32_t find_piece(const EncArgs &a, uint32_t flat) {
+    uint32_t lo = 0, hi = a.pieces - 1;
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1) / 2;
+        if (a.piece_start[mid] <= flat)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
 }
 
 __device__ __forceinline__ uint32_t find_segment_dec(const DecArgs &a, uint32_t flat) {
@@ -271,17 +278,18 @@ __device__ __forceinline__ uint32_t get_staged4(const uint8_t *p) {
 // reach it; the kernel then still ends and the stream is marked invalid.
 constexpr uint32_t kSpinLimit = 1u << 20;
 
-// Thread tid polls words idx(q) = tid * Q + q (q < Q) of a word array while
-// idx < count, until every one carries the token.  Payloads of valid words
-// land in pay[q] (0 for indices at or past count).  Returns false on timeout.
+// Thread tid polls words tid + kThreads q (q < Q) of a word array while the
+// index is below count, until every one carries the token.  Payloads of valid
+// words land in pay[q] (0 for indices at or past count).  Returns false on
+// timeout.
 template <int Q>
 __device__ __forceinline__ bool poll_words(const uint8_t *base, uint32_t count, Token t, uint32_t (&pay)[Q]) {
-    const uint32_t i0 = (uint32_t)threadIdx.x * Q;
+    const uint32_t i0 = threadIdx.x;
     uint32_t pend = 0;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         pay[q] = 0;
-        if (i0 + q < count) pend |= 1u << q;
+        if (i0 + kThreads * q < count) pend |= 1u << q;
     }
     for (uint32_t it = 0; pend; ++it) {
         if (it == kSpinLimit) return false;
@@ -289,7 +297,8 @@ __device__ __forceinline__ bool poll_words(const uint8_t *base, uint32_t count, 
         bool got[Q];
         uint32_t v[Q];
 #pragma unroll
-        for (int q = 0; q < Q; ++q) got[q] = (pend >> q & 1u) && get_word(base + (uint64_t)kWordBytes * (i0 + q), t, v[q]);
+        for (int q = 0; q < Q; ++q)
+            got[q] = (pend >> q & 1u) && get_word(base + (uint64_t)kWordBytes * (i0 + kThreads * q), t, v[q]);
 #pragma unroll
         for (int q = 0; q < Q; ++q)
             if (got[q]) {
@@ -340,9 +349,22 @@ struct EncShared {
     uint32_t wave_total[2][kWaves];
     uint32_t group[kEncGroups];               // zero-points per 4096-value group of the span
 };
+// A finalize block reads the span words of up to kFinWindow spans ending with
+// its own run; older spans of the segment are summed through run totals.
+constexpr uint32_t kFinWindow = 4 * kThreads;
+static_assert(kFinRunMax <= kFinWindow / 2, "the window holds the run and as many spans before it");
+// LDS landing zone of the copy: batches of spans whose staged bytes (rounded
+// up to 16) fit; any single span (at most kEncSpan bytes) does.
+constexpr uint32_t kLandBytes = 12288;
+static_assert(kLandBytes >= kEncSpan, "one span always lands");
 struct FinShared {
-    uint32_t pre[kFinRunMax + 1];  // zero-points of the run before each of its spans
-    uint32_t red[kWaves];
+    union {
+        uint32_t span[kFinWindow];                      // span-word payloads of the window
+        __align__(16) uint8_t land[kLandBytes + 32];    // later: landed staged bytes (+ slack)
+    };
+    uint32_t pre[kFinRunMax + 1];   // zero-points of the run before each of its spans
+    uint32_t land16[kFinRunMax + 1];  // 16-byte units of the run's spans before each span
+    uint32_t red[3][kWaves];
 };
 union CompressShared {
     EncShared e;
@@ -357,11 +379,9 @@ static_assert(kEncGroups == 2, "a span word holds the counts of two groups");
 // and stages the zero-point bytes in LDS.  The span then stores its zero-point
 // bytes to its staging slot, waits until every store of the block has
 // completed and publishes its span word for the finalize blocks.
-__device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t flat, EncShared &sh) {
+__device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uint32_t b, EncShared &sh) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const uint32_t s = find_segment_enc(args, flat);
-    const EncSeg &sg = args.seg[s];
-    const uint32_t b = flat - sg.tile_begin;  // block (span) index inside the segment
+    const EncSeg &sg = args.seg[s];  // b: block (span) index inside the segment
     const uint64_t n = sg.n;
     const Layout L = layout_for(n);
     const uint64_t blocks = enc_blocks(n);
@@ -495,25 +515,39 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t flat, 
                  sh.group[0] | (sh.group[1] << 16));
 }
 
-// Copy of one span's staged zero-point bytes (T bytes, 4-aligned source) to
-// stream offset dst_off (any alignment) by one wave.  Lane l writes
-// destination dwords k and k+1 (k = k0 + 2 l) of the run of dwords that holds
-// the bytes; a destination dword takes source bytes 4k - r .. 4k - r + 3 with
-// r = dst_off mod 4, i.e. a byte-aligned window over source dwords k-1 and k.
-// Dwords shared with the neighbouring spans get byte stores.
-__device__ __forceinline__ void copy_span(uint8_t *zp, uint64_t dst_off, const uint8_t *src, uint32_t T, int lane) {
+// Copy of staged zero-point bytes to the stream, in two phases.  Landing:
+// the staged bytes of a batch of spans come into an LDS landing zone with
+// direct global->LDS loads (16 bytes per lane, agent-scope), so every load of
+// the batch is in flight at once and holds no registers.  Writing: a span's T
+// bytes go to stream offset dst_off (any alignment); they cover destination
+// dwords 0 .. ndw-1 counted from dst_off rounded down to 4, and destination
+// dword k takes source bytes 4k - r .. 4k - r + 3 (r = dst_off mod 4): a
+// byte-aligned window over source dwords k-1 and k of the landed copy.  A wave
+// writes 128 destination dwords per round (lane l: dwords 2l, 2l + 1); dwords
+// shared with the neighbouring spans get byte stores.
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kCachePolicySc1 = 16;  // agent-scope coherence, as the atomics above
+
+__device__ __forceinline__ void land_span(const uint8_t *src, uint32_t units, uint8_t *land, int lane) {
+    for (uint32_t u0 = 0; u0 < units; u0 += kWave) {
+        if (u0 + (uint32_t)lane < units)
+            __builtin_amdgcn_global_load_lds((global_void *)(src + 16u * (u0 + (uint32_t)lane)),
+                                             (lds_void *)(land + 16u * u0), 16, 0, kCachePolicySc1);
+    }
+}
+
+__device__ __forceinline__ void write_span(uint8_t *zp, uint64_t dst_off, const uint8_t *land, uint32_t T, int lane) {
     if (T == 0) return;
     const uint32_t r = (uint32_t)(dst_off & 3u);
     uint8_t *const dst = zp + (dst_off - r);
-    const uint32_t ndw = (r + T + 3) / 4, srcdw = (T + 3) / 4;
-    uint32_t carry = 0;  // source dword k0 - 1
+    const uint32_t ndw = (r + T + 3) / 4;
+    const uint32_t *const w = reinterpret_cast<const uint32_t *>(land);
     for (uint32_t k0 = 0; k0 < ndw; k0 += 2 * kWave) {
         const uint32_t k = k0 + 2u * (uint32_t)lane;
-        const uint32_t s0 = k < srcdw ? get_staged4(src + 4u * k) : 0u;
-        const uint32_t s1 = k + 1 < srcdw ? get_staged4(src + 4u * (k + 1)) : 0u;
-        // source dword k-1: lane l-1's s1 (wave_shr:1); lane 0 keeps `carry`
-        const uint32_t sm1 = (uint32_t)__builtin_amdgcn_update_dpp((int)carry, (int)s1, 0x138, 0xF, 0xF, false);
-        carry = (uint32_t)__builtin_amdgcn_readlane((int)s1, kWave - 1);
+        if (k >= ndw) break;
+        // source dwords k-1 .. k+1 (the landing zone has slack past every span)
+        const uint32_t sm1 = k ? w[k - 1] : 0u, s0 = w[k], s1 = w[k + 1];
         const uint32_t d0 = r ? __builtin_amdgcn_alignbyte(s0, sm1, 4 - r) : s0;
         const uint32_t d1 = r ? __builtin_amdgcn_alignbyte(s1, s0, 4 - r) : s1;
 #pragma unroll
@@ -533,15 +567,17 @@ __device__ __forceinline__ void copy_span(uint8_t *zp, uint64_t dst_off, const u
 }
 
 // Finalize role: block jb of a segment completes the run of encoder spans
-// [first, first + count).  It waits for the run's span words, publishes the
-// run total, waits for the totals of every earlier run of the segment (their
-// sum places the run in the zero-point array), writes the run's table entries
-// and moves the staged zero-point bytes to their place.  The last block of
-// the segment also waits until every other block has passed its waits, then
-// writes the header, the final table entry and the stream size.
-__device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t fflat, FinShared &sh) {
+// [first, first + count).  It waits for the span words of the run and of the
+// spans just before it (the window, up to kFinWindow spans), publishes the run
+// total, and sums the totals of the segment's runs older than the window: the
+// sum places the run in the zero-point array.  It then writes the run's table
+// entries and moves the staged zero-point bytes to their place.  Spans whose
+// encoder blocks finish last are reached through their own span words, never
+// through another finalize block.  The last block of the segment also waits
+// until every other block has passed its waits, then writes the header, the
+// final table entry and the stream size.
+__device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, uint32_t jb, FinShared &sh) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const uint32_t s = find_segment_fin(args, fflat);
     const EncSeg &sg = args.seg[s];
     const uint64_t n = sg.n;
     const Layout L = layout_for(n);
@@ -549,9 +585,12 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t fflat
     const uint64_t nb = enc_blocks(n);
     const uint32_t nf = (uint32_t)fin_blocks(n);
     const uint32_t run = fin_run(nb);
-    const uint32_t jb = fflat - sg.fin_begin;
     const uint32_t first = jb * run;
     const uint32_t count = (uint32_t)min((uint64_t)run, nb - first);
+    const uint32_t end = first + count;
+    const uint32_t wr = end > kFinWindow ? (end - kFinWindow + run - 1) / run : 0u;  // runs read as totals
+    const uint32_t ws = wr * run;                                                   // first span of the window
+    const uint32_t nsw = end - ws, before = first - ws;
     const bool last = (jb == nf - 1);
     const Token tok{args.tok_lo, args.tok_hi};
     uint8_t *const out = sg.out;
@@ -560,47 +599,90 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t fflat
     static_assert(kFinRunMax <= 2 * kThreads, "two spans per thread");
     static_assert(kFinMaxBlocks <= 4 * kThreads, "four earlier runs per thread");
 
-    bool ok = true;
-    // ---- the run's span words (thread tid: spans 2 tid, 2 tid + 1 of the run)
-    uint32_t sp[2];
-    ok = poll_words<2>(scratch + S.span_words + (uint64_t)kWordBytes * first, count, tok, sp);
+    // ---- span words of the window
+    bool ok;
+    {
+        uint32_t sp[4];
+        ok = poll_words<4>(scratch + S.span_words + (uint64_t)kWordBytes * ws, nsw, tok, sp);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if ((uint32_t)tid + kThreads * q < nsw) sh.span[tid + kThreads * q] = sp[q];
+    }
     ok = __syncthreads_and(ok);
-    const uint32_t g00 = sp[0] & 0xFFFFu, g01 = sp[0] >> 16, g10 = sp[1] & 0xFFFFu, g11 = sp[1] >> 16;
-    const uint32_t T0 = g00 + g01, T1 = g10 + g11, pair = T0 + T1;
-    uint32_t ex = 0, A = 0;  // exclusive prefix of the thread's pair inside the run; run total
+
+    // ---- the run (thread tid: its spans 2 tid, 2 tid + 1): exclusive prefixes
+    // of zero-points and of landing units, the run total; the window's spans
+    // before the run: their sum
+    uint32_t g00 = 0, g01 = 0, g10 = 0, g11 = 0, ex = 0, A = 0, P = 0;
     if (ok) {
-        const uint32_t inc = wave_inclusive_scan(pair);
-        if (lane == kWave - 1) sh.red[wave] = inc;
+        if ((uint32_t)(2 * tid) < count) {
+            const uint32_t v = sh.span[before + 2 * tid];
+            g00 = v & 0xFFFFu;
+            g01 = v >> 16;
+        }
+        if ((uint32_t)(2 * tid + 1) < count) {
+            const uint32_t v = sh.span[before + 2 * tid + 1];
+            g10 = v & 0xFFFFu;
+            g11 = v >> 16;
+        }
+        uint32_t acc = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t i = (uint32_t)tid + kThreads * q;
+            if (i < before) acc += (sh.span[i] & 0xFFFFu) + (sh.span[i] >> 16);
+        }
+        const uint32_t T0 = g00 + g01, T1 = g10 + g11, pair = T0 + T1;
+        const uint32_t U0 = (T0 + 15) / 16, upair = U0 + (T1 + 15) / 16;
+        const uint32_t inc = wave_inclusive_scan(pair), uinc = wave_inclusive_scan(upair);
+        const uint32_t wacc = wave_sum(acc);
+        if (lane == kWave - 1) {
+            sh.red[0][wave] = inc;
+            sh.red[2][wave] = uinc;
+        }
+        if (lane == 0) sh.red[1][wave] = wacc;
         __syncthreads();
-        uint32_t base = 0;
+        uint32_t base = 0, ubase = 0, AU = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            base += w < wave ? sh.red[w] : 0u;
-            A += sh.red[w];
+            base += w < wave ? sh.red[0][w] : 0u;
+            ubase += w < wave ? sh.red[2][w] : 0u;
+            A += sh.red[0][w];
+            AU += sh.red[2][w];
+            P += sh.red[1][w];
         }
         ex = base + inc - pair;
+        const uint32_t uex = ubase + uinc - upair;
         if (tid == 0) put_word(scratch + S.run_words + (uint64_t)kWordBytes * jb, tok, A);
-        if ((uint32_t)(2 * tid) < count) sh.pre[2 * tid] = ex;
-        if ((uint32_t)(2 * tid + 1) < count) sh.pre[2 * tid + 1] = ex + T0;
-        if (tid == 0) sh.pre[count] = A;
+        if ((uint32_t)(2 * tid) < count) {
+            sh.pre[2 * tid] = ex;
+            sh.land16[2 * tid] = uex;
+        }
+        if ((uint32_t)(2 * tid + 1) < count) {
+            sh.pre[2 * tid + 1] = ex + T0;
+            sh.land16[2 * tid + 1] = uex + U0;
+        }
+        if (tid == 0) {
+            sh.pre[count] = A;
+            sh.land16[count] = AU;
+        }
     }
 
-    // ---- totals of the earlier runs (thread tid: runs 4 tid .. 4 tid + 3)
-    uint32_t P = 0;
-    if (ok) {
+    // ---- totals of the runs older than the window (segments over kFinWindow spans)
+    if (ok && wr) {
         uint32_t rp[4];
-        ok = poll_words<4>(scratch + S.run_words, jb, tok, rp);
-        const uint32_t acc = rp[0] + rp[1] + rp[2] + rp[3];
-        const uint32_t wacc = wave_sum(acc);
+        ok = poll_words<4>(scratch + S.run_words, wr, tok, rp);
+        const uint32_t wacc = wave_sum(rp[0] + rp[1] + rp[2] + rp[3]);
         __syncthreads();  // sh.red is reused
-        if (lane == 0) sh.red[wave] = wacc;
+        if (lane == 0) sh.red[1][wave] = wacc;
         ok = __syncthreads_and(ok);
-        P = sh.red[0] + sh.red[1] + sh.red[2] + sh.red[3];
+        P += sh.red[1][0] + sh.red[1][1] + sh.red[1][2] + sh.red[1][3];
     }
+    __syncthreads();  // sh.pre, sh.land16 complete; sh.span is no longer read
 
     if (ok) {
         // ---- table entries of the run's groups
         const uint64_t g0 = ((uint64_t)first + 2u * (uint32_t)tid) * kEncGroups;
+        const uint32_t T0 = g00 + g01;
         if ((uint32_t)(2 * tid) < count) {
             if (g0 < L.groups) tab[g0] = P + ex;
             if (g0 + 1 < L.groups) tab[g0 + 1] = P + ex + g00;
@@ -609,12 +691,37 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t fflat
             if (g0 + 2 < L.groups) tab[g0 + 2] = P + ex + T0;
             if (g0 + 3 < L.groups) tab[g0 + 3] = P + ex + T0 + g10;
         }
-        // ---- staged bytes -> the zero-point array: wave w moves spans w, w + 4, ...
+        // ---- staged bytes -> the zero-point array, a batch of spans at a time:
+        // spans [j0, j1) whose landing units fit the zone; wave w lands and
+        // writes spans j0 + w, j0 + w + 4, ...
         uint8_t *const zp = out + L.off_zp;
         const uint8_t *const slots = scratch + S.staging;
-        for (uint32_t j = wave; j < count; j += kWaves) {
-            const uint32_t p = sh.pre[j], T = sh.pre[j + 1] - p;
-            copy_span(zp, (uint64_t)P + p, slots + (uint64_t)(first + j) * kEncSpan, T, lane);
+        const uint32_t Pu = (uint32_t)__builtin_amdgcn_readfirstlane((int)P);
+        for (uint32_t j0 = 0; j0 < count;) {
+            const uint32_t u0 = sh.land16[j0];
+            uint32_t lo = j0 + 1, hi = count;  // largest j1 with land16[j1] - u0 <= kLandBytes / 16
+            while (lo < hi) {
+                const uint32_t mid = (lo + hi + 1) / 2;
+                if (sh.land16[mid] - u0 <= kLandBytes / 16)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            const uint32_t j1 = lo;
+            for (uint32_t j = j0 + wave; j < j1; j += kWaves) {
+                const uint32_t a16 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(sh.land16[j] - u0));
+                const uint32_t units = (uint32_t)__builtin_amdgcn_readfirstlane((int)(sh.land16[j + 1] - sh.land16[j]));
+                land_span(slots + (uint64_t)(first + j) * kEncSpan, units, sh.land + 16u * a16, lane);
+            }
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();  // the batch has landed
+            for (uint32_t j = j0 + wave; j < j1; j += kWaves) {
+                const uint32_t p = (uint32_t)__builtin_amdgcn_readfirstlane((int)sh.pre[j]);
+                const uint32_t T = (uint32_t)__builtin_amdgcn_readfirstlane((int)sh.pre[j + 1]) - p;
+                write_span(zp, (uint64_t)Pu + p, sh.land + 16u * (sh.land16[j] - u0), T, lane);
+            }
+            j0 = j1;
+            if (j0 < count) __syncthreads();  // the landing zone is reused
         }
     }
 
@@ -655,10 +762,12 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t fflat
 __global__ __launch_bounds__(kThreads) void compress_kernel(EncArgs args) {
     __shared__ CompressShared sh;
     const uint32_t flat = blockIdx.x;
-    if (flat < args.enc_blocks)
-        encode_span(args, flat, sh.e);
+    const uint32_t p = find_piece(args, flat);
+    const uint32_t info = args.piece_info[p], idx = flat - args.piece_start[p];
+    if (info & kPieceFinalize)
+        finalize_run(args, info & 0x7Fu, idx, sh.f);
     else
-        finalize_run(args, flat - args.enc_blocks, sh.f);
+        encode_span(args, info, idx, sh.e);
 }
 
 // ---------------------------------------------------------------------------
@@ -881,11 +990,15 @@ static uint64_t next_token() {
     return splitmix64(counter.fetch_add(1, std::memory_order_relaxed));
 }
 
+// A segment's finalize piece goes into the grid once this many encoder blocks
+// have followed its encoder piece (about the number of blocks the device
+// keeps in flight), or at the end of the grid.
+constexpr uint64_t kFinLagBlocks = 2048;
+
 extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void *stream) {
     if (!segs || k == 0 || k > ZC_MAX_BATCH) return ZC_ERR_INVALID_ARG;
     EncArgs a;
     std::memset(&a, 0, sizeof(a));
-    uint64_t blocks = 0, fblocks = 0;
     for (uint32_t i = 0; i < k; ++i) {
         const zc_enc_seg &g = segs[i];
         if (!g.out || g.n > kMaxElems || (g.n && !g.in) || !plan_ok(g.plan)) return ZC_ERR_INVALID_ARG;
@@ -897,24 +1010,45 @@ extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void 
         e.out = static_cast<uint8_t *>(g.out);
         e.out_bytes = reinterpret_cast<unsigned long long *>(g.out_bytes);
         e.n = (uint32_t)g.n;
-        e.tile_begin = (uint32_t)blocks;
-        e.fin_begin = (uint32_t)fblocks;
         std::memcpy(e.exps, g.plan.exps, 7);
         e.mode = (g.plan.exps[0] >= 1 && g.plan.exps[6] - g.plan.exps[0] == 6) ? kModeWindow : kModeTable;
-        blocks += enc_blocks(g.n);
-        fblocks += fin_blocks(g.n);
-        if (blocks + fblocks > 0xFFFFFFFFull) return ZC_ERR_INVALID_ARG;
     }
+    // grid order: encoder pieces in segment order; each finalize piece right
+    // after the first encoder piece that ends kFinLagBlocks or more encoder
+    // blocks past the end of its own segment's encoder piece
+    uint64_t pos = 0, enc_done = 0;
+    uint64_t enc_end[ZC_MAX_BATCH];
+    uint32_t next_fin = 0, np = 0;
+    auto add_piece = [&](uint32_t info, uint64_t blocks) {
+        a.piece_start[np] = (uint32_t)pos;
+        a.piece_info[np] = (uint8_t)info;
+        ++np;
+        pos += blocks;
+    };
+    for (uint32_t i = 0; i < k; ++i) {
+        const uint64_t nb = enc_blocks(segs[i].n);
+        add_piece(i, nb);
+        enc_done += nb;
+        enc_end[i] = enc_done;
+        while (next_fin < i && enc_done - enc_end[next_fin] >= kFinLagBlocks) {
+            add_piece(kPieceFinalize | next_fin, fin_blocks(segs[next_fin].n));
+            ++next_fin;
+        }
+        if (pos > 0xFFFFFFFFull) return ZC_ERR_INVALID_ARG;
+    }
+    for (; next_fin < k; ++next_fin) add_piece(kPieceFinalize | next_fin, fin_blocks(segs[next_fin].n));
+    if (pos > 0xFFFFFFFFull) return ZC_ERR_INVALID_ARG;
+    a.piece_start[np] = (uint32_t)pos;
     a.k = k;
-    a.enc_blocks = (uint32_t)blocks;
+    a.pieces = np;
     const uint64_t tok = next_token();
     a.tok_lo = (uint32_t)tok;
     a.tok_hi = (uint32_t)(tok >> 32);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    // finalize blocks follow every encoder block: workgroups are dispatched in
-    // index order, so each one they wait for has been dispatched before them
-    hipLaunchKernelGGL(compress_kernel, dim3((uint32_t)(blocks + fblocks)), dim3(kThreads), 0, st, a);
+    // every finalize block follows the encoder blocks it waits for: workgroups
+    // are dispatched in index order, so each of those has been dispatched first
+    hipLaunchKernelGGL(compress_kernel, dim3((uint32_t)pos), dim3(kThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
 }
 
