@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["lossless_bf16_exponent_amd/csrc/zc_codec.hip", "lossless_bf16_exponent_amd/csrc/zc_lane.h",
-                  "lossless_bf16_exponent_amd/csrc/zc_format.h"]
+                  "lossless_bf16_exponent_amd/csrc/zc_format.h", "lossless_bf16_exponent_amd/csrc/zc_grid.h"]
 
 
 def kernel_source_hash() -> str:

@@ -36,6 +36,7 @@
 
 #include "zc.h"
 #include "zc_format.h"
+#include "zc_grid.h"
 #include "zc_lane.h"
 
 namespace zc {
@@ -54,13 +55,8 @@ struct EncSeg {
 };
 static_assert(sizeof(EncSeg) == 40, "compact kernel arguments");
 
-// The compress grid is a sequence of pieces: the encoder blocks of a segment,
-// or its finalize blocks.  A segment's finalize piece always comes after its
-// encoder piece (its blocks wait for those); it is placed once enough later
-// encoder blocks follow that the segment has most likely finished, so that
-// finalize work overlaps the encoding of later segments.
-constexpr uint32_t kMaxPieces = 2 * ZC_MAX_BATCH;
-constexpr uint8_t kPieceFinalize = 0x80;  // piece_info: this bit, plus the segment in bits 0..6
+// The compress grid is a sequence of pieces (zc_grid.h).
+static_assert(kMaxSegments == ZC_MAX_BATCH, "one segment per batch entry");
 
 struct EncArgs {
     uint32_t k;
@@ -990,11 +986,6 @@ static uint64_t next_token() {
     return splitmix64(counter.fetch_add(1, std::memory_order_relaxed));
 }
 
-// A segment's finalize piece goes into the grid once this many encoder blocks
-// have followed its encoder piece (about the number of blocks the device
-// keeps in flight), or at the end of the grid.
-constexpr uint64_t kFinLagBlocks = 2048;
-
 extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void *stream) {
     if (!segs || k == 0 || k > ZC_MAX_BATCH) return ZC_ERR_INVALID_ARG;
     EncArgs a;
@@ -1013,32 +1004,14 @@ extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void 
         std::memcpy(e.exps, g.plan.exps, 7);
         e.mode = (g.plan.exps[0] >= 1 && g.plan.exps[6] - g.plan.exps[0] == 6) ? kModeWindow : kModeTable;
     }
-    // grid order: encoder pieces in segment order; each finalize piece right
-    // after the first encoder piece that ends kFinLagBlocks or more encoder
-    // blocks past the end of its own segment's encoder piece
-    uint64_t pos = 0, enc_done = 0;
-    uint64_t enc_end[ZC_MAX_BATCH];
-    uint32_t next_fin = 0, np = 0;
-    auto add_piece = [&](uint32_t info, uint64_t blocks) {
-        a.piece_start[np] = (uint32_t)pos;
-        a.piece_info[np] = (uint8_t)info;
-        ++np;
-        pos += blocks;
-    };
-    for (uint32_t i = 0; i < k; ++i) {
-        const uint64_t nb = enc_blocks(segs[i].n);
-        add_piece(i, nb);
-        enc_done += nb;
-        enc_end[i] = enc_done;
-        while (next_fin < i && enc_done - enc_end[next_fin] >= kFinLagBlocks) {
-            add_piece(kPieceFinalize | next_fin, fin_blocks(segs[next_fin].n));
-            ++next_fin;
-        }
-        if (pos > 0xFFFFFFFFull) return ZC_ERR_INVALID_ARG;
-    }
-    for (; next_fin < k; ++next_fin) add_piece(kPieceFinalize | next_fin, fin_blocks(segs[next_fin].n));
-    if (pos > 0xFFFFFFFFull) return ZC_ERR_INVALID_ARG;
-    a.piece_start[np] = (uint32_t)pos;
+    uint64_t ns[ZC_MAX_BATCH];
+    for (uint32_t i = 0; i < k; ++i) ns[i] = segs[i].n;
+    GridPlan grid;
+    if (!plan_grid(ns, k, grid)) return ZC_ERR_INVALID_ARG;
+    std::memcpy(a.piece_start, grid.piece_start, sizeof(a.piece_start));
+    std::memcpy(a.piece_info, grid.piece_info, sizeof(a.piece_info));
+    const uint32_t np = grid.pieces;
+    const uint64_t pos = grid.piece_start[np];
     a.k = k;
     a.pieces = np;
     const uint64_t tok = next_token();

@@ -50,6 +50,15 @@ def test_lane_helpers_selftest(tmp_path):
     assert r.returncode == 0, r.stdout + r.stderr
 
 
+def test_compress_grid_layout_selftest(tmp_path):
+    """Every span and finalize block gets one grid block, after all it waits for."""
+    exe = str(tmp_path / "grid_selftest")
+    subprocess.run([_build.hipcc(), "-O2", "-std=c++17", "-x", "c++", "-I", _build.CSRC,
+                    os.path.join(ROOT, "tests", "grid_selftest.cpp"), "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
 def _near_tie(sigma):
     p = np.sort(oracle.exponent_probabilities(sigma))[::-1]
     return p[6] - p[7] < 1e-12
