@@ -7,7 +7,8 @@ module, built with gcc and loaded with ctypes.
 
 The arithmetic follows the explainer pages of "ZipCCL: Efficient Lossless Data
 Compression of Communication Collectives for Accelerating LLM Training"
-(technical summary, sections 2.A and 2.B); the C file states every step.
+(technical summary, sections 2.A and 2.B, and the local reduction of the
+reduce-scatter path in section 2.D); the C file states every step.
 """
 from __future__ import annotations
 
@@ -62,6 +63,11 @@ class Oracle:
         lib.zco_encode.restype = ctypes.c_int
         lib.zco_decode.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p]
         lib.zco_decode.restype = ctypes.c_int
+        lib.zco_decode_reduce.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_uint64),
+                                          ctypes.c_uint32, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.zco_decode_reduce.restype = ctypes.c_int
+        lib.zco_float_to_bf16.argtypes = [ctypes.c_float]
+        lib.zco_float_to_bf16.restype = ctypes.c_uint16
         self.lib = lib
         self.path = path
 
@@ -114,6 +120,27 @@ class Oracle:
     def decode_into(self, stream: np.ndarray, n: int, out: np.ndarray) -> int:
         return int(self.lib.zco_decode(stream.ctypes.data, stream.size, int(n), out.ctypes.data))
 
+    def decode_reduce(self, streams, n: int, local=None):
+        """(status, BF16 patterns): the float32 sum of local (if given) and the
+        decoded streams, in that order, rounded to BF16 (section 2.D reading)."""
+        streams = [np.ascontiguousarray(s, dtype=np.uint8).reshape(-1) for s in streams]
+        k = len(streams)
+        ptrs = (ctypes.c_void_p * max(k, 1))(*[s.ctypes.data for s in streams])
+        sizes = (ctypes.c_uint64 * max(k, 1))(*[s.size for s in streams])
+        out = np.zeros(max(int(n), 1), dtype=np.uint16)
+        loc = None
+        if local is not None:
+            loc = np.ascontiguousarray(local, dtype=np.uint16).reshape(-1)
+            if loc.size != n:
+                raise ValueError("local has %d values, expected %d" % (loc.size, n))
+        rc = self.lib.zco_decode_reduce(ptrs, sizes, k, int(n), None if loc is None else loc.ctypes.data,
+                                        out.ctypes.data)
+        return int(rc), out[:int(n)]
+
+    def float_to_bf16(self, f: float) -> int:
+        """Nearest BF16 pattern to a float32 value (ties to even; NaN -> 0x7FC0)."""
+        return int(self.lib.zco_float_to_bf16(float(f)))
+
 
 def _plan_buf(exps):
     exps = tuple(int(e) for e in exps)
@@ -162,3 +189,11 @@ def decode(stream, n):
 
 def decode_into(stream, n, out):
     return default().decode_into(stream, n, out)
+
+
+def decode_reduce(streams, n, local=None):
+    return default().decode_reduce(streams, n, local)
+
+
+def float_to_bf16(f):
+    return default().float_to_bf16(f)

@@ -18,7 +18,9 @@
  *     8 bits go to a separate zero-point array (16 -> 11 bits when no value
  *     takes the zero-point path);
  *   - section 2.C: the 3-bit codes are kept as three separate 1-bit arrays and
- *     data blocks are padded to 128-byte boundaries.
+ *     data blocks are padded to 128-byte boundaries;
+ *   - section 2.D: a reduce-scatter may run as a zipped all-to-all followed by
+ *     a local reduction (zco_decode_reduce, at the end of this file).
  * Every step is written as a plain per-element loop in the pages' order; no
  * blocking, fusion or reordering.  Where the pages are silent (which exponent
  * gets which code, bit order in the planes, the header, the table of
@@ -37,6 +39,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ZCO_OK 0
@@ -329,5 +332,71 @@ int zco_decode(const uint8_t *in, uint64_t in_bytes, uint64_t n, uint16_t *x) {
         unsigned mantissa = sm[i] & 0x7Fu;
         x[i] = (uint16_t)((sign << 15) | (exponent << 7) | mantissa);
     }
+    return ZCO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Local reduction of the reduce-scatter path (section 2.D: a reduce-scatter  */
+/* may run as a zipped all-to-all followed by a local reduction)              */
+/* ------------------------------------------------------------------------ */
+/* Readings (the pages name the path only):
+ *   - each of the k streams carries one peer's BF16 contribution to the same
+ *     n elements; the receiver may also hold its own BF16 contribution
+ *     (`local`, uncompressed, nullable);
+ *   - per element the terms are added in IEEE single precision, in the order
+ *     local, stream 0, stream 1, ..., each addition rounded to nearest-even;
+ *     the first term enters exactly (no 0.0f + term, which would turn -0 into
+ *     +0);
+ *   - the float sum is rounded to BF16, nearest with ties to even; a NaN sum
+ *     becomes the quiet NaN 0x7FC0.
+ * A stream that fails strict decoding fails the whole reduction. */
+
+static float bf16_to_float(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Nearest BF16 to a float: the two candidates are the float truncated to its
+   upper 16 bits and the next BF16 away from zero; halfway goes to the one with
+   an even last mantissa bit.  Overflow past the largest BF16 gives infinity. */
+uint16_t zco_float_to_bf16(float f) {
+    if (isnan(f)) return 0x7FC0u;
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t lower = u >> 16, rest = u & 0xFFFFu;
+    if (rest > 0x8000u || (rest == 0x8000u && (lower & 1u))) lower += 1;
+    return (uint16_t)lower;
+}
+
+int zco_decode_reduce(const uint8_t *const *streams, const uint64_t *in_bytes, uint32_t k, uint64_t n,
+                      const uint16_t *local, uint16_t *out) {
+    if (n > 0xFFFFFFFFull || (k == 0 && !local)) return ZCO_ERR_INVALID_ARG;
+    float *acc = (float *)malloc((n ? n : 1) * sizeof(float));
+    uint16_t *term = (uint16_t *)malloc((n ? n : 1) * sizeof(uint16_t));
+    if (!acc || !term) {
+        free(acc);
+        free(term);
+        return ZCO_ERR_INVALID_ARG;
+    }
+    int first = 1;
+    if (local) {
+        for (uint64_t i = 0; i < n; ++i) acc[i] = bf16_to_float(local[i]);
+        first = 0;
+    }
+    for (uint32_t s = 0; s < k; ++s) {
+        int rc = zco_decode(streams[s], in_bytes[s], n, term);
+        if (rc != ZCO_OK) {
+            free(acc);
+            free(term);
+            return rc;
+        }
+        for (uint64_t i = 0; i < n; ++i) acc[i] = first ? bf16_to_float(term[i]) : acc[i] + bf16_to_float(term[i]);
+        first = 0;
+    }
+    for (uint64_t i = 0; i < n; ++i) out[i] = zco_float_to_bf16(acc[i]);
+    free(acc);
+    free(term);
     return ZCO_OK;
 }

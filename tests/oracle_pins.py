@@ -318,7 +318,137 @@ def pin_strict_decoder(orc) -> None:
         assert orc.decode(bad, n)[0] != 0, pos
 
 
+# --------------------------------------------------------------------------
+# local reduction of the reduce-scatter path (section 2.D; readings in the
+# oracle's C file: float32 sum, local first then the streams in order, first
+# term exact, BF16 round to nearest-even, NaN -> 0x7FC0)
+# --------------------------------------------------------------------------
+
+WINDOW_PLAN = (116, 117, 118, 119, 120, 121, 122)
+
+
+def bf16_value(b) -> np.ndarray:
+    """BF16 patterns -> float64 values (exact: a BF16 is the upper half of a float32)."""
+    return (np.asarray(b, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_pattern(v: float) -> int:
+    """The BF16 pattern of a value that is exactly representable."""
+    u = int(np.array([v], dtype=np.float32).view(np.uint32)[0])
+    assert u & 0xFFFF == 0, v
+    return u >> 16
+
+
+def nearest_bf16_brute(f32_bits: int) -> int:
+    """Nearest BF16 by comparing distances to the two neighbours in float64."""
+    f = float(np.array([f32_bits], dtype=np.uint32).view(np.float32)[0])
+    if f32_bits == 0x7F800000:
+        return 0x7F80                        # infinity is a BF16 already
+    lo = f32_bits >> 16                      # toward zero
+    hi = lo + 1                              # next BF16 away from zero
+    d_lo = abs(f - float(bf16_value([lo])[0]))
+    # past the largest finite BF16 the neighbour is 2^128 as if the exponent
+    # were unbounded (IEEE rounding); choosing it gives infinity, pattern 0x7F80
+    hi_v = float(bf16_value([hi])[0]) if hi < 0x7F80 else 2.0 ** 128
+    d_hi = abs(hi_v - f)
+    if d_lo < d_hi or (d_lo == d_hi and lo % 2 == 0):
+        return lo
+    return hi
+
+
+def pin_float_to_bf16_nearest_even(orc) -> None:
+    g = np.random.default_rng(11)
+    finite = g.integers(0, 0x7F800000, 20000, dtype=np.uint32)
+    ties = (g.integers(0, 0x7F7F, 2000, dtype=np.uint32) << 16) | 0x8000      # exactly halfway
+    near = (g.integers(0, 0x7F7F, 2000, dtype=np.uint32) << 16) | g.choice([0x7FFF, 0x8001, 0x0001, 0xFFFF], 2000)
+    special = np.array([0, 1, 0x7F7FFFFF, 0x7F7F8000, 0x7F7F7FFF, 0x00008000, 0x00018000, 0x3F808000,
+                        0x3F818000, 0x7F800000], dtype=np.uint32)
+    for bits in np.concatenate([finite, ties, near, special]):
+        for sign in (0, 0x80000000):
+            u = int(bits) | sign
+            f = float(np.array([u], dtype=np.uint32).view(np.float32)[0])
+            want = nearest_bf16_brute(int(bits)) | (sign >> 16)
+            assert orc.float_to_bf16(f) == want, (hex(u), hex(orc.float_to_bf16(f)), hex(want))
+    assert orc.float_to_bf16(float("nan")) == 0x7FC0
+
+
+def pin_reduce_single_stream_identity(orc) -> None:
+    """One stream and nothing else: every BF16 pattern comes back, NaNs as 0x7FC0."""
+    x = all_patterns(seed=5)
+    for plan in (WINDOW_PLAN, HAND_PLAN):
+        rc, y = orc.decode_reduce([orc.encode(x, plan)], x.size)
+        assert rc == 0
+        nan = ((x & 0x7F80) == 0x7F80) & ((x & 0x7F) != 0)
+        assert np.array_equal(y[~nan], x[~nan]) and bool((y[nan] == 0x7FC0).all())
+    rc, y = orc.decode_reduce([], x.size, local=x)   # the local contribution alone
+    assert rc == 0 and np.array_equal(y[~nan], x[~nan])
+
+
+def pin_reduce_order_and_signed_zero(orc) -> None:
+    """Cancellations that only the stated order gives: float32 rounds 2^24 + 1 to
+    2^24 (tie to even), so (2^24 + 1) - 2^24 = 0 while 2^24 - 2^24 + 1 = 1."""
+    big, one = bf16_pattern(2.0 ** 24), bf16_pattern(1.0)
+    neg_big = big | 0x8000
+    cases = [
+        # (local, streams, expected value)
+        (None, [big, one, neg_big], 0.0),       # stream order: (2^24 + 1) - 2^24
+        (None, [neg_big, one, big], 1.0),       # -2^24 + 1 is exact in float32, + 2^24 gives 1
+        (one, [big, neg_big], 0.0),             # local first: (1 + 2^24) - 2^24
+        (big, [one, neg_big], 0.0),
+        (None, [0x8000], -0.0), (None, [0x8000, 0x8000], -0.0), (None, [0x8000, 0x0000], 0.0),
+        (0x8000, [0x0000], 0.0), (0x8000, [], -0.0),
+    ]
+    for local, terms, want in cases:
+        streams = [orc.encode(np.array([t], dtype=np.uint16), WINDOW_PLAN) for t in terms]
+        rc, y = orc.decode_reduce(streams, 1, None if local is None else np.array([local], dtype=np.uint16))
+        assert rc == 0
+        got = float(bf16_value(y)[0])
+        assert got == want and np.signbit(got) == np.signbit(want), (local, terms, got, want)
+
+
+def pin_reduce_specials(orc) -> None:
+    inf, one = 0x7F80, bf16_pattern(1.0)
+    cases = [([inf, one], 0x7F80), ([inf, inf | 0x8000], 0x7FC0), ([0x7FC1, one], 0x7FC0),
+             ([bf16_pattern(2.0 ** 127) | 0x7F, bf16_pattern(2.0 ** 127) | 0x7F], 0x7F80)]   # overflow
+    for terms, want in cases:
+        streams = [orc.encode(np.array([t], dtype=np.uint16), HAND_PLAN) for t in terms]
+        rc, y = orc.decode_reduce(streams, 1)
+        assert rc == 0 and int(y[0]) == want, (terms, hex(int(y[0])), hex(want))
+
+
+def pin_reduce_error_bound(orc) -> None:
+    """Seven peers plus the local share of Gaussian gradients: the result is
+    within the float32 summation bound of the exact sum, plus half a BF16 ulp."""
+    g = np.random.default_rng(12)
+    n, k = 20_000, 7
+    xs = [workloads.bf16_bits_from_f32((g.standard_normal(n) * s).astype(np.float32))
+          for s in (1e-3, 2e-3, 5e-4, 1e-2, 3e-3, 1e-3, 7e-3, 2e-3)]
+    local, peers = xs[0], xs[1:]
+    streams = [orc.encode(x, WINDOW_PLAN) for x in peers]
+    rc, y = orc.decode_reduce(streams, n, local)
+    assert rc == 0
+    vals = np.stack([bf16_value(x) for x in xs])
+    exact = vals.sum(axis=0)
+    u = 2.0 ** -24
+    gamma = k * u / (1 - k * u)
+    got = bf16_value(y)
+    ulp = np.abs(got) * 2.0 ** -7 + 2.0 ** -133
+    assert bool((np.abs(got - exact) <= gamma * np.abs(vals).sum(axis=0) + ulp).all())
+    assert np.count_nonzero(got != exact) > 0   # the rounding is real, not a copy
+
+
+def pin_reduce_rejects_corrupt_stream(orc) -> None:
+    x = workloads.bf16_bits_from_f32((np.random.default_rng(13).standard_normal(5000) * 0.02).astype(np.float32))
+    good = orc.encode(x, WINDOW_PLAN)
+    bad = good.copy()
+    bad[0] ^= 1
+    assert orc.decode_reduce([good, bad], x.size)[0] == 4
+    assert orc.decode_reduce([good, good], x.size)[0] == 0
+
+
 ALL_PINS = [pin_probabilities_vs_scipy, pin_probabilities_monte_carlo, pin_plan_values,
             pin_scale_covariance, pin_coverage, pin_histogram_top7, pin_contiguity_exception,
             pin_roundtrip_exhaustive, pin_edge_sizes, pin_eleven_bits, pin_offsets_example,
-            pin_config1_zero_points, pin_strict_decoder]
+            pin_config1_zero_points, pin_strict_decoder,
+            pin_float_to_bf16_nearest_even, pin_reduce_single_stream_identity, pin_reduce_order_and_signed_zero,
+            pin_reduce_specials, pin_reduce_error_bound, pin_reduce_rejects_corrupt_stream]

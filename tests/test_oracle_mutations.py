@@ -46,6 +46,25 @@ MUTATIONS = {
                                  "if (code == 0) zp[zp_count++] = (uint8_t)(exponent ^ 1u);")],
     "mantissa_mask_short": [("unsigned mantissa = v & 0x7Fu;", "unsigned mantissa = v & 0x3Fu;")],
     "sm_section_unaligned": [("L.off_p0 = round_up_128(L.off_sm + n);", "L.off_p0 = L.off_sm + n;")],
+    # local reduction of the reduce-scatter path (section 2.D)
+    "reduce_local_added_last": [
+        ("        for (uint64_t i = 0; i < n; ++i) acc[i] = bf16_to_float(local[i]);\n        first = 0;\n", ""),
+        ("    for (uint64_t i = 0; i < n; ++i) out[i] = zco_float_to_bf16(acc[i]);\n",
+         "    if (local)\n        for (uint64_t i = 0; i < n; ++i)\n"
+         "            acc[i] = first ? bf16_to_float(local[i]) : acc[i] + bf16_to_float(local[i]);\n"
+         "    for (uint64_t i = 0; i < n; ++i) out[i] = zco_float_to_bf16(acc[i]);\n"),
+    ],
+    "reduce_streams_reversed": [("int rc = zco_decode(streams[s], in_bytes[s], n, term);",
+                                 "int rc = zco_decode(streams[k - 1 - s], in_bytes[k - 1 - s], n, term);")],
+    "reduce_accumulates_from_zero": [
+        ("acc[i] = first ? bf16_to_float(term[i]) : acc[i] + bf16_to_float(term[i]);",
+         "acc[i] = (first ? 0.0f : acc[i]) + bf16_to_float(term[i]);")],
+    "reduce_double_accumulator": [("float *acc = (float *)malloc((n ? n : 1) * sizeof(float));",
+                                   "double *acc = (double *)malloc((n ? n : 1) * sizeof(double));")],
+    "bf16_ties_away_from_zero": [("if (rest > 0x8000u || (rest == 0x8000u && (lower & 1u))) lower += 1;",
+                                  "if (rest >= 0x8000u) lower += 1;")],
+    "bf16_truncates": [("if (rest > 0x8000u || (rest == 0x8000u && (lower & 1u))) lower += 1;", "(void)rest;")],
+    "bf16_nan_not_canonical": [("    if (isnan(f)) return 0x7FC0u;\n", "")],
 }
 
 
