@@ -121,6 +121,31 @@ zc_status zc_compress(const void *d_in, uint64_t n, const zc_plan *plan, void *d
 zc_status zc_decompress(const void *d_in, uint64_t in_bytes, uint64_t n, void *d_out,
                         int32_t *d_status, void *stream);
 
+/* Section 2.D, the local reduction of a reduce-scatter that runs as a zipped
+ * all-to-all: each of the k streams (k = 0..ZC_MAX_BATCH) holds one peer's BF16
+ * contribution to the same n elements, compressed by zc_compress; d_local is
+ * the receiver's own contribution, uncompressed.  For every element i,
+ * d_out[i] = BF16 of the float32 sum of d_local[i] (when given) and the k
+ * decoded values, added in that order, each addition rounded to nearest (the
+ * first term enters exactly), the sum rounded to BF16 nearest with ties to
+ * even; a NaN sum gives 0x7FC0.  The result is a pure function of the inputs.
+ *   d_streams, in_bytes  host arrays of k device stream pointers (128-byte
+ *                        aligned) and the bytes readable at each
+ *   k                    0..ZC_MAX_BATCH; 0 needs d_local (it then rounds it)
+ *   n                    element count, 0 .. 2^32-1, the same for every stream
+ *   d_local              device, n BF16 values, 16-byte aligned, nullable
+ *   d_out                device, n BF16 values, 16-byte aligned; may be d_local
+ *                        itself (accumulate in place), no other overlap
+ *   d_status             device int32 (nullable): 0, or ZC_ERR_CORRUPT when a
+ *                        stream fails validation.  A bad header in any stream
+ *                        leaves d_out untouched; a table or plane inconsistency
+ *                        is caught per 8192-element tile, whose output is then
+ *                        unspecified (reads stay inside every stream).
+ * Errors returned: ZC_ERR_INVALID_ARG, ZC_ERR_MISALIGNED, ZC_ERR_CORRUPT (a
+ * stream shorter than any stream of n values can be), ZC_ERR_HIP. */
+zc_status zc_decompress_reduce(const void *const *d_streams, const uint64_t *in_bytes, uint32_t k, uint64_t n,
+                               const void *d_local, void *d_out, int32_t *d_status, void *stream);
+
 /* One message of a batched call.  Field meanings as in zc_compress. */
 typedef struct zc_enc_seg {
     const void *in;

@@ -83,6 +83,21 @@ struct DecArgs {
     DecSeg seg[ZC_MAX_BATCH];
 };
 
+// Local reduction of the reduce-scatter path: k streams of the same n values.
+struct RedStream {
+    const uint8_t *in;
+    uint64_t in_bytes;
+};
+
+struct RedArgs {
+    uint32_t k;
+    uint32_t n;
+    const uint16_t *local;  // nullable
+    uint16_t *out;
+    int32_t *status;        // nullable
+    RedStream s[ZC_MAX_BATCH];
+};
+
 struct ZeroRegion {
     uint32_t *ptr;
     uint64_t words;
@@ -936,7 +951,231 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
     if (bad && tid == 0 && sg.status) atomicMax(sg.status, (int32_t)ZC_ERR_CORRUPT);
 }
 
+// ---------------------------------------------------------------------------
+// local reduction of the reduce-scatter path (section 2.D): decode k streams
+// of the same n values and add them
+// ---------------------------------------------------------------------------
+
+// Header check of one stream against n (the fields every decoder checks); on
+// success the 8-byte code -> exponent table for v_perm and E.
+__device__ __forceinline__ bool stream_header_ok(const uint8_t *in, uint64_t in_bytes, uint64_t n, const Layout &L,
+                                                 uint32_t &tbl_lo, uint32_t &tbl_hi, uint64_t &E) {
+    const uint32_t h6 = ld_u32(in + 24), h7 = ld_u32(in + 28);
+    E = ld_u32(in + 32) | ((uint64_t)ld_u32(in + 36) << 32);
+    const uint64_t total = ld_u32(in + 40) | ((uint64_t)ld_u32(in + 44) << 32);
+    bool ok = ld_u32(in) == kMagic && ld_u32(in + 4) == ((uint32_t)kVersion | (kHeaderBytes << 16)) &&
+              ld_u32(in + 8) == (uint32_t)n && ld_u32(in + 12) == (uint32_t)(n >> 32) && ld_u32(in + 16) == kGroup &&
+              ld_u32(in + 20) == (uint32_t)L.groups && (h7 >> 24) == 0u && E <= n && total == L.off_zp + E &&
+              total <= in_bytes;
+    const uint32_t e[7] = {h6 & 0xFFu, (h6 >> 8) & 0xFFu, (h6 >> 16) & 0xFFu, h6 >> 24,
+                           h7 & 0xFFu, (h7 >> 8) & 0xFFu, (h7 >> 16) & 0xFFu};
+#pragma unroll
+    for (int k = 1; k < 7; ++k) ok = ok && e[k] > e[k - 1];
+#pragma unroll
+    for (int w = 12; w < 32; ++w) ok = ok && ld_u32(in + 4 * w) == 0u;
+    tbl_lo = h6 << 8;
+    tbl_hi = (h6 >> 24) | (h7 << 8);
+    return ok;
+}
+
+// BF16 value pair of a dword -> two floats (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Nearest BF16 to a float, ties to even (the bias 0x7FFF plus the lowest kept
+// bit carries into the kept half exactly when the dropped half is above one
+// half, or equal to it with an odd kept half); a NaN gives 0x7FC0.
+__device__ __forceinline__ uint32_t float_to_bf16(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (f != f) ? 0x7FC0u : ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+struct RedShared {
+    uint32_t planes[kTile / 8];
+    uint32_t zp32[kTile / 4 + 2];  // the tile's zero-point bytes from a dword-aligned start
+    uint32_t wave_total[2][kWaves];
+};
+
+// Decodes tile `t` of one stream into vals (per step: 4 dwords, 8 BF16 values
+// in element order).  Mirrors one sub-tile of decode_kernel.  Sets bad when the
+// table disagrees with the planes (reads stay inside the stream).
+__device__ __forceinline__ void decode_tile(const uint8_t *in, uint64_t n, const Layout &L, uint32_t t, uint32_t tbl_lo,
+                                            uint32_t tbl_hi, uint64_t E, RedShared &sh, uint32_t (&vals)[kSteps][4],
+                                            bool &bad) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const uint64_t tile0 = (uint64_t)t * kTile;
+    uint32_t pw0 = 0, pw1 = 0, pw2 = 0;
+    if (tile0 + 32u * (uint32_t)tid < n) {
+        const uint64_t off = tile0 / 8 + 4u * (uint32_t)tid;
+        pw0 = load_stream4(in + L.off_p0 + off);
+        pw1 = load_stream4(in + L.off_p1 + off);
+        pw2 = load_stream4(in + L.off_p2 + off);
+    }
+    uint32_t sm[kSteps][2];
+#pragma unroll
+    for (int u = 0; u < kSteps; ++u) {
+        const uint64_t base = tile0 + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
+        sm[u][0] = sm[u][1] = 0;
+        if (base < n) {
+            const uint2 v = load_stream8(in + kHeaderBytes + base);
+            sm[u][0] = v.x;
+            sm[u][1] = v.y;
+        }
+    }
+    const uint32_t *tab = reinterpret_cast<const uint32_t *>(in + L.off_tab);
+    uint32_t z[kGroupsPerTile + 1];
+#pragma unroll
+    for (int j = 0; j <= (int)kGroupsPerTile; ++j) {
+        const uint64_t g = (uint64_t)t * kGroupsPerTile + j;
+        z[j] = tab[g <= L.groups ? g : L.groups];
+    }
+    // table consistency; clamp so that every read stays inside the stream
+    const bool last = ((uint64_t)(t + 1) * kTile >= n);
+    if ((t == 0 && z[0] != 0) || (last && z[kGroupsPerTile] != E)) bad = true;
+#pragma unroll
+    for (int j = 0; j <= (int)kGroupsPerTile; ++j) {
+        const uint32_t lo = j ? z[j - 1] : 0u;
+        if (z[j] < lo || z[j] > E) bad = true;
+        z[j] = z[j] < lo ? lo : (z[j] > E ? (uint32_t)E : z[j]);
+    }
+    if (z[kGroupsPerTile] - z[0] > kTile) {
+        bad = true;
+#pragma unroll
+        for (int j = 0; j <= (int)kGroupsPerTile; ++j) z[j] = z[j] - z[0] > kTile ? z[0] + kTile : z[j];
+    }
+    // the tile's zero-point bytes: stream bytes [A0, A1)
+    const uint64_t A0 = L.off_zp + z[0], A1 = L.off_zp + z[kGroupsPerTile];
+    const uint64_t a0 = A0 & ~uint64_t(3), a1 = A1 & ~uint64_t(3);
+    const uint32_t ndw = (uint32_t)((a1 - a0) / 4);
+    for (uint32_t i = tid; i < ndw; i += kThreads) sh.zp32[i] = ld_u32(in + a0 + 4u * i);
+    if (tid == 0 && A1 > a1) {
+        uint32_t w = 0;
+        for (uint32_t i = 0; i < (uint32_t)(A1 - a1); ++i) w |= (uint32_t)in[a1 + i] << (8 * i);
+        sh.zp32[ndw] = w;
+    }
+    const uint8_t *const s_zp = reinterpret_cast<const uint8_t *>(sh.zp32) + (uint32_t)(A0 & 3u);
+    const uint32_t zspan = z[kGroupsPerTile] - z[0];
+    {
+        const uint32_t lo = perm(pw1, pw0, 0x05010400u), hi = perm(pw1, pw0, 0x07030602u);
+        uint4 q;
+        q.x = perm(pw2, lo, 0x0C040100u);
+        q.y = perm(pw2, lo, 0x0C050302u);
+        q.z = perm(pw2, hi, 0x0C060100u);
+        q.w = perm(pw2, hi, 0x0C070302u);
+        reinterpret_cast<uint4 *>(sh.planes)[tid] = q;
+    }
+    __syncthreads();  // sh.planes and sh.zp32
+    uint32_t e[kSteps][2], zmask[kSteps];
+#pragma unroll
+    for (int u = 0; u < kSteps; ++u) {
+        const uint64_t base = tile0 + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
+        const uint32_t vmask = base + 8 <= n ? 0xFFu : (base < n ? (1u << (uint32_t)(n - base)) - 1u : 0u);
+        const uint32_t planes = sh.planes[(wave * kSteps + u) * kWave + lane] & 0x00FFFFFFu;
+        uint32_t c_lo, c_hi;
+        planes_to_codes(planes, c_lo, c_hi);
+        e[u][0] = perm(tbl_hi, tbl_lo, c_lo);
+        e[u][1] = perm(tbl_hi, tbl_lo, c_hi);
+        zmask[u] = zero_point_mask(planes) & vmask;
+    }
+    const TileCounts tc = count_tile(zmask, lane, wave, sh.wave_total[0]);
+    if (tc.tile_total != z[kGroupsPerTile] - z[0] || tc.first_group != z[1] - z[0]) bad = true;
+#pragma unroll
+    for (int u = 0; u < kSteps; ++u) {
+        uint32_t m = zmask[u], r = tc.rank[u];
+        while (m) {
+            const uint32_t k = __builtin_ctz(m);
+            m &= m - 1;
+            const uint32_t v = r < zspan ? (uint32_t)s_zp[r] : 0u;
+            ++r;
+            put_byte8(e[u][0], e[u][1], k, v);
+        }
+        rebuild4(sm[u][0], e[u][0], vals[u][0], vals[u][1]);
+        rebuild4(sm[u][1], e[u][1], vals[u][2], vals[u][3]);
+    }
+    __syncthreads();  // sh is reused by the next stream
+}
+
+// One block per 8192-value tile.  Every block first checks every stream's
+// header, so a bad header anywhere leaves the whole output untouched.  The
+// float32 sums start from the local value (exact) or from the first stream's
+// value (exact), then take the streams in order.
+__global__ __launch_bounds__(kThreads) void reduce_kernel(RedArgs args) {
+    __shared__ RedShared sh;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const uint32_t t = blockIdx.x;
+    const uint64_t n = args.n;
+    const Layout L = layout_for(n);
+
+    bool ok = true;
+    for (uint32_t s = 0; s < args.k; ++s) {
+        uint32_t lo, hi;
+        uint64_t E;
+        ok = ok && stream_header_ok(args.s[s].in, args.s[s].in_bytes, n, L, lo, hi, E);
+    }
+    if (!ok) {
+        if (tid == 0 && args.status) *args.status = ZC_ERR_CORRUPT;
+        return;
+    }
+
+    float acc[kSteps][8];
+    bool have = false;  // uniform
+    if (args.local) {
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            const uint64_t base = (uint64_t)t * kTile + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
+            uint32_t w4[4] = {0, 0, 0, 0};
+            if (base + 8 <= n) {
+                const uint4 v = load_stream16(args.local + base);
+                w4[0] = v.x;
+                w4[1] = v.y;
+                w4[2] = v.z;
+                w4[3] = v.w;
+            } else {
+                for (uint32_t i = 0; base + i < n; ++i) w4[i / 2] |= (uint32_t)args.local[base + i] << (16 * (i % 2));
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[u][2 * j] = bf16_lo(w4[j]);
+                acc[u][2 * j + 1] = bf16_hi(w4[j]);
+            }
+        }
+        have = true;
+    }
+    bool bad = false;
+    for (uint32_t s = 0; s < args.k; ++s) {
+        const uint8_t *const in = args.s[s].in;
+        uint32_t tbl_lo, tbl_hi;
+        uint64_t E;
+        stream_header_ok(in, args.s[s].in_bytes, n, L, tbl_lo, tbl_hi, E);
+        uint32_t vals[kSteps][4];
+        decode_tile(in, n, L, t, tbl_lo, tbl_hi, E, sh, vals, bad);
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float a = bf16_lo(vals[u][j]), b = bf16_hi(vals[u][j]);
+                acc[u][2 * j] = have ? acc[u][2 * j] + a : a;
+                acc[u][2 * j + 1] = have ? acc[u][2 * j + 1] + b : b;
+            }
+        have = true;
+    }
+#pragma unroll
+    for (int u = 0; u < kSteps; ++u) {
+        const uint64_t base = (uint64_t)t * kTile + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = float_to_bf16(acc[u][2 * j]) | (float_to_bf16(acc[u][2 * j + 1]) << 16);
+        if (base + 8 <= n) {
+            store_stream16(args.out + base, o[0], o[1], o[2], o[3]);
+        } else {
+            for (uint32_t i = 0; base + i < n; ++i) args.out[base + i] = (uint16_t)(o[i / 2] >> (16 * (i % 2)));
+        }
+    }
+    if (bad && tid == 0 && args.status) atomicMax(args.status, (int32_t)ZC_ERR_CORRUPT);
+}
+
 }  // namespace zc
+
 
 // ===========================================================================
 // C ABI
@@ -1086,6 +1325,46 @@ extern "C" zc_status zc_decompress(const void *d_in, uint64_t in_bytes, uint64_t
     s.out = d_out;
     s.status = d_status;
     return zc_decompress_batch(&s, 1, stream);
+}
+
+extern "C" zc_status zc_decompress_reduce(const void *const *d_streams, const uint64_t *in_bytes, uint32_t k,
+                                          uint64_t n, const void *d_local, void *d_out, int32_t *d_status,
+                                          void *stream) {
+    if (k > ZC_MAX_BATCH || (k && (!d_streams || !in_bytes)) || (k == 0 && !d_local) || n > kMaxElems ||
+        (n && !d_out))
+        return ZC_ERR_INVALID_ARG;
+    if (((uintptr_t)d_local & 15u) || ((uintptr_t)d_out & 15u) || ((uintptr_t)d_status & 3u))
+        return ZC_ERR_MISALIGNED;
+    RedArgs a;
+    std::memset(&a, 0, sizeof(a));
+    const Layout L = layout_for(n);
+    for (uint32_t i = 0; i < k; ++i) {
+        if (!d_streams[i]) return ZC_ERR_INVALID_ARG;
+        if ((uintptr_t)d_streams[i] & 127u) return ZC_ERR_MISALIGNED;
+        if (in_bytes[i] < L.off_zp) return ZC_ERR_CORRUPT;  // no stream of n values is this short
+        a.s[i].in = static_cast<const uint8_t *>(d_streams[i]);
+        a.s[i].in_bytes = in_bytes[i];
+    }
+    a.k = k;
+    a.n = (uint32_t)n;
+    a.local = static_cast<const uint16_t *>(d_local);
+    a.out = static_cast<uint16_t *>(d_out);
+    a.status = d_status;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (d_status) {
+        ZeroArgs z;
+        std::memset(&z, 0, sizeof(z));
+        z.count = 1;
+        z.r[0].ptr = reinterpret_cast<uint32_t *>(d_status);
+        z.r[0].words = 1;
+        const zc_status rc = launch_zero(z, st);
+        if (rc != ZC_OK) return rc;
+    }
+    // n = 0 still runs one block: every header is checked, nothing is written
+    const uint64_t blocks = n ? (n + kTile - 1) / kTile : 1;
+    hipLaunchKernelGGL(reduce_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, st, a);
+    return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
 }
 
 static uint32_t rd32(const uint8_t *p) {

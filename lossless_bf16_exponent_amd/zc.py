@@ -60,13 +60,18 @@ _lib.zc_compress_batch.argtypes = [ctypes.POINTER(zc_enc_seg), ctypes.c_uint32, 
 _lib.zc_compress_batch.restype = ctypes.c_int
 _lib.zc_decompress_batch.argtypes = [ctypes.POINTER(zc_dec_seg), ctypes.c_uint32, ctypes.c_void_p]
 _lib.zc_decompress_batch.restype = ctypes.c_int
+_lib.zc_decompress_reduce.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_uint64),
+                                     ctypes.c_uint32, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+_lib.zc_decompress_reduce.restype = ctypes.c_int
 _lib.zc_read_header.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(zc_stream_info)]
 _lib.zc_read_header.restype = ctypes.c_int
 _lib.zc_status_string.argtypes = [ctypes.c_int]
 _lib.zc_status_string.restype = ctypes.c_char_p
 
 EXPORTED = ("zc_plan_from_sigma", "zc_max_compressed_bytes", "zc_compress", "zc_decompress",
-            "zc_compress_batch", "zc_decompress_batch", "zc_read_header", "zc_status_string")
+            "zc_compress_batch", "zc_decompress_batch", "zc_decompress_reduce", "zc_read_header",
+            "zc_status_string")
 
 
 class ZcError(RuntimeError):
@@ -129,6 +134,16 @@ def zc_compress(d_in, n, plan, d_out, out_capacity, d_out_bytes=None, stream=Non
 def zc_decompress(d_in, in_bytes, n, d_out, d_status=None, stream=None) -> None:
     _check(_lib.zc_decompress(_ptr(d_in), int(in_bytes), int(n), _ptr(d_out), _ptr(d_status),
                               _stream(stream)), "zc_decompress")
+
+
+def zc_decompress_reduce(d_streams, in_bytes, n, d_local, d_out, d_status=None, stream=None) -> None:
+    """d_streams / in_bytes: sequences of k stream pointers and their readable sizes."""
+    d_streams, in_bytes = list(d_streams), list(in_bytes)
+    k = len(d_streams)
+    ptrs = (ctypes.c_void_p * max(1, k))(*[_ptr(p) for p in d_streams])
+    sizes = (ctypes.c_uint64 * max(1, k))(*[int(b) for b in in_bytes])
+    _check(_lib.zc_decompress_reduce(ptrs, sizes, k, int(n), _ptr(d_local), _ptr(d_out), _ptr(d_status),
+                                     _stream(stream)), "zc_decompress_reduce")
 
 
 def make_enc_segs(segs) -> ctypes.Array:
