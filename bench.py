@@ -104,6 +104,50 @@ def cpu_baseline(w, plans, max_segments: int, min_seconds: float = 10.0, max_pas
             "seconds": round(t_enc + t_dec, 3)}
 
 
+def reduce_measurement(zc, steps: int) -> dict:
+    """The receive side of a reduce-scatter run as a zipped all-to-all (section
+    2.D): one rank's 32 Mi-value shard, compressed contributions of 7 peers
+    plus the local share, reduced by zc_decompress_reduce.  Peer p's values are
+    N(0, sigma_p^2) with sigma_p the first eight layer sigmas of the gradient
+    bucket, each compressed with its own plan.  HIP events around K calls."""
+    import numpy as np
+    import torch
+
+    from lossless_bf16_exponent_amd import workloads
+
+    n, peers = 1 << 25, 7
+    sig = workloads.config3_sigmas()[:peers + 1]
+    g = np.random.default_rng(21)
+    xs = [torch.from_numpy(workloads.bf16_bits_from_f32(g.standard_normal(n).astype(np.float32)
+                                                          * np.float32(s)).view(np.int16)).cuda() for s in sig]
+    cap = zc.zc_max_compressed_bytes(n)
+    bufs = [torch.empty(cap, dtype=torch.uint8, device="cuda") for _ in range(peers)]
+    sizes = torch.zeros(peers, dtype=torch.int64, device="cuda")
+    for p in range(peers):
+        zc.zc_compress(xs[p + 1], n, zc.zc_plan_from_sigma(float(sig[p + 1])), bufs[p], cap, sizes.data_ptr() + 8 * p)
+    torch.cuda.synchronize()
+    totals = [int(v) for v in sizes.cpu()]
+    out = torch.empty(n, dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    ptrs = [b.data_ptr() for b in bufs]
+    for _ in range(3):
+        zc.zc_decompress_reduce(ptrs, totals, n, xs[0], out, None, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        zc.zc_decompress_reduce(ptrs, totals, n, xs[0], out, None, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    alg = sum(totals) + 4 * n  # the peer streams and the local share read, the result written
+    achieved = alg / (ms * 1e-3) / 1e9
+    return {"shard_values": n, "peers": peers, "local": True, "us": round(ms * 1e3, 2),
+            "uncompressed_gbps": round(2.0 * n * (peers + 1) / (ms * 1e-3) / 1e9, 1),
+            "algorithmic_bytes": int(alg), "achieved_gbps": round(achieved, 1),
+            "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4), "kernel": "reduce_kernel"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +156,7 @@ def main() -> int:
     ap.add_argument("--workload", default="3", help="workload id (1, 2, 3, 4, 5a, 5b); default 3")
     ap.add_argument("--cpu-segments", type=int, default=32, help="segments in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-reduce", action="store_true", help="skip the reduce-scatter receive-side measurement")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -268,6 +313,10 @@ def main() -> int:
         "gpu_step_ms": round(gpu_step_ms, 4),
         "kernel_sha": kernel_source_hash(),
     }
+    if not args.no_reduce:
+        del out, dec
+        torch.cuda.empty_cache()
+        rec["reduce_scatter_local"] = reduce_measurement(zc, args.steps)
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w, plans, args.cpu_segments)
