@@ -787,6 +787,35 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(EncArgs args) {
 
 __device__ __forceinline__ uint32_t ld_u32(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
 
+// Header of a stream of n values: all 32 words load at once (uniform, scalar
+// loads) and every field is tested without short-circuiting, so that no test
+// waits for the one before it (a reduce block checks k headers up front).  On success tbl_lo/tbl_hi hold the code ->
+// exponent table for v_perm (byte 0, code 000, is a placeholder) and E the
+// zero-point count.
+__device__ __forceinline__ bool header_ok(const uint8_t *in, uint64_t in_bytes, uint64_t n, const Layout &L,
+                                          uint32_t &tbl_lo, uint32_t &tbl_hi, uint64_t &E) {
+    uint32_t w[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) w[i] = ld_u32(in + 4 * i);
+    uint32_t pad = 0;
+#pragma unroll
+    for (int i = 12; i < 32; ++i) pad |= w[i];
+    E = w[8] | ((uint64_t)w[9] << 32);
+    const uint64_t total = w[10] | ((uint64_t)w[11] << 32);
+    const uint32_t h6 = w[6], h7 = w[7];
+    const uint32_t e[7] = {h6 & 0xFFu, (h6 >> 8) & 0xFFu, (h6 >> 16) & 0xFFu, h6 >> 24,
+                           h7 & 0xFFu, (h7 >> 8) & 0xFFu, (h7 >> 16) & 0xFFu};
+    bool ok = (w[0] == kMagic) & (w[1] == ((uint32_t)kVersion | (kHeaderBytes << 16))) & (w[2] == (uint32_t)n) &
+              (w[3] == (uint32_t)(n >> 32)) & (w[4] == kGroup) & (w[5] == (uint32_t)L.groups) & ((h7 >> 24) == 0u) &
+              (E <= n) & (total == L.off_zp + E) & (total <= in_bytes) & (pad == 0u);
+#pragma unroll
+    for (int k = 1; k < 7; ++k) ok = ok & (e[k] > e[k - 1]);
+    tbl_lo = h6 << 8;
+    tbl_hi = (h6 >> 24) | (h7 << 8);
+    return ok;
+}
+
+
 // A block decodes kDecSubTiles consecutive tiles (its span).  Every plane and
 // sign+mantissa load of the span, and the span's zero-point table entries,
 // are issued before the header is checked (all of them lie inside the n-value
@@ -843,7 +872,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
         z[j] = tab[g <= L.groups ? g : L.groups];
     }
 
-    // ---- header: every block checks it, so a bad header stops all of them
+    // ---- header: every block checks it, so a bad header stops all of them.
+    // (Tested field by field: this keeps the table entries above on scalar
+    // loads issued with the data loads; the checks overlap those loads.)
     const uint32_t h6 = ld_u32(in + 24), h7 = ld_u32(in + 28);
     const uint64_t E = ld_u32(in + 32) | ((uint64_t)ld_u32(in + 36) << 32);
     const uint64_t total = ld_u32(in + 40) | ((uint64_t)ld_u32(in + 44) << 32);
@@ -955,28 +986,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
 // local reduction of the reduce-scatter path (section 2.D): decode k streams
 // of the same n values and add them
 // ---------------------------------------------------------------------------
-
-// Header check of one stream against n (the fields every decoder checks); on
-// success the 8-byte code -> exponent table for v_perm and E.
-__device__ __forceinline__ bool stream_header_ok(const uint8_t *in, uint64_t in_bytes, uint64_t n, const Layout &L,
-                                                 uint32_t &tbl_lo, uint32_t &tbl_hi, uint64_t &E) {
-    const uint32_t h6 = ld_u32(in + 24), h7 = ld_u32(in + 28);
-    E = ld_u32(in + 32) | ((uint64_t)ld_u32(in + 36) << 32);
-    const uint64_t total = ld_u32(in + 40) | ((uint64_t)ld_u32(in + 44) << 32);
-    bool ok = ld_u32(in) == kMagic && ld_u32(in + 4) == ((uint32_t)kVersion | (kHeaderBytes << 16)) &&
-              ld_u32(in + 8) == (uint32_t)n && ld_u32(in + 12) == (uint32_t)(n >> 32) && ld_u32(in + 16) == kGroup &&
-              ld_u32(in + 20) == (uint32_t)L.groups && (h7 >> 24) == 0u && E <= n && total == L.off_zp + E &&
-              total <= in_bytes;
-    const uint32_t e[7] = {h6 & 0xFFu, (h6 >> 8) & 0xFFu, (h6 >> 16) & 0xFFu, h6 >> 24,
-                           h7 & 0xFFu, (h7 >> 8) & 0xFFu, (h7 >> 16) & 0xFFu};
-#pragma unroll
-    for (int k = 1; k < 7; ++k) ok = ok && e[k] > e[k - 1];
-#pragma unroll
-    for (int w = 12; w < 32; ++w) ok = ok && ld_u32(in + 4 * w) == 0u;
-    tbl_lo = h6 << 8;
-    tbl_hi = (h6 >> 24) | (h7 << 8);
-    return ok;
-}
 
 // BF16 value pair of a dword -> two floats (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -1110,7 +1119,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(RedArgs args) {
     for (uint32_t s = 0; s < args.k; ++s) {
         uint32_t lo, hi;
         uint64_t E;
-        ok = ok && stream_header_ok(args.s[s].in, args.s[s].in_bytes, n, L, lo, hi, E);
+        ok = header_ok(args.s[s].in, args.s[s].in_bytes, n, L, lo, hi, E) & ok;
     }
     if (!ok) {
         if (tid == 0 && args.status) *args.status = ZC_ERR_CORRUPT;
@@ -1146,7 +1155,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(RedArgs args) {
         const uint8_t *const in = args.s[s].in;
         uint32_t tbl_lo, tbl_hi;
         uint64_t E;
-        stream_header_ok(in, args.s[s].in_bytes, n, L, tbl_lo, tbl_hi, E);
+        header_ok(in, args.s[s].in_bytes, n, L, tbl_lo, tbl_hi, E);
         uint32_t vals[kSteps][4];
         decode_tile(in, n, L, t, tbl_lo, tbl_hi, E, sh, vals, bad);
 #pragma unroll
