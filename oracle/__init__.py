@@ -7,8 +7,10 @@ module, built with gcc and loaded with ctypes.
 
 The arithmetic follows the explainer pages of "ZipCCL: Efficient Lossless Data
 Compression of Communication Collectives for Accelerating LLM Training"
-(technical summary, sections 2.A and 2.B, and the local reduction of the
-reduce-scatter path in section 2.D); the C file states every step.
+(technical summary, sections 2.A and 2.B, the plan variants -- histogram and
+sigma estimate -- that section 2.A contrasts with the closed form, and the
+local reduction of the reduce-scatter path in section 2.D); the C file states
+every step.
 """
 from __future__ import annotations
 
@@ -68,6 +70,12 @@ class Oracle:
         lib.zco_decode_reduce.restype = ctypes.c_int
         lib.zco_float_to_bf16.argtypes = [ctypes.c_float]
         lib.zco_float_to_bf16.restype = ctypes.c_uint16
+        lib.zco_exponent_histogram.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)]
+        lib.zco_exponent_histogram.restype = None
+        lib.zco_plan_from_histogram.argtypes = [ctypes.POINTER(ctypes.c_uint64), u8p]
+        lib.zco_plan_from_histogram.restype = ctypes.c_int
+        lib.zco_estimate_sigma.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)]
+        lib.zco_estimate_sigma.restype = ctypes.c_double
         self.lib = lib
         self.path = path
 
@@ -137,6 +145,26 @@ class Oracle:
                                         out.ctypes.data)
         return int(rc), out[:int(n)]
 
+    def exponent_histogram(self, x: np.ndarray) -> np.ndarray:
+        """Count of every BF16 exponent field (0..255) among the patterns x."""
+        x = np.ascontiguousarray(x, dtype=np.uint16).reshape(-1)
+        h = (ctypes.c_uint64 * 256)()
+        self.lib.zco_exponent_histogram(x.ctypes.data, x.size, h)
+        return np.array(h[:], dtype=np.uint64)
+
+    def plan_from_histogram(self, hist) -> tuple:
+        """The seven most frequent exponent fields, ascending (ties to the smaller)."""
+        h = (ctypes.c_uint64 * 256)(*[int(v) for v in hist])
+        buf = (ctypes.c_uint8 * 7)()
+        self.lib.zco_plan_from_histogram(h, buf)
+        return tuple(int(v) for v in buf)
+
+    def estimate_sigma(self, x: np.ndarray):
+        """(sigma, finite count): root mean square of the finite BF16 values."""
+        x = np.ascontiguousarray(x, dtype=np.uint16).reshape(-1)
+        m = ctypes.c_uint64(0)
+        return float(self.lib.zco_estimate_sigma(x.ctypes.data, x.size, ctypes.byref(m))), int(m.value)
+
     def float_to_bf16(self, f: float) -> int:
         """Nearest BF16 pattern to a float32 value (ties to even; NaN -> 0x7FC0)."""
         return int(self.lib.zco_float_to_bf16(float(f)))
@@ -197,3 +225,15 @@ def decode_reduce(streams, n, local=None):
 
 def float_to_bf16(f):
     return default().float_to_bf16(f)
+
+
+def exponent_histogram(x):
+    return default().exponent_histogram(x)
+
+
+def plan_from_histogram(hist):
+    return default().plan_from_histogram(hist)
+
+
+def estimate_sigma(x):
+    return default().estimate_sigma(x)

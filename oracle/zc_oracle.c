@@ -20,12 +20,15 @@
  *   - section 2.C: the 3-bit codes are kept as three separate 1-bit arrays and
  *     data blocks are padded to 128-byte boundaries;
  *   - section 2.D: a reduce-scatter may run as a zipped all-to-all followed by
- *     a local reduction (zco_decode_reduce, at the end of this file).
+ *     a local reduction (zco_decode_reduce);
+ *   - the online statistics that section 2.A avoids, for comparison: the
+ *     exponent histogram with its top-7 plan, and a sigma estimate
+ *     (zco_exponent_histogram, zco_plan_from_histogram, zco_estimate_sigma,
+ *     at the end of this file).
  * Every step is written as a plain per-element loop in the pages' order; no
  * blocking, fusion or reordering.  Where the pages are silent (which exponent
  * gets which code, bit order in the planes, the header, the table of
- * zero-point offsets) the readings used are listed in the design doc and repeated
- * at the point of use below.
+ * zero-point offsets) the reading used is stated at the point of use below.
  *
  * Byte layout of one compressed stream (all integers little-endian, every
  * section starts on a 128-byte boundary, every pad byte is zero):
@@ -107,14 +110,11 @@ int zco_exponent_probabilities(double sigma, double p[256]) {
 }
 
 /*
- * The 7 most probable exponents, returned in ascending order.  Ties between
- * equal probabilities go to the smaller exponent.  Code k (1..7) stands for
- * exps[k-1].
+ * The 7 exponent fields of largest weight w[e], returned in ascending order.
+ * Ties between equal weights go to the smaller field.  Code k (1..7) stands
+ * for exps[k-1].
  */
-int zco_plan_from_sigma(double sigma, uint8_t exps[7]) {
-    double p[256];
-    int rc = zco_exponent_probabilities(sigma, p);
-    if (rc != ZCO_OK) return rc;
+static void top7_ascending(const double w[256], uint8_t exps[7]) {
     int taken[256];
     memset(taken, 0, sizeof(taken));
     int chosen[7];
@@ -122,7 +122,7 @@ int zco_plan_from_sigma(double sigma, uint8_t exps[7]) {
         int best = -1;
         for (int e = 0; e < 256; ++e) {
             if (taken[e]) continue;
-            if (best < 0 || p[e] > p[best]) best = e; /* strict '>' keeps the smaller e on ties */
+            if (best < 0 || w[e] > w[best]) best = e; /* strict '>' keeps the smaller e on ties */
         }
         taken[best] = 1;
         chosen[k] = best;
@@ -137,6 +137,14 @@ int zco_plan_from_sigma(double sigma, uint8_t exps[7]) {
         chosen[j + 1] = v;
     }
     for (int k = 0; k < 7; ++k) exps[k] = (uint8_t)chosen[k];
+}
+
+/* The 7 most probable exponents of N(0, sigma^2) (section 2.A). */
+int zco_plan_from_sigma(double sigma, uint8_t exps[7]) {
+    double p[256];
+    int rc = zco_exponent_probabilities(sigma, p);
+    if (rc != ZCO_OK) return rc;
+    top7_ascending(p, exps);
     return ZCO_OK;
 }
 
@@ -399,4 +407,44 @@ int zco_decode_reduce(const uint8_t *const *streams, const uint64_t *in_bytes, u
     free(acc);
     free(term);
     return ZCO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Plan variants (section 2.A: the table of seven comes from sigma "instead   */
+/* of costly online histogram construction or sorting"; both routes are      */
+/* written out here so that they can be compared)                             */
+/* ------------------------------------------------------------------------ */
+
+/* Count of every exponent field in x. */
+void zco_exponent_histogram(const uint16_t *x, uint64_t n, uint64_t hist[256]) {
+    for (int e = 0; e < 256; ++e) hist[e] = 0;
+    for (uint64_t i = 0; i < n; ++i) hist[(x[i] >> 7) & 0xFFu] += 1;
+}
+
+/* The seven most frequent exponent fields, ascending; equal counts go to the
+   smaller field (so fields that never occur fill up from 0 when fewer than
+   seven occur).  Counts below 2^53 convert to double exactly. */
+int zco_plan_from_histogram(const uint64_t hist[256], uint8_t exps[7]) {
+    double w[256];
+    for (int e = 0; e < 256; ++e) w[e] = (double)hist[e];
+    top7_ascending(w, exps);
+    return ZCO_OK;
+}
+
+/* Sigma of a tensor for the closed-form plan.  Reading: the pages model the
+   values as N(0, sigma^2); the estimate is the root mean square of the finite
+   values (exponent field below 255), i.e. the maximum-likelihood sigma of a
+   zero-mean Gaussian.  Squares of BF16 values are exact in double; the sum is
+   taken in element order.  Returns 0 when no value is finite. */
+double zco_estimate_sigma(const uint16_t *x, uint64_t n, uint64_t *finite) {
+    double sum = 0.0;
+    uint64_t m = 0;
+    for (uint64_t i = 0; i < n; ++i) {
+        if (((x[i] >> 7) & 0xFFu) == 0xFFu) continue;
+        double v = (double)bf16_to_float(x[i]);
+        sum += v * v;
+        m += 1;
+    }
+    if (finite) *finite = m;
+    return m ? sqrt(sum / (double)m) : 0.0;
 }

@@ -18,9 +18,14 @@ Sources of truth used here, none of them the oracle's own code:
     [sections 2.A and 2.B];
   * the invariant that scaling sigma by 2^k shifts every probability by k
     exponents exactly (powers of two scale without rounding);
-  * exhaustive enumeration of all 65,536 BF16 bit patterns.
+  * exhaustive enumeration of all 65,536 BF16 bit patterns;
+  * for the plan variants: numpy's bincount of the exponent fields, exact sums
+    (math.fsum, correctly rounded) for the sigma estimate, and values whose
+    root mean square is exact (powers of two at both ends of the BF16 range).
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 from scipy import special, stats
@@ -446,9 +451,112 @@ def pin_reduce_rejects_corrupt_stream(orc) -> None:
     assert orc.decode_reduce([good, good], x.size)[0] == 0
 
 
+
+# --------------------------------------------------------------------------
+# plan variants: exponent histogram, histogram top-7, sigma estimate
+# (section 2.A contrasts its sigma-derived table with an online histogram)
+# --------------------------------------------------------------------------
+
+def pin_exponent_histogram(orc) -> None:
+    """Every exponent field holds 256 of the 65,536 patterns (1 sign bit and 7
+    mantissa bits); powers of two land on field k + 127; a Gaussian draw agrees
+    with numpy's bincount; an empty input counts nothing."""
+    h = orc.exponent_histogram(np.arange(65536, dtype=np.uint16))
+    assert h.dtype == np.uint64 and (h == 256).all()
+    for k in (-133, -127, -126, -1, 0, 1, 127):
+        b = bf16_pattern(math.ldexp(1.0, k))
+        h = orc.exponent_histogram(np.array([b, b | 0x8000], np.uint16))
+        field = max(k + 127, 0)
+        assert h[field] == 2 and h.sum() == 2, (k, np.nonzero(h))
+    rng = np.random.default_rng(11)
+    x = workloads.bf16_bits_from_f32((rng.standard_normal(200_003) * 0.013).astype(np.float32))
+    x[::997] = rng.integers(0, 65536, x[::997].size)
+    assert (orc.exponent_histogram(x) == np.bincount(exponent_field(x), minlength=256)).all()
+    assert orc.exponent_histogram(np.zeros(0, np.uint16)).sum() == 0
+
+
+def pin_plan_from_histogram(orc) -> None:
+    """Top-7 of counts: the histogram of quantile-stratified Gaussian samples
+    gives the seven most probable fields of N(0, sigma^2) by scipy (away from
+    near-ties), and on counts with many ties the seven largest by (count,
+    smaller field first), ascending."""
+    checked = 0
+    n = 65536
+    q = special.ndtri((np.arange(n) + 0.5) / n)
+    for f in np.arange(0.0, 1.0, 1.0 / 32):
+        for base in (-12.0, -6.0, 0.0):
+            sigma = 2.0 ** (base + f)
+            p = scipy_probabilities(sigma)
+            ref = np.sort(p)[::-1]
+            if ref[6] - ref[7] < 1e-3 + 4.0 / n:
+                continue
+            x = workloads.bf16_bits_from_f32((q * sigma).astype(np.float32))
+            assert orc.plan_from_histogram(orc.exponent_histogram(x)) == top7(p), sigma
+            checked += 1
+    assert checked > 60
+    rng = np.random.default_rng(5)
+    for trial in range(200):
+        hist = rng.integers(0, 4, 256).astype(np.uint64) * rng.integers(1, 3)
+        hist[rng.integers(0, 256, 3)] += np.uint64(1 << 40)  # above 32 bits
+        got = orc.plan_from_histogram(hist)
+        assert got == top7(hist.astype(np.float64)) and list(got) == sorted(got), trial
+    assert orc.plan_from_histogram(np.zeros(256, np.uint64)) == (0, 1, 2, 3, 4, 5, 6)
+    one = np.zeros(256, np.uint64)
+    one[200] = 5
+    assert orc.plan_from_histogram(one) == (0, 1, 2, 3, 4, 5, 200)
+    tied = np.zeros(256, np.uint64)
+    tied[[120, 50, 110, 60, 100, 70, 90, 80]] = 9
+    assert orc.plan_from_histogram(tied) == (50, 60, 70, 80, 90, 100, 110)
+    big = np.zeros(256, np.uint64)
+    big[10] = (1 << 33) + 1
+    big[11:18] = 1 << 33
+    assert orc.plan_from_histogram(big) == (10, 11, 12, 13, 14, 15, 16)
+
+
+def pin_estimate_sigma(orc) -> None:
+    """Root mean square of the finite values: exact where the mean square is a
+    power of two or a single repeated square, sqrt(3) for {1, 2, 2}, NaN and
+    Inf skipped, both ends of the BF16 range without overflow or underflow,
+    and within the sequential-sum bound of math.fsum's correctly rounded sum."""
+    s, m = orc.estimate_sigma(np.zeros(0, np.uint16))
+    assert (s, m) == (0.0, 0)
+    nan, inf = 0x7FC0, 0x7F80
+    s, m = orc.estimate_sigma(np.array([nan, inf, inf | 0x8000, 0x7F81], np.uint16))
+    assert (s, m) == (0.0, 0)
+    one, two = bf16_pattern(1.0), bf16_pattern(2.0)
+    s, m = orc.estimate_sigma(np.array([one, nan, inf, two | 0x8000, inf | 0x8000, two], np.uint16))
+    assert m == 3 and abs(s - math.sqrt(3.0)) <= 2.0 ** -52 * math.sqrt(3.0), s
+    rng = np.random.default_rng(9)
+    for v in (0.75, math.ldexp(1.0, -133), math.ldexp(1.0, -126), math.ldexp(255.0, 120), 1.0):
+        b = bf16_pattern(v)
+        x = np.where(rng.random(1001) < 0.5, b, b | 0x8000).astype(np.uint16)
+        s, m = orc.estimate_sigma(x)
+        assert m == 1001 and s == v, (v, s)
+    # zeros count as finite values
+    s, m = orc.estimate_sigma(np.array([0, 0x8000, one, 0], np.uint16))
+    assert m == 4 and s == 0.5
+    for sigma in (0.013, 3.0e-6):
+        x = workloads.bf16_bits_from_f32((rng.standard_normal(50_001) * sigma).astype(np.float32))
+        x[::1009] = nan
+        fin = x[exponent_field(x) != 255]
+        v = bf16_value(fin).astype(np.float64)
+        exact = math.sqrt(math.fsum(v * v) / v.size)
+        s, m = orc.estimate_sigma(x)
+        assert m == fin.size
+        assert abs(s - exact) <= (v.size + 4) * 2.0 ** -53 * exact, (sigma, s, exact)
+        assert abs(s / sigma - 1.0) < 0.02
+    # quantile-stratified samples: the estimate recovers sigma
+    n = 65536
+    q = special.ndtri((np.arange(n) + 0.5) / n)
+    for sigma in (0.02, 1.7e-3, 250.0):
+        x = workloads.bf16_bits_from_f32((q * sigma).astype(np.float32))
+        s, m = orc.estimate_sigma(x)
+        assert m == n and abs(s / sigma - 1.0) < 2e-3, (sigma, s)
+
 ALL_PINS = [pin_probabilities_vs_scipy, pin_probabilities_monte_carlo, pin_plan_values,
             pin_scale_covariance, pin_coverage, pin_histogram_top7, pin_contiguity_exception,
             pin_roundtrip_exhaustive, pin_edge_sizes, pin_eleven_bits, pin_offsets_example,
             pin_config1_zero_points, pin_strict_decoder,
             pin_float_to_bf16_nearest_even, pin_reduce_single_stream_identity, pin_reduce_order_and_signed_zero,
-            pin_reduce_specials, pin_reduce_error_bound, pin_reduce_rejects_corrupt_stream]
+            pin_reduce_specials, pin_reduce_error_bound, pin_reduce_rejects_corrupt_stream,
+            pin_exponent_histogram, pin_plan_from_histogram, pin_estimate_sigma]

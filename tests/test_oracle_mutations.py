@@ -29,8 +29,8 @@ MUTATIONS = {
         ("if (exps[k] == exponent) code = k + 1;", "if (exps[k] == exponent) code = 7 - k;"),
         ("unsigned exponent = c ? exps[c - 1] : zp[k++];", "unsigned exponent = c ? exps[7 - c] : zp[k++];"),
     ],
-    "tie_break_to_larger_exponent": [("if (best < 0 || p[e] > p[best]) best = e;",
-                                      "if (best < 0 || p[e] >= p[best]) best = e;")],
+    "tie_break_to_larger_exponent": [("if (best < 0 || w[e] > w[best]) best = e;",
+                                      "if (best < 0 || w[e] >= w[best]) best = e;")],
     "missing_sqrt2": [("const double s = sigma * sqrt(2.0);", "const double s = sigma;")],
     "octave_off_by_one": [("double lo = ldexp(1.0, e - 127);", "double lo = ldexp(1.0, e - 128);"),
                           ("double hi = ldexp(1.0, e - 126);", "double hi = ldexp(1.0, e - 127);")],
@@ -65,6 +65,18 @@ MUTATIONS = {
                                   "if (rest >= 0x8000u) lower += 1;")],
     "bf16_truncates": [("if (rest > 0x8000u || (rest == 0x8000u && (lower & 1u))) lower += 1;", "(void)rest;")],
     "bf16_nan_not_canonical": [("    if (isnan(f)) return 0x7FC0u;\n", "")],
+    # plan variants (section 2.A): exponent histogram and sigma estimate
+    "histogram_shift_off_by_one": [("hist[(x[i] >> 7) & 0xFFu] += 1;", "hist[(x[i] >> 8) & 0xFFu] += 1;")],
+    "histogram_plan_unsorted": [("    top7_ascending(w, exps);\n",
+                                 "    top7_ascending(w, exps);\n"
+                                 "    { uint8_t t = exps[0]; for (int k = 0; k < 6; ++k) exps[k] = exps[k + 1]; exps[6] = t; }\n")],
+    "histogram_plan_counts_truncated": [("for (int e = 0; e < 256; ++e) w[e] = (double)hist[e];",
+                                         "for (int e = 0; e < 256; ++e) w[e] = (double)(uint32_t)hist[e];")],
+    "sigma_counts_nonfinite": [("        if (((x[i] >> 7) & 0xFFu) == 0xFFu) continue;\n", "")],
+    "sigma_divides_by_n": [("return m ? sqrt(sum / (double)m) : 0.0;", "return m ? sqrt(sum / (double)n) : 0.0;")],
+    "sigma_float_accumulator": [("    double sum = 0.0;\n    uint64_t m = 0;", "    float sum = 0.0f;\n    uint64_t m = 0;")],
+    "sigma_no_sqrt": [("return m ? sqrt(sum / (double)m) : 0.0;", "return m ? sum / (double)m : 0.0;")],
+    "sigma_abs_not_square": [("        sum += v * v;\n", "        sum += fabs(v);\n")],
 }
 
 
