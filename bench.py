@@ -148,6 +148,66 @@ def reduce_measurement(zc, steps: int) -> dict:
             "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4), "kernel": "reduce_kernel"}
 
 
+def stats_measurement(zc, x, seg_ns, steps: int) -> dict:
+    """The online statistics that section 2.A replaces by its sigma-derived
+    table, on the resident gradient bucket: the exponent histogram and the
+    sigma estimate of the whole buffer (HIP events around K back-to-back
+    calls; algorithmic bytes = the 2n input bytes read), and the wall time of
+    the histogram route to a table for every segment (one histogram per
+    segment, one copy of the counts to the host, host top-7), against the
+    closed-form route (host table from the known sigma)."""
+    import numpy as np
+    import torch
+
+    n = x.numel()
+    ws = torch.empty(zc.zc_stats_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    hist = torch.zeros(256, dtype=torch.int64, device="cuda")
+    sig = torch.zeros(2, dtype=torch.float64, device="cuda")
+    stream = torch.cuda.current_stream()
+    xb = x.data_ptr()
+    hist_call = lambda: zc.zc_exponent_histogram(xb, n, ws, ws.numel(), hist, stream)
+    sig_call = lambda: zc.zc_estimate_sigma(xb, n, ws, ws.numel(), sig.data_ptr(), sig.data_ptr() + 8, stream)
+    out = {"values": n, "kernels": {"histogram": "hist_kernel + hist_sum_kernel",
+                                    "sigma": "sigma_kernel + sigma_final_kernel"}}
+    for name, call in (("histogram", hist_call), ("sigma", sig_call)):
+        for _ in range(3):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        gbps = 2.0 * n / (ms * 1e-3) / 1e9
+        out[name] = {"us": round(ms * 1e3, 2), "achieved_gbps": round(gbps, 1),
+                     "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": 2 * n}
+    if int(hist.sum().item()) != n:
+        raise RuntimeError("histogram does not count every value")
+    out["sigma"]["finite_values"] = int(sig[1:].view(torch.int64).item())
+
+    # the histogram route to one table per segment, host clock
+    offs = np.concatenate([[0], np.cumsum(seg_ns)]).astype(np.int64)
+    hs = torch.zeros((len(seg_ns), 256), dtype=torch.int64, device="cuda")
+    wss = [torch.empty(zc.zc_stats_workspace_bytes(m), dtype=torch.uint8, device="cuda") for m in seg_ns]
+    def route():
+        for i, m in enumerate(seg_ns):
+            zc.zc_exponent_histogram(xb + 2 * int(offs[i]), m, wss[i], wss[i].numel(), hs[i], stream)
+        h = hs.cpu().numpy()
+        return [zc.zc_plan_from_histogram(h[i]) for i in range(len(seg_ns))]
+    route()
+    reps = max(3, min(steps, 20))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        route()
+    out["histogram_route_us_per_bucket"] = round((time.perf_counter() - t0) * 1e6 / reps, 1)
+    out["histogram_route"] = ("%d segment histograms + one copy of the counts to the host + %d host top-7 tables"
+                              % (len(seg_ns), len(seg_ns)))
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +217,7 @@ def main() -> int:
     ap.add_argument("--cpu-segments", type=int, default=32, help="segments in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reduce", action="store_true", help="skip the reduce-scatter receive-side measurement")
+    ap.add_argument("--no-stats", action="store_true", help="skip the histogram / sigma-estimate measurement")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -313,6 +374,9 @@ def main() -> int:
         "gpu_step_ms": round(gpu_step_ms, 4),
         "kernel_sha": kernel_source_hash(),
     }
+    if not args.no_stats:
+        rec["plan_variants"] = stats_measurement(zc, x, ns, args.steps)
+        rec["plan_variants"]["sigma_table_us_per_bucket"] = round(plan_us * len(ns), 2)
     if not args.no_reduce:
         del out, dec
         torch.cuda.empty_cache()

@@ -146,6 +146,40 @@ zc_status zc_decompress(const void *d_in, uint64_t in_bytes, uint64_t n, void *d
 zc_status zc_decompress_reduce(const void *const *d_streams, const uint64_t *in_bytes, uint32_t k, uint64_t n,
                                const void *d_local, void *d_out, int32_t *d_status, void *stream);
 
+/* The online statistics that section 2.A replaces by its sigma-derived table,
+ * for comparison with it and for callers with no trusted sigma.  Both calls
+ * read the n BF16 values once and use a caller-owned device workspace of
+ * zc_stats_workspace_bytes(n) bytes (16-byte aligned; contents unspecified
+ * afterwards; two calls in flight at once need two workspaces).  Errors
+ * returned: ZC_ERR_INVALID_ARG (NULL output or workspace, NULL d_in with
+ * n > 0, n > 2^32-1), ZC_ERR_MISALIGNED (d_in or workspace not 16-byte,
+ * outputs not 8-byte aligned), ZC_ERR_CAPACITY (workspace too small),
+ * ZC_ERR_HIP. */
+uint64_t zc_stats_workspace_bytes(uint64_t n);
+
+/* d_hist (device, 256 u64) receives, for e = 0..255, the number of the n BF16
+ * values whose exponent field (bits 14..7) is e.  Exact for every n. */
+zc_status zc_exponent_histogram(const void *d_in, uint64_t n, void *d_workspace, uint64_t workspace_bytes,
+                                uint64_t *d_hist, void *stream);
+
+/* The table of the seven largest counts of a 256-entry histogram (host
+ * array), ascending; equal counts go to the smaller field, so a histogram with
+ * fewer than seven non-zero fields is filled up with the smallest unused
+ * fields.  Host only, pure.  NULL hist or out gives ZC_ERR_INVALID_ARG. */
+zc_status zc_plan_from_histogram(const uint64_t *hist, zc_plan *out);
+
+/* Sigma for zc_plan_from_sigma: the root mean square of the finite values
+ * (exponent field below 255; zeros count), sqrt(sum x^2 / m), which is the
+ * maximum-likelihood sigma of the zero-mean Gaussian of section 2.A; 0 when no
+ * value is finite.  The squares are exact in float64 and are summed in float64
+ * in an order fixed by n alone (per-thread sums over a fixed grid, then fixed
+ * trees), so the result is reproducible and within (m + 1024) * 2^-53 relative
+ * of the exact root mean square.
+ *   d_sigma   device double, receives sigma
+ *   d_finite  device u64 (nullable), receives m, the count of finite values */
+zc_status zc_estimate_sigma(const void *d_in, uint64_t n, void *d_workspace, uint64_t workspace_bytes,
+                            double *d_sigma, uint64_t *d_finite, void *stream);
+
 /* One message of a batched call.  Field meanings as in zc_compress. */
 typedef struct zc_enc_seg {
     const void *in;

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libzc.so")
-SOURCES = [os.path.join(CSRC, "zc_codec.hip"), os.path.join(CSRC, "zc_plan.cpp")]
+SOURCES = [os.path.join(CSRC, "zc_codec.hip"), os.path.join(CSRC, "zc_stats.hip"), os.path.join(CSRC, "zc_plan.cpp")]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions stay disabled for every HIP translation unit.
@@ -39,10 +39,10 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-def assembly(out_path: str) -> str:
+def assembly(out_path: str, source: str = SOURCES[0]) -> str:
     """Device assembly of the kernels (for inspection of the generated gfx950 code)."""
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC,
-           "--cuda-device-only", "-S", SOURCES[0], "-o", out_path]
+           "--cuda-device-only", "-S", source, "-o", out_path]
     subprocess.run(cmd, check=True)
     return out_path
 

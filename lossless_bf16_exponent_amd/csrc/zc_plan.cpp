@@ -12,6 +12,10 @@
 // half-normal tail Q(a) = P(|X| >= a) = erfc(a / (sigma sqrt 2)), the field
 // probability is Q(2^(e-127)) - Q(2^(e-126)).  The seven most probable fields
 // (ties to the smaller field) form the table, reported in ascending order.
+//
+// zc_plan_from_histogram is the online route the pages avoid: the seven
+// largest counts of a measured exponent histogram, with the same tie rule and
+// order.
 #include <algorithm>
 #include <cmath>
 
@@ -33,6 +37,17 @@ extern "C" zc_status zc_plan_from_sigma(double sigma, zc_plan *out) {
     int order[256];
     for (int e = 0; e < 256; ++e) order[e] = e;
     std::stable_sort(order, order + 256, [&](int a, int b) { return prob[a] > prob[b]; });
+    std::sort(order, order + 7);
+    for (int k = 0; k < 7; ++k) out->exps[k] = static_cast<uint8_t>(order[k]);
+    out->reserved = 0;
+    return ZC_OK;
+}
+
+extern "C" zc_status zc_plan_from_histogram(const uint64_t *hist, zc_plan *out) {
+    if (!hist || !out) return ZC_ERR_INVALID_ARG;
+    int order[256];
+    for (int e = 0; e < 256; ++e) order[e] = e;
+    std::stable_sort(order, order + 256, [&](int a, int b) { return hist[a] > hist[b]; });
     std::sort(order, order + 7);
     for (int k = 0; k < 7; ++k) out->exps[k] = static_cast<uint8_t>(order[k]);
     out->reserved = 0;

@@ -64,6 +64,16 @@ _lib.zc_decompress_reduce.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.PO
                                      ctypes.c_uint32, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p]
 _lib.zc_decompress_reduce.restype = ctypes.c_int
+_lib.zc_stats_workspace_bytes.argtypes = [ctypes.c_uint64]
+_lib.zc_stats_workspace_bytes.restype = ctypes.c_uint64
+_lib.zc_exponent_histogram.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+_lib.zc_exponent_histogram.restype = ctypes.c_int
+_lib.zc_plan_from_histogram.argtypes = [ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(zc_plan)]
+_lib.zc_plan_from_histogram.restype = ctypes.c_int
+_lib.zc_estimate_sigma.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+_lib.zc_estimate_sigma.restype = ctypes.c_int
 _lib.zc_read_header.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(zc_stream_info)]
 _lib.zc_read_header.restype = ctypes.c_int
 _lib.zc_status_string.argtypes = [ctypes.c_int]
@@ -71,7 +81,8 @@ _lib.zc_status_string.restype = ctypes.c_char_p
 
 EXPORTED = ("zc_plan_from_sigma", "zc_max_compressed_bytes", "zc_compress", "zc_decompress",
             "zc_compress_batch", "zc_decompress_batch", "zc_decompress_reduce", "zc_read_header",
-            "zc_status_string")
+            "zc_status_string", "zc_stats_workspace_bytes", "zc_exponent_histogram", "zc_plan_from_histogram",
+            "zc_estimate_sigma")
 
 
 class ZcError(RuntimeError):
@@ -144,6 +155,31 @@ def zc_decompress_reduce(d_streams, in_bytes, n, d_local, d_out, d_status=None, 
     sizes = (ctypes.c_uint64 * max(1, k))(*[int(b) for b in in_bytes])
     _check(_lib.zc_decompress_reduce(ptrs, sizes, k, int(n), _ptr(d_local), _ptr(d_out), _ptr(d_status),
                                      _stream(stream)), "zc_decompress_reduce")
+
+
+def zc_stats_workspace_bytes(n: int) -> int:
+    return int(_lib.zc_stats_workspace_bytes(int(n)))
+
+
+def zc_exponent_histogram(d_in, n, d_workspace, workspace_bytes, d_hist, stream=None) -> None:
+    _check(_lib.zc_exponent_histogram(_ptr(d_in), int(n), _ptr(d_workspace), int(workspace_bytes), _ptr(d_hist),
+                                      _stream(stream)), "zc_exponent_histogram")
+
+
+def zc_plan_from_histogram(hist) -> tuple:
+    """hist: 256 counts (any sequence of non-negative integers) held on the host."""
+    counts = [int(v) for v in hist]
+    if len(counts) != 256:
+        raise ValueError("a histogram has 256 counts")
+    h = (ctypes.c_uint64 * 256)(*counts)
+    p = zc_plan()
+    _check(_lib.zc_plan_from_histogram(h, ctypes.byref(p)), "zc_plan_from_histogram")
+    return tuple(int(v) for v in p.exps)
+
+
+def zc_estimate_sigma(d_in, n, d_workspace, workspace_bytes, d_sigma, d_finite=None, stream=None) -> None:
+    _check(_lib.zc_estimate_sigma(_ptr(d_in), int(n), _ptr(d_workspace), int(workspace_bytes), _ptr(d_sigma),
+                                  _ptr(d_finite), _stream(stream)), "zc_estimate_sigma")
 
 
 def make_enc_segs(segs) -> ctypes.Array:

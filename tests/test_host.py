@@ -1,8 +1,8 @@
 """Host-side checks of the HIP library that need no GPU: it loads and exports
 every entry point of include/zc.h, its sigma plan equals the oracle's, every
 host-detectable error returns its status before anything is enqueued, the
-header parser agrees with oracle streams, and the per-lane bit helpers pass
-their CPU self-test."""
+header parser agrees with oracle streams, the host histogram plan equals the
+oracle's, and the per-lane bit helpers pass their CPU self-test."""
 import ctypes
 import os
 import re
@@ -148,6 +148,41 @@ def test_decompress_host_errors(zc):
     assert st(FAKE_OUT + 16, 1 << 20, n, FAKE_IN, 0, 0) == zc.ZC_ERR_MISALIGNED
     assert st(FAKE_OUT, 1 << 20, n, FAKE_IN + 8, 0, 0) == zc.ZC_ERR_MISALIGNED
     assert st(FAKE_OUT, 1 << 20, n, FAKE_IN, FAKE_IN + 2, 0) == zc.ZC_ERR_MISALIGNED
+
+
+def test_library_histogram_plan_equals_oracle(zc):
+    rng = np.random.default_rng(17)
+    cases = [np.zeros(256, np.uint64), np.full(256, 3, np.uint64)]
+    for trial in range(300):
+        h = rng.integers(0, 5, 256).astype(np.uint64)
+        if trial % 3 == 0:
+            h[rng.integers(0, 256, 9)] += np.uint64(rng.integers(1, 1 << 52))  # the oracle is exact below 2^53
+        cases.append(h)
+    x = workloads.bf16_bits_from_f32((rng.standard_normal(100_000) * 0.02).astype(np.float32))
+    cases.append(oracle.exponent_histogram(x))
+    for h in cases:
+        assert zc.zc_plan_from_histogram(h) == oracle.plan_from_histogram(h)
+    assert zc.raw_status("zc_plan_from_histogram", None, ctypes.byref(zc.zc_plan())) == zc.ZC_ERR_INVALID_ARG
+    assert zc.raw_status("zc_plan_from_histogram", (ctypes.c_uint64 * 256)(), None) == zc.ZC_ERR_INVALID_ARG
+
+
+def test_stats_host_errors(zc):
+    ws = zc.zc_stats_workspace_bytes(1 << 28)
+    assert ws > 0 and zc.zc_stats_workspace_bytes(1 << 32) == 0
+    assert zc.zc_stats_workspace_bytes(0) == ws  # the workspace does not depend on n
+    FAKE_WS, FAKE_H = 0x7F2000000000, 0x7F3000000000
+    for fn, extra in (("zc_exponent_histogram", ()), ("zc_estimate_sigma", (0,))):
+        st = lambda d_in, n, w, wb, out, *more: zc.raw_status(fn, d_in, n, w, wb, out, *(more or extra), 0)
+        assert st(FAKE_IN, 1000, FAKE_WS, ws - 1, FAKE_H) == zc.ZC_ERR_CAPACITY
+        assert st(0, 1000, FAKE_WS, ws, FAKE_H) == zc.ZC_ERR_INVALID_ARG
+        assert st(FAKE_IN, 1000, 0, ws, FAKE_H) == zc.ZC_ERR_INVALID_ARG
+        assert st(FAKE_IN, 1000, FAKE_WS, ws, 0) == zc.ZC_ERR_INVALID_ARG
+        assert st(FAKE_IN, 1 << 32, FAKE_WS, ws, FAKE_H) == zc.ZC_ERR_INVALID_ARG
+        assert st(FAKE_IN + 2, 1000, FAKE_WS, ws, FAKE_H) == zc.ZC_ERR_MISALIGNED
+        assert st(FAKE_IN, 1000, FAKE_WS + 8, ws, FAKE_H) == zc.ZC_ERR_MISALIGNED
+        assert st(FAKE_IN, 1000, FAKE_WS, ws, FAKE_H + 4) == zc.ZC_ERR_MISALIGNED
+    assert zc.raw_status("zc_estimate_sigma", FAKE_IN, 1000, FAKE_WS, ws, FAKE_H, FAKE_H + 12, 0) == \
+        zc.ZC_ERR_MISALIGNED
 
 
 def test_read_header_of_oracle_streams(zc):
