@@ -63,6 +63,8 @@ class Oracle:
         lib.zco_encode.argtypes = [ctypes.c_void_p, ctypes.c_uint64, u8p, ctypes.c_void_p,
                                    ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)]
         lib.zco_encode.restype = ctypes.c_int
+        lib.zco_encode_fallback.argtypes = lib.zco_encode.argtypes
+        lib.zco_encode_fallback.restype = ctypes.c_int
         lib.zco_decode.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p]
         lib.zco_decode.restype = ctypes.c_int
         lib.zco_decode_reduce.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_uint64),
@@ -102,19 +104,20 @@ class Oracle:
     def max_bytes(self, n: int) -> int:
         return int(self.lib.zco_max_bytes(int(n)))
 
-    def encode(self, x: np.ndarray, exps) -> np.ndarray:
-        """Compressed stream (uint8 array of exactly total_bytes) of BF16 patterns x."""
+    def encode(self, x: np.ndarray, exps, raw_fallback: bool = False) -> np.ndarray:
+        """Compressed stream (uint8 array of exactly total_bytes) of BF16 patterns x;
+        with raw_fallback, the raw stream whenever the coded one would be larger."""
         x = np.ascontiguousarray(x, dtype=np.uint16).reshape(-1)
         cap = self.max_bytes(x.size)
         out = np.empty(cap, dtype=np.uint8)
-        total = self.encode_into(x, exps, out)
+        total = self.encode_into(x, exps, out, raw_fallback)
         return out[:total]
 
-    def encode_into(self, x: np.ndarray, exps, out: np.ndarray) -> int:
+    def encode_into(self, x: np.ndarray, exps, out: np.ndarray, raw_fallback: bool = False) -> int:
         """Encode into a caller buffer; returns total bytes."""
         total = ctypes.c_uint64(0)
-        rc = self.lib.zco_encode(x.ctypes.data, x.size, _plan_buf(exps), out.ctypes.data, out.size,
-                                 ctypes.byref(total))
+        fn = self.lib.zco_encode_fallback if raw_fallback else self.lib.zco_encode
+        rc = fn(x.ctypes.data, x.size, _plan_buf(exps), out.ctypes.data, out.size, ctypes.byref(total))
         if rc != OK:
             raise ValueError("oracle encode failed with status %d" % rc)
         return int(total.value)
@@ -203,12 +206,12 @@ def max_bytes(n):
     return default().max_bytes(n)
 
 
-def encode(x, exps):
-    return default().encode(x, exps)
+def encode(x, exps, raw_fallback=False):
+    return default().encode(x, exps, raw_fallback)
 
 
-def encode_into(x, exps, out):
-    return default().encode_into(x, exps, out)
+def encode_into(x, exps, out, raw_fallback=False):
+    return default().encode_into(x, exps, out, raw_fallback)
 
 
 def decode(stream, n):

@@ -39,6 +39,8 @@
  *   plane2  8*ceil(n/64) B             bit 2 of every code
  *   TAB     4*(NG+1) B, NG=ceil(n/4096)  zero-point count before each group
  *   ZP      E B                        full exponent of every zero-point value
+ * Header byte 31 is the mode: 0 for this coded layout, 1 for the raw fallback
+ * (zco_encode_fallback): the header, then the n words unchanged.
  */
 #include <math.h>
 #include <stdint.h>
@@ -54,6 +56,8 @@
 #define ZCO_VERSION 1u
 #define ZCO_HEADER_BYTES 128u
 #define ZCO_GROUP 4096u
+#define ZCO_MODE_CODED 0u /* header byte 31 */
+#define ZCO_MODE_RAW 1u
 
 /* ------------------------------------------------------------------------ */
 /* little helpers                                                            */
@@ -255,10 +259,33 @@ int zco_encode(const uint16_t *x, uint64_t n, const uint8_t exps[7], uint8_t *ou
     put_u32(out + 16, ZCO_GROUP);
     put_u32(out + 20, (uint32_t)L.groups);
     for (int k = 0; k < 7; ++k) out[24 + k] = exps[k];
-    out[31] = 0;
+    out[31] = ZCO_MODE_CODED;
     put_u64(out + 32, zp_count);
     put_u64(out + 40, total);
     *total_bytes = total;
+    return ZCO_OK;
+}
+
+/*
+ * Encode with a raw fallback.  The pages describe no fallback; with many
+ * zero-point values the coded stream grows past the 16 bits of the input
+ * (each such value costs 8 + 3 + 8 bits).  Reading used here: the result is
+ * whichever is smaller, the coded stream or the raw one; a tie keeps the
+ * coded stream.  A raw stream has the same header with byte 31 ("mode") = 1
+ * and total_bytes = 128 + 2n (exps and E still describe the coded form that
+ * was not kept); the n BF16 words follow the header unchanged, little-endian.
+ */
+int zco_encode_fallback(const uint16_t *x, uint64_t n, const uint8_t exps[7], uint8_t *out, uint64_t cap,
+                        uint64_t *total_bytes) {
+    int rc = zco_encode(x, n, exps, out, cap, total_bytes);
+    if (rc != ZCO_OK) return rc;
+    const uint64_t raw_total = ZCO_HEADER_BYTES + 2 * n;
+    if (*total_bytes > raw_total) {
+        out[31] = ZCO_MODE_RAW;
+        put_u64(out + 40, raw_total);
+        for (uint64_t i = 0; i < n; ++i) put_u16(out + ZCO_HEADER_BYTES + 2 * i, x[i]);
+        *total_bytes = raw_total;
+    }
     return ZCO_OK;
 }
 
@@ -282,7 +309,7 @@ static unsigned code_at(const uint8_t *const plane[3], uint64_t i) {
 int zco_decode(const uint8_t *in, uint64_t in_bytes, uint64_t n, uint16_t *x) {
     if (n > 0xFFFFFFFFull) return ZCO_ERR_INVALID_ARG;
     zco_layout_t L = layout_of(n);
-    if (in_bytes < L.off_zp) return ZCO_ERR_CORRUPT;
+    if (in_bytes < ZCO_HEADER_BYTES) return ZCO_ERR_CORRUPT;
 
     /* header */
     if (get_u32(in + 0) != ZCO_MAGIC) return ZCO_ERR_CORRUPT;
@@ -294,10 +321,19 @@ int zco_decode(const uint8_t *in, uint64_t in_bytes, uint64_t n, uint16_t *x) {
     uint8_t exps[7];
     for (int k = 0; k < 7; ++k) exps[k] = in[24 + k];
     if (!plan_is_valid(exps)) return ZCO_ERR_CORRUPT;
-    if (in[31] != 0) return ZCO_ERR_CORRUPT;
+    const uint8_t mode = in[31];
+    if (mode != ZCO_MODE_CODED && mode != ZCO_MODE_RAW) return ZCO_ERR_CORRUPT;
     uint64_t zp_count = get_u64(in + 32);
     uint64_t total = get_u64(in + 40);
     if (zp_count > n) return ZCO_ERR_CORRUPT;
+    if (mode == ZCO_MODE_RAW) {
+        /* raw fallback: the header, then the n words unchanged */
+        if (total != ZCO_HEADER_BYTES + 2 * n) return ZCO_ERR_CORRUPT;
+        if (total > in_bytes) return ZCO_ERR_CORRUPT;
+        if (!bytes_are_zero(in + 48, ZCO_HEADER_BYTES - 48)) return ZCO_ERR_CORRUPT;
+        for (uint64_t i = 0; i < n; ++i) x[i] = get_u16(in + ZCO_HEADER_BYTES + 2 * i);
+        return ZCO_OK;
+    }
     if (total != L.off_zp + zp_count) return ZCO_ERR_CORRUPT;
     if (total > in_bytes) return ZCO_ERR_CORRUPT;
     if (!bytes_are_zero(in + 48, ZCO_HEADER_BYTES - 48)) return ZCO_ERR_CORRUPT;

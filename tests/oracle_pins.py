@@ -553,10 +553,92 @@ def pin_estimate_sigma(orc) -> None:
         s, m = orc.estimate_sigma(x)
         assert m == n and abs(s / sigma - 1.0) < 2e-3, (sigma, s)
 
+
+# --------------------------------------------------------------------------
+# raw fallback (reading in the oracle's C file: keep whichever of the coded
+# and the raw stream is smaller; a tie keeps the coded one)
+# --------------------------------------------------------------------------
+
+def with_escapes(n: int, E: int, seed: int) -> np.ndarray:
+    """n BF16 patterns of which exactly E have an exponent field outside
+    WINDOW_PLAN (116..122); signs and mantissas random."""
+    g = np.random.default_rng(seed)
+    e = g.integers(116, 123, n)
+    idx = g.choice(n, E, replace=False)
+    esc = g.integers(0, 249, E)
+    e[idx] = np.where(esc >= 116, esc + 7, esc)  # 0..115 and 123..255
+    return ((g.integers(0, 2, n) << 15) | (e << 7) | g.integers(0, 128, n)).astype(np.uint16)
+
+
+def check_raw_stream(x: np.ndarray, exps, E: int, s: np.ndarray) -> None:
+    n = x.size
+    b = s.tobytes()
+    assert s.size == 128 + 2 * n
+    assert b[0:4] == MAGIC and int.from_bytes(b[4:6], "little") == 1 and int.from_bytes(b[6:8], "little") == 128
+    assert int.from_bytes(b[8:16], "little") == n and int.from_bytes(b[16:20], "little") == GROUP
+    assert int.from_bytes(b[20:24], "little") == (n + GROUP - 1) // GROUP
+    assert tuple(b[24:31]) == tuple(exps) and b[31] == 1
+    assert int.from_bytes(b[32:40], "little") == E and int.from_bytes(b[40:48], "little") == 128 + 2 * n
+    assert b[48:128] == bytes(80)
+    assert b[128:] == x.astype("<u2").tobytes()
+
+
+def pin_raw_fallback_rule(orc) -> None:
+    """Raw (the header and the 2n input bytes) exactly when the coded size
+    off_zp + E is above 128 + 2n; at a tie, and below, the plain encoder's
+    stream byte for byte; both decode to the input."""
+    ties = 0
+    for n in (1, 7, 100, 1000, 4096, 10_000, 65_539):
+        lay = orc.layout(n)
+        T = 128 + 2 * n - lay["off_zp"]  # the largest E that keeps the coded stream
+        for E in sorted({e for e in (0, T - 1, T, T + 1, n) if 0 <= e <= n}):
+            x = with_escapes(n, E, n + E)
+            coded = orc.encode(x, WINDOW_PLAN)
+            assert coded.size == lay["off_zp"] + E
+            s = orc.encode(x, WINDOW_PLAN, raw_fallback=True)
+            if lay["off_zp"] + E > 128 + 2 * n:
+                check_raw_stream(x, WINDOW_PLAN, E, s)
+            else:
+                assert np.array_equal(s, coded)
+                ties += E == T
+            rc, y = orc.decode(s, n)
+            assert rc == 0 and np.array_equal(y, x), (n, E)
+    assert ties >= 4
+    # n = 0 codes to the header and four empty sections (640 bytes) against a
+    # raw 128: the fallback keeps the header alone
+    s = orc.encode(np.zeros(0, np.uint16), WINDOW_PLAN, raw_fallback=True)
+    check_raw_stream(np.zeros(0, np.uint16), WINDOW_PLAN, 0, s)
+    assert orc.decode(s, 0)[0] == 0
+
+
+def pin_strict_raw_decoder(orc) -> None:
+    """A raw stream is checked as strictly as a coded one."""
+    n = 1000
+    x = with_escapes(n, n, 3)
+    s = orc.encode(x, WINDOW_PLAN, raw_fallback=True)
+    assert s.size == 128 + 2 * n and orc.decode(s, n)[0] == 0
+    assert orc.decode(np.concatenate([s, np.zeros(64, np.uint8)]), n)[0] == 0  # spare bytes after the stream
+    assert orc.decode(s[:-1], n)[0] != 0
+    assert orc.decode(s, n - 1)[0] != 0
+    # (exps and E of a raw stream are informational: another ascending table or
+    # another E <= n is not detectable)
+    for pos in (0, 4, 6, 8, 16, 20, 30, 31, 39, 40, 41, 47, 48, 100, 127):
+        bad = s.copy()
+        bad[pos] ^= 0x40
+        assert orc.decode(bad, n)[0] != 0, pos
+    for mode in (0, 2, 255):
+        bad = s.copy()
+        bad[31] = mode
+        assert orc.decode(bad, n)[0] != 0, mode
+    bad = s.copy()
+    bad[32:40] = np.frombuffer((n + 1).to_bytes(8, "little"), np.uint8)  # E > n
+    assert orc.decode(bad, n)[0] != 0
+
 ALL_PINS = [pin_probabilities_vs_scipy, pin_probabilities_monte_carlo, pin_plan_values,
             pin_scale_covariance, pin_coverage, pin_histogram_top7, pin_contiguity_exception,
             pin_roundtrip_exhaustive, pin_edge_sizes, pin_eleven_bits, pin_offsets_example,
             pin_config1_zero_points, pin_strict_decoder,
             pin_float_to_bf16_nearest_even, pin_reduce_single_stream_identity, pin_reduce_order_and_signed_zero,
             pin_reduce_specials, pin_reduce_error_bound, pin_reduce_rejects_corrupt_stream,
-            pin_exponent_histogram, pin_plan_from_histogram, pin_estimate_sigma]
+            pin_exponent_histogram, pin_plan_from_histogram, pin_estimate_sigma,
+            pin_raw_fallback_rule, pin_strict_raw_decoder]

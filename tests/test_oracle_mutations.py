@@ -77,6 +77,21 @@ MUTATIONS = {
     "sigma_float_accumulator": [("    double sum = 0.0;\n    uint64_t m = 0;", "    float sum = 0.0f;\n    uint64_t m = 0;")],
     "sigma_no_sqrt": [("return m ? sqrt(sum / (double)m) : 0.0;", "return m ? sum / (double)m : 0.0;")],
     "sigma_abs_not_square": [("        sum += v * v;\n", "        sum += fabs(v);\n")],
+    # raw fallback
+    "fallback_tie_goes_raw": [("if (*total_bytes > raw_total) {", "if (*total_bytes >= raw_total) {")],
+    "fallback_never_taken": [("if (*total_bytes > raw_total) {", "if (0) {")],
+    "fallback_mode_byte_not_set": [("        out[31] = ZCO_MODE_RAW;\n", "")],
+    "fallback_payload_byte_swapped_both_sides": [
+        ("put_u16(out + ZCO_HEADER_BYTES + 2 * i, x[i]);",
+         "put_u16(out + ZCO_HEADER_BYTES + 2 * i, (uint16_t)((x[i] >> 8) | (x[i] << 8)));"),
+        ("x[i] = get_u16(in + ZCO_HEADER_BYTES + 2 * i);",
+         "{ uint16_t w = get_u16(in + ZCO_HEADER_BYTES + 2 * i); x[i] = (uint16_t)((w >> 8) | (w << 8)); }"),
+    ],
+    "raw_decoder_skips_pad_check": [
+        ("        if (!bytes_are_zero(in + 48, ZCO_HEADER_BYTES - 48)) return ZCO_ERR_CORRUPT;\n"
+         "        for (uint64_t i = 0; i < n; ++i) x[i] = get_u16",
+         "        for (uint64_t i = 0; i < n; ++i) x[i] = get_u16")],
+    "raw_decoder_skips_total_check": [("        if (total != ZCO_HEADER_BYTES + 2 * n) return ZCO_ERR_CORRUPT;\n", "")],
 }
 
 
