@@ -25,7 +25,7 @@
  *   offset 0        header, 128 B:
  *                     u32 magic 0x3143435A ("ZCC1") | u16 version 1 | u16 128
  *                     u64 n | u32 group elements 4096 | u32 NG = ceil(n/4096)
- *                     u8 exps[7] | u8 0 | u64 E (zero-point count)
+ *                     u8 exps[7] | u8 mode (0 coded, 1 raw) | u64 E (zero-point count)
  *                     u64 total_bytes | 80 zero bytes
  *   128             SM: n bytes, byte i = sign(x_i) << 7 | mantissa(x_i)
  *   off_p0          plane 0: ceil(n/64) little-endian u64 words; bit (i mod 64)
@@ -37,9 +37,16 @@
  *         off_p0 = A(128+n), off_p1 = off_p0 + A(8W), off_p2 = off_p1 + A(8W),
  *         off_tab = off_p2 + A(8W), off_zp = off_tab + A(4(NG+1)),
  *         total_bytes = off_zp + E.
- * Code k (1..7) stands for exps[k-1]; exps is strictly ascending.  The stream
- * is a pure function of (input bits, plan): it does not depend on launch
- * geometry, device, stream or batching.
+ * Code k (1..7) stands for exps[k-1]; exps is strictly ascending.
+ * Raw fallback (mode 1, only when the plan asks for it with
+ * ZC_PLAN_RAW_FALLBACK): the pages describe none, but a value on the
+ * zero-point path costs 19 bits, so a tensor with many of them codes to more
+ * than its 16 bits per value.  When off_zp + E > 128 + 2n the stream is the
+ * same header with mode 1 and total_bytes = 128 + 2n, followed by the n input
+ * values unchanged (exps and E then describe the coded form that was not
+ * kept); a tie keeps the coded form.  The stream is a pure function of
+ * (input bits, plan): it does not depend on launch geometry, device, stream
+ * or batching.
  *
  * Conventions for every call:
  *   - all buffers belong to the caller; the library never allocates, frees or
@@ -71,11 +78,14 @@ typedef enum zc_status {
 
 /* The exponent table ("codebook" of section 2.A): code k <-> exps[k-1].
  * exps must be strictly ascending (7 distinct values, any of 0..255);
- * reserved must be 0. */
+ * flags is 0 or ZC_PLAN_RAW_FALLBACK (store the stream raw when coding would
+ * make it larger, see the stream format above). */
 typedef struct zc_plan {
     uint8_t exps[7];
-    uint8_t reserved;
+    uint8_t flags;
 } zc_plan;
+
+#define ZC_PLAN_RAW_FALLBACK 1u
 
 /* Section 2.A: the table from sigma alone.  For X ~ N(0, sigma^2) the
  * probability of exponent field e is P(2^(e-127) <= |X| < 2^(e-126)) for
@@ -101,13 +111,17 @@ uint64_t zc_max_compressed_bytes(uint64_t n);
  *   d_out_bytes   device u64 (nullable): receives total_bytes
  *   stream        hipStream_t
  * Errors: ZC_ERR_INVALID_ARG, ZC_ERR_MISALIGNED, ZC_ERR_CAPACITY, ZC_ERR_HIP.
- * The stream size is also in header bytes 40..47 once the work completes. */
+ * The stream size is also in header bytes 40..47 once the work completes.
+ * With ZC_PLAN_RAW_FALLBACK a second, small launch follows on the same stream
+ * (it copies the input behind the header where the header says raw). */
 zc_status zc_compress(const void *d_in, uint64_t n, const zc_plan *plan, void *d_out,
                       uint64_t out_capacity, uint64_t *d_out_bytes, void *stream);
 
 /* Inverse of zc_compress.
- *   d_in      device, 128-byte aligned, the stream (in_bytes readable bytes)
- *   in_bytes  bytes available at d_in (>= total_bytes of the stream)
+ *   d_in      device, 128-byte aligned, the stream, coded or raw (in_bytes
+ *             readable bytes)
+ *   in_bytes  bytes available at d_in (>= total_bytes of the stream; below
+ *             both off_zp of n values and 128 + 2n, ZC_ERR_CORRUPT is returned)
  *   n         the element count the caller expects
  *   d_out     device, 16-byte aligned, n BF16 values
  *   d_status  device int32 (nullable): set to 0 on success or ZC_ERR_CORRUPT.
@@ -213,10 +227,11 @@ zc_status zc_decompress_batch(const zc_dec_seg *segs, uint32_t k, void *stream);
 /* Host-side view of a stream header (first 128 bytes copied to the host). */
 typedef struct zc_stream_info {
     uint64_t n;
-    uint64_t zero_points; /* E */
+    uint64_t zero_points; /* E (of the coded form, also for a raw stream) */
     uint64_t total_bytes;
     uint32_t groups;
-    zc_plan plan;
+    zc_plan plan;         /* flags is 0 */
+    uint32_t raw;         /* 1 for the raw fallback form */
 } zc_stream_info;
 
 /* Validate and unpack a header held in host memory (len >= 128).

@@ -51,7 +51,8 @@ struct EncSeg {
     unsigned long long *out_bytes;
     uint32_t n;
     uint8_t exps[7];
-    uint8_t mode;  // kModeWindow or kModeTable
+    uint8_t mode;      // kModeWindow or kModeTable
+    uint8_t raw_ok;    // the plan allows the raw fallback
 };
 static_assert(sizeof(EncSeg) == 40, "compact kernel arguments");
 
@@ -747,7 +748,12 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
         ok = __syncthreads_and(ok);
     }
     const uint32_t E = P + A;
-    const uint64_t total = L.off_zp + E;
+    // raw fallback: when the plan allows it and coding has made the stream
+    // larger than the input, the header says raw and the raw pass (a second
+    // launch) copies the input behind it
+    const uint64_t raw_total = kHeaderBytes + 2 * n;
+    const bool raw = sg.raw_ok && L.off_zp + E > raw_total;
+    const uint64_t total = raw ? raw_total : L.off_zp + E;
     if (ok && tid == 0) tab[L.groups] = E;
     if (tid < 32) {
         uint32_t w = 0;
@@ -759,7 +765,7 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
             case 4: w = kGroup; break;
             case 5: w = (uint32_t)L.groups; break;
             case 6: w = sg.exps[0] | (sg.exps[1] << 8) | (sg.exps[2] << 16) | ((uint32_t)sg.exps[3] << 24); break;
-            case 7: w = sg.exps[4] | (sg.exps[5] << 8) | (sg.exps[6] << 16); break;
+            case 7: w = sg.exps[4] | (sg.exps[5] << 8) | (sg.exps[6] << 16) | ((raw ? kModeRaw : kModeCoded) << 24); break;
             case 8: w = E; break;
             case 10: w = (uint32_t)total; break;
             case 11: w = (uint32_t)(total >> 32); break;
@@ -787,13 +793,16 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(EncArgs args) {
 
 __device__ __forceinline__ uint32_t ld_u32(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
 
-// Header of a stream of n values: all 32 words load at once (uniform, scalar
-// loads) and every field is tested without short-circuiting, so that no test
-// waits for the one before it (a reduce block checks k headers up front).  On success tbl_lo/tbl_hi hold the code ->
-// exponent table for v_perm (byte 0, code 000, is a placeholder) and E the
-// zero-point count.
+// Header of a stream of n values, coded or raw: all 32 words load at once
+// (uniform, scalar loads) and every field is tested without short-circuiting,
+// so that no test waits for the one before it (a reduce block checks k headers
+// up front).  On success `raw` tells the mode; for a coded stream tbl_lo/tbl_hi
+// hold the code -> exponent table for v_perm (byte 0, code 000, is a
+// placeholder) and E the zero-point count.  A raw stream (the fallback) is the
+// header and the n values unchanged: total_bytes = 128 + 2n; its exps and E
+// describe the coded form that was not kept.
 __device__ __forceinline__ bool header_ok(const uint8_t *in, uint64_t in_bytes, uint64_t n, const Layout &L,
-                                          uint32_t &tbl_lo, uint32_t &tbl_hi, uint64_t &E) {
+                                          uint32_t &tbl_lo, uint32_t &tbl_hi, uint64_t &E, bool &raw) {
     uint32_t w[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) w[i] = ld_u32(in + 4 * i);
@@ -805,9 +814,12 @@ __device__ __forceinline__ bool header_ok(const uint8_t *in, uint64_t in_bytes, 
     const uint32_t h6 = w[6], h7 = w[7];
     const uint32_t e[7] = {h6 & 0xFFu, (h6 >> 8) & 0xFFu, (h6 >> 16) & 0xFFu, h6 >> 24,
                            h7 & 0xFFu, (h7 >> 8) & 0xFFu, (h7 >> 16) & 0xFFu};
+    const uint32_t mode = h7 >> 24;
+    raw = mode == kModeRaw;
+    const bool sized = ((mode == kModeCoded) & (total == L.off_zp + E)) | (raw & (total == kHeaderBytes + 2 * n));
     bool ok = (w[0] == kMagic) & (w[1] == ((uint32_t)kVersion | (kHeaderBytes << 16))) & (w[2] == (uint32_t)n) &
-              (w[3] == (uint32_t)(n >> 32)) & (w[4] == kGroup) & (w[5] == (uint32_t)L.groups) & ((h7 >> 24) == 0u) &
-              (E <= n) & (total == L.off_zp + E) & (total <= in_bytes) & (pad == 0u);
+              (w[3] == (uint32_t)(n >> 32)) & (w[4] == kGroup) & (w[5] == (uint32_t)L.groups) & sized &
+              (E <= n) & (total <= in_bytes) & (pad == 0u);
 #pragma unroll
     for (int k = 1; k < 7; ++k) ok = ok & (e[k] > e[k - 1]);
     tbl_lo = h6 << 8;
@@ -815,6 +827,23 @@ __device__ __forceinline__ bool header_ok(const uint8_t *in, uint64_t in_bytes, 
     return ok;
 }
 
+__device__ __forceinline__ bool raw_header_ok(const uint8_t *in, uint64_t in_bytes, uint64_t n, const Layout &L) {
+    uint32_t lo, hi;
+    uint64_t E;
+    bool raw;
+    return header_ok(in, in_bytes, n, L, lo, hi, E, raw) & raw;
+}
+
+// Values [v0, v1) of a raw stream to out (v0 a multiple of 8; the whole block).
+__device__ __forceinline__ void copy_raw(const uint8_t *in, uint16_t *out, uint64_t v0, uint64_t v1) {
+    const uint16_t *src = reinterpret_cast<const uint16_t *>(in + kHeaderBytes);
+    const uint64_t full = v0 + ((v1 - v0) & ~uint64_t(7));
+    for (uint64_t v = v0 + 8u * threadIdx.x; v < full; v += 8u * kThreads) {
+        const uint4 q = load_stream16(src + v);
+        store_stream16(out + v, q.x, q.y, q.z, q.w);
+    }
+    for (uint64_t v = full + threadIdx.x; v < v1; v += kThreads) out[v] = src[v];
+}
 
 // A block decodes kDecSubTiles consecutive tiles (its span).  Every plane and
 // sign+mantissa load of the span, and the span's zero-point table entries,
@@ -891,6 +920,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
         for (int w = 12; w < 32; ++w) ok = ok && ld_u32(in + 4 * w) == 0u;
     }
     if (!ok) {
+        // not a coded stream: the raw fallback form, or corrupt
+        if (raw_header_ok(in, sg.in_bytes, n, L)) {
+            copy_raw(in, sg.out, span0, min(span0 + kDecSpan, n));
+            return;
+        }
         if (tid == 0 && sg.status) *sg.status = ZC_ERR_CORRUPT;
         return;
     }
@@ -980,6 +1014,63 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
         if (sub + 1 < kDecSubTiles) __syncthreads();  // s_planes is rewritten by the next sub-tile
     }
     if (bad && tid == 0 && sg.status) atomicMax(sg.status, (int32_t)ZC_ERR_CORRUPT);
+}
+
+// Segments whose buffer is shorter than the coded layout of n values can only
+// hold a raw stream: checked and copied without any read at a coded offset.
+__global__ __launch_bounds__(kThreads) void decode_raw_kernel(DecArgs args) {
+    const uint32_t flat = blockIdx.x;
+    const uint32_t s = find_segment_dec(args, flat);
+    const DecSeg &sg = args.seg[s];
+    const uint64_t n = sg.n;
+    const Layout L = layout_for(n);
+    const uint64_t span0 = (uint64_t)(flat - sg.tile_begin) * kDecSpan;
+    if (!raw_header_ok(sg.in, sg.in_bytes, n, L)) {
+        if (threadIdx.x == 0 && sg.status) *sg.status = ZC_ERR_CORRUPT;
+        return;
+    }
+    copy_raw(sg.in, sg.out, span0, min(span0 + kDecSpan, n));
+}
+
+// ---------------------------------------------------------------------------
+// raw pass of the compressor: for every segment whose plan allows the
+// fallback, the input goes behind the header when the header says raw.  A
+// fixed grid strides over the spans of all such segments, so that segments
+// that stayed coded cost one cached header read per span.
+// ---------------------------------------------------------------------------
+
+struct RawSeg {
+    const uint16_t *in;
+    uint8_t *out;
+    uint32_t n;
+    uint32_t span_begin;  // first span of this segment
+};
+
+struct RawArgs {
+    uint32_t k;
+    uint32_t spans;
+    RawSeg seg[ZC_MAX_BATCH];
+};
+
+constexpr uint32_t kRawBlocks = 2048;
+
+__global__ __launch_bounds__(kThreads) void raw_pass_kernel(RawArgs args) {
+    for (uint32_t c = blockIdx.x; c < args.spans; c += gridDim.x) {
+        uint32_t s = 0;
+        for (uint32_t i = 1; i < args.k; ++i)
+            if (args.seg[i].span_begin <= c) s = i;
+        const RawSeg &sg = args.seg[s];
+        if ((ld_u32(sg.out + 28) >> 24) != kModeRaw) continue;
+        const uint64_t v0 = (uint64_t)(c - sg.span_begin) * kDecSpan;
+        const uint64_t v1 = min(v0 + kDecSpan, (uint64_t)sg.n);
+        uint16_t *dst = reinterpret_cast<uint16_t *>(sg.out + kHeaderBytes);
+        const uint64_t full = v0 + ((v1 - v0) & ~uint64_t(7));
+        for (uint64_t v = v0 + 8u * threadIdx.x; v < full; v += 8u * kThreads) {
+            const uint4 q = load_stream16(sg.in + v);
+            store_stream16(dst + v, q.x, q.y, q.z, q.w);
+        }
+        for (uint64_t v = full + threadIdx.x; v < v1; v += kThreads) dst[v] = sg.in[v];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1119,7 +1210,8 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(RedArgs args) {
     for (uint32_t s = 0; s < args.k; ++s) {
         uint32_t lo, hi;
         uint64_t E;
-        ok = header_ok(args.s[s].in, args.s[s].in_bytes, n, L, lo, hi, E) & ok;
+        bool raw;
+        ok = header_ok(args.s[s].in, args.s[s].in_bytes, n, L, lo, hi, E, raw) & ok;
     }
     if (!ok) {
         if (tid == 0 && args.status) *args.status = ZC_ERR_CORRUPT;
@@ -1155,9 +1247,31 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(RedArgs args) {
         const uint8_t *const in = args.s[s].in;
         uint32_t tbl_lo, tbl_hi;
         uint64_t E;
-        header_ok(in, args.s[s].in_bytes, n, L, tbl_lo, tbl_hi, E);
+        bool raw;
+        header_ok(in, args.s[s].in_bytes, n, L, tbl_lo, tbl_hi, E, raw);
         uint32_t vals[kSteps][4];
-        decode_tile(in, n, L, t, tbl_lo, tbl_hi, E, sh, vals, bad);
+        if (raw) {
+            // the raw fallback form: the values follow the header
+            const uint16_t *src = reinterpret_cast<const uint16_t *>(in + kHeaderBytes);
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u) {
+                const uint64_t base = (uint64_t)t * kTile + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
+                uint32_t w4[4] = {0, 0, 0, 0};
+                if (base + 8 <= n) {
+                    const uint4 q = load_stream16(src + base);
+                    w4[0] = q.x;
+                    w4[1] = q.y;
+                    w4[2] = q.z;
+                    w4[3] = q.w;
+                } else {
+                    for (uint32_t i = 0; base + i < n; ++i) w4[i / 2] |= (uint32_t)src[base + i] << (16 * (i % 2));
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) vals[u][j] = w4[j];
+            }
+        } else {
+            decode_tile(in, n, L, t, tbl_lo, tbl_hi, E, sh, vals, bad);
+        }
 #pragma unroll
         for (int u = 0; u < kSteps; ++u)
 #pragma unroll
@@ -1193,7 +1307,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(RedArgs args) {
 using namespace zc;
 
 static bool plan_ok(const zc_plan &p) {
-    if (p.reserved != 0) return false;
+    if (p.flags & ~(uint8_t)ZC_PLAN_RAW_FALLBACK) return false;
     for (int k = 1; k < 7; ++k)
         if (p.exps[k] <= p.exps[k - 1]) return false;
     return true;
@@ -1251,6 +1365,7 @@ extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void 
         e.n = (uint32_t)g.n;
         std::memcpy(e.exps, g.plan.exps, 7);
         e.mode = (g.plan.exps[0] >= 1 && g.plan.exps[6] - g.plan.exps[0] == 6) ? kModeWindow : kModeTable;
+        e.raw_ok = (g.plan.flags & ZC_PLAN_RAW_FALLBACK) ? 1 : 0;
     }
     uint64_t ns[ZC_MAX_BATCH];
     for (uint32_t i = 0; i < k; ++i) ns[i] = segs[i].n;
@@ -1270,6 +1385,24 @@ extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void 
     // every finalize block follows the encoder blocks it waits for: workgroups
     // are dispatched in index order, so each of those has been dispatched first
     hipLaunchKernelGGL(compress_kernel, dim3((uint32_t)pos), dim3(kThreads), 0, st, a);
+    if (hipGetLastError() != hipSuccess) return ZC_ERR_HIP;
+    // the raw pass, for the segments whose plan allows the fallback
+    RawArgs r;
+    std::memset(&r, 0, sizeof(r));
+    uint64_t spans = 0;
+    for (uint32_t i = 0; i < k; ++i) {
+        if (!(segs[i].plan.flags & ZC_PLAN_RAW_FALLBACK) || segs[i].n == 0) continue;
+        RawSeg &g = r.seg[r.k++];
+        g.in = a.seg[i].in;
+        g.out = a.seg[i].out;
+        g.n = a.seg[i].n;
+        g.span_begin = (uint32_t)spans;
+        spans += (segs[i].n + kDecSpan - 1) / kDecSpan;
+    }
+    if (!r.k) return ZC_OK;
+    r.spans = (uint32_t)spans;
+    const uint32_t blocks = spans < kRawBlocks ? (uint32_t)spans : kRawBlocks;
+    hipLaunchKernelGGL(raw_pass_kernel, dim3(blocks), dim3(kThreads), 0, st, r);
     return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
 }
 
@@ -1288,41 +1421,51 @@ extern "C" zc_status zc_compress(const void *d_in, uint64_t n, const zc_plan *pl
 
 extern "C" zc_status zc_decompress_batch(const zc_dec_seg *segs, uint32_t k, void *stream) {
     if (!segs || k == 0 || k > ZC_MAX_BATCH) return ZC_ERR_INVALID_ARG;
-    DecArgs a;
-    std::memset(&a, 0, sizeof(a));
+    // a[0]: decode_kernel; a[1]: decode_raw_kernel, for buffers shorter than
+    // the coded layout (only a raw stream fits there)
+    DecArgs a[2];
+    std::memset(a, 0, sizeof(a));
     ZeroArgs z;
     std::memset(&z, 0, sizeof(z));
-    uint64_t tiles = 0;
+    uint64_t tiles[2] = {0, 0};
     for (uint32_t i = 0; i < k; ++i) {
         const zc_dec_seg &g = segs[i];
         if (!g.in || g.n > kMaxElems || (g.n && !g.out)) return ZC_ERR_INVALID_ARG;
         if (((uintptr_t)g.in & 127u) || ((uintptr_t)g.out & 15u) || ((uintptr_t)g.status & 3u))
             return ZC_ERR_MISALIGNED;
         const Layout L = layout_for(g.n);
-        if (g.in_bytes < L.off_zp) return ZC_ERR_CORRUPT;  // no stream of n values is this short
-        DecSeg &d = a.seg[i];
+        // no stream of n values is shorter than both forms
+        if (g.in_bytes < L.off_zp && g.in_bytes < kHeaderBytes + 2 * g.n) return ZC_ERR_CORRUPT;
+        const int which = g.in_bytes < L.off_zp ? 1 : 0;
+        DecSeg &d = a[which].seg[a[which].k++];
         d.in = static_cast<const uint8_t *>(g.in);
         d.out = static_cast<uint16_t *>(g.out);
         d.status = g.status;
         d.in_bytes = g.in_bytes;
         d.n = (uint32_t)g.n;
-        d.tile_begin = (uint32_t)tiles;
-        tiles += dec_blocks(g.n);
-        if (tiles > 0xFFFFFFFFull) return ZC_ERR_INVALID_ARG;
+        d.tile_begin = (uint32_t)tiles[which];
+        tiles[which] += dec_blocks(g.n);
+        if (tiles[which] > 0xFFFFFFFFull) return ZC_ERR_INVALID_ARG;
         if (g.status) {
             z.r[z.count].ptr = reinterpret_cast<uint32_t *>(g.status);
             z.r[z.count].words = 1;
             ++z.count;
         }
     }
-    a.k = k;
-    a.total_tiles = (uint32_t)tiles;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     zc_status rc = launch_zero(z, st);
     if (rc != ZC_OK) return rc;
-    hipLaunchKernelGGL(decode_kernel, dim3(a.total_tiles), dim3(kThreads), 0, st, a);
-    return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
+    for (int which = 0; which < 2; ++which) {
+        if (!a[which].k) continue;
+        a[which].total_tiles = (uint32_t)tiles[which];
+        if (which == 0)
+            hipLaunchKernelGGL(decode_kernel, dim3(a[0].total_tiles), dim3(kThreads), 0, st, a[0]);
+        else
+            hipLaunchKernelGGL(decode_raw_kernel, dim3(a[1].total_tiles), dim3(kThreads), 0, st, a[1]);
+        if (hipGetLastError() != hipSuccess) return ZC_ERR_HIP;
+    }
+    return ZC_OK;
 }
 
 extern "C" zc_status zc_decompress(const void *d_in, uint64_t in_bytes, uint64_t n, void *d_out, int32_t *d_status,
@@ -1350,7 +1493,8 @@ extern "C" zc_status zc_decompress_reduce(const void *const *d_streams, const ui
     for (uint32_t i = 0; i < k; ++i) {
         if (!d_streams[i]) return ZC_ERR_INVALID_ARG;
         if ((uintptr_t)d_streams[i] & 127u) return ZC_ERR_MISALIGNED;
-        if (in_bytes[i] < L.off_zp) return ZC_ERR_CORRUPT;  // no stream of n values is this short
+        // no stream of n values is shorter than both forms
+        if (in_bytes[i] < L.off_zp && in_bytes[i] < kHeaderBytes + 2 * n) return ZC_ERR_CORRUPT;
         a.s[i].in = static_cast<const uint8_t *>(d_streams[i]);
         a.s[i].in_bytes = in_bytes[i];
     }
@@ -1398,9 +1542,12 @@ extern "C" zc_status zc_read_header(const void *host_header, uint64_t len, zc_st
     const Layout L = layout_for(n);
     zc_plan p;
     std::memcpy(p.exps, h + 24, 7);
-    p.reserved = h[31];
+    p.flags = 0;
+    const uint32_t mode = h[31];
     const uint64_t E = rd64(h + 32), total = rd64(h + 40);
-    if (rd32(h + 20) != L.groups || !plan_ok(p) || E > n || total != L.off_zp + E) return ZC_ERR_CORRUPT;
+    if (mode != kModeCoded && mode != kModeRaw) return ZC_ERR_CORRUPT;
+    const uint64_t expect = mode == kModeRaw ? kHeaderBytes + 2 * n : L.off_zp + E;
+    if (rd32(h + 20) != L.groups || !plan_ok(p) || E > n || total != expect) return ZC_ERR_CORRUPT;
     for (int i = 48; i < 128; ++i)
         if (h[i]) return ZC_ERR_CORRUPT;
     out->n = n;
@@ -1408,6 +1555,7 @@ extern "C" zc_status zc_read_header(const void *host_header, uint64_t len, zc_st
     out->total_bytes = total;
     out->groups = (uint32_t)L.groups;
     out->plan = p;
+    out->raw = mode == kModeRaw ? 1u : 0u;
     return ZC_OK;
 }
 

@@ -25,6 +25,8 @@ constexpr uint16_t kVersion = 1;
 constexpr uint32_t kHeaderBytes = 128;
 constexpr uint32_t kGroup = 4096;  // elements per zero-point table entry
 constexpr uint64_t kMaxElems = 0xFFFFFFFFull;
+constexpr uint32_t kModeCoded = 0;  // header byte 31: the coded layout
+constexpr uint32_t kModeRaw = 1;    // header byte 31: the raw fallback (header, then the n values)
 
 // Encoder / decoder tiling (not part of the format; the stream does not depend
 // on it).  A lane owns 8 consecutive elements (one 16-byte load) per step; a

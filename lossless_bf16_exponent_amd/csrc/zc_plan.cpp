@@ -39,7 +39,7 @@ extern "C" zc_status zc_plan_from_sigma(double sigma, zc_plan *out) {
     std::stable_sort(order, order + 256, [&](int a, int b) { return prob[a] > prob[b]; });
     std::sort(order, order + 7);
     for (int k = 0; k < 7; ++k) out->exps[k] = static_cast<uint8_t>(order[k]);
-    out->reserved = 0;
+    out->flags = 0;
     return ZC_OK;
 }
 
@@ -50,6 +50,6 @@ extern "C" zc_status zc_plan_from_histogram(const uint64_t *hist, zc_plan *out) 
     std::stable_sort(order, order + 256, [&](int a, int b) { return hist[a] > hist[b]; });
     std::sort(order, order + 7);
     for (int k = 0; k < 7; ++k) out->exps[k] = static_cast<uint8_t>(order[k]);
-    out->reserved = 0;
+    out->flags = 0;
     return ZC_OK;
 }

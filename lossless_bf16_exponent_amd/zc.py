@@ -25,10 +25,11 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 ZC_OK, ZC_ERR_INVALID_ARG, ZC_ERR_CAPACITY, ZC_ERR_MISALIGNED, ZC_ERR_CORRUPT, ZC_ERR_HIP = range(6)
 ZC_MAX_BATCH = 64
+ZC_PLAN_RAW_FALLBACK = 1
 
 
 class zc_plan(ctypes.Structure):
-    _fields_ = [("exps", ctypes.c_uint8 * 7), ("reserved", ctypes.c_uint8)]
+    _fields_ = [("exps", ctypes.c_uint8 * 7), ("flags", ctypes.c_uint8)]
 
 
 class zc_enc_seg(ctypes.Structure):
@@ -43,7 +44,7 @@ class zc_dec_seg(ctypes.Structure):
 
 class zc_stream_info(ctypes.Structure):
     _fields_ = [("n", ctypes.c_uint64), ("zero_points", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64),
-                ("groups", ctypes.c_uint32), ("plan", zc_plan)]
+                ("groups", ctypes.c_uint32), ("plan", zc_plan), ("raw", ctypes.c_uint32)]
 
 
 _lib.zc_plan_from_sigma.argtypes = [ctypes.c_double, ctypes.POINTER(zc_plan)]
@@ -115,6 +116,12 @@ def _plan(exps) -> zc_plan:
     if len(exps) != 7:
         raise ValueError("a plan has exactly seven exponents")
     return zc_plan((ctypes.c_uint8 * 7)(*exps), 0)
+
+
+def plan_with_raw_fallback(exps) -> zc_plan:
+    """The plan `exps` with ZC_PLAN_RAW_FALLBACK set (pass it wherever a plan goes)."""
+    p = _plan(tuple(exps.exps) if isinstance(exps, zc_plan) else exps)
+    return zc_plan(p.exps, ZC_PLAN_RAW_FALLBACK)
 
 
 def _check(rc: int, where: str) -> None:
@@ -218,7 +225,7 @@ def zc_read_header(header: bytes) -> dict:
     info = zc_stream_info()
     _check(_lib.zc_read_header(buf, len(header), ctypes.byref(info)), "zc_read_header")
     return {"n": int(info.n), "zero_points": int(info.zero_points), "total_bytes": int(info.total_bytes),
-            "groups": int(info.groups), "plan": tuple(int(v) for v in info.plan.exps)}
+            "groups": int(info.groups), "plan": tuple(int(v) for v in info.plan.exps), "raw": bool(info.raw)}
 
 
 def raw_status(fn: str, *args) -> int:

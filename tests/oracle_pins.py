@@ -604,8 +604,9 @@ def pin_raw_fallback_rule(orc) -> None:
             rc, y = orc.decode(s, n)
             assert rc == 0 and np.array_equal(y, x), (n, E)
     assert ties >= 4
-    # n = 0 codes to the header and four empty sections (640 bytes) against a
-    # raw 128: the fallback keeps the header alone
+    # n = 0 codes to 256 bytes (the header and a one-entry table) against a raw
+    # 128: the fallback keeps the header alone
+    assert orc.layout(0)["off_zp"] == 256
     s = orc.encode(np.zeros(0, np.uint16), WINDOW_PLAN, raw_fallback=True)
     check_raw_stream(np.zeros(0, np.uint16), WINDOW_PLAN, 0, s)
     assert orc.decode(s, 0)[0] == 0

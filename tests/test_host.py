@@ -98,9 +98,9 @@ FAKE_OUT = 0x7F1000000000
 PLAN = (116, 117, 118, 119, 120, 121, 122)
 
 
-def _compress_status(zc, d_in=FAKE_IN, n=1000, plan=PLAN, reserved=0, d_out=FAKE_OUT, cap=None, d_bytes=0):
+def _compress_status(zc, d_in=FAKE_IN, n=1000, plan=PLAN, flags=0, d_out=FAKE_OUT, cap=None, d_bytes=0):
     p = zc._plan(plan)
-    p.reserved = reserved
+    p.flags = flags
     if cap is None:
         cap = zc.zc_max_compressed_bytes(n) - 1  # one byte short: every other check must fire first
     return zc.raw_status("zc_compress", d_in, n, ctypes.byref(p), d_out, cap, d_bytes, 0)
@@ -113,7 +113,9 @@ def test_compress_host_errors(zc):
     assert _compress_status(zc, n=1 << 32, cap=1 << 40) == zc.ZC_ERR_INVALID_ARG
     assert _compress_status(zc, plan=(116, 116, 118, 119, 120, 121, 122)) == zc.ZC_ERR_INVALID_ARG
     assert _compress_status(zc, plan=(122, 121, 120, 119, 118, 117, 116)) == zc.ZC_ERR_INVALID_ARG
-    assert _compress_status(zc, reserved=1) == zc.ZC_ERR_INVALID_ARG
+    assert _compress_status(zc, flags=2) == zc.ZC_ERR_INVALID_ARG
+    assert _compress_status(zc, flags=0x81) == zc.ZC_ERR_INVALID_ARG
+    assert _compress_status(zc, flags=zc.ZC_PLAN_RAW_FALLBACK) == zc.ZC_ERR_CAPACITY  # a valid flag
     assert _compress_status(zc, d_in=FAKE_IN + 2) == zc.ZC_ERR_MISALIGNED
     assert _compress_status(zc, d_out=FAKE_OUT + 64) == zc.ZC_ERR_MISALIGNED
     assert _compress_status(zc, d_bytes=FAKE_OUT + 4) == zc.ZC_ERR_MISALIGNED
@@ -194,7 +196,7 @@ def test_read_header_of_oracle_streams(zc):
         info = zc.zc_read_header(s[:128].tobytes())
         E = int(np.isin(oracle_pins.exponent_field(x), exps, invert=True).sum())
         assert info == {"n": n, "zero_points": E, "total_bytes": s.size,
-                        "groups": (n + 4095) // 4096, "plan": exps}
+                        "groups": (n + 4095) // 4096, "plan": exps, "raw": False}
         for pos in (0, 4, 16, 20, 25, 31, 33, 41, 100):
             bad = s[:128].copy()
             bad[pos] ^= 0x40
@@ -210,6 +212,21 @@ def test_read_header_of_oracle_streams(zc):
             pass
     with pytest.raises(zc.ZcError):
         zc.zc_read_header(bytes(64))
+
+
+def test_read_header_of_raw_streams(zc):
+    for n, E in ((0, 0), (100, 3), (10_000, 10_000)):
+        x = oracle_pins.with_escapes(n, E, 2)
+        s = oracle.encode(x, oracle_pins.WINDOW_PLAN, raw_fallback=True)
+        assert s.size == 128 + 2 * n
+        info = zc.zc_read_header(s[:128].tobytes())
+        assert info == {"n": n, "zero_points": E, "total_bytes": 128 + 2 * n,
+                        "groups": (n + 4095) // 4096, "plan": oracle_pins.WINDOW_PLAN, "raw": True}
+        for pos, val in ((31, 2), (31, 0), (40, s[40] ^ 4), (90, 1)):
+            bad = s[:128].copy()
+            bad[pos] = val
+            with pytest.raises(zc.ZcError):
+                zc.zc_read_header(bad.tobytes())
 
 
 def test_status_strings(zc):
