@@ -42,11 +42,14 @@ HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["lossless_bf16_exponent_amd/csrc/zc_codec.hip", "lossless_bf16_exponent_amd/csrc/zc_lane.h",
                   "lossless_bf16_exponent_amd/csrc/zc_format.h", "lossless_bf16_exponent_amd/csrc/zc_grid.h"]
+STATS_SOURCES = ["lossless_bf16_exponent_amd/csrc/zc_stats.hip"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
+    """Hash of the codec kernel sources (or of `sources`): a counter summary
+    is used only while the kernels it measured are unchanged."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -208,6 +211,52 @@ def stats_measurement(zc, x, seg_ns, steps: int) -> dict:
     return out
 
 
+def fallback_measurement(zc, steps: int) -> dict:
+    """The raw fallback on the stress workload that coding expands most
+    (2^24 uniformly random non-NaN/Inf BF16 patterns under the sigma = 0.02
+    plan, 18.8 bits per value coded): compress with ZC_PLAN_RAW_FALLBACK (the
+    coded pass, then the raw pass that copies the input behind the raw header)
+    and decompress of the raw stream, HIP events around K calls each."""
+    import numpy as np
+    import torch
+
+    from lossless_bf16_exponent_amd import workloads
+
+    w = workloads.get("5b")
+    n = w.n
+    x = torch.from_numpy(w.buffer.view(np.int16)).cuda()
+    plan = zc.plan_with_raw_fallback(zc.zc_plan_from_sigma(w.segments[0].sigma))
+    cap = zc.zc_max_compressed_bytes(n)
+    out = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    size = torch.zeros(1, dtype=torch.int64, device="cuda")
+    dec = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    enc_call = lambda: zc.zc_compress(x, n, plan, out, cap, size, stream)
+    dec_call = lambda: zc.zc_decompress(out, cap, n, dec, None, stream)
+    enc_call()
+    dec_call()
+    torch.cuda.synchronize()
+    total = int(size.item())
+    if total != 128 + 2 * n or out[31].item() != 1 or not torch.equal(dec, x):
+        raise RuntimeError("the fallback did not give a lossless raw stream")
+    res = {"workload": w.name, "values": n, "stream_bytes": total, "raw": True}
+    for name, call in (("compress", enc_call), ("decompress", dec_call)):
+        for _ in range(3):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[name + "_us"] = round(ms * 1e3, 2)
+        res[name + "_gbps"] = round(2.0 * n / (ms * 1e-3) / 1e9, 1)
+    res["kernels"] = {"compress": "compress_kernel + raw_pass_kernel", "decompress": "decode_kernel (raw branch)"}
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,6 +267,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reduce", action="store_true", help="skip the reduce-scatter receive-side measurement")
     ap.add_argument("--no-stats", action="store_true", help="skip the histogram / sigma-estimate measurement")
+    ap.add_argument("--no-fallback", action="store_true", help="skip the raw-fallback measurement")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -377,9 +427,12 @@ def main() -> int:
     if not args.no_stats:
         rec["plan_variants"] = stats_measurement(zc, x, ns, args.steps)
         rec["plan_variants"]["sigma_table_us_per_bucket"] = round(plan_us * len(ns), 2)
-    if not args.no_reduce:
+    if not args.no_reduce or not args.no_fallback:
         del out, dec
         torch.cuda.empty_cache()
+    if not args.no_fallback:
+        rec["raw_fallback"] = fallback_measurement(zc, args.steps)
+    if not args.no_reduce:
         rec["reduce_scatter_local"] = reduce_measurement(zc, args.steps)
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
