@@ -22,7 +22,7 @@
 //     same-address serialization.  The 8 waves of a block share the columns
 //     through LDS atomics without return.  Two blocks fill a CU.  Each block
 //     writes its 256 counts to a row of the workspace; a second small kernel
-//     sums the columns.  No global atomics (same-address device atomics
+//     (one block per bin) sums the columns.  No global atomics (same-address device atomics
 //     serialize behind a round trip each).
 //   * Sigma: float64 sums of exact squares (a BF16 square has 16 significant
 //     bits and stays inside the double range), per thread in element order,
@@ -174,27 +174,32 @@ __global__ __launch_bounds__(kHistThreads) void hist_kernel(HistArgs a) {
     if (!half) a.rows[(uint64_t)blockIdx.x * kBins + bin] = s;
 }
 
-// hist[b] = sum over the rows of column b.  32 blocks of 256 threads: block
-// g owns bins 8g..8g+7; thread t adds rows t/8, t/8 + 32, ... of bin 8g + t%8.
+// hist[b] = sum over the rows of column b: one block per bin, every thread
+// adds kHistBlocks / 256 rows with all of its loads in flight at once (the
+// pass is a single round trip; the rows' cache lines are shared by the
+// blocks of 16 neighbouring bins).
 struct HistSumArgs {
     const uint32_t *rows;
     unsigned long long *hist;
 };
 
-__global__ __launch_bounds__(256) void hist_sum_kernel(HistSumArgs a) {
-    __shared__ unsigned long long part[256];
-    const uint32_t tid = threadIdx.x;
-    const uint32_t bin = blockIdx.x * 8 + (tid & 7u);
+constexpr int kSumThreads = 256;
+static_assert(kHistBlocks % kSumThreads == 0, "whole rows per thread");
+
+__global__ __launch_bounds__(kSumThreads) void hist_sum_kernel(HistSumArgs a) {
+    __shared__ unsigned long long part[kSumThreads / 64];
+    const uint32_t tid = threadIdx.x, bin = blockIdx.x;
+    uint32_t v[kHistBlocks / kSumThreads];
+#pragma unroll
+    for (uint32_t i = 0; i < kHistBlocks / kSumThreads; ++i) v[i] = a.rows[(uint64_t)(tid + i * kSumThreads) * kBins + bin];
     unsigned long long s = 0;
-#pragma unroll 4
-    for (uint32_t r = tid >> 3; r < kHistBlocks; r += 32) s += a.rows[(uint64_t)r * kBins + bin];
-    part[tid] = s;
+#pragma unroll
+    for (uint32_t i = 0; i < kHistBlocks / kSumThreads; ++i) s += v[i];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    if ((tid & 63u) == 0) part[tid >> 6] = s;
     __syncthreads();
-    if (tid < 8) {
-        unsigned long long t = 0;
-        for (uint32_t r = 0; r < 32; ++r) t += part[r * 8 + tid];
-        a.hist[blockIdx.x * 8 + tid] = t;
-    }
+    if (tid == 0) a.hist[bin] = part[0] + part[1] + part[2] + part[3];
 }
 
 // ---------------------------------------------------------------------------
@@ -334,11 +339,19 @@ __global__ __launch_bounds__(256) void sigma_final_kernel(SigFinalArgs a) {
     __shared__ double ssum[4];
     __shared__ unsigned long long scnt[4];
     const uint32_t tid = threadIdx.x;
+    double ps[kSigBlocks / 256];
+    unsigned long long pc[kSigBlocks / 256];
+#pragma unroll
+    for (uint32_t i = 0; i < kSigBlocks / 256; ++i) {  // every load in flight at once
+        ps[i] = a.part_sum[tid + 256 * i];
+        pc[i] = a.part_count[tid + 256 * i];
+    }
     double s = 0.0;
     unsigned long long c = 0;
-    for (uint32_t r = tid; r < kSigBlocks; r += 256) {
-        s += a.part_sum[r];
-        c += a.part_count[r];
+#pragma unroll
+    for (uint32_t i = 0; i < kSigBlocks / 256; ++i) {
+        s += ps[i];
+        c += pc[i];
     }
     s = wave_sum(s);
     c = wave_sum(c);
@@ -389,7 +402,7 @@ extern "C" zc_status zc_exponent_histogram(const void *d_in, uint64_t n, void *d
     HistSumArgs s;
     s.rows = h.rows;
     s.hist = reinterpret_cast<unsigned long long *>(d_hist);
-    hipLaunchKernelGGL(hist_sum_kernel, dim3(kBins / 8), dim3(256), 0, st, s);
+    hipLaunchKernelGGL(hist_sum_kernel, dim3(kBins), dim3(kSumThreads), 0, st, s);
     return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
 }
 
