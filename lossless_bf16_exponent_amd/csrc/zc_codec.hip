@@ -801,11 +801,16 @@ __device__ __forceinline__ uint32_t ld_u32(const uint8_t *p) { return *reinterpr
 // placeholder) and E the zero-point count.  A raw stream (the fallback) is the
 // header and the n values unchanged: total_bytes = 128 + 2n; its exps and E
 // describe the coded form that was not kept.
+typedef __attribute__((address_space(4))) const uint32_t const_u32;
+
 __device__ __forceinline__ bool header_ok(const uint8_t *in, uint64_t in_bytes, uint64_t n, const Layout &L,
                                           uint32_t &tbl_lo, uint32_t &tbl_hi, uint64_t &E, bool &raw) {
+    // constant address space: scalar loads, which never wait behind the
+    // vector loads in flight
+    const_u32 *h = (const_u32 *)in;
     uint32_t w[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) w[i] = ld_u32(in + 4 * i);
+    for (int i = 0; i < 32; ++i) w[i] = h[i];
     uint32_t pad = 0;
 #pragma unroll
     for (int i = 12; i < 32; ++i) pad |= w[i];
@@ -845,6 +850,36 @@ __device__ __forceinline__ void copy_raw(const uint8_t *in, uint16_t *out, uint6
     for (uint64_t v = full + threadIdx.x; v < v1; v += kThreads) out[v] = src[v];
 }
 
+// Gather of the zero-point bytes of an 8-value step without a loop: the
+// step's zero-points are the bytes [r, r + popcount(m)) of the slice, in
+// order.  sel[m] holds, for each of the 8 positions, the index among the set
+// bits of m (a v_perm selector into those bytes) or 0x0C (a zero byte) where
+// the bit is clear; the same selector applied to all-ones bytes gives the
+// byte mask of the positions to replace.
+__device__ __forceinline__ void zp_selectors(uint2 *sel) {  // 256 entries, filled by the block
+    for (uint32_t m = threadIdx.x; m < 256; m += kThreads) {
+        uint32_t lo = 0, hi = 0, idx = 0;
+        for (uint32_t p = 0; p < 8; ++p) {
+            const uint32_t b = (m >> p) & 1u ? idx++ : 0x0Cu;
+            if (p < 4)
+                lo |= b << (8 * p);
+            else
+                hi |= b << (8 * (p - 4));
+        }
+        sel[m] = make_uint2(lo, hi);
+    }
+}
+
+__device__ __forceinline__ void put_zero_points(uint32_t &e_lo, uint32_t &e_hi, uint32_t m, uint32_t r,
+                                                const uint32_t *zw, const uint2 *sel) {
+    const uint32_t d0 = zw[r / 4], d1 = zw[r / 4 + 1], d2 = zw[r / 4 + 2];
+    const uint32_t sh = r & 3u;
+    const uint32_t z_lo = __builtin_amdgcn_alignbyte(d1, d0, sh), z_hi = __builtin_amdgcn_alignbyte(d2, d1, sh);
+    const uint2 s = sel[m];
+    e_lo = bfi(perm(~0u, ~0u, s.x), perm(z_hi, z_lo, s.x), e_lo);
+    e_hi = bfi(perm(~0u, ~0u, s.y), perm(z_hi, z_lo, s.y), e_hi);
+}
+
 // A block decodes kDecSubTiles consecutive tiles (its span).  Every plane and
 // sign+mantissa load of the span, and the span's zero-point table entries,
 // are issued before the header is checked (all of them lie inside the n-value
@@ -852,8 +887,9 @@ __device__ __forceinline__ void copy_raw(const uint8_t *in, uint16_t *out, uint6
 // is then staged in LDS with dword loads and gathered by rank.
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
     __shared__ uint32_t s_planes[kTile / 8];
-    __shared__ uint32_t s_zp32[kDecSpan / 4 + 2];  // the span's zero-point bytes from a dword-aligned start
-    __shared__ uint32_t s_wave_total[2][kWaves];
+    __shared__ uint32_t s_zp32[kDecSpan / 4 + 3];  // the span's zero-point bytes from a dword-aligned start
+    __shared__ uint32_t s_wave_total[2][kWaves];    // (+ slack for the 3-dword reads of the gather)
+    __shared__ uint2 s_sel[256];
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const uint32_t flat = blockIdx.x;
@@ -957,8 +993,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
         for (uint32_t i = 0; i < (uint32_t)(A1 - a1); ++i) w |= (uint32_t)in[a1 + i] << (8 * i);
         s_zp32[ndw] = w;
     }
-    const uint8_t *const s_zp = reinterpret_cast<const uint8_t *>(s_zp32) + shift;
     const uint32_t zspan = z[kDecGroups] - z[0];
+    zp_selectors(s_sel);  // visible after the first sub-tile's barrier
 
 #pragma unroll
     for (int sub = 0; sub < kDecSubTiles; ++sub) {
@@ -992,14 +1028,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
         const uint32_t rank0 = zb - z[0];
 #pragma unroll
         for (int u = 0; u < kSteps; ++u) {
-            uint32_t m = zmask[u], r = rank0 + tc.rank[u];
-            while (m) {
-                const uint32_t k = __builtin_ctz(m);
-                m &= m - 1;
-                const uint32_t v = r < zspan ? (uint32_t)s_zp[r] : 0u;
-                ++r;
-                put_byte8(e[u][0], e[u][1], k, v);
-            }
+            // slice byte j sits at byte shift + j of s_zp32; a rank past the
+            // slice (a corrupt table, already flagged) reads the slack instead
+            const uint32_t rk = rank0 + tc.rank[u];
+            put_zero_points(e[u][0], e[u][1], zmask[u], shift + (rk <= zspan ? rk : zspan), s_zp32, s_sel);
             const uint64_t base = tile0 + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
             uint32_t o0, o1, o2, o3;
             rebuild4(sm[sub][u][0], e[u][0], o0, o1);
@@ -1090,140 +1122,309 @@ __device__ __forceinline__ uint32_t float_to_bf16(float f) {
     return (f != f) ? 0x7FC0u : ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-struct RedShared {
-    uint32_t planes[kTile / 8];
-    uint32_t zp32[kTile / 4 + 2];  // the tile's zero-point bytes from a dword-aligned start
-    uint32_t wave_total[2][kWaves];
+// The reduce kernel works on 4096-value tiles (one zero-point group each).
+// Every stream's sign+mantissa bytes and plane bytes for the tile land in LDS
+// through direct-to-LDS loads (no registers), in one of two stages, and its
+// zero-point slice lands in one of two slice buffers.  While stream s is
+// decoded from LDS, the slice of stream s + 1 and the data of stream s + 2 are
+// in flight: a stream costs at most one round trip of waiting, and the
+// registers hold only the 16 float32 accumulators of a thread and one step's
+// decode state, so that many blocks fit on a CU.
+constexpr uint32_t kRedTile = 4096;
+constexpr int kRedSteps = 2;  // 8-value steps per thread
+static_assert(kRedTile == (uint32_t)kThreads * 8 * kRedSteps, "a thread owns 16 values");
+static_assert(kRedTile == kGroup, "a tile is one zero-point group");
+constexpr uint32_t kRedPlaneBytes = kRedTile / 8;  // per plane per tile
+constexpr uint32_t kRedZpWords = kRedTile / 4 + 3;  // slack for the 3-dword reads of the gather
+
+struct RedStage {
+    uint8_t sm[kRedTile];
+    uint8_t planes[3 * kRedPlaneBytes];  // planes 0, 1, 2 back to back
 };
 
-// Decodes tile `t` of one stream into vals (per step: 4 dwords, 8 BF16 values
-// in element order).  Mirrors one sub-tile of decode_kernel.  Sets bad when the
-// table disagrees with the planes (reads stay inside the stream).
-__device__ __forceinline__ void decode_tile(const uint8_t *in, uint64_t n, const Layout &L, uint32_t t, uint32_t tbl_lo,
-                                            uint32_t tbl_hi, uint64_t E, RedShared &sh, uint32_t (&vals)[kSteps][4],
-                                            bool &bad) {
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const uint64_t tile0 = (uint64_t)t * kTile;
-    uint32_t pw0 = 0, pw1 = 0, pw2 = 0;
-    if (tile0 + 32u * (uint32_t)tid < n) {
-        const uint64_t off = tile0 / 8 + 4u * (uint32_t)tid;
-        pw0 = load_stream4(in + L.off_p0 + off);
-        pw1 = load_stream4(in + L.off_p1 + off);
-        pw2 = load_stream4(in + L.off_p2 + off);
-    }
-    uint32_t sm[kSteps][2];
-#pragma unroll
-    for (int u = 0; u < kSteps; ++u) {
-        const uint64_t base = tile0 + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
-        sm[u][0] = sm[u][1] = 0;
-        if (base < n) {
-            const uint2 v = load_stream8(in + kHeaderBytes + base);
-            sm[u][0] = v.x;
-            sm[u][1] = v.y;
-        }
-    }
-    const uint32_t *tab = reinterpret_cast<const uint32_t *>(in + L.off_tab);
-    uint32_t z[kGroupsPerTile + 1];
-#pragma unroll
-    for (int j = 0; j <= (int)kGroupsPerTile; ++j) {
-        const uint64_t g = (uint64_t)t * kGroupsPerTile + j;
-        z[j] = tab[g <= L.groups ? g : L.groups];
-    }
-    // table consistency; clamp so that every read stays inside the stream
-    const bool last = ((uint64_t)(t + 1) * kTile >= n);
-    if ((t == 0 && z[0] != 0) || (last && z[kGroupsPerTile] != E)) bad = true;
-#pragma unroll
-    for (int j = 0; j <= (int)kGroupsPerTile; ++j) {
-        const uint32_t lo = j ? z[j - 1] : 0u;
-        if (z[j] < lo || z[j] > E) bad = true;
-        z[j] = z[j] < lo ? lo : (z[j] > E ? (uint32_t)E : z[j]);
-    }
-    if (z[kGroupsPerTile] - z[0] > kTile) {
-        bad = true;
-#pragma unroll
-        for (int j = 0; j <= (int)kGroupsPerTile; ++j) z[j] = z[j] - z[0] > kTile ? z[0] + kTile : z[j];
-    }
-    // the tile's zero-point bytes: stream bytes [A0, A1)
-    const uint64_t A0 = L.off_zp + z[0], A1 = L.off_zp + z[kGroupsPerTile];
-    const uint64_t a0 = A0 & ~uint64_t(3), a1 = A1 & ~uint64_t(3);
-    const uint32_t ndw = (uint32_t)((a1 - a0) / 4);
-    for (uint32_t i = tid; i < ndw; i += kThreads) sh.zp32[i] = ld_u32(in + a0 + 4u * i);
-    if (tid == 0 && A1 > a1) {
-        uint32_t w = 0;
-        for (uint32_t i = 0; i < (uint32_t)(A1 - a1); ++i) w |= (uint32_t)in[a1 + i] << (8 * i);
-        sh.zp32[ndw] = w;
-    }
-    const uint8_t *const s_zp = reinterpret_cast<const uint8_t *>(sh.zp32) + (uint32_t)(A0 & 3u);
-    const uint32_t zspan = z[kGroupsPerTile] - z[0];
-    {
-        const uint32_t lo = perm(pw1, pw0, 0x05010400u), hi = perm(pw1, pw0, 0x07030602u);
-        uint4 q;
-        q.x = perm(pw2, lo, 0x0C040100u);
-        q.y = perm(pw2, lo, 0x0C050302u);
-        q.z = perm(pw2, hi, 0x0C060100u);
-        q.w = perm(pw2, hi, 0x0C070302u);
-        reinterpret_cast<uint4 *>(sh.planes)[tid] = q;
-    }
-    __syncthreads();  // sh.planes and sh.zp32
-    uint32_t e[kSteps][2], zmask[kSteps];
-#pragma unroll
-    for (int u = 0; u < kSteps; ++u) {
-        const uint64_t base = tile0 + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
-        const uint32_t vmask = base + 8 <= n ? 0xFFu : (base < n ? (1u << (uint32_t)(n - base)) - 1u : 0u);
-        const uint32_t planes = sh.planes[(wave * kSteps + u) * kWave + lane] & 0x00FFFFFFu;
-        uint32_t c_lo, c_hi;
-        planes_to_codes(planes, c_lo, c_hi);
-        e[u][0] = perm(tbl_hi, tbl_lo, c_lo);
-        e[u][1] = perm(tbl_hi, tbl_lo, c_hi);
-        zmask[u] = zero_point_mask(planes) & vmask;
-    }
-    const TileCounts tc = count_tile(zmask, lane, wave, sh.wave_total[0]);
-    if (tc.tile_total != z[kGroupsPerTile] - z[0] || tc.first_group != z[1] - z[0]) bad = true;
-#pragma unroll
-    for (int u = 0; u < kSteps; ++u) {
-        uint32_t m = zmask[u], r = tc.rank[u];
-        while (m) {
-            const uint32_t k = __builtin_ctz(m);
-            m &= m - 1;
-            const uint32_t v = r < zspan ? (uint32_t)s_zp[r] : 0u;
-            ++r;
-            put_byte8(e[u][0], e[u][1], k, v);
-        }
-        rebuild4(sm[u][0], e[u][0], vals[u][0], vals[u][1]);
-        rebuild4(sm[u][1], e[u][1], vals[u][2], vals[u][3]);
-    }
-    __syncthreads();  // sh is reused by the next stream
+struct RedZp {
+    uint32_t w[kRedZpWords];  // the tile's zero-point bytes from a dword-aligned start
+};
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8); only vmcnt is constrained.
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitVm2 = 0x0F72;
+
+// Direct-to-LDS loads of the reduce kernel, written as inline assembly: the
+// compiler then adds no waits of its own for them (it would wait for every
+// such load in flight before each LDS read, the next stream's included); the
+// kernel waits for them itself with explicit counts.  Loads return in order,
+// so the compiler's waits for its own loads stay correct with these in flight.
+// The LDS address is the wave-uniform base in M0 plus 16 (or 4) bytes per lane.
+__device__ __forceinline__ uint32_t lds_base(const void *lds) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds);
+}
+__device__ __forceinline__ void lds_load16(const void *src, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(m0), "v"(src)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load4(const void *src, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off nt" ::"s"(m0), "v"(src)
+                 : "memory", "m0");
 }
 
-// One block per 8192-value tile.  Every block first checks every stream's
+// Uniform per-stream facts, re-read from the (cached) header where needed.
+struct RedMeta {
+    const uint8_t *in;
+    uint64_t in_bytes;
+    uint64_t E;
+    uint32_t tbl_lo, tbl_hi;
+    bool raw;
+};
+
+// Per-stream facts of a checked header, kept in LDS: E (two words), the code
+// table (two words).  Bit 31 of E's high word marks a raw stream (E <= 2^32).
+struct RedHdr {
+    uint32_t e_lo, e_hi, tbl_lo, tbl_hi;
+};
+
+__device__ __forceinline__ RedMeta red_meta(const RedArgs &args, uint32_t s, const RedHdr *hdr) {
+    RedMeta m;
+    m.in = args.s[s].in;
+    m.in_bytes = args.s[s].in_bytes;
+    const uint4 h = *reinterpret_cast<const uint4 *>(hdr + s);
+    const uint32_t e_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)h.y);
+    m.E = (uint32_t)__builtin_amdgcn_readfirstlane((int)h.x) | ((uint64_t)(e_hi & 0x7FFFFFFFu) << 32);
+    m.raw = (e_hi >> 31) != 0u;
+    m.tbl_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)h.z);
+    m.tbl_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)h.w);
+    return m;
+}
+
+// Every stream's header at once: the 32 words of each go to LDS with one
+// vector load per thread and word (all in flight together), then thread s
+// checks stream s.  Returns the block-wide verdict; hdr[s] receives stream s's
+// facts.  `words` (k * 32 words) may alias memory that is not yet in use.
+__device__ __forceinline__ bool red_check_headers(const RedArgs &args, uint64_t n, const Layout &L, uint32_t *words,
+                                                  RedHdr *hdr) {
+    const uint32_t k = args.k, tid = threadIdx.x;
+    for (uint32_t i = tid; i < 32u * k; i += kThreads)
+        words[i] = *reinterpret_cast<const uint32_t *>(args.s[i / 32].in + 4u * (i % 32));
+    __syncthreads();
+    bool ok = true;
+    if (tid < k) {
+        const uint32_t *w = words + 32u * tid;
+        uint32_t pad = 0;
+        for (int i = 12; i < 32; ++i) pad |= w[i];
+        const uint64_t E = w[8] | ((uint64_t)w[9] << 32);
+        const uint64_t total = w[10] | ((uint64_t)w[11] << 32);
+        const uint32_t h6 = w[6], h7 = w[7];
+        const uint32_t mode = h7 >> 24;
+        const bool raw = mode == kModeRaw;
+        const bool sized = ((mode == kModeCoded) & (total == L.off_zp + E)) | (raw & (total == kHeaderBytes + 2 * n));
+        ok = (w[0] == kMagic) & (w[1] == ((uint32_t)kVersion | (kHeaderBytes << 16))) & (w[2] == (uint32_t)n) &
+             (w[3] == (uint32_t)(n >> 32)) & (w[4] == kGroup) & (w[5] == (uint32_t)L.groups) & sized & (E <= n) &
+             (total <= args.s[tid].in_bytes) & (pad == 0u);
+        const uint32_t e[7] = {h6 & 0xFFu, (h6 >> 8) & 0xFFu, (h6 >> 16) & 0xFFu, h6 >> 24,
+                               h7 & 0xFFu, (h7 >> 8) & 0xFFu, (h7 >> 16) & 0xFFu};
+        for (int j = 1; j < 7; ++j) ok = ok & (e[j] > e[j - 1]);
+        RedHdr r;
+        r.e_lo = (uint32_t)E;
+        r.e_hi = (uint32_t)(E >> 32) | (raw ? 0x80000000u : 0u);
+        r.tbl_lo = h6 << 8;
+        r.tbl_hi = (h6 >> 24) | (h7 << 8);
+        hdr[tid] = r;
+    }
+    return __syncthreads_and(ok);
+}
+
+// Table entries of tile t (scalar loads): zero-point values before the tile
+// and before the next one.
+__device__ __forceinline__ void red_table(const RedMeta &m, const Layout &L, uint32_t t, uint32_t &z0, uint32_t &z1) {
+    const_u32 *tab = (const_u32 *)(m.in + L.off_tab);
+    const uint64_t g0 = t < L.groups ? t : L.groups, g1 = t + 1 < L.groups ? t + 1 : L.groups;
+    z0 = tab[g0];
+    z1 = tab[g1];
+}
+
+// Sign+mantissa and plane bytes of tile t of a coded stream into a stage: two
+// direct-to-LDS loads per wave (1 KiB of sign+mantissa bytes; 384 bytes of the
+// three planes, lanes 0..23).  A chunk past the end reads the stream's first
+// bytes instead (always inside the buffer); those values are masked later.
+__device__ __forceinline__ void red_issue_data(const RedMeta &m, const Layout &L, uint64_t n, uint64_t tile0,
+                                               RedStage &st, int lane, int wave) {
+    const uint64_t v = tile0 + 1024u * (uint32_t)wave + 16u * (uint32_t)lane;
+    const uint8_t *src = v < n ? m.in + kHeaderBytes + v : m.in;
+    lds_load16(src, lds_base(st.sm + 1024u * (uint32_t)wave));
+    const uint32_t pbase = lds_base(st.planes + 384u * (uint32_t)wave);
+    if (lane < 24) {
+        const uint32_t cb = 384u * (uint32_t)wave + 16u * (uint32_t)lane;  // byte of the three planes
+        const uint32_t plane = cb / kRedPlaneBytes, off = cb % kRedPlaneBytes;
+        const uint64_t pv = (tile0 / 8 + off) * 8;  // first value of the chunk
+        const uint8_t *psrc = pv < n ? m.in + L.off_p0 + plane * L.plane_bytes + tile0 / 8 + off : m.in;
+        lds_load16(psrc, pbase);
+    }
+}
+
+// Checks and clamps the table entries (reads stay inside the stream; a
+// mismatch sets bad) and lands the slice [off_zp + z0, off_zp + z1) in LDS.
+// Whole dwords go direct to LDS.  A partial last dword is read whole when the
+// buffer holds all of it, else byte by byte.
+__device__ __forceinline__ void red_issue_zp(const RedMeta &m, const Layout &L, uint32_t t, uint32_t &z0, uint32_t &z1,
+                                             bool last, RedZp &zs, int lane, int wave, bool &bad) {
+    if ((t == 0 && z0 != 0) || (last && z1 != m.E)) bad = true;
+    if (z0 > m.E) { bad = true; z0 = (uint32_t)m.E; }
+    if (z1 < z0 || z1 > m.E) { bad = true; z1 = z1 < z0 ? z0 : (uint32_t)m.E; }
+    if (z1 - z0 > kRedTile) { bad = true; z1 = z0 + kRedTile; }
+    const uint64_t A0 = L.off_zp + z0, A1 = L.off_zp + z1;
+    const uint64_t a0 = A0 & ~uint64_t(3);
+    const uint64_t a1 = (A1 + 3 <= m.in_bytes) ? ((A1 + 3) & ~uint64_t(3)) : (A1 & ~uint64_t(3));
+    const uint32_t ndw = (uint32_t)((a1 - a0) / 4);
+    for (uint32_t i0 = 64u * (uint32_t)wave; i0 < ndw; i0 += kThreads) {
+        const uint32_t base = lds_base(zs.w + i0);
+        if (i0 + (uint32_t)lane < ndw) lds_load4(m.in + a0 + 4u * (i0 + (uint32_t)lane), base);
+    }
+    if (A1 > a1 && wave == 0 && lane == 0) {  // a partial dword at the very end of the buffer
+        uint32_t w = 0;
+        for (uint32_t i = 0; i < (uint32_t)(A1 - a1); ++i) w |= (uint32_t)m.in[a1 + i] << (8 * i);
+        zs.w[ndw] = w;
+    }
+}
+
+// Zero-point ranks inside a 4096-value tile: 2 steps per lane, order wave,
+// step, lane, value.  No barrier: every wave counts the zero-point codes of
+// the whole tile from the plane words in LDS (lane l: 32-value chunks l and
+// l + 64; one packed DPP scan), which gives its own offset and the total.
+__device__ __forceinline__ uint32_t red_ranks(const RedStage &st, uint64_t tile0, uint64_t n,
+                                              const uint32_t (&zmask)[kRedSteps], int lane, int wave,
+                                              uint32_t (&rank)[kRedSteps]) {
+    const uint32_t *pw = reinterpret_cast<const uint32_t *>(st.planes);
+    auto chunk_count = [&](uint32_t c) {
+        uint32_t z = ~(pw[c] | pw[kRedPlaneBytes / 4 + c] | pw[2 * kRedPlaneBytes / 4 + c]);
+        const uint64_t v0 = tile0 + 32u * c;
+        if (v0 + 32 > n) z = v0 >= n ? 0u : z & ((1u << (uint32_t)(n - v0)) - 1u);
+        return (uint32_t)__builtin_popcount(z);
+    };
+    const uint32_t a = chunk_count((uint32_t)lane) | (chunk_count((uint32_t)lane + 64u) << 16);
+    const uint32_t ai = wave_inclusive_scan(a);
+    const uint32_t h31 = (uint32_t)__builtin_amdgcn_readlane((int)ai, 31);
+    const uint32_t h63 = (uint32_t)__builtin_amdgcn_readlane((int)ai, kWave - 1);
+    const uint32_t A1 = h31 & 0xFFFFu, A = h63 & 0xFFFFu, B1 = h31 >> 16, B = h63 >> 16;  // values [0,1024), [0,2048), ...
+    const uint32_t wave_off = wave == 0 ? 0u : (wave == 1 ? A1 : (wave == 2 ? A : A + B1));
+    const uint32_t c0 = __builtin_popcount(zmask[0]), c1 = __builtin_popcount(zmask[1]);
+    const uint32_t s = c0 | (c1 << 16);
+    const uint32_t si = wave_inclusive_scan(s);
+    const uint32_t st_ = (uint32_t)__builtin_amdgcn_readlane((int)si, kWave - 1);
+    const uint32_t se = si - s;
+    rank[0] = wave_off + (se & 0xFFFFu);
+    rank[1] = wave_off + (st_ & 0xFFFFu) + (se >> 16);
+    return A + B;
+}
+
+// The sums start at -0.0 when there is no local share: -0.0 + x is x exactly
+// for every x (+0 and -0 included), so the first term enters exactly.
+__device__ __forceinline__ void red_accumulate(const uint32_t (&vals)[kRedSteps][4], float (&acc)[kRedSteps][8]) {
+#pragma unroll
+    for (int u = 0; u < kRedSteps; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[u][2 * j] += bf16_lo(vals[u][j]);
+            acc[u][2 * j + 1] += bf16_hi(vals[u][j]);
+        }
+}
+
+// (Each path accumulates on its own: a merge after the raw path's register
+// loads would make the coded path wait for every load in flight.)
+__device__ __forceinline__ void red_add(const RedMeta &m, uint64_t n, uint64_t tile0, const RedStage &st,
+                                        const RedZp &zs, uint32_t z0, uint32_t z1, const uint2 *sel,
+                                        float (&acc)[kRedSteps][8], bool &bad, int lane, int wave) {
+    uint32_t vals[kRedSteps][4];
+    if (m.raw) {
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(m.in + kHeaderBytes);
+#pragma unroll
+        for (int u = 0; u < kRedSteps; ++u) {
+            const uint64_t base = tile0 + 512u * (uint32_t)(wave * kRedSteps + u) + 8u * (uint32_t)lane;
+            uint32_t w4[4] = {0, 0, 0, 0};
+            if (base + 8 <= n) {
+                const uint4 q = load_stream16(src + base);
+                w4[0] = q.x;
+                w4[1] = q.y;
+                w4[2] = q.z;
+                w4[3] = q.w;
+            } else {
+                for (uint32_t i = 0; base + i < n; ++i) w4[i / 2] |= (uint32_t)src[base + i] << (16 * (i % 2));
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vals[u][j] = w4[j];
+        }
+        red_accumulate(vals, acc);
+    } else {
+        uint32_t e[kRedSteps][2], zmask[kRedSteps], sm[kRedSteps][2];
+#pragma unroll
+        for (int u = 0; u < kRedSteps; ++u) {
+            const uint32_t lb = 512u * (uint32_t)(wave * kRedSteps + u) + 8u * (uint32_t)lane;
+            const uint64_t base = tile0 + lb;
+            const uint32_t vmask = base + 8 <= n ? 0xFFu : (base < n ? (1u << (uint32_t)(n - base)) - 1u : 0u);
+            const uint2 q = *reinterpret_cast<const uint2 *>(st.sm + lb);
+            sm[u][0] = q.x;
+            sm[u][1] = q.y;
+            const uint32_t planes = (uint32_t)st.planes[lb / 8] | ((uint32_t)st.planes[kRedPlaneBytes + lb / 8] << 8) |
+                                    ((uint32_t)st.planes[2 * kRedPlaneBytes + lb / 8] << 16);
+            uint32_t c_lo, c_hi;
+            planes_to_codes(planes, c_lo, c_hi);
+            e[u][0] = perm(m.tbl_hi, m.tbl_lo, c_lo);
+            e[u][1] = perm(m.tbl_hi, m.tbl_lo, c_hi);
+            zmask[u] = zero_point_mask(planes) & vmask;
+        }
+        uint32_t rank[kRedSteps];
+        const uint32_t total = red_ranks(st, tile0, n, zmask, lane, wave, rank);
+        if (total != z1 - z0) bad = true;
+        // slice byte j sits at byte (z0 & 3) + j of zs.w (the slice starts on a
+        // dword boundary at or before off_zp + z0; off_zp is 128-aligned)
+        const uint32_t lead = z0 & 3u, zspan = z1 - z0;
+#pragma unroll
+        for (int u = 0; u < kRedSteps; ++u) {
+            // a rank past the slice (a corrupt table, already flagged) reads
+            // the buffer's slack instead
+            const uint32_t r = lead + (rank[u] <= zspan ? rank[u] : zspan);
+            put_zero_points(e[u][0], e[u][1], zmask[u], r, zs.w, sel);
+            rebuild4(sm[u][0], e[u][0], vals[u][0], vals[u][1]);
+            rebuild4(sm[u][1], e[u][1], vals[u][2], vals[u][3]);
+        }
+        red_accumulate(vals, acc);
+    }
+}
+
+// One block per 4096-value tile.  Every block first checks every stream's
 // header, so a bad header anywhere leaves the whole output untouched.  The
-// float32 sums start from the local value (exact) or from the first stream's
-// value (exact), then take the streams in order.
+// float32 sums start from the local value, or from -0.0 (so that the first
+// stream's value enters exactly), then take the streams in order.
 __global__ __launch_bounds__(kThreads) void reduce_kernel(RedArgs args) {
-    __shared__ RedShared sh;
+    __shared__ RedStage s_st[2];
+    __shared__ RedZp s_zp[2];
+    __shared__ RedHdr s_hdr[ZC_MAX_BATCH];
+    __shared__ uint2 s_sel[256];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const uint32_t t = blockIdx.x;
     const uint64_t n = args.n;
     const Layout L = layout_for(n);
+    const uint64_t tile0 = (uint64_t)t * kRedTile;
+    const bool last = tile0 + kRedTile >= n;
+    const uint32_t k = args.k;
 
-    bool ok = true;
-    for (uint32_t s = 0; s < args.k; ++s) {
-        uint32_t lo, hi;
-        uint64_t E;
-        bool raw;
-        ok = header_ok(args.s[s].in, args.s[s].in_bytes, n, L, lo, hi, E, raw) & ok;
-    }
-    if (!ok) {
+    zp_selectors(s_sel);  // visible after the barrier in the header check
+    // the headers' words use the stages, which are free until the first load
+    static_assert(sizeof(s_st) >= 4u * 32u * ZC_MAX_BATCH, "room for every header");
+    if (!red_check_headers(args, n, L, reinterpret_cast<uint32_t *>(s_st), s_hdr)) {
         if (tid == 0 && args.status) *args.status = ZC_ERR_CORRUPT;
         return;
     }
 
-    float acc[kSteps][8];
-    bool have = false;  // uniform
+    float acc[kRedSteps][8];
+#pragma unroll
+    for (int u = 0; u < kRedSteps; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[u][j] = -0.0f;
     if (args.local) {
 #pragma unroll
-        for (int u = 0; u < kSteps; ++u) {
-            const uint64_t base = (uint64_t)t * kTile + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
+        for (int u = 0; u < kRedSteps; ++u) {
+            const uint64_t base = tile0 + 512u * (uint32_t)(wave * kRedSteps + u) + 8u * (uint32_t)lane;
             uint32_t w4[4] = {0, 0, 0, 0};
             if (base + 8 <= n) {
                 const uint4 v = load_stream16(args.local + base);
@@ -1240,51 +1441,61 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(RedArgs args) {
                 acc[u][2 * j + 1] = bf16_hi(w4[j]);
             }
         }
-        have = true;
     }
+
     bool bad = false;
-    for (uint32_t s = 0; s < args.k; ++s) {
-        const uint8_t *const in = args.s[s].in;
-        uint32_t tbl_lo, tbl_hi;
-        uint64_t E;
-        bool raw;
-        header_ok(in, args.s[s].in_bytes, n, L, tbl_lo, tbl_hi, E, raw);
-        uint32_t vals[kSteps][4];
-        if (raw) {
-            // the raw fallback form: the values follow the header
-            const uint16_t *src = reinterpret_cast<const uint16_t *>(in + kHeaderBytes);
-#pragma unroll
-            for (int u = 0; u < kSteps; ++u) {
-                const uint64_t base = (uint64_t)t * kTile + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
-                uint32_t w4[4] = {0, 0, 0, 0};
-                if (base + 8 <= n) {
-                    const uint4 q = load_stream16(src + base);
-                    w4[0] = q.x;
-                    w4[1] = q.y;
-                    w4[2] = q.z;
-                    w4[3] = q.w;
-                } else {
-                    for (uint32_t i = 0; base + i < n; ++i) w4[i / 2] |= (uint32_t)src[base + i] << (16 * (i % 2));
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) vals[u][j] = w4[j];
-            }
-        } else {
-            decode_tile(in, n, L, t, tbl_lo, tbl_hi, E, sh, vals, bad);
+    if (k) {
+        // Stream s sits in stage s % 2 and slice buffer s % 2.  Prologue:
+        // data(0), slice(0), data(1); a raw stream issues neither.
+        RedMeta cur = red_meta(args, 0, s_hdr), nxt = cur;
+        uint32_t cz0 = 0, cz1 = 0, nz0 = 0, nz1 = 0;
+        if (!cur.raw) {
+            red_issue_data(cur, L, n, tile0, s_st[0], lane, wave);
+            red_table(cur, L, t, cz0, cz1);
+            red_issue_zp(cur, L, t, cz0, cz1, last, s_zp[0], lane, wave, bad);
         }
-#pragma unroll
-        for (int u = 0; u < kSteps; ++u)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float a = bf16_lo(vals[u][j]), b = bf16_hi(vals[u][j]);
-                acc[u][2 * j] = have ? acc[u][2 * j] + a : a;
-                acc[u][2 * j + 1] = have ? acc[u][2 * j + 1] + b : b;
+        if (k > 1) {
+            nxt = red_meta(args, 1, s_hdr);
+            if (!nxt.raw) {
+                red_issue_data(nxt, L, n, tile0, s_st[1], lane, wave);
+                red_table(nxt, L, t, nz0, nz1);
             }
-        have = true;
+        }
+        for (uint32_t s = 0; s < k; ++s) {
+            const uint32_t x = s & 1u;
+            // the loads still allowed in flight: the data of stream s + 1 (two
+            // per wave), issued after everything stream s needs
+            if (s + 1 < k && !nxt.raw)
+                __builtin_amdgcn_s_waitcnt(kWaitVm2);
+            else
+                __builtin_amdgcn_s_waitcnt(kWaitVm0);
+            __syncthreads();
+            // slice buffer x ^ 1 was last read by stream s - 1, before the
+            // barrier that ended its step: the next slice goes out now, and
+            // lands while stream s is decoded
+            if (s + 1 < k && !nxt.raw) red_issue_zp(nxt, L, t, nz0, nz1, last, s_zp[x ^ 1u], lane, wave, bad);
+            red_add(cur, n, tile0, s_st[x], s_zp[x], cz0, cz1, s_sel, acc, bad, lane, wave);
+            __syncthreads();  // stage x is free
+            RedMeta nn = nxt;
+            uint32_t n0 = 0, n1 = 0;
+            if (s + 2 < k) {
+                nn = red_meta(args, s + 2, s_hdr);
+                if (!nn.raw) {
+                    red_issue_data(nn, L, n, tile0, s_st[x], lane, wave);
+                    red_table(nn, L, t, n0, n1);
+                }
+            }
+            cur = nxt;
+            cz0 = nz0;
+            cz1 = nz1;
+            nxt = nn;
+            nz0 = n0;
+            nz1 = n1;
+        }
     }
 #pragma unroll
-    for (int u = 0; u < kSteps; ++u) {
-        const uint64_t base = (uint64_t)t * kTile + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
+    for (int u = 0; u < kRedSteps; ++u) {
+        const uint64_t base = tile0 + 512u * (uint32_t)(wave * kRedSteps + u) + 8u * (uint32_t)lane;
         uint32_t o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[j] = float_to_bf16(acc[u][2 * j]) | (float_to_bf16(acc[u][2 * j + 1]) << 16);
@@ -1515,7 +1726,7 @@ extern "C" zc_status zc_decompress_reduce(const void *const *d_streams, const ui
         if (rc != ZC_OK) return rc;
     }
     // n = 0 still runs one block: every header is checked, nothing is written
-    const uint64_t blocks = n ? (n + kTile - 1) / kTile : 1;
+    const uint64_t blocks = n ? (n + kRedTile - 1) / kRedTile : 1;
     hipLaunchKernelGGL(reduce_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
 }
