@@ -1395,7 +1395,9 @@ __device__ __forceinline__ void red_add(const RedMeta &m, uint64_t n, uint64_t t
 // header, so a bad header anywhere leaves the whole output untouched.  The
 // float32 sums start from the local value, or from -0.0 (so that the first
 // stream's value enters exactly), then take the streams in order.
-__global__ __launch_bounds__(kThreads) void reduce_kernel(RedArgs args) {
+// Six waves per SIMD: the register budget (80) costs a few spills, which
+// measured cheaper than the fifth block per CU it buys is worth.
+__global__ __launch_bounds__(kThreads, 6) void reduce_kernel(RedArgs args) {
     __shared__ RedStage s_st[2];
     __shared__ RedZp s_zp[2];
     __shared__ RedHdr s_hdr[ZC_MAX_BATCH];
