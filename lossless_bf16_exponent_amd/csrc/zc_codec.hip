@@ -541,21 +541,29 @@ typedef __attribute__((address_space(1))) void global_void;
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kCachePolicySc1 = 16;  // agent-scope coherence, as the atomics above
 
-__device__ __forceinline__ void land_span(const uint8_t *src, uint32_t units, uint8_t *land, int lane) {
-    for (uint32_t u0 = 0; u0 < units; u0 += kWave) {
+// Chunks c0, c0 + stride, ... of kWave units each (the waves of a block share
+// a span's chunks, so one large span is not left to a single wave).
+__device__ __forceinline__ void land_span(const uint8_t *src, uint32_t units, uint8_t *land, int lane, uint32_t c0,
+                                          uint32_t stride) {
+    for (uint32_t u0 = kWave * c0; u0 < units; u0 += kWave * stride) {
         if (u0 + (uint32_t)lane < units)
             __builtin_amdgcn_global_load_lds((global_void *)(src + 16u * (u0 + (uint32_t)lane)),
                                              (lds_void *)(land + 16u * u0), 16, 0, kCachePolicySc1);
     }
 }
 
-__device__ __forceinline__ void write_span(uint8_t *zp, uint64_t dst_off, const uint8_t *land, uint32_t T, int lane) {
+// Rounds c0, c0 + stride, ... of 2 * kWave destination dwords each.
+__device__ __forceinline__ uint32_t span_dwords(uint64_t dst_off, uint32_t T) {
+    return T ? ((uint32_t)(dst_off & 3u) + T + 3) / 4 : 0u;
+}
+__device__ __forceinline__ void write_span(uint8_t *zp, uint64_t dst_off, const uint8_t *land, uint32_t T, int lane,
+                                           uint32_t c0, uint32_t stride) {
     if (T == 0) return;
     const uint32_t r = (uint32_t)(dst_off & 3u);
     uint8_t *const dst = zp + (dst_off - r);
     const uint32_t ndw = (r + T + 3) / 4;
     const uint32_t *const w = reinterpret_cast<const uint32_t *>(land);
-    for (uint32_t k0 = 0; k0 < ndw; k0 += 2 * kWave) {
+    for (uint32_t k0 = 2 * kWave * c0; k0 < ndw; k0 += 2 * kWave * stride) {
         const uint32_t k = k0 + 2u * (uint32_t)lane;
         if (k >= ndw) break;
         // source dwords k-1 .. k+1 (the landing zone has slack past every span)
@@ -720,17 +728,31 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
                     hi = mid - 1;
             }
             const uint32_t j1 = lo;
-            for (uint32_t j = j0 + wave; j < j1; j += kWaves) {
+            // Many spans in the batch: wave w takes spans j0 + w, j0 + w + 4, ...
+            // Fewer spans than waves (spans of many zero-points): the chunks of
+            // the spans (64 units to land; 128 destination dwords to write) are
+            // numbered across the batch and wave w takes every kWaves-th one,
+            // so a large span is not left to one wave.
+            const bool split = j1 - j0 < (uint32_t)kWaves;
+            const uint32_t jw = split ? j0 : j0 + (uint32_t)wave, js = split ? 1u : (uint32_t)kWaves;
+            uint32_t g = 0;
+            for (uint32_t j = jw; j < j1; j += js) {
                 const uint32_t a16 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(sh.land16[j] - u0));
                 const uint32_t units = (uint32_t)__builtin_amdgcn_readfirstlane((int)(sh.land16[j + 1] - sh.land16[j]));
-                land_span(slots + (uint64_t)(first + j) * kEncSpan, units, sh.land + 16u * a16, lane);
+                land_span(slots + (uint64_t)(first + j) * kEncSpan, units, sh.land + 16u * a16, lane,
+                          split ? ((uint32_t)wave + kWaves - g % kWaves) % kWaves : 0u, split ? kWaves : 1u);
+                g += (units + kWave - 1) / kWave;
             }
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();  // the batch has landed
-            for (uint32_t j = j0 + wave; j < j1; j += kWaves) {
+            g = 0;
+            for (uint32_t j = jw; j < j1; j += js) {
                 const uint32_t p = (uint32_t)__builtin_amdgcn_readfirstlane((int)sh.pre[j]);
                 const uint32_t T = (uint32_t)__builtin_amdgcn_readfirstlane((int)sh.pre[j + 1]) - p;
-                write_span(zp, (uint64_t)Pu + p, sh.land + 16u * (sh.land16[j] - u0), T, lane);
+                const uint64_t dst = (uint64_t)Pu + p;
+                write_span(zp, dst, sh.land + 16u * (sh.land16[j] - u0), T, lane,
+                           split ? ((uint32_t)wave + kWaves - g % kWaves) % kWaves : 0u, split ? kWaves : 1u);
+                g += (span_dwords(dst, T) + 2 * kWave - 1) / (2 * kWave);
             }
             j0 = j1;
             if (j0 < count) __syncthreads();  // the landing zone is reused
