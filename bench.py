@@ -272,7 +272,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures the codec on one GPU; multi-GPU runs are not part of this build "
+        print("bench.py measures the codec on one GPU; runs on several GPUs are not supported "
               "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
         return 2
 
