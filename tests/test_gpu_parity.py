@@ -132,6 +132,38 @@ def test_output_buffer_reuse_and_old_contents(zc):
             assert np.array_equal(buf[:ref.size].cpu().numpy(), ref), (n, i)
 
 
+def test_calls_in_flight_on_two_streams(zc):
+    """Compress calls on two HIP streams at once (each call has its own token
+    and scratch), several rounds with no synchronization between the streams,
+    then decodes on both streams: every stream equals the oracle's and every
+    decode the input.  Default stream priority on both."""
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    cases = [(2_000_003, 0.02, WINDOW_PLAN), (1_500_001, 1e-3, oracle.plan_from_sigma(1e-3)),
+             (700_001, 0.16, WINDOW_PLAN), (3_000_017, 0.05, oracle_pins.HAND_PLAN)]
+    xs = [gaussian(n, sig, 300 + i) for i, (n, sig, _) in enumerate(cases)]
+    dev = [to_device(x) for x in xs]
+    caps = [zc.zc_max_compressed_bytes(n) for n, _, _ in cases]
+    bufs = [torch.empty(c, dtype=torch.uint8, device="cuda") for c in caps]
+    sizes = torch.zeros(len(cases), dtype=torch.int64, device="cuda")
+    outs = [torch.empty_like(d) for d in dev]
+    st = torch.full((len(cases),), -1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    for rnd in range(3):
+        for i, (n, _, plan) in enumerate(cases):
+            s = sa if i % 2 == 0 else sb
+            zc.zc_compress(dev[i], n, plan, bufs[i], caps[i], sizes.data_ptr() + 8 * i, stream=s)
+    for i, (n, _, _) in enumerate(cases):
+        s = sa if i % 2 == 0 else sb
+        zc.zc_decompress(bufs[i], caps[i], n, outs[i], st.data_ptr() + 4 * i, stream=s)
+    torch.cuda.synchronize()
+    assert not st.cpu().numpy().any()
+    for i, (n, _, plan) in enumerate(cases):
+        ref = oracle.encode(xs[i], plan)
+        assert int(sizes[i].item()) == ref.size, i
+        assert np.array_equal(bufs[i][:ref.size].cpu().numpy(), ref), i
+        assert torch.equal(outs[i], dev[i]), i
+
+
 def test_decoder_reads_oracle_streams(zc):
     """The GPU decoder on streams written by the oracle (not by the GPU encoder)."""
     for n, plan in ((1_000_003, WINDOW_PLAN), (9000, oracle_pins.HAND_PLAN), (0, WINDOW_PLAN)):
