@@ -372,7 +372,7 @@ static_assert(kLandBytes >= kEncSpan, "one span always lands");
 struct FinShared {
     union {
         uint32_t span[kFinWindow];                      // span-word payloads of the window
-        __align__(16) uint8_t land[kLandBytes + 32];    // later: landed staged bytes (+ slack)
+        __align__(16) uint8_t land[kLandBytes + 48];    // later: landed staged bytes (+ slack for reads past a span)
     };
     uint32_t pre[kFinRunMax + 1];   // zero-points of the run before each of its spans
     uint32_t land16[kFinRunMax + 1];  // 16-byte units of the run's spans before each span
@@ -537,6 +537,39 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
 // byte-aligned window over source dwords k-1 and k of the landed copy.  A wave
 // writes 128 destination dwords per round (lane l: dwords 2l, 2l + 1); dwords
 // shared with the neighbouring spans get byte stores.
+// Writes several small spans at once: a group of 16 lanes per span, each lane
+// 8 consecutive destination dwords per round (128 per span-round).  Same
+// destination bytes and byte-exact edges as write_span; sources: the span's
+// landed copy (the zone has slack past every span).
+__device__ __forceinline__ void write_span_group(uint8_t *zp, uint64_t dst_off, const uint8_t *land, uint32_t T,
+                                                 uint32_t gl) {
+    if (T == 0) return;
+    const uint32_t r = (uint32_t)(dst_off & 3u);
+    uint8_t *const dst = zp + (dst_off - r);
+    const uint32_t ndw = (r + T + 3) / 4;
+    const uint32_t *const w = reinterpret_cast<const uint32_t *>(land);
+    for (uint32_t k0 = 8u * gl; k0 < ndw; k0 += 128u) {
+        uint32_t src[9];  // source dwords k0 - 1 .. k0 + 7
+        src[0] = k0 ? w[k0 - 1] : 0u;
+        const uint4 a = *reinterpret_cast<const uint4 *>(w + k0), b = *reinterpret_cast<const uint4 *>(w + k0 + 4);
+        src[1] = a.x; src[2] = a.y; src[3] = a.z; src[4] = a.w;
+        src[5] = b.x; src[6] = b.y; src[7] = b.z; src[8] = b.w;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t m = k0 + (uint32_t)i;
+            if (m >= ndw) break;
+            const uint32_t d = r ? __builtin_amdgcn_alignbyte(src[i + 1], src[i], 4 - r) : src[i + 1];
+            const int64_t b0 = (int64_t)4 * m - r;  // source index of the dword's byte 0
+            if (b0 >= 0 && b0 + 4 <= (int64_t)T) {
+                *reinterpret_cast<uint32_t *>(dst + 4u * m) = d;
+            } else {
+                for (int j = 0; j < 4; ++j)
+                    if (b0 + j >= 0 && b0 + j < (int64_t)T) dst[4u * m + j] = (uint8_t)(d >> (8 * j));
+            }
+        }
+    }
+}
+
 typedef __attribute__((address_space(1))) void global_void;
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kCachePolicySc1 = 16;  // agent-scope coherence, as the atomics above
@@ -745,14 +778,26 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
             }
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();  // the batch has landed
-            g = 0;
-            for (uint32_t j = jw; j < j1; j += js) {
-                const uint32_t p = (uint32_t)__builtin_amdgcn_readfirstlane((int)sh.pre[j]);
-                const uint32_t T = (uint32_t)__builtin_amdgcn_readfirstlane((int)sh.pre[j + 1]) - p;
-                const uint64_t dst = (uint64_t)Pu + p;
-                write_span(zp, dst, sh.land + 16u * (sh.land16[j] - u0), T, lane,
-                           split ? ((uint32_t)wave + kWaves - g % kWaves) % kWaves : 0u, split ? kWaves : 1u);
-                g += (span_dwords(dst, T) + 2 * kWave - 1) / (2 * kWave);
+            if (split) {
+                g = 0;
+                for (uint32_t j = jw; j < j1; j += js) {
+                    const uint32_t p = (uint32_t)__builtin_amdgcn_readfirstlane((int)sh.pre[j]);
+                    const uint32_t T = (uint32_t)__builtin_amdgcn_readfirstlane((int)sh.pre[j + 1]) - p;
+                    const uint64_t dst = (uint64_t)Pu + p;
+                    write_span(zp, dst, sh.land + 16u * (sh.land16[j] - u0), T, lane,
+                               ((uint32_t)wave + kWaves - g % kWaves) % kWaves, kWaves);
+                    g += (span_dwords(dst, T) + 2 * kWave - 1) / (2 * kWave);
+                }
+            } else {
+                // four of the wave's spans at a time, 16 lanes each
+                const uint32_t grp = (uint32_t)lane >> 4, gl = (uint32_t)lane & 15u;
+                for (uint32_t jq = jw; jq < j1; jq += 4u * kWaves) {
+                    const uint32_t j = jq + grp * kWaves;
+                    if (j < j1) {
+                        const uint32_t p = sh.pre[j], T = sh.pre[j + 1] - p;
+                        write_span_group(zp, (uint64_t)Pu + p, sh.land + 16u * (sh.land16[j] - u0), T, gl);
+                    }
+                }
             }
             j0 = j1;
             if (j0 < count) __syncthreads();  // the landing zone is reused
