@@ -720,6 +720,49 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
         }
     }
 
+    __syncthreads();  // sh.pre, sh.land16 complete; sh.span is no longer read
+
+    // ---- staged bytes -> the zero-point array, a batch of spans at a time:
+    // spans [j0, j1) whose landing units fit the zone.  The first batch lands
+    // while the totals of older runs are still awaited (the landing needs only
+    // the run's own prefixes; the destination needs those totals).
+    uint8_t *const zp = out + L.off_zp;
+    const uint8_t *const slots = scratch + S.staging;
+    auto batch_end = [&](uint32_t j0, uint32_t u0) {  // largest j1 with land16[j1] - u0 <= kLandBytes / 16
+        uint32_t lo = j0 + 1, hi = count;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi + 1) / 2;
+            if (sh.land16[mid] - u0 <= kLandBytes / 16)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        return lo;
+    };
+    // Many spans in a batch: wave w takes spans j0 + w, j0 + w + 4, ...  Fewer
+    // spans than waves (spans of many zero-points): the chunks of the spans (64
+    // units to land; 128 destination dwords to write) are numbered across the
+    // batch and wave w takes every kWaves-th one, so a large span is not left
+    // to one wave.
+    auto land_batch = [&](uint32_t j0, uint32_t j1, uint32_t u0) {
+        const bool split = j1 - j0 < (uint32_t)kWaves;
+        const uint32_t jw = split ? j0 : j0 + (uint32_t)wave, js = split ? 1u : (uint32_t)kWaves;
+        uint32_t g = 0;
+        for (uint32_t j = jw; j < j1; j += js) {
+            const uint32_t a16 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(sh.land16[j] - u0));
+            const uint32_t units = (uint32_t)__builtin_amdgcn_readfirstlane((int)(sh.land16[j + 1] - sh.land16[j]));
+            land_span(slots + (uint64_t)(first + j) * kEncSpan, units, sh.land + 16u * a16, lane,
+                      split ? ((uint32_t)wave + kWaves - g % kWaves) % kWaves : 0u, split ? kWaves : 1u);
+            g += (units + kWave - 1) / kWave;
+        }
+    };
+    uint32_t j0 = 0, j1 = 0, u0 = 0;
+    if (ok) {
+        u0 = sh.land16[0];
+        j1 = batch_end(0, u0);
+        land_batch(0, j1, u0);
+    }
+
     // ---- totals of the runs older than the window (segments over kFinWindow spans)
     if (ok && wr) {
         uint32_t rp[4];
@@ -730,7 +773,6 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
         ok = __syncthreads_and(ok);
         P += sh.red[1][0] + sh.red[1][1] + sh.red[1][2] + sh.red[1][3];
     }
-    __syncthreads();  // sh.pre, sh.land16 complete; sh.span is no longer read
 
     if (ok) {
         // ---- table entries of the run's groups
@@ -744,43 +786,14 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
             if (g0 + 2 < L.groups) tab[g0 + 2] = P + ex + T0;
             if (g0 + 3 < L.groups) tab[g0 + 3] = P + ex + T0 + g10;
         }
-        // ---- staged bytes -> the zero-point array, a batch of spans at a time:
-        // spans [j0, j1) whose landing units fit the zone; wave w lands and
-        // writes spans j0 + w, j0 + w + 4, ...
-        uint8_t *const zp = out + L.off_zp;
-        const uint8_t *const slots = scratch + S.staging;
         const uint32_t Pu = (uint32_t)__builtin_amdgcn_readfirstlane((int)P);
-        for (uint32_t j0 = 0; j0 < count;) {
-            const uint32_t u0 = sh.land16[j0];
-            uint32_t lo = j0 + 1, hi = count;  // largest j1 with land16[j1] - u0 <= kLandBytes / 16
-            while (lo < hi) {
-                const uint32_t mid = (lo + hi + 1) / 2;
-                if (sh.land16[mid] - u0 <= kLandBytes / 16)
-                    lo = mid;
-                else
-                    hi = mid - 1;
-            }
-            const uint32_t j1 = lo;
-            // Many spans in the batch: wave w takes spans j0 + w, j0 + w + 4, ...
-            // Fewer spans than waves (spans of many zero-points): the chunks of
-            // the spans (64 units to land; 128 destination dwords to write) are
-            // numbered across the batch and wave w takes every kWaves-th one,
-            // so a large span is not left to one wave.
-            const bool split = j1 - j0 < (uint32_t)kWaves;
-            const uint32_t jw = split ? j0 : j0 + (uint32_t)wave, js = split ? 1u : (uint32_t)kWaves;
-            uint32_t g = 0;
-            for (uint32_t j = jw; j < j1; j += js) {
-                const uint32_t a16 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(sh.land16[j] - u0));
-                const uint32_t units = (uint32_t)__builtin_amdgcn_readfirstlane((int)(sh.land16[j + 1] - sh.land16[j]));
-                land_span(slots + (uint64_t)(first + j) * kEncSpan, units, sh.land + 16u * a16, lane,
-                          split ? ((uint32_t)wave + kWaves - g % kWaves) % kWaves : 0u, split ? kWaves : 1u);
-                g += (units + kWave - 1) / kWave;
-            }
+        for (;;) {
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();  // the batch has landed
+            const bool split = j1 - j0 < (uint32_t)kWaves;
             if (split) {
-                g = 0;
-                for (uint32_t j = jw; j < j1; j += js) {
+                uint32_t g = 0;
+                for (uint32_t j = j0; j < j1; ++j) {
                     const uint32_t p = (uint32_t)__builtin_amdgcn_readfirstlane((int)sh.pre[j]);
                     const uint32_t T = (uint32_t)__builtin_amdgcn_readfirstlane((int)sh.pre[j + 1]) - p;
                     const uint64_t dst = (uint64_t)Pu + p;
@@ -791,7 +804,7 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
             } else {
                 // four of the wave's spans at a time, 16 lanes each
                 const uint32_t grp = (uint32_t)lane >> 4, gl = (uint32_t)lane & 15u;
-                for (uint32_t jq = jw; jq < j1; jq += 4u * kWaves) {
+                for (uint32_t jq = j0 + (uint32_t)wave; jq < j1; jq += 4u * kWaves) {
                     const uint32_t j = jq + grp * kWaves;
                     if (j < j1) {
                         const uint32_t p = sh.pre[j], T = sh.pre[j + 1] - p;
@@ -800,9 +813,14 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
                 }
             }
             j0 = j1;
-            if (j0 < count) __syncthreads();  // the landing zone is reused
+            if (j0 >= count) break;
+            __syncthreads();  // the landing zone is reused
+            u0 = sh.land16[j0];
+            j1 = batch_end(j0, u0);
+            land_batch(j0, j1, u0);
         }
     }
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no landing left in flight (a given-up call)
 
     if (!last) {
         if (ok && tid == 0) put_word(scratch + S.done_words + (uint64_t)kWordBytes * jb, tok, 1u);
