@@ -745,15 +745,44 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
     // batch and wave w takes every kWaves-th one, so a large span is not left
     // to one wave.
     auto land_batch = [&](uint32_t j0, uint32_t j1, uint32_t u0) {
-        const bool split = j1 - j0 < (uint32_t)kWaves;
-        const uint32_t jw = split ? j0 : j0 + (uint32_t)wave, js = split ? 1u : (uint32_t)kWaves;
-        uint32_t g = 0;
-        for (uint32_t j = jw; j < j1; j += js) {
-            const uint32_t a16 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(sh.land16[j] - u0));
-            const uint32_t units = (uint32_t)__builtin_amdgcn_readfirstlane((int)(sh.land16[j + 1] - sh.land16[j]));
-            land_span(slots + (uint64_t)(first + j) * kEncSpan, units, sh.land + 16u * a16, lane,
-                      split ? ((uint32_t)wave + kWaves - g % kWaves) % kWaves : 0u, split ? kWaves : 1u);
-            g += (units + kWave - 1) / kWave;
+        if (j1 - j0 < (uint32_t)kWaves) {
+            uint32_t g = 0;
+            for (uint32_t j = j0; j < j1; ++j) {
+                const uint32_t a16 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(sh.land16[j] - u0));
+                const uint32_t units =
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)(sh.land16[j + 1] - sh.land16[j]));
+                land_span(slots + (uint64_t)(first + j) * kEncSpan, units, sh.land + 16u * a16, lane,
+                          ((uint32_t)wave + kWaves - g % kWaves) % kWaves, kWaves);
+                g += (units + kWave - 1) / kWave;
+            }
+            return;
+        }
+        // Wave w lands a contiguous range of the batch's spans (at most 64), whose
+        // landing units are contiguous in LDS: one load instruction covers 64
+        // units of several spans; a lane finds the span of its unit among the
+        // range's starts (held one per lane).
+        const uint32_t per = (j1 - j0 + kWaves - 1) / kWaves;
+        for (uint32_t a = j0 + (uint32_t)wave * per; a < min(j1, j0 + ((uint32_t)wave + 1) * per); a += kWave) {
+            const uint32_t b = min(min(j1, j0 + ((uint32_t)wave + 1) * per), a + kWave);
+            const uint32_t nsp = b - a;
+            const uint32_t my_start = (uint32_t)lane < nsp ? sh.land16[a + lane] : 0u;
+            const uint32_t ua = (uint32_t)__builtin_amdgcn_readfirstlane((int)sh.land16[a]);
+            const uint32_t ub = (uint32_t)__builtin_amdgcn_readfirstlane((int)sh.land16[b]);
+            for (uint32_t U0 = ua; U0 < ub; U0 += kWave) {
+                const uint32_t U = U0 + (uint32_t)lane;
+                uint32_t js = 0, st = ua;  // the last span of the range starting at or before U
+                for (uint32_t i = 1; i < nsp; ++i) {
+                    const uint32_t si = (uint32_t)__builtin_amdgcn_readlane((int)my_start, (int)i);
+                    if (si <= U) {
+                        js = i;
+                        st = si;
+                    }
+                }
+                if (U < ub)
+                    __builtin_amdgcn_global_load_lds(
+                        (global_void *)(slots + (uint64_t)(first + a + js) * kEncSpan + 16u * (U - st)),
+                        (lds_void *)(sh.land + 16u * (U0 - u0)), 16, 0, kCachePolicySc1);
+            }
         }
     };
     uint32_t j0 = 0, j1 = 0, u0 = 0;
