@@ -1236,80 +1236,42 @@ __device__ __forceinline__ uint32_t float_to_bf16(float f) {
     return (f != f) ? 0x7FC0u : ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// The reduce kernel works on 4096-value tiles (one zero-point group each).
-// Every stream's sign+mantissa bytes and plane bytes for the tile land in LDS
-// through direct-to-LDS loads (no registers), in one of two stages, and its
-// zero-point slice lands in one of two slice buffers.  While stream s is
-// decoded from LDS, the slice of stream s + 1 and the data of stream s + 2 are
-// in flight: a stream costs at most one round trip of waiting, and the
-// registers hold only the 16 float32 accumulators of a thread and one step's
-// decode state, so that many blocks fit on a CU.
+// Work split.  A 4096-value tile (one zero-point group) is decoded by two
+// waves, one per 2048-value half, each lane owning 32 consecutive values; a
+// block holds two tiles.  The waves do not wait for each other while they
+// work: each keeps its lanes' sign+mantissa and plane words in registers (the
+// next stream's in flight while the current one is decoded) and stages its
+// own zero-point slice in LDS.  Half 0's zero-points start at the group's
+// table entry and half 1's end at the next group's, so neither needs the
+// other's count.  At the end the two halves of a tile compare, stream by
+// stream, where the first one's zero-points end and the second one's begin: a
+// table that disagrees with the planes sets the status.
 constexpr uint32_t kRedTile = 4096;
-constexpr int kRedSteps = 2;  // 8-value steps per thread
-static_assert(kRedTile == (uint32_t)kThreads * 8 * kRedSteps, "a thread owns 16 values");
 static_assert(kRedTile == kGroup, "a tile is one zero-point group");
-constexpr uint32_t kRedPlaneBytes = kRedTile / 8;  // per plane per tile
-constexpr uint32_t kRedZpWords = kRedTile / 4 + 3;  // slack for the 3-dword reads of the gather
-
-struct RedStage {
-    uint8_t sm[kRedTile];
-    uint8_t planes[3 * kRedPlaneBytes];  // planes 0, 1, 2 back to back
-};
-
-struct RedZp {
-    uint32_t w[kRedZpWords];  // the tile's zero-point bytes from a dword-aligned start
-};
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
-// lgkmcnt 11:8); only vmcnt is constrained.
-constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitVm2 = 0x0F72;
-
-// Direct-to-LDS loads of the reduce kernel, written as inline assembly: the
-// compiler then adds no waits of its own for them (it would wait for every
-// such load in flight before each LDS read, the next stream's included); the
-// kernel waits for them itself with explicit counts.  Loads return in order,
-// so the compiler's waits for its own loads stay correct with these in flight.
-// The LDS address is the wave-uniform base in M0 plus 16 (or 4) bytes per lane.
-__device__ __forceinline__ uint32_t lds_base(const void *lds) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds);
-}
-__device__ __forceinline__ void lds_load16(const void *src, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(m0), "v"(src)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void lds_load4(const void *src, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off nt" ::"s"(m0), "v"(src)
-                 : "memory", "m0");
-}
-
-// Uniform per-stream facts, re-read from the (cached) header where needed.
-struct RedMeta {
-    const uint8_t *in;
-    uint64_t in_bytes;
-    uint64_t E;
-    uint32_t tbl_lo, tbl_hi;
-    bool raw;
-};
+constexpr uint32_t kRedHalf = kRedTile / 2;
+static_assert(kRedHalf / kWave == 32, "a lane's zero-point flags fill one dword");
+constexpr uint32_t kRedTilesPerBlock = kWaves / 2;
+// Zero-point bytes a wave stages per stream (a quarter of its tile's values).
+// A half with more zero-points than that reads them from memory one by one.
+constexpr uint32_t kRedSliceCap = 1024;
+// the staged bytes from a dword-aligned start (up to 3 bytes of lead-in), and
+// the gather's 3-dword reads at the last zero-point
+constexpr uint32_t kRedSliceWords = 260;
+static_assert(kRedSliceWords >= (kRedSliceCap + 3) / 4 + 3, "room for the gather's reads");
 
 // Per-stream facts of a checked header, kept in LDS: E (two words), the code
-// table (two words).  Bit 31 of E's high word marks a raw stream (E <= 2^32).
+// table (two words).  Bit 31 of E's high word marks a raw stream.
 struct RedHdr {
     uint32_t e_lo, e_hi, tbl_lo, tbl_hi;
 };
 
-__device__ __forceinline__ RedMeta red_meta(const RedArgs &args, uint32_t s, const RedHdr *hdr) {
-    RedMeta m;
-    m.in = args.s[s].in;
-    m.in_bytes = args.s[s].in_bytes;
-    const uint4 h = *reinterpret_cast<const uint4 *>(hdr + s);
-    const uint32_t e_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)h.y);
-    m.E = (uint32_t)__builtin_amdgcn_readfirstlane((int)h.x) | ((uint64_t)(e_hi & 0x7FFFFFFFu) << 32);
-    m.raw = (e_hi >> 31) != 0u;
-    m.tbl_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)h.z);
-    m.tbl_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)h.w);
-    return m;
-}
+struct RedShared {
+    uint32_t slice[kWaves][2][kRedSliceWords];  // before the first stream: every header's 32 words
+    uint32_t edge[kWaves][ZC_MAX_BATCH];        // per stream: where half 0's zero-points end / half 1's begin
+    RedHdr hdr[ZC_MAX_BATCH];
+    uint2 sel[256];
+};
+static_assert(sizeof(RedShared::slice) >= 4u * 32u * ZC_MAX_BATCH, "room for every header");
 
 // Every stream's header at once: the 32 words of each go to LDS with one
 // vector load per thread and word (all in flight together), then thread s
@@ -1348,280 +1310,331 @@ __device__ __forceinline__ bool red_check_headers(const RedArgs &args, uint64_t 
     return __syncthreads_and(ok);
 }
 
-// Table entries of tile t (scalar loads): zero-point values before the tile
-// and before the next one.
-__device__ __forceinline__ void red_table(const RedMeta &m, const Layout &L, uint32_t t, uint32_t &z0, uint32_t &z1) {
-    const_u32 *tab = (const_u32 *)(m.in + L.off_tab);
-    const uint64_t g0 = t < L.groups ? t : L.groups, g1 = t + 1 < L.groups ? t + 1 : L.groups;
-    z0 = tab[g0];
-    z1 = tab[g1];
+// Uniform per-stream facts of a checked header.  E <= n < 2^32.
+struct RedMeta {
+    const uint8_t *in;
+    uint64_t in_bytes;
+    uint32_t E;
+    uint32_t tbl_lo, tbl_hi;  // exponent of code c in byte c of {tbl_hi:tbl_lo} (byte 0 unused)
+    bool raw;
+};
+
+__device__ __forceinline__ RedMeta red_meta(const RedArgs &args, uint32_t s, const RedHdr *hdr) {
+    RedMeta m;
+    m.in = args.s[s].in;
+    m.in_bytes = args.s[s].in_bytes;
+    const uint4 h = *reinterpret_cast<const uint4 *>(hdr + s);
+    m.E = (uint32_t)__builtin_amdgcn_readfirstlane((int)h.x);
+    m.raw = ((uint32_t)__builtin_amdgcn_readfirstlane((int)h.y) >> 31) != 0u;
+    m.tbl_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)h.z);
+    m.tbl_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)h.w);
+    return m;
 }
 
-// Sign+mantissa and plane bytes of tile t of a coded stream into a stage: two
-// direct-to-LDS loads per wave (1 KiB of sign+mantissa bytes; 384 bytes of the
-// three planes, lanes 0..23).  A chunk past the end reads the stream's first
-// bytes instead (always inside the buffer); those values are masked later.
-__device__ __forceinline__ void red_issue_data(const RedMeta &m, const Layout &L, uint64_t n, uint64_t tile0,
-                                               RedStage &st, int lane, int wave) {
-    const uint64_t v = tile0 + 1024u * (uint32_t)wave + 16u * (uint32_t)lane;
-    const uint8_t *src = v < n ? m.in + kHeaderBytes + v : m.in;
-    lds_load16(src, lds_base(st.sm + 1024u * (uint32_t)wave));
-    const uint32_t pbase = lds_base(st.planes + 384u * (uint32_t)wave);
-    if (lane < 24) {
-        const uint32_t cb = 384u * (uint32_t)wave + 16u * (uint32_t)lane;  // byte of the three planes
-        const uint32_t plane = cb / kRedPlaneBytes, off = cb % kRedPlaneBytes;
-        const uint64_t pv = (tile0 / 8 + off) * 8;  // first value of the chunk
-        const uint8_t *psrc = pv < n ? m.in + L.off_p0 + plane * L.plane_bytes + tile0 / 8 + off : m.in;
-        lds_load16(psrc, pbase);
-    }
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): vmcnt(0), the others unconstrained.
+constexpr int kWaitVm0 = 0x0F70;
+
+// Direct-to-LDS dword load, written as inline assembly so that the compiler
+// adds no waits of its own for it; the kernel waits with an explicit count.
+// The LDS address is the wave-uniform base in M0 plus 4 bytes per lane.
+__device__ __forceinline__ uint32_t lds_base(const void *lds) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds);
+}
+__device__ __forceinline__ void lds_load4(const void *src, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off nt" ::"s"(m0), "v"(src)
+                 : "memory", "m0");
 }
 
-// Checks and clamps the table entries (reads stay inside the stream; a
-// mismatch sets bad) and lands the slice [off_zp + z0, off_zp + z1) in LDS.
-// Whole dwords go direct to LDS.  A partial last dword is read whole when the
-// buffer holds all of it, else byte by byte.
-__device__ __forceinline__ void red_issue_zp(const RedMeta &m, const Layout &L, uint32_t t, uint32_t &z0, uint32_t &z1,
-                                             bool last, RedZp &zs, int lane, int wave, bool &bad) {
-    if ((t == 0 && z0 != 0) || (last && z1 != m.E)) bad = true;
-    if (z0 > m.E) { bad = true; z0 = (uint32_t)m.E; }
-    if (z1 < z0 || z1 > m.E) { bad = true; z1 = z1 < z0 ? z0 : (uint32_t)m.E; }
-    if (z1 - z0 > kRedTile) { bad = true; z1 = z0 + kRedTile; }
-    const uint64_t A0 = L.off_zp + z0, A1 = L.off_zp + z1;
+// The lane's values: [v0, v0 + nv) inside the stream, nv = 0..32.
+struct RedLane {
+    uint64_t v0;
+    uint32_t nv;
+    uint32_t vmask;   // bit i: value v0 + i exists
+    uint32_t sm_off;  // byte offsets of its sign+mantissa bytes and plane words (0 past the end: always readable)
+    uint32_t pl_off;
+};
+
+// The lane's sign+mantissa bytes (32) and plane words (one per plane).
+struct RedData {
+    uint4 sm0, sm1;
+    uint32_t p0, p1, p2;
+};
+
+__device__ __forceinline__ void red_load(RedData &d, const RedMeta &m, const Layout &L, const RedLane &ln) {
+    const uint8_t *sm = m.in + kHeaderBytes;
+    const uint8_t *pl = m.in + L.off_p0;
+    d.sm0 = load_stream16(sm + ln.sm_off);
+    d.sm1 = load_stream16(sm + ln.sm_off + 16u);
+    d.p0 = load_stream4(pl + ln.pl_off);
+    d.p1 = load_stream4(pl + L.plane_bytes + ln.pl_off);
+    d.p2 = load_stream4(pl + 2 * L.plane_bytes + ln.pl_off);
+}
+
+// Zero-points [lo, lo + len) of a stream into buf: whole dwords direct to
+// LDS (from the dword holding zero-point lo); a partial last dword is read
+// whole when the buffer holds all of it, else byte by byte.
+__device__ __forceinline__ void red_stage_range(const RedMeta &m, const Layout &L, uint32_t lo, uint32_t len,
+                                                uint32_t *buf, int lane) {
+    const uint64_t A0 = L.off_zp + lo, A1 = A0 + len;
     const uint64_t a0 = A0 & ~uint64_t(3);
     const uint64_t a1 = (A1 + 3 <= m.in_bytes) ? ((A1 + 3) & ~uint64_t(3)) : (A1 & ~uint64_t(3));
     const uint32_t ndw = (uint32_t)((a1 - a0) / 4);
-    for (uint32_t i0 = 64u * (uint32_t)wave; i0 < ndw; i0 += kThreads) {
-        const uint32_t base = lds_base(zs.w + i0);
-        if (i0 + (uint32_t)lane < ndw) lds_load4(m.in + a0 + 4u * (i0 + (uint32_t)lane), base);
-    }
-    if (A1 > a1 && wave == 0 && lane == 0) {  // a partial dword at the very end of the buffer
+    for (uint32_t i0 = 0; i0 < ndw; i0 += kWave)
+        if (i0 + (uint32_t)lane < ndw) lds_load4(m.in + a0 + 4u * (i0 + (uint32_t)lane), lds_base(buf + i0));
+    if (A1 > a1 && lane == 0) {  // a partial dword at the very end of the buffer
         uint32_t w = 0;
         for (uint32_t i = 0; i < (uint32_t)(A1 - a1); ++i) w |= (uint32_t)m.in[a1 + i] << (8 * i);
-        zs.w[ndw] = w;
+        buf[ndw] = w;
     }
 }
 
-// Zero-point ranks inside a 4096-value tile: 2 steps per lane, order wave,
-// step, lane, value.  No barrier: every wave counts the zero-point codes of
-// the whole tile from the plane words in LDS (lane l: 32-value chunks l and
-// l + 64; one packed DPP scan), which gives its own offset and the total.
-__device__ __forceinline__ uint32_t red_ranks(const RedStage &st, uint64_t tile0, uint64_t n,
-                                              const uint32_t (&zmask)[kRedSteps], int lane, int wave,
-                                              uint32_t (&rank)[kRedSteps]) {
-    const uint32_t *pw = reinterpret_cast<const uint32_t *>(st.planes);
-    auto chunk_count = [&](uint32_t c) {
-        uint32_t z = ~(pw[c] | pw[kRedPlaneBytes / 4 + c] | pw[2 * kRedPlaneBytes / 4 + c]);
-        const uint64_t v0 = tile0 + 32u * c;
-        if (v0 + 32 > n) z = v0 >= n ? 0u : z & ((1u << (uint32_t)(n - v0)) - 1u);
-        return (uint32_t)__builtin_popcount(z);
-    };
-    const uint32_t a = chunk_count((uint32_t)lane) | (chunk_count((uint32_t)lane + 64u) << 16);
-    const uint32_t ai = wave_inclusive_scan(a);
-    const uint32_t h31 = (uint32_t)__builtin_amdgcn_readlane((int)ai, 31);
-    const uint32_t h63 = (uint32_t)__builtin_amdgcn_readlane((int)ai, kWave - 1);
-    const uint32_t A1 = h31 & 0xFFFFu, A = h63 & 0xFFFFu, B1 = h31 >> 16, B = h63 >> 16;  // values [0,1024), [0,2048), ...
-    const uint32_t wave_off = wave == 0 ? 0u : (wave == 1 ? A1 : (wave == 2 ? A : A + B1));
-    const uint32_t c0 = __builtin_popcount(zmask[0]), c1 = __builtin_popcount(zmask[1]);
-    const uint32_t s = c0 | (c1 << 16);
-    const uint32_t si = wave_inclusive_scan(s);
-    const uint32_t st_ = (uint32_t)__builtin_amdgcn_readlane((int)si, kWave - 1);
-    const uint32_t se = si - s;
-    rank[0] = wave_off + (se & 0xFFFFu);
-    rank[1] = wave_off + (st_ & 0xFFFFu) + (se >> 16);
-    return A + B;
+// Table entries of tile t, checked and clamped to the stream (a mismatch sets
+// bad), and the zero-points [lo, lo + len) the wave stages in buf: the first
+// ones of the group for half 0, the last ones for half 1, at most
+// kRedSliceCap.
+__device__ __forceinline__ void red_stage(const RedMeta &m, const Layout &L, uint32_t t, bool last, uint32_t half,
+                                          uint32_t &z0, uint32_t &z1, uint32_t &lo, uint32_t &len, uint32_t *buf,
+                                          int lane, bool &bad) {
+    const_u32 *tab = (const_u32 *)(m.in + L.off_tab);
+    z0 = tab[t];
+    z1 = tab[t + 1];  // t + 1 <= groups: the table's last entry at most
+    if ((t == 0 && z0 != 0) || (last && z1 != m.E)) bad = true;
+    if (z0 > m.E) { bad = true; z0 = m.E; }
+    if (z1 < z0 || z1 > m.E) { bad = true; z1 = z1 < z0 ? z0 : m.E; }
+    if (z1 - z0 > kRedTile) { bad = true; z1 = z0 + kRedTile; }
+    len = min(z1 - z0, kRedSliceCap);
+    lo = half ? z1 - len : z0;
+    red_stage_range(m, L, lo, len, buf, lane);
 }
 
-// The sums start at -0.0 when there is no local share: -0.0 + x is x exactly
-// for every x (+0 and -0 included), so the first term enters exactly.
-__device__ __forceinline__ void red_accumulate(const uint32_t (&vals)[kRedSteps][4], float (&acc)[kRedSteps][8]) {
-#pragma unroll
-    for (int u = 0; u < kRedSteps; ++u)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            acc[u][2 * j] += bf16_lo(vals[u][j]);
-            acc[u][2 * j + 1] += bf16_hi(vals[u][j]);
-        }
+// Plane bytes of the lane's 8-value unit u: [plane 0, plane 1, plane 2, 0].
+__device__ __forceinline__ uint32_t red_planes(const RedData &d, uint32_t u) {
+    const uint32_t w01 = perm(d.p1, d.p0, u | ((4u + u) << 8) | 0x0C0C0000u);
+    return perm(d.p2, w01, 0x0100u | ((4u + u) << 16) | 0x0C000000u);
 }
 
-// (Each path accumulates on its own: a merge after the raw path's register
-// loads would make the coded path wait for every load in flight.)
-__device__ __forceinline__ void red_add(const RedMeta &m, uint64_t n, uint64_t tile0, const RedStage &st,
-                                        const RedZp &zs, uint32_t z0, uint32_t z1, const uint2 *sel,
-                                        float (&acc)[kRedSteps][8], bool &bad, int lane, int wave) {
-    uint32_t vals[kRedSteps][4];
-    if (m.raw) {
-        const uint16_t *src = reinterpret_cast<const uint16_t *>(m.in + kHeaderBytes);
+// Adds 8 values (sign+mantissa dwords sm_lo / sm_hi, exponent bytes e_lo /
+// e_hi) to acc8.  The float of a BF16 value has the value's high byte (sign,
+// exponent >> 1) on top and its low byte (exponent & 1, mantissa) below it:
+// one byte select per value.
+__device__ __forceinline__ void red_add8(float *acc8, uint32_t sm_lo, uint32_t sm_hi, uint32_t e_lo, uint32_t e_hi) {
+    const uint32_t h0 = bfi(0x80808080u, sm_lo, e_lo >> 1), l0 = bfi(0x7F7F7F7Fu, sm_lo, e_lo << 7);
+    const uint32_t h1 = bfi(0x80808080u, sm_hi, e_hi >> 1), l1 = bfi(0x7F7F7F7Fu, sm_hi, e_hi << 7);
 #pragma unroll
-        for (int u = 0; u < kRedSteps; ++u) {
-            const uint64_t base = tile0 + 512u * (uint32_t)(wave * kRedSteps + u) + 8u * (uint32_t)lane;
-            uint32_t w4[4] = {0, 0, 0, 0};
-            if (base + 8 <= n) {
-                const uint4 q = load_stream16(src + base);
-                w4[0] = q.x;
-                w4[1] = q.y;
-                w4[2] = q.z;
-                w4[3] = q.w;
-            } else {
-                for (uint32_t i = 0; base + i < n; ++i) w4[i / 2] |= (uint32_t)src[base + i] << (16 * (i % 2));
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) vals[u][j] = w4[j];
-        }
-        red_accumulate(vals, acc);
+    for (uint32_t j = 0; j < 4; ++j) {
+        const uint32_t sel = 0x0C0Cu | (j << 16) | ((4u + j) << 24);
+        acc8[j] += __uint_as_float(perm(h0, l0, sel));
+        acc8[4 + j] += __uint_as_float(perm(h1, l1, sel));
+    }
+}
+
+// The wave's zero-point flags (bit i: value v0 + i of the lane) and their
+// exclusive prefix count over the lanes; returns the wave's count.
+__device__ __forceinline__ uint32_t red_flags(const RedData &d, const RedLane &ln, uint32_t &z32, uint32_t &excl) {
+    z32 = ~(d.p0 | d.p1 | d.p2) & ln.vmask;
+    const uint32_t cnt = (uint32_t)__builtin_popcount(z32);
+    const uint32_t incl = wave_inclusive_scan(cnt);
+    excl = incl - cnt;
+    return (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+}
+
+// Where a raw stream's (or the local share's) values are read: the tile's
+// values wv (uniform; the tile's first value always exists), the lane's byte
+// offset from there, whether all 2048 values of the wave exist (uniform).
+// When not, the lane reads value by value from tail_off (its own offset, or 0
+// for a lane past the end), at most value tail_last (nv - 1, or 0) from there.
+struct RedRaw {
+    const uint8_t *wv;
+    uint32_t lane_off;
+    bool full;
+    uint32_t tail_off, tail_last;
+};
+
+// The 8 values of unit u of a raw stream as 4 BF16 pairs (missing values
+// repeat an existing one; their sums are never stored).
+__device__ __forceinline__ void red_raw_unit(const RedRaw &rw, uint32_t u, uint32_t (&w)[4]) {
+    if (rw.full) {
+        const uint4 v = load_stream16(rw.wv + (rw.lane_off + 16u * u));
+        w[0] = v.x;
+        w[1] = v.y;
+        w[2] = v.z;
+        w[3] = v.w;
     } else {
-        uint32_t e[kRedSteps][2], zmask[kRedSteps], sm[kRedSteps][2];
+        // (an opaque copy: offsets computed from it are not hoisted out of the
+        // stream loop, where they would hold 32 registers)
+        uint32_t lastv = rw.tail_last, loff = rw.tail_off;
+        asm volatile("" : "+v"(lastv), "+v"(loff));
 #pragma unroll
-        for (int u = 0; u < kRedSteps; ++u) {
-            const uint32_t lb = 512u * (uint32_t)(wave * kRedSteps + u) + 8u * (uint32_t)lane;
-            const uint64_t base = tile0 + lb;
-            const uint32_t vmask = base + 8 <= n ? 0xFFu : (base < n ? (1u << (uint32_t)(n - base)) - 1u : 0u);
-            const uint2 q = *reinterpret_cast<const uint2 *>(st.sm + lb);
-            sm[u][0] = q.x;
-            sm[u][1] = q.y;
-            const uint32_t planes = (uint32_t)st.planes[lb / 8] | ((uint32_t)st.planes[kRedPlaneBytes + lb / 8] << 8) |
-                                    ((uint32_t)st.planes[2 * kRedPlaneBytes + lb / 8] << 16);
-            uint32_t c_lo, c_hi;
-            planes_to_codes(planes, c_lo, c_hi);
-            e[u][0] = perm(m.tbl_hi, m.tbl_lo, c_lo);
-            e[u][1] = perm(m.tbl_hi, m.tbl_lo, c_hi);
-            zmask[u] = zero_point_mask(planes) & vmask;
+        for (uint32_t j = 0; j < 4; ++j) {
+            const uint32_t i = 8u * u + 2u * j;
+            const uint32_t lo = *reinterpret_cast<const uint16_t *>(rw.wv + (loff + 2u * min(i, lastv)));
+            const uint32_t hi = *reinterpret_cast<const uint16_t *>(rw.wv + (loff + 2u * min(i + 1u, lastv)));
+            w[j] = lo | (hi << 16);
         }
-        uint32_t rank[kRedSteps];
-        const uint32_t total = red_ranks(st, tile0, n, zmask, lane, wave, rank);
-        if (total != z1 - z0) bad = true;
-        // slice byte j sits at byte (z0 & 3) + j of zs.w (the slice starts on a
-        // dword boundary at or before off_zp + z0; off_zp is 128-aligned)
-        const uint32_t lead = z0 & 3u, zspan = z1 - z0;
-#pragma unroll
-        for (int u = 0; u < kRedSteps; ++u) {
-            // a rank past the slice (a corrupt table, already flagged) reads
-            // the buffer's slack instead
-            const uint32_t r = lead + (rank[u] <= zspan ? rank[u] : zspan);
-            put_zero_points(e[u][0], e[u][1], zmask[u], r, zs.w, sel);
-            rebuild4(sm[u][0], e[u][0], vals[u][0], vals[u][1]);
-            rebuild4(sm[u][1], e[u][1], vals[u][2], vals[u][3]);
-        }
-        red_accumulate(vals, acc);
     }
 }
 
-// One block per 4096-value tile.  Every block first checks every stream's
-// header, so a bad header anywhere leaves the whole output untouched.  The
-// float32 sums start from the local value, or from -0.0 (so that the first
-// stream's value enters exactly), then take the streams in order.
-// Six waves per SIMD: the register budget (80) costs a few spills, which
-// measured cheaper than the fifth block per CU it buys is worth.
-__global__ __launch_bounds__(kThreads, 6) void reduce_kernel(RedArgs args) {
-    __shared__ RedStage s_st[2];
-    __shared__ RedZp s_zp[2];
-    __shared__ RedHdr s_hdr[ZC_MAX_BATCH];
-    __shared__ uint2 s_sel[256];
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const uint32_t t = blockIdx.x;
+// Decodes the lane's 32 values of a stream and adds them to acc.  Coded: the
+// lane's first zero-point is byte r0 of buf and each 8-value unit's are
+// contiguous there.  Raw: the values are read as they are and split like the
+// encoder splits them (sign+mantissa bytes, exponent bytes), so that every
+// stream's values enter the sums through the same instructions.
+__device__ __forceinline__ void red_decode(const RedMeta &m, const RedData &d, uint32_t z32, uint32_t r0,
+                                           const uint32_t *buf, const uint2 *sel, const RedRaw &rw,
+                                           float (&acc)[32]) {
+    const uint32_t smw[8] = {d.sm0.x, d.sm0.y, d.sm0.z, d.sm0.w, d.sm1.x, d.sm1.y, d.sm1.z, d.sm1.w};
+#pragma unroll
+    for (uint32_t u = 0; u < 4; ++u) {
+        uint32_t sm_lo, sm_hi, e_lo, e_hi;
+        if (m.raw) {
+            uint32_t w[4];
+            red_raw_unit(rw, u, w);
+            sm_lo = sign_mantissa4(w[0], w[1]);
+            sm_hi = sign_mantissa4(w[2], w[3]);
+            e_lo = exponents4(exponent_high(w[0]), exponent_high(w[1]));
+            e_hi = exponents4(exponent_high(w[2]), exponent_high(w[3]));
+        } else {
+            uint32_t c_lo, c_hi;
+            planes_to_codes(red_planes(d, u), c_lo, c_hi);
+            e_lo = perm(m.tbl_hi, m.tbl_lo, c_lo);
+            e_hi = perm(m.tbl_hi, m.tbl_lo, c_hi);
+            const uint32_t r = u ? r0 + (uint32_t)__builtin_popcount(z32 & ((1u << (8u * u)) - 1u)) : r0;
+            put_zero_points(e_lo, e_hi, (z32 >> (8u * u)) & 0xFFu, r, buf, sel);
+            sm_lo = smw[2u * u];
+            sm_hi = smw[2u * u + 1u];
+        }
+        red_add8(acc + 8u * u, sm_lo, sm_hi, e_lo, e_hi);
+        __builtin_amdgcn_sched_barrier(0);  // one unit's registers live at a time
+    }
+}
+
+// A block checks every stream's header first (a bad header anywhere leaves the
+// whole output untouched), then each wave decodes its half-tile of every
+// stream in order.  The float32 sums start from the local value, or from -0.0
+// (-0.0 + x is x for every x, so the first stream enters exactly).
+__global__ __launch_bounds__(kThreads) void reduce_kernel(RedArgs args) {
+    __shared__ RedShared sh;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: tile, half and addresses in SGPRs
     const uint64_t n = args.n;
     const Layout L = layout_for(n);
-    const uint64_t tile0 = (uint64_t)t * kRedTile;
-    const bool last = tile0 + kRedTile >= n;
     const uint32_t k = args.k;
+    const uint32_t half = (uint32_t)wave & 1u;
+    const uint32_t t = blockIdx.x * kRedTilesPerBlock + (uint32_t)wave / 2;
+    const bool active = t < L.groups;
+    const bool last = t + 1 == L.groups;
 
-    zp_selectors(s_sel);  // visible after the barrier in the header check
-    // the headers' words use the stages, which are free until the first load
-    static_assert(sizeof(s_st) >= 4u * 32u * ZC_MAX_BATCH, "room for every header");
-    if (!red_check_headers(args, n, L, reinterpret_cast<uint32_t *>(s_st), s_hdr)) {
+    zp_selectors(sh.sel);  // visible after the barriers of the header check
+    if (!red_check_headers(args, n, L, &sh.slice[0][0][0], sh.hdr)) {
         if (tid == 0 && args.status) *args.status = ZC_ERR_CORRUPT;
         return;
     }
 
-    float acc[kRedSteps][8];
+    RedLane ln;
+    ln.v0 = (uint64_t)t * kRedTile + kRedHalf * half + 32u * (uint32_t)lane;
+    ln.nv = ln.v0 < n ? (uint32_t)min(n - ln.v0, (uint64_t)32) : 0u;
+    ln.vmask = ln.nv == 32 ? ~0u : (1u << ln.nv) - 1u;
+    ln.sm_off = ln.nv ? (uint32_t)ln.v0 : 0u;
+    ln.pl_off = ln.nv ? (uint32_t)(ln.v0 / 8) : 0u;
+
+    // where the lane reads BF16 arrays (the local share, raw streams)
+    const uint64_t tile0 = (uint64_t)t * kRedTile;
+    RedRaw rw;
+    rw.lane_off = 2u * (kRedHalf * half + 32u * (uint32_t)lane);
+    rw.full = tile0 + kRedHalf * (half + 1u) <= n;
+    rw.tail_off = ln.nv ? rw.lane_off : 0u;
+    rw.tail_last = ln.nv ? ln.nv - 1u : 0u;
+
+    float acc[32];
+    if (args.local && active) {
+        rw.wv = reinterpret_cast<const uint8_t *>(args.local + tile0);
 #pragma unroll
-    for (int u = 0; u < kRedSteps; ++u)
+        for (uint32_t u = 0; u < 4; ++u) {
+            uint32_t w[4];
+            red_raw_unit(rw, u, w);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[u][j] = -0.0f;
-    if (args.local) {
-#pragma unroll
-        for (int u = 0; u < kRedSteps; ++u) {
-            const uint64_t base = tile0 + 512u * (uint32_t)(wave * kRedSteps + u) + 8u * (uint32_t)lane;
-            uint32_t w4[4] = {0, 0, 0, 0};
-            if (base + 8 <= n) {
-                const uint4 v = load_stream16(args.local + base);
-                w4[0] = v.x;
-                w4[1] = v.y;
-                w4[2] = v.z;
-                w4[3] = v.w;
-            } else {
-                for (uint32_t i = 0; base + i < n; ++i) w4[i / 2] |= (uint32_t)args.local[base + i] << (16 * (i % 2));
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc[u][2 * j] = bf16_lo(w4[j]);
-                acc[u][2 * j + 1] = bf16_hi(w4[j]);
+            for (uint32_t j = 0; j < 4; ++j) {
+                acc[8 * u + 2 * j] = bf16_lo(w[j]);
+                acc[8 * u + 2 * j + 1] = bf16_hi(w[j]);
             }
         }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) acc[i] = -0.0f;
     }
 
     bool bad = false;
-    if (k) {
-        // Stream s sits in stage s % 2 and slice buffer s % 2.  Prologue:
-        // data(0), slice(0), data(1); a raw stream issues neither.
-        RedMeta cur = red_meta(args, 0, s_hdr), nxt = cur;
-        uint32_t cz0 = 0, cz1 = 0, nz0 = 0, nz1 = 0;
+    if (active && k) {
+        RedMeta cur = red_meta(args, 0, sh.hdr);
+        RedData dc, dn;
+        uint32_t z0 = 0, z1 = 0, lo = 0, len = 0;
         if (!cur.raw) {
-            red_issue_data(cur, L, n, tile0, s_st[0], lane, wave);
-            red_table(cur, L, t, cz0, cz1);
-            red_issue_zp(cur, L, t, cz0, cz1, last, s_zp[0], lane, wave, bad);
-        }
-        if (k > 1) {
-            nxt = red_meta(args, 1, s_hdr);
-            if (!nxt.raw) {
-                red_issue_data(nxt, L, n, tile0, s_st[1], lane, wave);
-                red_table(nxt, L, t, nz0, nz1);
-            }
+            red_stage(cur, L, t, last, half, z0, z1, lo, len, sh.slice[wave][0], lane, bad);
+            red_load(dc, cur, L, ln);
         }
         for (uint32_t s = 0; s < k; ++s) {
-            const uint32_t x = s & 1u;
-            // the loads still allowed in flight: the data of stream s + 1 (two
-            // per wave), issued after everything stream s needs
-            if (s + 1 < k && !nxt.raw)
-                __builtin_amdgcn_s_waitcnt(kWaitVm2);
-            else
-                __builtin_amdgcn_s_waitcnt(kWaitVm0);
-            __syncthreads();
-            // slice buffer x ^ 1 was last read by stream s - 1, before the
-            // barrier that ended its step: the next slice goes out now, and
-            // lands while stream s is decoded
-            if (s + 1 < k && !nxt.raw) red_issue_zp(nxt, L, t, nz0, nz1, last, s_zp[x ^ 1u], lane, wave, bad);
-            red_add(cur, n, tile0, s_st[x], s_zp[x], cz0, cz1, s_sel, acc, bad, lane, wave);
-            __syncthreads();  // stage x is free
-            RedMeta nn = nxt;
-            uint32_t n0 = 0, n1 = 0;
-            if (s + 2 < k) {
-                nn = red_meta(args, s + 2, s_hdr);
-                if (!nn.raw) {
-                    red_issue_data(nn, L, n, tile0, s_st[x], lane, wave);
-                    red_table(nn, L, t, n0, n1);
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);  // stream s's words and slice have landed
+            RedMeta nxt = cur;
+            uint32_t nz0 = 0, nz1 = 0, nlo = 0, nlen = 0;
+            const bool staged = s + 1 < k && !(nxt = red_meta(args, s + 1, sh.hdr)).raw;
+            if (staged) {  // the next stream's slice and words go out now
+                red_stage(nxt, L, t, last, half, nz0, nz1, nlo, nlen, sh.slice[wave][(s + 1) & 1u], lane, bad);
+                red_load(dn, nxt, L, ln);
+            }
+            uint32_t edge = 0, z32 = 0, r0 = 0, x = s & 1u;
+            bool heavy = false;
+            rw.wv = cur.in + kHeaderBytes + 2 * tile0;
+            if (!cur.raw) {
+                uint32_t excl;
+                const uint32_t c = red_flags(dc, ln, z32, excl);
+                edge = half ? z1 - c : z0 + c;
+                // half 0's zero-points open the staged slice, half 1's close it
+                r0 = (lo & 3u) + (half ? len - c : 0u) + excl;
+                heavy = c > len;
+                if (heavy) {
+                    // More zero-points than staged (or than the table allows): the
+                    // half's own ones, at most 2048 bytes, go to both slice buffers
+                    // (back to back); the next stream's slice is staged again after.
+                    const uint32_t a = half ? (c <= z1 ? z1 - c : 0u) : z0;
+                    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+                    red_stage_range(cur, L, a, min(c, cur.E - a), sh.slice[wave][0], lane);
+                    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+                    r0 = (a & 3u) + excl;
+                    x = 0;
                 }
             }
+            red_decode(cur, dc, z32, r0, sh.slice[wave][x], sh.sel, rw, acc);
+            if (heavy && staged) red_stage_range(nxt, L, nlo, nlen, sh.slice[wave][(s + 1) & 1u], lane);
+            if (lane == 0) sh.edge[wave][s] = edge;
             cur = nxt;
-            cz0 = nz0;
-            cz1 = nz1;
-            nxt = nn;
-            nz0 = n0;
-            nz1 = n1;
+            dc = dn;
+            z0 = nz0;
+            z1 = nz1;
+            lo = nlo;
+            len = nlen;
         }
     }
+    __syncthreads();  // the edges of both halves
+    if (active && half == 0)
+        for (uint32_t s = (uint32_t)lane; s < k; s += kWave)
+            if (sh.edge[wave][s] != sh.edge[wave + 1][s]) bad = true;
+
+    if (active && ln.nv) {
+        uint32_t o[16];
 #pragma unroll
-    for (int u = 0; u < kRedSteps; ++u) {
-        const uint64_t base = tile0 + 512u * (uint32_t)(wave * kRedSteps + u) + 8u * (uint32_t)lane;
-        uint32_t o[4];
+        for (int i = 0; i < 16; ++i) o[i] = float_to_bf16(acc[2 * i]) | (float_to_bf16(acc[2 * i + 1]) << 16);
+        uint16_t *dst = args.out + ln.v0;
+        if (ln.nv == 32) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = float_to_bf16(acc[u][2 * j]) | (float_to_bf16(acc[u][2 * j + 1]) << 16);
-        if (base + 8 <= n) {
-            store_stream16(args.out + base, o[0], o[1], o[2], o[3]);
+            for (int q = 0; q < 4; ++q) store_stream16(dst + 8 * q, o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
         } else {
-            for (uint32_t i = 0; base + i < n; ++i) args.out[base + i] = (uint16_t)(o[i / 2] >> (16 * (i % 2)));
+#pragma unroll
+            for (uint32_t i = 0; i < 32; ++i)
+                if (i < ln.nv) dst[i] = (uint16_t)(o[i / 2] >> (16 * (i % 2)));
         }
     }
-    if (bad && tid == 0 && args.status) atomicMax(args.status, (int32_t)ZC_ERR_CORRUPT);
+    if (bad && args.status) atomicMax(args.status, (int32_t)ZC_ERR_CORRUPT);
 }
 
 }  // namespace zc
@@ -1842,7 +1855,8 @@ extern "C" zc_status zc_decompress_reduce(const void *const *d_streams, const ui
         if (rc != ZC_OK) return rc;
     }
     // n = 0 still runs one block: every header is checked, nothing is written
-    const uint64_t blocks = n ? (n + kRedTile - 1) / kRedTile : 1;
+    const uint64_t tiles = (n + kRedTile - 1) / kRedTile;
+    const uint64_t blocks = tiles ? (tiles + kRedTilesPerBlock - 1) / kRedTilesPerBlock : 1;
     hipLaunchKernelGGL(reduce_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
 }

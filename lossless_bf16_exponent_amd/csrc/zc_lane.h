@@ -74,27 +74,27 @@ ZC_HD uint32_t window_codes4(uint32_t t0, uint32_t t1, uint32_t base_hi) {
     return perm(v1, v0, kSelHighBytes);
 }
 
-// 4x4 bit transpose of the low nibbles of the four bytes: bit b of byte k
-// moves to bit k of byte b (k, b in 0..3).  Two exchange stages (single bits
-// across a distance of 7, then 2x2 blocks across 14).  Result bits outside the
-// low nibbles are unspecified; the low nibbles depend on the low nibbles only.
-ZC_HD uint32_t nibble_transpose(uint32_t x) {
-    x = bfi(0x0A050A05u, x, bfi(0x000A000Au, x >> 7, x << 7));
-    x = bfi(0x0C0C0303u, x, bfi(0x00000C0Cu, x >> 14, x << 14));
+// Two 4x4 bit transposes at once, one on the low nibbles of the four bytes and
+// one on the high nibbles: bit b of byte k moves to bit k of byte b, and bit
+// 4 + b of byte k to bit 4 + k of byte b (k, b in 0..3).  Two exchange stages
+// (single bits across a distance of 7, then 2x2 blocks across 14); every
+// exchanged pair lies inside one nibble matrix, so the two never mix.
+ZC_HD uint32_t nibble_transpose2(uint32_t x) {
+    x = bfi(0xAA55AA55u, x, bfi(0x00AA00AAu, x >> 7, x << 7));
+    x = bfi(0xCCCC3333u, x, bfi(0x0000CCCCu, x >> 14, x << 14));
     return x;
 }
 
-// Code bytes of 8 values (c_lo: values 0..3, c_hi: 4..7; bits 0..2 hold the
-// code) -> plane bytes: byte b of the result holds bit b of the 8 codes, value
-// k in bit k.  Byte 3 is unspecified.
-ZC_HD uint32_t codes_to_planes(uint32_t c_lo, uint32_t c_hi) {
-    return bfi(0x0F0F0F0Fu, nibble_transpose(c_lo), nibble_transpose(c_hi) << 4);
-}
+// Code bytes of 8 values (c_lo: values 0..3, c_hi: 4..7; each byte at most 8)
+// -> plane bytes: byte b of the result holds bit b of the 8 codes, value k in
+// bit k.  Byte 3 (bit 3 of the codes) is unspecified.
+ZC_HD uint32_t codes_to_planes(uint32_t c_lo, uint32_t c_hi) { return nibble_transpose2(c_lo | (c_hi << 4)); }
 
 // Inverse: plane bytes (byte b = plane b, byte 3 ignored) -> code bytes 0..7.
 ZC_HD void planes_to_codes(uint32_t planes, uint32_t &c_lo, uint32_t &c_hi) {
-    c_lo = nibble_transpose(planes) & 0x07070707u;
-    c_hi = nibble_transpose(planes >> 4) & 0x07070707u;
+    const uint32_t x = nibble_transpose2(planes);
+    c_lo = x & 0x07070707u;
+    c_hi = (x >> 4) & 0x07070707u;
 }
 
 // Zero-point mask of 8 values: bit k set when value k has code 000.

@@ -121,3 +121,52 @@ def test_reduce_full_shard(zc):
     got, status, _ = gpu_reduce(zc, xs[1:], plans, xs[0])
     assert status == 0
     assert np.array_equal(got, oracle_reduce(xs[1:], plans, xs[0]))
+
+
+def half_escapes(n, counts, seed):
+    """WINDOW_PLAN-coded patterns where the 2048-value half h of every tile holds
+    counts[h % len(counts)] zero-points (fewer if the half is shorter)."""
+    g = np.random.default_rng(seed)
+    e = g.integers(116, 123, n)
+    for h, v0 in enumerate(range(0, n, 2048)):
+        m = min(2048, n - v0)
+        c = min(counts[h % len(counts)], m)
+        idx = v0 + g.choice(m, c, replace=False)
+        esc = g.integers(0, 249, c)
+        e[idx] = np.where(esc >= 116, esc + 7, esc)
+    return ((g.integers(0, 2, n) << 15) | (e << 7) | g.integers(0, 128, n)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("n", [4096 * 3 + 2049, 4096 * 4, 2048 + 17])
+def test_reduce_many_zero_points_per_half(zc, n):
+    """Halves with more zero-points than a wave stages (more than 1024) read
+    them another way; exactly 1024 still fits.  Mixed with an ordinary peer, a
+    half-filled last tile and the local share."""
+    cycles = [[0, 1024, 1025, 2048, 300, 1500], [1024, 0, 2048, 1025, 1500, 300], [2048, 2048, 1, 1024]]
+    peers = [half_escapes(n, c, 300 + i) for i, c in enumerate(cycles)] + [gaussian(n, 3e-3, 31)]
+    plans = [WINDOW_PLAN] * 3 + [oracle.plan_from_sigma(3e-3)]
+    local = gaussian(n, 1e-3, 32)
+    got, status, _ = gpu_reduce(zc, peers, plans, local)
+    assert status == 0
+    assert np.array_equal(got, oracle_reduce(peers, plans, local))
+
+
+@pytest.mark.parametrize("v", [4096 + 5, 4096 + 2048 + 1000, 3 * 4096 + 2047])
+def test_reduce_plane_count_mismatch_is_caught(zc, v):
+    """A value's code turned into the zero-point code (its three plane bits
+    cleared) changes its half's zero-point count against the table: the two
+    halves of the tile then disagree on where one's zero-points end and the
+    other's begin, and the status says so."""
+    n = 30_000
+    x = gaussian(n, 0.02, 40)
+    lay = oracle.layout(n)
+    s = oracle.encode(x, WINDOW_PLAN)
+    bits = [(s[lay["off_p%d" % p] + v // 8] >> (v % 8)) & 1 for p in range(3)]
+    assert any(bits), "value %d already a zero-point" % v
+    bad = s.copy()
+    for p in range(3):
+        bad[lay["off_p%d" % p] + v // 8] &= ~np.uint8(1 << (v % 8))
+    good = oracle.encode(gaussian(n, 0.01, 41), WINDOW_PLAN)
+    bufs = [torch.from_numpy(np.concatenate([b, np.zeros(256, np.uint8)])).cuda() for b in (good, bad)]
+    _, status, _ = gpu_reduce(zc, [x, x], None, streams=([b.data_ptr() for b in bufs], [good.size, bad.size]))
+    assert status == 4
