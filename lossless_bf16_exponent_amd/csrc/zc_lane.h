@@ -79,10 +79,13 @@ ZC_HD uint32_t window_codes4(uint32_t t0, uint32_t t1, uint32_t base_hi) {
 // 4 + b of byte k to bit 4 + k of byte b (k, b in 0..3).  Two exchange stages
 // (single bits across a distance of 7, then 2x2 blocks across 14); every
 // exchanged pair lies inside one nibble matrix, so the two never mix.
+// Each stage swaps bit p with bit p + d for p in a mask, written as
+// t = (x ^ x >> d) & mask, x ^= t ^ t << d (two 3-input bit operations).
 ZC_HD uint32_t nibble_transpose2(uint32_t x) {
-    x = bfi(0xAA55AA55u, x, bfi(0x00AA00AAu, x >> 7, x << 7));
-    x = bfi(0xCCCC3333u, x, bfi(0x0000CCCCu, x >> 14, x << 14));
-    return x;
+    uint32_t t = (x ^ (x >> 7)) & 0x00AA00AAu;
+    x = x ^ t ^ (t << 7);
+    t = (x ^ (x >> 14)) & 0x0000CCCCu;
+    return x ^ t ^ (t << 14);
 }
 
 // Code bytes of 8 values (c_lo: values 0..3, c_hi: 4..7; each byte at most 8)
