@@ -1334,6 +1334,11 @@ __device__ __forceinline__ RedMeta red_meta(const RedArgs &args, uint32_t s, con
 // s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8): vmcnt(0), the others unconstrained.
 constexpr int kWaitVm0 = 0x0F70;
+// Lanes of one wave exchanging data through LDS: the wave's LDS accesses
+// complete in order, so waiting for its own is enough; the memory clobber
+// keeps the compiler from moving accesses across (per lane, the addresses
+// written and read look unrelated).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Direct-to-LDS dword load, written as inline assembly so that the compiler
 // adds no waits of its own for it; the kernel waits with an explicit count.
@@ -1546,22 +1551,56 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(RedArgs args) {
     rw.tail_off = ln.nv ? rw.lane_off : 0u;
     rw.tail_last = ln.nv ? ln.nv - 1u : 0u;
 
+    // A wave whose 2048 values all exist moves its local share in and its
+    // result out through its slice buffers (free at both times), in two
+    // rounds of 1024 values: each global access instruction then covers 1 KiB
+    // of consecutive bytes, where lanes of 32 consecutive values would touch
+    // every cache line in part (measured: a quarter of the kernel's time).
+    uint8_t *const xpose = reinterpret_cast<uint8_t *>(sh.slice[wave][0]);
+    static_assert(sizeof(RedShared::slice[0]) >= 2048, "a round of 1024 values fits a wave's slice buffers");
+    const uint64_t half0 = tile0 + kRedHalf * half;  // the wave's first value
+
     float acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] = -0.0f;
     if (args.local && active) {
-        rw.wv = reinterpret_cast<const uint8_t *>(args.local + tile0);
+        if (rw.full) {
 #pragma unroll
-        for (uint32_t u = 0; u < 4; ++u) {
-            uint32_t w[4];
-            red_raw_unit(rw, u, w);
+            for (uint32_t r = 0; r < 2; ++r) {
+                const uint8_t *src = reinterpret_cast<const uint8_t *>(args.local + half0 + 1024u * r);
+                const uint4 a = load_stream16(src + 16u * (uint32_t)lane);
+                const uint4 b = load_stream16(src + 1024u + 16u * (uint32_t)lane);
+                *reinterpret_cast<uint4 *>(xpose + 16u * (uint32_t)lane) = a;
+                *reinterpret_cast<uint4 *>(xpose + 1024u + 16u * (uint32_t)lane) = b;
+                wave_lds_sync();
+                if ((uint32_t)lane / 32u == r) {
+                    const uint8_t *mine = xpose + 64u * ((uint32_t)lane % 32u);
 #pragma unroll
-            for (uint32_t j = 0; j < 4; ++j) {
-                acc[8 * u + 2 * j] = bf16_lo(w[j]);
-                acc[8 * u + 2 * j + 1] = bf16_hi(w[j]);
+                    for (uint32_t q = 0; q < 4; ++q) {
+                        const uint4 v = *reinterpret_cast<const uint4 *>(mine + 16u * q);
+                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (uint32_t j = 0; j < 4; ++j) {
+                            acc[8 * q + 2 * j] = bf16_lo(w[j]);
+                            acc[8 * q + 2 * j + 1] = bf16_hi(w[j]);
+                        }
+                    }
+                }
+                wave_lds_sync();  // (the next round rewrites the buffer: reads first)
+            }
+        } else {
+            rw.wv = reinterpret_cast<const uint8_t *>(args.local + tile0);
+#pragma unroll
+            for (uint32_t u = 0; u < 4; ++u) {
+                uint32_t w[4];
+                red_raw_unit(rw, u, w);
+#pragma unroll
+                for (uint32_t j = 0; j < 4; ++j) {
+                    acc[8 * u + 2 * j] = bf16_lo(w[j]);
+                    acc[8 * u + 2 * j + 1] = bf16_hi(w[j]);
+                }
             }
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) acc[i] = -0.0f;
     }
 
     bool bad = false;
@@ -1620,15 +1659,30 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(RedArgs args) {
         for (uint32_t s = (uint32_t)lane; s < k; s += kWave)
             if (sh.edge[wave][s] != sh.edge[wave + 1][s]) bad = true;
 
-    if (active && ln.nv) {
+    if (active) {
         uint32_t o[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[i] = float_to_bf16(acc[2 * i]) | (float_to_bf16(acc[2 * i + 1]) << 16);
-        uint16_t *dst = args.out + ln.v0;
-        if (ln.nv == 32) {
+        if (rw.full) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) store_stream16(dst + 8 * q, o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-        } else {
+            for (uint32_t r = 0; r < 2; ++r) {
+                if ((uint32_t)lane / 32u == r) {
+                    uint8_t *mine = xpose + 64u * ((uint32_t)lane % 32u);
+#pragma unroll
+                    for (uint32_t q = 0; q < 4; ++q)
+                        *reinterpret_cast<uint4 *>(mine + 16u * q) =
+                            make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+                }
+                wave_lds_sync();
+                uint8_t *dst = reinterpret_cast<uint8_t *>(args.out + half0 + 1024u * r);
+                const uint4 a = *reinterpret_cast<const uint4 *>(xpose + 16u * (uint32_t)lane);
+                const uint4 b = *reinterpret_cast<const uint4 *>(xpose + 1024u + 16u * (uint32_t)lane);
+                store_stream16(dst + 16u * (uint32_t)lane, a.x, a.y, a.z, a.w);
+                store_stream16(dst + 1024u + 16u * (uint32_t)lane, b.x, b.y, b.z, b.w);
+                wave_lds_sync();  // (the next round rewrites the buffer: reads first)
+            }
+        } else if (ln.nv) {
+            uint16_t *dst = args.out + ln.v0;
 #pragma unroll
             for (uint32_t i = 0; i < 32; ++i)
                 if (i < ln.nv) dst[i] = (uint16_t)(o[i / 2] >> (16 * (i % 2)));
