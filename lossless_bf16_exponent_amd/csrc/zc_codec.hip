@@ -1334,6 +1334,12 @@ __device__ __forceinline__ RedMeta red_meta(const RedArgs &args, uint32_t s, con
 // s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8): vmcnt(0), the others unconstrained.
 constexpr int kWaitVm0 = 0x0F70;
+
+// Wait for every load of the wave, direct-to-LDS ones included, as a compiler
+// barrier as well (inline assembly with a memory clobber): no LDS read moves
+// above it.  Used where the reads of LDS that such loads wrote do not depend
+// on any later load.
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Lanes of one wave exchanging data through LDS: the wave's LDS accesses
 // complete in order, so waiting for its own is enough; the memory clobber
 // keeps the compiler from moving accesses across (per lane, the addresses
@@ -1613,7 +1619,11 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(RedArgs args) {
             red_load(dc, cur, L, ln);
         }
         for (uint32_t s = 0; s < k; ++s) {
-            __builtin_amdgcn_s_waitcnt(kWaitVm0);  // stream s's words and slice have landed
+            // Stream s's words and slice have landed.  (This wait orders no LDS
+            // read for the compiler; it does not need to: the slice's reads
+            // take their addresses from stream s's plane words, which the
+            // compiler waits for, and the slice was issued before them.)
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);
             RedMeta nxt = cur;
             uint32_t nz0 = 0, nz1 = 0, nlo = 0, nlen = 0;
             const bool staged = s + 1 < k && !(nxt = red_meta(args, s + 1, sh.hdr)).raw;
@@ -1636,15 +1646,18 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(RedArgs args) {
                     // half's own ones, at most 2048 bytes, go to both slice buffers
                     // (back to back); the next stream's slice is staged again after.
                     const uint32_t a = half ? (c <= z1 ? z1 - c : 0u) : z0;
-                    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+                    wait_loads();
                     red_stage_range(cur, L, a, min(c, cur.E - a), sh.slice[wave][0], lane);
-                    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+                    wait_loads();
                     r0 = (a & 3u) + excl;
                     x = 0;
                 }
             }
             red_decode(cur, dc, z32, r0, sh.slice[wave][x], sh.sel, rw, acc);
-            if (heavy && staged) red_stage_range(nxt, L, nlo, nlen, sh.slice[wave][(s + 1) & 1u], lane);
+            if (heavy && staged) {
+                red_stage_range(nxt, L, nlo, nlen, sh.slice[wave][(s + 1) & 1u], lane);
+                wait_loads();  // (issued after the next stream's plane words: not covered by waiting for them)
+            }
             if (lane == 0) sh.edge[wave][s] = edge;
             cur = nxt;
             dc = dn;
