@@ -107,12 +107,19 @@ def cpu_baseline(w, plans, max_segments: int, min_seconds: float = 10.0, max_pas
             "seconds": round(t_enc + t_dec, 3)}
 
 
+REDUCE_WARMUP_CALLS = 150
+
+
 def reduce_measurement(zc, steps: int) -> dict:
     """The receive side of a reduce-scatter run as a zipped all-to-all (section
     2.D): one rank's 32 Mi-value shard, compressed contributions of 7 peers
     plus the local share, reduced by zc_decompress_reduce.  Peer p's values are
     N(0, sigma_p^2) with sigma_p the first eight layer sigmas of the gradient
-    bucket, each compressed with its own plan.  HIP events around K calls."""
+    bucket, each compressed with its own plan.  HIP events around K calls,
+    after REDUCE_WARMUP_CALLS calls: per-call timings on MI355X show about 20
+    fast calls, then about 80 calls some 20 % slower, then a steady state (the
+    device settling after a burst of this kernel), which is what a training
+    job that reduces bucket after bucket sees."""
     import numpy as np
     import torch
 
@@ -133,7 +140,7 @@ def reduce_measurement(zc, steps: int) -> dict:
     out = torch.empty(n, dtype=torch.int16, device="cuda")
     stream = torch.cuda.current_stream()
     ptrs = [b.data_ptr() for b in bufs]
-    for _ in range(3):
+    for _ in range(REDUCE_WARMUP_CALLS):
         zc.zc_decompress_reduce(ptrs, totals, n, xs[0], out, None, stream)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -145,7 +152,8 @@ def reduce_measurement(zc, steps: int) -> dict:
     ms = e0.elapsed_time(e1) / steps
     alg = sum(totals) + 4 * n  # the peer streams and the local share read, the result written
     achieved = alg / (ms * 1e-3) / 1e9
-    return {"shard_values": n, "peers": peers, "local": True, "us": round(ms * 1e3, 2),
+    return {"shard_values": n, "peers": peers, "local": True, "warmup_calls": REDUCE_WARMUP_CALLS,
+            "us": round(ms * 1e3, 2),
             "uncompressed_gbps": round(2.0 * n * (peers + 1) / (ms * 1e-3) / 1e9, 1),
             "algorithmic_bytes": int(alg), "achieved_gbps": round(achieved, 1),
             "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4), "kernel": "reduce_kernel"}
