@@ -95,7 +95,7 @@ ZC_HD Layout layout_for(uint64_t n) {
 // Finalize blocks: each one completes a run of consecutive encoder spans.  A
 // run has at least kFinRunMin spans, more when a segment would otherwise need
 // over kFinMaxBlocks finalize blocks.
-constexpr uint32_t kFinRunMin = 32;
+constexpr uint32_t kFinRunMin = 16;
 constexpr uint32_t kFinMaxBlocks = 1024;
 ZC_HD uint32_t fin_run(uint64_t nb) {
     const uint64_t r = (nb + kFinMaxBlocks - 1) / kFinMaxBlocks;
