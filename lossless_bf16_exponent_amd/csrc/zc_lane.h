@@ -114,16 +114,7 @@ ZC_HD void rebuild4(uint32_t sm, uint32_t e, uint32_t &d0, uint32_t &d1) {
     d1 = perm(hi, lo, 0x07030602u);
 }
 
-// Replace byte k (0..7) of the 8-byte value {hi:lo} with b.
-ZC_HD void put_byte8(uint32_t &lo, uint32_t &hi, uint32_t k, uint32_t b) {
-    uint32_t sh = 8u * (k & 3u);
-    uint32_t m = 0xFFu << sh;
-    if (k < 4)
-        lo = bfi(m, b << sh, lo);
-    else
-        hi = bfi(m, b << sh, hi);
-}
-
+// Byte k (0..7) of the 8-byte value {hi:lo}.
 ZC_HD uint32_t get_byte8(uint32_t lo, uint32_t hi, uint32_t k) {
     return ((k < 4 ? lo : hi) >> (8u * (k & 3u))) & 0xFFu;
 }
