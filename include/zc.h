@@ -153,8 +153,9 @@ zc_status zc_decompress(const void *d_in, uint64_t in_bytes, uint64_t n, void *d
  *   d_status             device int32 (nullable): 0, or ZC_ERR_CORRUPT when a
  *                        stream fails validation.  A bad header in any stream
  *                        leaves d_out untouched; a table or plane inconsistency
- *                        is caught per 8192-element tile, whose output is then
- *                        unspecified (reads stay inside every stream).
+ *                        is caught per 4096-element group (one table entry),
+ *                        whose output is then unspecified (reads stay inside
+ *                        every stream).
  * Errors returned: ZC_ERR_INVALID_ARG, ZC_ERR_MISALIGNED, ZC_ERR_CORRUPT (a
  * stream shorter than any stream of n values can be), ZC_ERR_HIP. */
 zc_status zc_decompress_reduce(const void *const *d_streams, const uint64_t *in_bytes, uint32_t k, uint64_t n,
