@@ -99,7 +99,7 @@ def test_reduce_rejects_bad_stream_and_writes_nothing(zc):
     bufs = [torch.from_numpy(np.concatenate([s, np.zeros(256, np.uint8)])).cuda() for s in (streams[0], bad)]
     got, status, _ = gpu_reduce(zc, peers, None, streams=([b.data_ptr() for b in bufs], [s.size for s in streams]))
     assert status == 4 and bool((got == 0x1357).all())
-    # a table entry off by one: caught per tile
+    # a table entry off by one: caught per 4096-value group
     lay = oracle.layout(n)
     bad = streams[1].copy()
     bad[lay["off_tab"] + 4] ^= 0x01
