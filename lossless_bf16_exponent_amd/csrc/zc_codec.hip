@@ -82,6 +82,7 @@ struct DecArgs {
     uint32_t k;
     uint32_t total_tiles;
     DecSeg seg[ZC_MAX_BATCH];
+    uint32_t tile_begin[ZC_MAX_BATCH];  // seg[i].tile_begin, contiguous for the block -> segment lookup
 };
 
 // Local reduction of the reduce-scatter path: k streams of the same n values.
@@ -167,6 +168,26 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(v), kWave - 1);
 }
 
+// How many of v[1 .. count) are at or below flat, for non-decreasing v: the
+// index of the last entry at or below it.  Lane i reads entries 1 + i,
+// 65 + i, ... with one vector load per 64 entries and a ballot counts the
+// hits, so the lookup costs one round trip whatever the count (a loop of
+// dependent reads, one per entry or per halving, cost a decoder block 32 of
+// them at its start, 7 % of the bucket's decompress time).  All lanes of the
+// wave must be active.
+template <uint32_t kEntries>
+__device__ __forceinline__ uint32_t count_at_or_below(const uint32_t *v, uint32_t count, uint32_t flat) {
+    const uint32_t lane = __lane_id();
+    uint32_t total = 0;
+#pragma unroll
+    for (uint32_t c = 0; c < (kEntries - 1 + kWave - 1) / kWave; ++c) {
+        const uint32_t i = 1u + (uint32_t)kWave * c + lane;
+        const bool hit = i < count && v[i] <= flat;  // (read only below count: inside the array)
+        total += (uint32_t)__builtin_popcountll(__ballot(hit));
+    }
+    return total;
+}
+
 // The piece holding grid block `flat` (binary search over the piece starts).
 __device__ __forceinline__ uint32_t find_piece(const EncArgs &a, uint32_t flat) {
     uint32_t lo = 0, hi = a.pieces - 1;
@@ -180,11 +201,9 @@ __device__ __forceinline__ uint32_t find_piece(const EncArgs &a, uint32_t flat) 
     return lo;
 }
 
+// The decode segment holding grid block `flat`.
 __device__ __forceinline__ uint32_t find_segment_dec(const DecArgs &a, uint32_t flat) {
-    uint32_t s = 0;
-    for (uint32_t i = 1; i < a.k; ++i)
-        if (a.seg[i].tile_begin <= flat) s = i;
-    return s;
+    return count_at_or_below<ZC_MAX_BATCH>(a.tile_begin, a.k, flat);
 }
 
 // Zero-point counts of the four steps of a lane -> tile-local ranks of the
@@ -1851,6 +1870,7 @@ extern "C" zc_status zc_decompress_batch(const zc_dec_seg *segs, uint32_t k, voi
         d.in_bytes = g.in_bytes;
         d.n = (uint32_t)g.n;
         d.tile_begin = (uint32_t)tiles[which];
+        a[which].tile_begin[a[which].k - 1] = d.tile_begin;
         tiles[which] += dec_blocks(g.n);
         if (tiles[which] > 0xFFFFFFFFull) return ZC_ERR_INVALID_ARG;
         if (g.status) {
