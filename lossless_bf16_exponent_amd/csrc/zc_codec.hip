@@ -65,7 +65,11 @@ struct EncArgs {
     uint32_t tok_lo, tok_hi;  // the call's token (scratch words of other calls never match it)
     EncSeg seg[ZC_MAX_BATCH];
     uint32_t piece_start[kMaxPieces + 1];  // first grid block of each piece; the last entry is the grid size
-    uint8_t piece_info[kMaxPieces];
+    // Words, not bytes: with a byte array the compiler shared the address
+    // base + p between the byte read and the start read, giving the scalar
+    // load of piece_start[p] a base that is not 4-byte aligned, which the
+    // scalar unit does not honour (every finalize block saw piece start 0).
+    uint32_t piece_info[kMaxPieces];
 };
 
 struct DecSeg {
@@ -188,17 +192,9 @@ __device__ __forceinline__ uint32_t count_at_or_below(const uint32_t *v, uint32_
     return total;
 }
 
-// The piece holding grid block `flat` (binary search over the piece starts).
+// The piece holding grid block `flat`.
 __device__ __forceinline__ uint32_t find_piece(const EncArgs &a, uint32_t flat) {
-    uint32_t lo = 0, hi = a.pieces - 1;
-    while (lo < hi) {
-        const uint32_t mid = (lo + hi + 1) / 2;
-        if (a.piece_start[mid] <= flat)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
+    return count_at_or_below<kMaxPieces + 1>(a.piece_start, a.pieces, flat);
 }
 
 // The decode segment holding grid block `flat`.
@@ -1798,7 +1794,7 @@ extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void 
     GridPlan grid;
     if (!plan_grid(ns, k, grid)) return ZC_ERR_INVALID_ARG;
     std::memcpy(a.piece_start, grid.piece_start, sizeof(a.piece_start));
-    std::memcpy(a.piece_info, grid.piece_info, sizeof(a.piece_info));
+    for (uint32_t i = 0; i < kMaxPieces; ++i) a.piece_info[i] = grid.piece_info[i];
     const uint32_t np = grid.pieces;
     const uint64_t pos = grid.piece_start[np];
     a.k = k;
