@@ -71,6 +71,9 @@ struct EncArgs {
     // scalar unit does not honour (every finalize block saw piece start 0).
     uint32_t piece_info[kMaxPieces];
 };
+// Kept within the conventional 4 KiB kernel-argument budget, counting up to
+// 256 bytes of the runtime's hidden arguments.
+static_assert(sizeof(EncArgs) + 256 <= 4096, "compress arguments fit the kernarg segment");
 
 struct DecSeg {
     const uint8_t *in;
@@ -88,6 +91,7 @@ struct DecArgs {
     DecSeg seg[ZC_MAX_BATCH];
     uint32_t tile_begin[ZC_MAX_BATCH];  // seg[i].tile_begin, contiguous for the block -> segment lookup
 };
+static_assert(sizeof(DecArgs) + 256 <= 4096, "decompress arguments fit the kernarg segment");
 
 // Local reduction of the reduce-scatter path: k streams of the same n values.
 struct RedStream {

@@ -112,6 +112,21 @@ def test_batch_equals_single_and_is_deterministic(zc):
             assert np.array_equal(to_host_u16(o[:x.size]), x)
 
 
+def test_max_batch_of_64_segments(zc):
+    """The largest batch: 64 segments in one compress launch (128 grid pieces, so
+    the block -> piece lookup spans two wave-wide chunks) and one decompress
+    launch (64 segment starts), with empty, tiny, ragged and multi-tile
+    segments and a mix of plans."""
+    sizes = [0, 1, 4097, 8193, 65_536, 300_001, 17, 8192 * 5]
+    xs, plans = [], []
+    for i in range(64):
+        n = sizes[i % len(sizes)]
+        sigma = (0.02, 1e-3, 0.5, 3e-5)[i % 4]
+        xs.append(gaussian(n, sigma, 1000 + i))
+        plans.append(TABLE_PLANS[i % len(TABLE_PLANS)] if i % 5 == 0 else zc.zc_plan_from_sigma(sigma))
+    roundtrip_check(zc, xs, plans)
+
+
 def test_output_buffer_reuse_and_old_contents(zc):
     """Calls in a row into one output buffer that starts with random bytes: the
     scratch words left behind by earlier calls (or by anything else) must never
