@@ -233,3 +233,17 @@ def test_status_strings(zc):
     for code in range(6):
         assert zc.zc_status_string(code)
     assert zc.zc_status_string(99) == "unknown status"
+
+
+def test_product_never_touches_the_oracle():
+    """The package (binding, build script, kernels) neither imports nor links
+    nor loads anything under oracle/: the oracle is test infrastructure only."""
+    pkg = os.path.join(ROOT, "lossless_bf16_exponent_amd")
+    pattern = re.compile(r"^\s*(?:import|from)\s+oracle\b|liboracle|zc_oracle|oracle/|#\s*include\s*\"[^\"]*oracle",
+                         re.M)
+    for dirpath, _, files in os.walk(pkg):
+        for name in files:
+            if name.endswith((".py", ".hip", ".h", ".cpp", ".c")):
+                text = open(os.path.join(dirpath, name), encoding="utf-8").read()
+                assert not pattern.search(text), os.path.join(dirpath, name)
+    assert not any("oracle" in part for part in _build.compile_command("x.so"))
