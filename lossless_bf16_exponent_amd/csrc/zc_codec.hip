@@ -914,10 +914,14 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(EncArgs args) {
     const uint32_t flat = blockIdx.x;
     const uint32_t p = find_piece(args, flat);
     const uint32_t info = args.piece_info[p], idx = flat - args.piece_start[p];
-    if (info & kPieceFinalize)
+    if (info & kPieceFinalize) {
+        // A finalize block's waves issue ahead of the encoder waves sharing its
+        // CU: the last runs' landing and writing are the call's tail.
+        __builtin_amdgcn_s_setprio(2);
         finalize_run(args, info & 0x7Fu, idx, sh.f);
-    else
+    } else {
         encode_span(args, info, idx, sh.e);
+    }
 }
 
 // ---------------------------------------------------------------------------
