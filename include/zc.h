@@ -113,7 +113,15 @@ uint64_t zc_max_compressed_bytes(uint64_t n);
  * Errors: ZC_ERR_INVALID_ARG, ZC_ERR_MISALIGNED, ZC_ERR_CAPACITY, ZC_ERR_HIP.
  * The stream size is also in header bytes 40..47 once the work completes.
  * With ZC_PLAN_RAW_FALLBACK a second, small launch follows on the same stream
- * (it copies the input behind the header where the header says raw). */
+ * (it copies the input behind the header where the header says raw).
+ * Given-up call: workgroups of the launch wait for words that earlier
+ * workgroups of the same launch write, each wait bounded (about a second).
+ * With workgroups dispatched in index order no wait runs out.  Should one run
+ * out anyway, the call still ends and ZC_OK has already been returned, but the
+ * stream's header has a zero magic (every decoder rejects it with
+ * ZC_ERR_CORRUPT) and *d_out_bytes reads 0: a caller that sends
+ * *d_out_bytes bytes sends nothing, and a caller that reads the header sees
+ * an invalid stream.  Neither outcome passes for a valid stream. */
 zc_status zc_compress(const void *d_in, uint64_t n, const zc_plan *plan, void *d_out,
                       uint64_t out_capacity, uint64_t *d_out_bytes, void *stream);
 
@@ -219,7 +227,8 @@ typedef struct zc_dec_seg {
 /* Compress k (1..ZC_MAX_BATCH) independent tensors in one launch, each with its
  * own plan and output buffer (per-layer gradient segments, per-destination
  * all-to-all segments).  Each output equals what zc_compress gives for that
- * segment alone.  segs is a host array read before the call returns. */
+ * segment alone (the given-up outcome of zc_compress included, per segment).
+ * segs is a host array read before the call returns. */
 zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void *stream);
 
 /* Decompress k (1..ZC_MAX_BATCH) streams in one launch. */

@@ -39,6 +39,24 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+GIVEUP_LIB = os.path.join(ROOT, "tests", "libzc_giveup.so")
+
+
+def build_giveup(verbose: bool = False) -> str:
+    """The library with a spin limit of 0, for the test of the give-up path of
+    compress: every cross-workgroup wait of the compress kernel gives up at
+    once, from the host's point of view exactly as a dispatch that broke
+    workgroup order would.  Test infrastructure only; never loaded by the
+    package."""
+    tmp = GIVEUP_LIB + ".tmp%d" % os.getpid()
+    cmd = compile_command(tmp, extra=("-DZC_SPIN_LIMIT=0",))
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, GIVEUP_LIB)
+    return GIVEUP_LIB
+
+
 def assembly(out_path: str, source: str = SOURCES[0]) -> str:
     """Device assembly of the kernels (for inspection of the generated gfx950 code)."""
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC,

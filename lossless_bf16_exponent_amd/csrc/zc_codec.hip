@@ -306,8 +306,13 @@ __device__ __forceinline__ uint32_t get_staged4(const uint8_t *p) {
 // Waits of finalize blocks poll at most this often before the call is given
 // up (with s_sleep between polls this is well over a second, far beyond the
 // longest encode).  Only a dispatch that did not follow workgroup order could
-// reach it; the kernel then still ends and the stream is marked invalid.
-constexpr uint32_t kSpinLimit = 1u << 20;
+// reach it; the kernel then still ends, the header gets a zero magic (every
+// decoder rejects the stream) and the stream size reads 0.  A test build sets
+// ZC_SPIN_LIMIT to 0 so that every wait gives up at once.
+#ifndef ZC_SPIN_LIMIT
+#define ZC_SPIN_LIMIT (1u << 20)
+#endif
+constexpr uint32_t kSpinLimit = ZC_SPIN_LIMIT;
 
 // Thread tid polls words tid + kThreads q (q < Q) of a word array while the
 // index is below count, until every one carries the token.  Payloads of valid

@@ -1,0 +1,90 @@
+"""The give-up path of compress.  Finalize work waits on words written by
+other workgroups of the same launch; every wait is bounded, and a call whose
+wait runs out must still end, leave a stream that every decoder rejects and
+report a stream size of 0.  With workgroups dispatched in index order no wait
+can run out, so the test uses a build of the library whose spin limit is 0
+(every wait gives up at once), loaded next to the shipped library."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import require_gpu, slot, to_device
+from lossless_bf16_exponent_amd import _build, workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def zc():
+    return require_gpu()
+
+
+@pytest.fixture(scope="module")
+def giveup(zc):
+    if not os.path.exists(_build.GIVEUP_LIB):
+        raise RuntimeError("%s is not built (run __graft_entry__.build())" % _build.GIVEUP_LIB)
+    lib = ctypes.CDLL(_build.GIVEUP_LIB)
+    lib.zc_compress.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(zc.zc_plan), ctypes.c_void_p,
+                                ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.zc_compress.restype = ctypes.c_int
+    lib.zc_compress_batch.argtypes = [ctypes.POINTER(zc.zc_enc_seg), ctypes.c_uint32, ctypes.c_void_p]
+    lib.zc_compress_batch.restype = ctypes.c_int
+    return lib
+
+
+def gaussian(n, sigma, seed):
+    g = np.random.default_rng(seed)
+    return workloads.bf16_bits_from_f32((g.standard_normal(n) * sigma).astype(np.float32))
+
+
+def test_given_up_compress_reports_nothing_and_decoders_reject_it(zc, giveup):
+    ns = [300_007, 0, 8192 * 40 + 5, 1_000_003]
+    plans = [zc.zc_plan_from_sigma(s) for s in (0.02, 1.0, 1e-3, 0.16)]
+    plans[3] = zc.plan_with_raw_fallback(plans[3])
+    xs = [gaussian(n, s, i) for i, (n, s) in enumerate(zip(ns, (0.02, 1.0, 1e-3, 0.16)))]
+    devs = [to_device(x) if x.size else None for x in xs]
+    caps = [zc.zc_max_compressed_bytes(n) for n in ns]
+    offs = np.concatenate([[0], np.cumsum([slot(c) for c in caps])]).astype(np.int64)
+    buf = torch.full((int(offs[-1]),), 0x5A, dtype=torch.uint8, device="cuda")
+    sizes = torch.full((len(ns),), 12345, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    # one call alone, then the four in one batched launch
+    p0 = zc._plan(plans[0])
+    rc = giveup.zc_compress(devs[0].data_ptr(), ns[0], ctypes.byref(p0), buf.data_ptr(), caps[0],
+                            sizes.data_ptr(), stream.cuda_stream)
+    assert rc == zc.ZC_OK
+    torch.cuda.synchronize()  # the kernels ended
+    assert int(sizes[0].item()) == 0
+    assert int.from_bytes(buf[0:4].cpu().numpy().tobytes(), "little") == 0
+
+    sizes.fill_(12345)
+    arr, k = zc.make_enc_segs([(devs[i] if ns[i] else 0, ns[i], plans[i], buf.data_ptr() + int(offs[i]), caps[i],
+                                sizes.data_ptr() + 8 * i) for i in range(len(ns))])
+    assert giveup.zc_compress_batch(arr, k, stream.cuda_stream) == zc.ZC_OK
+    torch.cuda.synchronize()
+    assert sizes.cpu().numpy().tolist() == [0] * len(ns)
+    for i in range(len(ns)):
+        o = int(offs[i])
+        assert int.from_bytes(buf[o:o + 4].cpu().numpy().tobytes(), "little") == 0, i
+
+    # the shipped decoder rejects every such stream and writes nothing
+    status = torch.full((len(ns),), -1, dtype=torch.int32, device="cuda")
+    outs = [torch.full((max(n, 1),), 0x1357, dtype=torch.int16, device="cuda") for n in ns]
+    zc.zc_decompress_batch([(buf.data_ptr() + int(offs[i]), caps[i], ns[i], outs[i], status.data_ptr() + 4 * i)
+                            for i in range(len(ns))])
+    torch.cuda.synchronize()
+    assert status.cpu().numpy().tolist() == [zc.ZC_ERR_CORRUPT] * len(ns)
+    for o in outs:
+        assert bool((o == 0x1357).all())
+
+    # and the shipped library, in the same process, still compresses correctly
+    import oracle
+    zc.zc_compress(devs[0], ns[0], plans[0], buf, caps[0], sizes)
+    torch.cuda.synchronize()
+    ref = oracle.encode(xs[0], plans[0])
+    assert int(sizes[0].item()) == ref.size
+    assert np.array_equal(buf[:ref.size].cpu().numpy(), ref)
