@@ -50,7 +50,8 @@
  *
  * Conventions for every call:
  *   - all buffers belong to the caller; the library never allocates, frees or
- *     synchronizes, and keeps no state between calls;
+ *     synchronizes, and keeps no state between calls (the one exception is the
+ *     static device workspace of zc_exponent_histogram_noalloc);
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); device
  *     work is enqueued on it and the call returns without waiting;
  *   - "device" pointers are HIP device memory of the current device;
@@ -184,6 +185,22 @@ uint64_t zc_stats_workspace_bytes(uint64_t n);
  * values whose exponent field (bits 14..7) is e.  Exact for every n. */
 zc_status zc_exponent_histogram(const void *d_in, uint64_t n, void *d_workspace, uint64_t workspace_bytes,
                                 uint64_t *d_hist, void *stream);
+
+/* zc_exponent_histogram for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops or harnesses that forbid hipMalloc):
+ * the same two launches and the same result, with the workspace held by the
+ * library in a static device array of zc_stats_workspace_bytes() bytes
+ * (512 KiB), one per GPU, kept until the process ends.  It calls no hipMalloc,
+ * hipFree or other allocating routine.  All calls on one GPU share that array:
+ * calls whose work overlaps on one GPU (several streams, several host
+ * threads) race and must be serialized by the caller; calls in one stream are
+ * ordered by it.  The array needs no clearing between calls.
+ *   d_in    device, n BF16 values, 16-byte aligned (n = 0 .. 2^32-1)
+ *   d_hist  device, 256 u64, 8-byte aligned
+ * Errors returned: ZC_ERR_INVALID_ARG (NULL d_hist, NULL d_in with n > 0,
+ * n > 2^32-1), ZC_ERR_MISALIGNED, ZC_ERR_HIP (a failed launch, or the address
+ * of the array could not be obtained on the current device). */
+zc_status zc_exponent_histogram_noalloc(const void *d_in, uint64_t n, uint64_t *d_hist, void *stream);
 
 /* The table of the seven largest counts of a 256-entry histogram (host
  * array), ascending; equal counts go to the smaller field, so a histogram with

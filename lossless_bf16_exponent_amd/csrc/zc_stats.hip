@@ -32,8 +32,10 @@
 //     (two register sets in turn).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "zc.h"
 
@@ -386,24 +388,75 @@ static zc_status check_stats_args(const void *d_in, uint64_t n, const void *d_ws
     return ZC_OK;
 }
 
-extern "C" zc_status zc_exponent_histogram(const void *d_in, uint64_t n, void *d_workspace, uint64_t workspace_bytes,
-                                           uint64_t *d_hist, void *stream) {
-    const zc_status rc = check_stats_args(d_in, n, d_workspace, workspace_bytes, d_hist);
-    if (rc != ZC_OK) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
+// The two histogram launches over a workspace of kWorkspaceBytes at `rows`.
+// Every block of hist_kernel writes its whole row (also with no tile, n = 0
+// included) and hist_sum_kernel reads only those rows, so the workspace never
+// needs clearing.
+static zc_status launch_histogram(const void *d_in, uint64_t n, uint32_t *rows, uint64_t *d_hist, hipStream_t st) {
     (void)hipGetLastError();
     HistArgs h;
     h.in = static_cast<const uint16_t *>(d_in);
     h.n = n;
-    h.rows = static_cast<uint32_t *>(d_workspace);
-    // every block writes its row, also when it has no tile (n = 0 included)
+    h.rows = rows;
     hipLaunchKernelGGL(hist_kernel, dim3(kHistBlocks), dim3(kHistThreads), 0, st, h);
     if (hipGetLastError() != hipSuccess) return ZC_ERR_HIP;
     HistSumArgs s;
-    s.rows = h.rows;
+    s.rows = rows;
     s.hist = reinterpret_cast<unsigned long long *>(d_hist);
     hipLaunchKernelGGL(hist_sum_kernel, dim3(kBins), dim3(kSumThreads), 0, st, s);
     return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
+}
+
+extern "C" zc_status zc_exponent_histogram(const void *d_in, uint64_t n, void *d_workspace, uint64_t workspace_bytes,
+                                           uint64_t *d_hist, void *stream) {
+    const zc_status rc = check_stats_args(d_in, n, d_workspace, workspace_bytes, d_hist);
+    if (rc != ZC_OK) return rc;
+    return launch_histogram(d_in, n, static_cast<uint32_t *>(d_workspace), d_hist, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// The histogram without a caller workspace, for callers that cannot allocate
+// device memory (code under HIP graph capture, serving loops that forbid
+// hipMalloc).  The workspace is this file-scope device array: every GPU that
+// runs the call holds one copy of it until the process ends.  Host code never
+// uses the array's name as an address (on the host it is only a stand-in for
+// the symbol): the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) uint8_t scratch[kWorkspaceBytes];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void *> g_scratch[kMaxDevices];
+static std::mutex g_scratch_mutex;
+
+// The current device's copy of `scratch`, looked up on the first call on that
+// device; NULL when HIP cannot report it.
+static void *device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void *q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        p = q;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+extern "C" zc_status zc_exponent_histogram_noalloc(const void *d_in, uint64_t n, uint64_t *d_hist, void *stream) {
+    if (n > kMaxElems || !d_hist || (n && !d_in)) return ZC_ERR_INVALID_ARG;
+    if (((uintptr_t)d_in & 15u) || ((uintptr_t)d_hist & 7u)) return ZC_ERR_MISALIGNED;
+    void *ws = device_scratch();
+    if (!ws) return ZC_ERR_HIP;
+    return launch_histogram(d_in, n, static_cast<uint32_t *>(ws), d_hist, static_cast<hipStream_t>(stream));
 }
 
 extern "C" zc_status zc_estimate_sigma(const void *d_in, uint64_t n, void *d_workspace, uint64_t workspace_bytes,

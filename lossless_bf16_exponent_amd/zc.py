@@ -70,6 +70,8 @@ _lib.zc_stats_workspace_bytes.restype = ctypes.c_uint64
 _lib.zc_exponent_histogram.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64,
                                        ctypes.c_void_p, ctypes.c_void_p]
 _lib.zc_exponent_histogram.restype = ctypes.c_int
+_lib.zc_exponent_histogram_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+_lib.zc_exponent_histogram_noalloc.restype = ctypes.c_int
 _lib.zc_plan_from_histogram.argtypes = [ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(zc_plan)]
 _lib.zc_plan_from_histogram.restype = ctypes.c_int
 _lib.zc_estimate_sigma.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64,
@@ -83,7 +85,7 @@ _lib.zc_status_string.restype = ctypes.c_char_p
 EXPORTED = ("zc_plan_from_sigma", "zc_max_compressed_bytes", "zc_compress", "zc_decompress",
             "zc_compress_batch", "zc_decompress_batch", "zc_decompress_reduce", "zc_read_header",
             "zc_status_string", "zc_stats_workspace_bytes", "zc_exponent_histogram", "zc_plan_from_histogram",
-            "zc_estimate_sigma")
+            "zc_estimate_sigma", "zc_exponent_histogram_noalloc")
 
 
 class ZcError(RuntimeError):
@@ -171,6 +173,11 @@ def zc_stats_workspace_bytes(n: int) -> int:
 def zc_exponent_histogram(d_in, n, d_workspace, workspace_bytes, d_hist, stream=None) -> None:
     _check(_lib.zc_exponent_histogram(_ptr(d_in), int(n), _ptr(d_workspace), int(workspace_bytes), _ptr(d_hist),
                                       _stream(stream)), "zc_exponent_histogram")
+
+
+def zc_exponent_histogram_noalloc(d_in, n, d_hist, stream=None) -> None:
+    _check(_lib.zc_exponent_histogram_noalloc(_ptr(d_in), int(n), _ptr(d_hist), _stream(stream)),
+           "zc_exponent_histogram_noalloc")
 
 
 def zc_plan_from_histogram(hist) -> tuple:
