@@ -9,20 +9,28 @@
 // coalesced 128-bit accesses, the 3-bit codes as three 1-bit arrays.
 //
 // Design on gfx950 (pure HBM-bandwidth path, no MFMA):
-//   * a 256-thread block codes one 8192-element tile; a lane loads 8 values
+//   * a 256-thread block codes one 8192-element span; a lane loads 8 values
 //     with one 128-bit load per step, so every wave-wide load or store is a
 //     contiguous 1 KiB (input), 512 B (sign+mantissa) or 64 B (plane) run;
 //   * codes and bit planes come from dword-wide byte shuffles (zc_lane.h), and
 //     the per-lane plane bytes are regrouped through LDS into whole dwords per
 //     plane before they are stored;
-//   * zero-point bytes are placed by an exclusive scan in two passes: inside
-//     a block (lane DPP scan -> wave -> sub-tile) while it codes its 32768-
-//     value span, which it leaves with its zero-point count and its staged
-//     zero-point bytes in the output's scratch tail; then a small finalize
-//     pass scans the span counts, fills the table and moves the staged bytes
-//     to their place.  No block ever waits for another one: under a saturated
-//     memory system every cross-block handshake costs a full round trip per
-//     block, which measured slower than the extra 2 bytes per zero-point;
+//   * zero-point bytes are placed by an exclusive scan across the tensor.  In
+//     a launch longer than the device holds at once, encoder blocks never wait:
+//     each leaves its zero-point count (a span word) and its zero-point bytes
+//     staged in the output's scratch tail.  Finalize blocks of the same launch,
+//     placed about a device's worth of blocks behind the spans they complete,
+//     sum the counts through a hierarchy of run and chunk words, fill the
+//     table and move the staged bytes to their place.  A launch the device
+//     holds at once is coded in direct mode: each block finds its own place
+//     and writes its bytes there, with no staging.  Blocks wait only for
+//     blocks of the same launch with lower indices, which workgroup dispatch
+//     in index order has started first; every wait is bounded, and a call
+//     whose wait runs out still ends, with a zero magic in its header and a
+//     stream size of 0.  The segment's last block writes the header once every
+//     other block of the segment has passed its waits (zc_grid.h places the
+//     roles; the scratch words are described below, with the reasons the
+//     handshakes are device-scope accesses and not release/acquire pairs);
 //   * the decoder needs no scan across tiles: the table of zero-point counts
 //     per 4096-element group gives every tile its slice of the zero-point
 //     array, which is staged in LDS and gathered by rank.
@@ -51,10 +59,11 @@ struct EncSeg {
     unsigned long long *out_bytes;
     uint32_t n;
     uint8_t exps[7];
-    uint8_t mode;      // kModeWindow or kModeTable
-    uint8_t raw_ok;    // the plan allows the raw fallback
+    uint8_t flags;     // kSegTable, kSegRawOk
 };
 static_assert(sizeof(EncSeg) == 40, "compact kernel arguments");
+constexpr uint8_t kSegTable = 1;  // codes from a 256-byte LDS table (else: the window's saturating arithmetic)
+constexpr uint8_t kSegRawOk = 2;  // the plan allows the raw fallback
 
 // The compress grid is a sequence of pieces (zc_grid.h).
 static_assert(kMaxSegments == ZC_MAX_BATCH, "one segment per batch entry");
@@ -64,12 +73,13 @@ struct EncArgs {
     uint32_t pieces;
     uint32_t tok_lo, tok_hi;  // the call's token (scratch words of other calls never match it)
     EncSeg seg[ZC_MAX_BATCH];
-    uint32_t piece_start[kMaxPieces + 1];  // first grid block of each piece; the last entry is the grid size
-    // Words, not bytes: with a byte array the compiler shared the address
-    // base + p between the byte read and the start read, giving the scalar
-    // load of piece_start[p] a base that is not 4-byte aligned, which the
-    // scalar unit does not honour (every finalize block saw piece start 0).
-    uint32_t piece_info[kMaxPieces];
+    // Piece words (zc_grid.h: first grid block, kind, segment; the last entry
+    // holds the grid size) and each piece's first span or run.  Words, not
+    // bytes: with a byte array the compiler once shared an address base + p
+    // between a byte read and a word read, giving a scalar load a base that is
+    // not 4-byte aligned, which the scalar unit does not honour.
+    uint32_t piece[kMaxPieces + 1];
+    uint32_t first[kMaxPieces];
 };
 // Kept within the conventional 4 KiB kernel-argument budget, counting up to
 // 256 bytes of the runtime's hidden arguments.
@@ -118,8 +128,6 @@ struct ZeroArgs {
     ZeroRegion r[ZC_MAX_BATCH];
 };
 
-constexpr uint8_t kModeWindow = 0;  // exps = w+1 .. w+7 with w >= 0: codes by saturating arithmetic
-constexpr uint8_t kModeTable = 1;   // any other ascending set: codes from a 256-byte LDS table
 
 
 // ---------------------------------------------------------------------------
@@ -184,21 +192,22 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
 // them at its start, 7 % of the bucket's decompress time).  All lanes of the
 // wave must be active.
 template <uint32_t kEntries>
-__device__ __forceinline__ uint32_t count_at_or_below(const uint32_t *v, uint32_t count, uint32_t flat) {
+__device__ __forceinline__ uint32_t count_at_or_below(const uint32_t *v, uint32_t count, uint32_t flat,
+                                                      uint32_t mask = ~0u) {
     const uint32_t lane = __lane_id();
     uint32_t total = 0;
 #pragma unroll
     for (uint32_t c = 0; c < (kEntries - 1 + kWave - 1) / kWave; ++c) {
         const uint32_t i = 1u + (uint32_t)kWave * c + lane;
-        const bool hit = i < count && v[i] <= flat;  // (read only below count: inside the array)
+        const bool hit = i < count && (v[i] & mask) <= flat;  // (read only below count: inside the array)
         total += (uint32_t)__builtin_popcountll(__ballot(hit));
     }
     return total;
 }
 
-// The piece holding grid block `flat`.
+// The piece holding grid block `flat` (piece words keep the block in their low 24 bits).
 __device__ __forceinline__ uint32_t find_piece(const EncArgs &a, uint32_t flat) {
-    return count_at_or_below<kMaxPieces + 1>(a.piece_start, a.pieces, flat);
+    return count_at_or_below<kMaxPieces + 1>(a.piece, a.pieces, flat, kBlockMask);
 }
 
 // The decode segment holding grid block `flat`.
@@ -271,9 +280,26 @@ __global__ __launch_bounds__(256) void zero_kernel(ZeroArgs a) {
 // 64-bit token in bits 63..32 and the same 32-bit payload in bits 31..0.  A
 // reader accepts a word only when both token halves match and both payloads
 // agree, so old contents pass for fresh with probability about 2^-64.
-// Stores and loads are agent-scope atomics (`sc1`), which go through to the
-// device's coherence point: the writer and the reader may sit on different
-// XCDs, whose L2 caches are not coherent with each other.
+//
+// Ordering between blocks.  The writer and the reader may sit on different
+// XCDs, whose L2 caches are not coherent with each other.  Every access to
+// memory that one block writes and another block of the same launch reads (the
+// words and the staged zero-point bytes) is a device-scope (agent) access:
+// relaxed agent-scope atomics, which gfx950 issues with the sc1 cache policy,
+// and direct-to-LDS loads with that policy.  An sc1 store writes through the
+// L2 to the device's coherence point and its vmcnt completion means it has
+// reached that point; an sc1 load is served from that point, never from a
+// stale line of the reader's L2.  So a writer that stores data with sc1, waits
+// for vmcnt(0) and then stores a word, and a reader that loads the word and
+// only then issues its sc1 loads of the data (their addresses depend on the
+// word's payload), see the data the word announces.  This is what a
+// release/acquire pair would give, without its L2 maintenance: the compiler
+// implements an agent-scope release as buffer_wbl2 sc1 (write back every
+// dirty L2 line) and an acquire as buffer_inv sc1 (invalidate the L2), which
+// only data accessed without sc1 needs.  Measured with release stores and
+// acquire loads on the words instead, compress of the 256 Mi-value bucket took
+// 3,058 us instead of 155 us.  Words that announce no data (counts, done
+// flags) need no wait before their store.
 struct Token {
     uint32_t lo, hi;
 };
@@ -293,33 +319,28 @@ __device__ __forceinline__ bool get_word(const uint8_t *w, Token t, uint32_t &pa
 }
 
 // Staged zero-point bytes move between blocks the same way (agent-scope
-// stores and loads), 8 and 4 bytes at a time.
+// stores), 8 bytes at a time.
 __device__ __forceinline__ void put_staged8(uint8_t *p, uint32_t lo, uint32_t hi) {
     __hip_atomic_store(reinterpret_cast<uint64_t *>(p), (uint64_t)lo | ((uint64_t)hi << 32), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t get_staged4(const uint8_t *p) {
-    return __hip_atomic_load(reinterpret_cast<uint32_t *>(const_cast<uint8_t *>(p)), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-}
 
-// Waits of finalize blocks poll at most this often before the call is given
-// up (with s_sleep between polls this is well over a second, far beyond the
-// longest encode).  Only a dispatch that did not follow workgroup order could
-// reach it; the kernel then still ends, the header gets a zero magic (every
-// decoder rejects the stream) and the stream size reads 0.  A test build sets
-// ZC_SPIN_LIMIT to 0 so that every wait gives up at once.
+// Waits poll at most this often before the call is given up (with s_sleep
+// between polls this is well over a second, far beyond the longest encode).
+// Only a dispatch that did not follow workgroup order could reach it; the
+// kernel then still ends, the header gets a zero magic (every decoder rejects
+// the stream) and the stream size reads 0.  A test build sets ZC_SPIN_LIMIT to
+// 0 so that every wait gives up at once.
 #ifndef ZC_SPIN_LIMIT
 #define ZC_SPIN_LIMIT (1u << 20)
 #endif
 constexpr uint32_t kSpinLimit = ZC_SPIN_LIMIT;
 
-// Thread tid polls words tid + kThreads q (q < Q) of a word array while the
-// index is below count, until every one carries the token.  Payloads of valid
-// words land in pay[q] (0 for indices at or past count).  Returns false on
-// timeout.
-template <int Q>
-__device__ __forceinline__ bool poll_words(const uint8_t *base, uint32_t count, Token t, uint32_t (&pay)[Q]) {
+// Thread tid polls words addr(i), i = tid + kThreads q (q < Q, i < count),
+// until every one carries the token.  Payloads of valid words land in pay[q]
+// (0 for indices at or past count).  Returns false on timeout.
+template <int Q, typename Addr>
+__device__ __forceinline__ bool poll_list(uint32_t count, Addr addr, Token t, uint32_t (&pay)[Q]) {
     const uint32_t i0 = threadIdx.x;
     uint32_t pend = 0;
 #pragma unroll
@@ -333,8 +354,7 @@ __device__ __forceinline__ bool poll_words(const uint8_t *base, uint32_t count, 
         bool got[Q];
         uint32_t v[Q];
 #pragma unroll
-        for (int q = 0; q < Q; ++q)
-            got[q] = (pend >> q & 1u) && get_word(base + (uint64_t)kWordBytes * (i0 + kThreads * q), t, v[q]);
+        for (int q = 0; q < Q; ++q) got[q] = (pend >> q & 1u) && get_word(addr(i0 + kThreads * q), t, v[q]);
 #pragma unroll
         for (int q = 0; q < Q; ++q)
             if (got[q]) {
@@ -343,6 +363,26 @@ __device__ __forceinline__ bool poll_words(const uint8_t *base, uint32_t count, 
             }
     }
     return true;
+}
+
+// The same over words base[0 .. count).
+template <int Q>
+__device__ __forceinline__ bool poll_words(const uint8_t *base, uint32_t count, Token t, uint32_t (&pay)[Q]) {
+    return poll_list<Q>(count, [base](uint32_t i) { return base + (uint64_t)kWordBytes * i; }, t, pay);
+}
+
+// Sum of v over the block (every thread gets it); red: kWaves words of LDS.
+// Starts and ends with a barrier, so red may be reused right after.
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t *red) {
+    const uint32_t w = wave_sum(v);
+    __syncthreads();
+    if (__lane_id() == 0) red[threadIdx.x / kWave] = w;
+    __syncthreads();
+    uint32_t t = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) t += red[i];
+    __syncthreads();
+    return t;
 }
 
 // ---------------------------------------------------------------------------
@@ -380,176 +420,30 @@ __device__ __forceinline__ Step load_step(const uint16_t *in, uint64_t base, uin
 // LDS of a compress block; the encoder and finalize roles share it.
 struct EncShared {
     uint32_t planes[kTile / 8];              // per 8-value group: plane bytes 0, 1, 2
-    __align__(16) uint8_t zp[kEncSpan + 16];  // the span's zero-point bytes, in order
+    __align__(16) uint8_t zp[kEncSpan + 16];  // the span's zero-point bytes, in order (+ slack for reads past them)
     uint8_t code[256];                        // table mode: exponent -> code
     uint32_t wave_total[2][kWaves];
     uint32_t group[kEncGroups];               // zero-points per 4096-value group of the span
+    uint32_t red[kWaves];
 };
-// A finalize block reads the span words of up to kFinWindow spans ending with
-// its own run; older spans of the segment are summed through run totals.
-constexpr uint32_t kFinWindow = 4 * kThreads;
-static_assert(kFinRunMax <= kFinWindow / 2, "the window holds the run and as many spans before it");
 // LDS landing zone of the copy: batches of spans whose staged bytes (rounded
 // up to 16) fit; any single span (at most kEncSpan bytes) does.
 constexpr uint32_t kLandBytes = 12288;
 static_assert(kLandBytes >= kEncSpan, "one span always lands");
 struct FinShared {
-    union {
-        uint32_t span[kFinWindow];                      // span-word payloads of the window
-        __align__(16) uint8_t land[kLandBytes + 48];    // later: landed staged bytes (+ slack for reads past a span)
-    };
-    uint32_t pre[kFinRunMax + 1];   // zero-points of the run before each of its spans
-    uint32_t land16[kFinRunMax + 1];  // 16-byte units of the run's spans before each span
-    uint32_t red[3][kWaves];
+    __align__(16) uint8_t land[kLandBytes + 48];  // landed staged bytes (+ slack for reads past a span)
+    uint32_t pre[kRun + 1];     // zero-points of the run before each of its spans
+    uint32_t land16[kRun + 1];  // 16-byte units of the run's spans before each span
+    uint32_t g0[kRun];          // zero-points in the first group of each span
+    uint32_t red[kWaves];
 };
 union CompressShared {
     EncShared e;
     FinShared f;
 };
 static_assert(kEncGroups == 2, "a span word holds the counts of two groups");
-
-// Encoder role.  A block codes kEncSubTiles consecutive 8192-value sub-tiles
-// (its span).  All loads of the span are issued up front.  Phase A turns every
-// step into sign+mantissa bytes (stored at once), exponent bytes and plane
-// bytes; phase B ranks the zero-point values, regroups and stores the planes
-// and stages the zero-point bytes in LDS.  The span then stores its zero-point
-// bytes to its staging slot, waits until every store of the block has
-// completed and publishes its span word for the finalize blocks.
-__device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uint32_t b, EncShared &sh) {
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const EncSeg &sg = args.seg[s];  // b: block (span) index inside the segment
-    const uint64_t n = sg.n;
-    const Layout L = layout_for(n);
-    const uint64_t blocks = enc_blocks(n);
-    const uint8_t mode = sg.mode;
-    const uint64_t span0 = (uint64_t)b * kEncSpan;
-    uint8_t *const out = sg.out;
-    uint8_t *const scratch = out + L.off_scratch;
-    const Scratch S = scratch_for(n);
-
-    if (mode == kModeTable) {
-        uint32_t c = 0;
-#pragma unroll
-        for (int k = 0; k < 7; ++k) c = (sg.exps[k] == (uint32_t)tid) ? (uint32_t)(k + 1) : c;
-        sh.code[tid] = (uint8_t)c;
-    }
-    const uint32_t wbase = (uint32_t)sg.exps[0] - 1u;  // window mode only (exps[0] >= 1)
-    const uint32_t base_hi = (wbase << 8) | (wbase << 24);
-
-    // ---- every load of the span in flight at once
-    Step in[kEncSubTiles][kSteps];
-#pragma unroll
-    for (int sub = 0; sub < kEncSubTiles; ++sub)
-#pragma unroll
-        for (int u = 0; u < kSteps; ++u)
-            in[sub][u] = load_step(sg.in, span0 + (uint64_t)sub * kTile + 512u * (uint32_t)(wave * kSteps + u) +
-                                              8u * (uint32_t)lane, n);
-    if (mode == kModeTable) __syncthreads();  // sh.code ready
-
-    // ---- phase A: split, code, planes; count the span's zero-points
-    uint32_t ex[kEncSubTiles][kSteps][2], pl[kEncSubTiles][kSteps], zm[kEncSubTiles][kSteps];
-#pragma unroll
-    for (int sub = 0; sub < kEncSubTiles; ++sub) {
-#pragma unroll
-        for (int u = 0; u < kSteps; ++u) {
-            const uint64_t base = span0 + (uint64_t)sub * kTile + 512u * (uint32_t)(wave * kSteps + u) +
-                                  8u * (uint32_t)lane;
-            const uint32_t *d = in[sub][u].d;
-            const uint32_t sm0 = sign_mantissa4(d[0], d[1]);
-            const uint32_t sm1 = sign_mantissa4(d[2], d[3]);
-            const uint32_t t0 = exponent_high(d[0]), t1 = exponent_high(d[1]);
-            const uint32_t t2 = exponent_high(d[2]), t3 = exponent_high(d[3]);
-            ex[sub][u][0] = exponents4(t0, t1);
-            ex[sub][u][1] = exponents4(t2, t3);
-            uint32_t c_lo, c_hi;
-            if (mode == kModeWindow) {
-                c_lo = window_codes4(t0, t1, base_hi);
-                c_hi = window_codes4(t2, t3, base_hi);
-            } else {
-                c_lo = c_hi = 0;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    c_lo |= (uint32_t)sh.code[(ex[sub][u][0] >> (8 * k)) & 0xFFu] << (8 * k);
-                    c_hi |= (uint32_t)sh.code[(ex[sub][u][1] >> (8 * k)) & 0xFFu] << (8 * k);
-                }
-            }
-            // values at or past n carry no code bits and are no zero-points
-            const uint32_t vm = in[sub][u].vmask;
-            pl[sub][u] = codes_to_planes(c_lo, c_hi) & (vm * 0x010101u);
-            zm[sub][u] = zero_point_mask(pl[sub][u]) & vm;
-            if (vm) store_stream8(out + kHeaderBytes + base, sm0, sm1);
-        }
-    }
-    // ---- phase B: ranks, plane regrouping, zero-point staging
-    uint32_t running = 0;  // zero-points of the span so far (uniform)
-#pragma unroll
-    for (int sub = 0; sub < kEncSubTiles; ++sub) {
-        const uint64_t tile0 = span0 + (uint64_t)sub * kTile;
-#pragma unroll
-        for (int u = 0; u < kSteps; ++u) sh.planes[(wave * kSteps + u) * kWave + lane] = pl[sub][u];
-        const TileCounts tc = count_tile(zm[sub], lane, wave, sh.wave_total[sub & 1]);
-        {
-            const uint4 q = reinterpret_cast<const uint4 *>(sh.planes)[tid];
-            const uint32_t lo01 = perm(q.y, q.x, 0x05010400u), hi23 = perm(q.w, q.z, 0x05010400u);
-            const uint32_t p0 = perm(hi23, lo01, 0x05040100u);
-            const uint32_t p1 = perm(hi23, lo01, 0x07060302u);
-            const uint32_t p2 = perm(perm(q.w, q.z, 0x0C0C0602u), perm(q.y, q.x, 0x0C0C0602u), 0x05040100u);
-            if (tile0 + 32u * (uint32_t)tid < n) {
-                const uint64_t off = tile0 / 8 + 4u * (uint32_t)tid;
-                store_stream4(out + L.off_p0 + off, p0);
-                store_stream4(out + L.off_p1 + off, p1);
-                store_stream4(out + L.off_p2 + off, p2);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kSteps; ++u) {
-            uint32_t m = zm[sub][u], r = running + tc.rank[u];
-            while (m) {
-                const uint32_t k = __builtin_ctz(m);
-                m &= m - 1;
-                sh.zp[r++] = (uint8_t)get_byte8(ex[sub][u][0], ex[sub][u][1], k);
-            }
-        }
-        if (tid == 0) {
-            sh.group[2 * sub] = tc.first_group;
-            sh.group[2 * sub + 1] = tc.tile_total - tc.first_group;
-        }
-        running += tc.tile_total;
-        __syncthreads();  // sh.planes is rewritten by the next sub-tile; sh.zp and sh.group are complete
-    }
-
-    // ---- the span's zero-point bytes -> its staging slot
-    const uint32_t T = running;
-    {
-        uint8_t *const slot = scratch + S.staging + (uint64_t)b * kEncSpan;
-        for (uint32_t i = tid; 16 * i < T; i += kThreads) {
-            const uint4 v = reinterpret_cast<const uint4 *>(sh.zp)[i];
-            put_staged8(slot + 16 * i, v.x, v.y);
-            put_staged8(slot + 16 * i + 8, v.z, v.w);
-        }
-    }
-
-    // ---- pads the data stores never touch (the last span of the segment)
-    if (b == blocks - 1) {
-        const uint64_t sm_end = kHeaderBytes + 8 * ((n + 7) / 8);
-        for (uint64_t i = sm_end + tid; i < L.off_p0; i += kThreads) out[i] = 0;
-        const uint64_t pl_end = 4 * ((n + 31) / 32);
-        for (uint64_t i = pl_end + tid; i < L.plane_bytes; i += kThreads) {
-            out[L.off_p0 + i] = 0;
-            out[L.off_p1 + i] = 0;
-            out[L.off_p2 + i] = 0;
-        }
-        for (uint64_t i = L.off_tab + 4 * (L.groups + 1) + tid; i < L.off_zp; i += kThreads) out[i] = 0;
-    }
-
-    // ---- publish: every store of every thread has completed (the staged
-    // bytes at the coherence point) before the span word is written
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (tid == 0)
-        put_word(scratch + S.span_words + (uint64_t)kWordBytes * b, Token{args.tok_lo, args.tok_hi},
-                 sh.group[0] | (sh.group[1] << 16));
-}
+static_assert(kRun <= kWave, "a run's spans are scanned by one wave");
+static_assert(kGroupSpans - 1 + kMaxDirectGroups <= kThreads, "a direct block polls its words in one round");
 
 // Copy of staged zero-point bytes to the stream, in two phases.  Landing:
 // the staged bytes of a batch of spans come into an LDS landing zone with
@@ -643,113 +537,324 @@ __device__ __forceinline__ void write_span(uint8_t *zp, uint64_t dst_off, const 
     }
 }
 
-// Finalize role: block jb of a segment completes the run of encoder spans
-// [first, first + count).  It waits for the span words of the run and of the
-// spans just before it (the window, up to kFinWindow spans), publishes the run
-// total, and sums the totals of the segment's runs older than the window: the
-// sum places the run in the zero-point array.  It then writes the run's table
-// entries and moves the staged zero-point bytes to their place.  Spans whose
-// encoder blocks finish last are reached through their own span words, never
-// through another finalize block.  The last block of the segment also waits
-// until every other block has passed its waits, then writes the header, the
-// final table entry and the stream size.
-__device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, uint32_t jb, FinShared &sh) {
+
+// The header, the table's last entry and the stream size of a segment with E
+// zero-points.  ok = false (a wait given up somewhere in the segment) leaves a
+// zero magic, which every decoder rejects, and a stream size of 0.  Raw
+// fallback: when the plan allows it and coding has made the stream larger
+// than the input, the header says raw and the raw pass (a second launch)
+// copies the input behind it.
+__device__ __forceinline__ void write_header(const EncSeg &sg, const Layout &L, uint64_t E, bool ok) {
+    const int tid = threadIdx.x;
+    const uint64_t n = sg.n;
+    uint8_t *const out = sg.out;
+    const uint64_t raw_total = kHeaderBytes + 2 * n;
+    const bool raw = (sg.flags & kSegRawOk) && L.off_zp + E > raw_total;
+    const uint64_t total = raw ? raw_total : L.off_zp + E;
+    if (ok && tid == 0) reinterpret_cast<uint32_t *>(out + L.off_tab)[L.groups] = (uint32_t)E;
+    if (tid < 32) {
+        uint32_t w = 0;
+        switch (tid) {
+            case 0: w = ok ? kMagic : 0u; break;
+            case 1: w = (uint32_t)kVersion | (kHeaderBytes << 16); break;
+            case 2: w = (uint32_t)n; break;
+            case 3: w = (uint32_t)(n >> 32); break;
+            case 4: w = kGroup; break;
+            case 5: w = (uint32_t)L.groups; break;
+            case 6: w = sg.exps[0] | (sg.exps[1] << 8) | (sg.exps[2] << 16) | ((uint32_t)sg.exps[3] << 24); break;
+            case 7: w = sg.exps[4] | (sg.exps[5] << 8) | (sg.exps[6] << 16) | ((raw ? kModeRaw : kModeCoded) << 24); break;
+            case 8: w = (uint32_t)E; break;
+            case 9: w = (uint32_t)(E >> 32); break;
+            case 10: w = (uint32_t)total; break;
+            case 11: w = (uint32_t)(total >> 32); break;
+            default: break;
+        }
+        reinterpret_cast<uint32_t *>(out)[tid] = w;
+    }
+    if (tid == 0 && sg.out_bytes) *sg.out_bytes = ok ? total : 0ull;
+}
+
+// Direct role (every block of a launch that the device holds at once;
+// zc_grid.h).  The block publishes its span word, then finds the zero-points
+// before its span: those of earlier groups of kGroupSpans spans through their
+// group words, and of the earlier spans of its own group through their span
+// words.  It then writes its table entries and its zero-point bytes (from
+// LDS) in place: nothing is staged.  The last span of each group first sums
+// its group's span words and publishes the group word, so that no group word
+// waits for another one.  The segment's last span writes the header once every
+// other block of the segment has passed its waits.
+__device__ __forceinline__ void direct_place(const EncArgs &args, uint32_t s, uint32_t b, uint32_t T,
+                                             EncShared &sh) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const EncSeg &sg = args.seg[s];
     const uint64_t n = sg.n;
     const Layout L = layout_for(n);
     const Scratch S = scratch_for(n);
-    const uint64_t nb = enc_blocks(n);
-    const uint32_t nf = (uint32_t)fin_blocks(n);
-    const uint32_t run = fin_run(nb);
-    const uint32_t first = jb * run;
-    const uint32_t count = (uint32_t)min((uint64_t)run, nb - first);
-    const uint32_t end = first + count;
-    const uint32_t wr = end > kFinWindow ? (end - kFinWindow + run - 1) / run : 0u;  // runs read as totals
-    const uint32_t ws = wr * run;                                                   // first span of the window
-    const uint32_t nsw = end - ws, before = first - ws;
-    const bool last = (jb == nf - 1);
+    const uint32_t nb = (uint32_t)enc_blocks(n);
+    const Token tok{args.tok_lo, args.tok_hi};
+    uint8_t *const out = sg.out;
+    uint8_t *const scratch = out + L.off_scratch;
+    const uint8_t *const span_w = scratch + S.span_words;
+    const uint8_t *const group_w = scratch + S.group_words;
+    const uint32_t g = b / kGroupSpans, g0 = g * kGroupSpans;  // g0: the group's first span
+    const bool group_last = b % kGroupSpans == kGroupSpans - 1 || b + 1 == nb;
+    const uint32_t c0 = sh.group[0], c1 = sh.group[1];
+    // a count announces no data: no wait before it
+    if (tid == 0) put_word(scratch + S.span_words + (uint64_t)kWordBytes * b, tok, c0 | (c1 << 16));
+
+    bool ok = true;
+    uint32_t sib = 0;  // zero-points of the group's spans before b (the group's last span only)
+    if (group_last) {
+        uint32_t sp[1];
+        ok = poll_words<1>(span_w + (uint64_t)kWordBytes * g0, b - g0, tok, sp);
+        ok = __syncthreads_and(ok);
+        sib = block_sum((sp[0] & 0xFFFFu) + (sp[0] >> 16), sh.red);
+        if (ok && tid == 0) put_word(scratch + S.group_words + (uint64_t)kWordBytes * g, tok, sib + c0 + c1);
+    }
+    // the group's earlier spans (unless summed above) and the earlier groups
+    const uint32_t nsib = group_last ? 0u : b - g0;
+    uint32_t pay[1] = {0};
+    if (ok)
+        ok = poll_list<1>(
+            nsib + g,
+            [&](uint32_t i) {
+                return i < nsib ? span_w + (uint64_t)kWordBytes * (g0 + i)
+                                : group_w + (uint64_t)kWordBytes * (i - nsib);
+            },
+            tok, pay);
+    ok = __syncthreads_and(ok);
+    const uint32_t mine = (uint32_t)tid < nsib ? (pay[0] & 0xFFFFu) + (pay[0] >> 16) : pay[0];
+    const uint32_t P = sib + block_sum(mine, sh.red);
+
+    if (ok) {
+        uint32_t *const tab = reinterpret_cast<uint32_t *>(out + L.off_tab);
+        const uint64_t gi = (uint64_t)b * kEncGroups;
+        if (tid == 0 && gi < L.groups) tab[gi] = P;
+        if (tid == 1 && gi + 1 < L.groups) tab[gi + 1] = P + c0;
+        write_span(out + L.off_zp, P, sh.zp, T, lane, (uint32_t)wave, kWaves);
+    }
+    // data needs no wait before a done word: nothing in this launch reads it
+    if (b + 1 < nb) {
+        if (ok && tid == 0) put_word(scratch + S.span_done + (uint64_t)kWordBytes * b, tok, 1u);
+        return;
+    }
+    // the segment's last span: every earlier span has passed its waits
+    if (ok) {
+        uint32_t dn[8];
+        static_assert(kDirectMax <= 8 * kThreads, "one round polls every done word");
+        ok = poll_words<8>(scratch + S.span_done, b, tok, dn);
+    }
+    ok = __syncthreads_and(ok);
+    write_header(sg, L, (uint64_t)P + c0 + c1, ok);
+}
+
+// Encoder role.  A block codes kEncSubTiles consecutive 8192-value sub-tiles
+// (its span).  All loads of the span are issued up front.  Phase A turns every
+// step into sign+mantissa bytes (stored at once), exponent bytes and plane
+// bytes; phase B ranks the zero-point values, regroups and stores the planes
+// and collects the zero-point bytes in LDS.  A staged span then stores its
+// zero-point bytes to its staging slot, waits until every store of the block
+// has completed and publishes its span word for the finalize blocks; a direct
+// span places its bytes itself (direct_place).
+__device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uint32_t b, bool direct,
+                                            EncShared &sh) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const EncSeg &sg = args.seg[s];  // b: block (span) index inside the segment
+    const uint64_t n = sg.n;
+    const Layout L = layout_for(n);
+    const uint64_t blocks = enc_blocks(n);
+    const bool table = (sg.flags & kSegTable) != 0;
+    const uint64_t span0 = (uint64_t)b * kEncSpan;
+    uint8_t *const out = sg.out;
+    uint8_t *const scratch = out + L.off_scratch;
+    const Scratch S = scratch_for(n);
+
+    if (table) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int k = 0; k < 7; ++k) c = (sg.exps[k] == (uint32_t)tid) ? (uint32_t)(k + 1) : c;
+        sh.code[tid] = (uint8_t)c;
+    }
+    const uint32_t wbase = (uint32_t)sg.exps[0] - 1u;  // window mode only (exps[0] >= 1)
+    const uint32_t base_hi = (wbase << 8) | (wbase << 24);
+
+    // ---- every load of the span in flight at once
+    Step in[kEncSubTiles][kSteps];
+#pragma unroll
+    for (int sub = 0; sub < kEncSubTiles; ++sub)
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u)
+            in[sub][u] = load_step(sg.in, span0 + (uint64_t)sub * kTile + 512u * (uint32_t)(wave * kSteps + u) +
+                                              8u * (uint32_t)lane, n);
+    if (table) __syncthreads();  // sh.code ready
+
+    // ---- phase A: split, code, planes; count the span's zero-points
+    uint32_t ex[kEncSubTiles][kSteps][2], pl[kEncSubTiles][kSteps], zm[kEncSubTiles][kSteps];
+#pragma unroll
+    for (int sub = 0; sub < kEncSubTiles; ++sub) {
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            const uint64_t base = span0 + (uint64_t)sub * kTile + 512u * (uint32_t)(wave * kSteps + u) +
+                                  8u * (uint32_t)lane;
+            const uint32_t *d = in[sub][u].d;
+            const uint32_t sm0 = sign_mantissa4(d[0], d[1]);
+            const uint32_t sm1 = sign_mantissa4(d[2], d[3]);
+            const uint32_t t0 = exponent_high(d[0]), t1 = exponent_high(d[1]);
+            const uint32_t t2 = exponent_high(d[2]), t3 = exponent_high(d[3]);
+            ex[sub][u][0] = exponents4(t0, t1);
+            ex[sub][u][1] = exponents4(t2, t3);
+            uint32_t c_lo, c_hi;
+            if (!table) {
+                c_lo = window_codes4(t0, t1, base_hi);
+                c_hi = window_codes4(t2, t3, base_hi);
+            } else {
+                c_lo = c_hi = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    c_lo |= (uint32_t)sh.code[(ex[sub][u][0] >> (8 * k)) & 0xFFu] << (8 * k);
+                    c_hi |= (uint32_t)sh.code[(ex[sub][u][1] >> (8 * k)) & 0xFFu] << (8 * k);
+                }
+            }
+            // values at or past n carry no code bits and are no zero-points
+            const uint32_t vm = in[sub][u].vmask;
+            pl[sub][u] = codes_to_planes(c_lo, c_hi) & (vm * 0x010101u);
+            zm[sub][u] = zero_point_mask(pl[sub][u]) & vm;
+            if (vm) store_stream8(out + kHeaderBytes + base, sm0, sm1);
+        }
+    }
+    // ---- phase B: ranks, plane regrouping, zero-point staging
+    uint32_t running = 0;  // zero-points of the span so far (uniform)
+#pragma unroll
+    for (int sub = 0; sub < kEncSubTiles; ++sub) {
+        const uint64_t tile0 = span0 + (uint64_t)sub * kTile;
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) sh.planes[(wave * kSteps + u) * kWave + lane] = pl[sub][u];
+        const TileCounts tc = count_tile(zm[sub], lane, wave, sh.wave_total[sub & 1]);
+        {
+            const uint4 q = reinterpret_cast<const uint4 *>(sh.planes)[tid];
+            const uint32_t lo01 = perm(q.y, q.x, 0x05010400u), hi23 = perm(q.w, q.z, 0x05010400u);
+            const uint32_t p0 = perm(hi23, lo01, 0x05040100u);
+            const uint32_t p1 = perm(hi23, lo01, 0x07060302u);
+            const uint32_t p2 = perm(perm(q.w, q.z, 0x0C0C0602u), perm(q.y, q.x, 0x0C0C0602u), 0x05040100u);
+            if (tile0 + 32u * (uint32_t)tid < n) {
+                const uint64_t off = tile0 / 8 + 4u * (uint32_t)tid;
+                store_stream4(out + L.off_p0 + off, p0);
+                store_stream4(out + L.off_p1 + off, p1);
+                store_stream4(out + L.off_p2 + off, p2);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            uint32_t m = zm[sub][u], r = running + tc.rank[u];
+            while (m) {
+                const uint32_t k = __builtin_ctz(m);
+                m &= m - 1;
+                sh.zp[r++] = (uint8_t)get_byte8(ex[sub][u][0], ex[sub][u][1], k);
+            }
+        }
+        if (tid == 0) {
+            sh.group[2 * sub] = tc.first_group;
+            sh.group[2 * sub + 1] = tc.tile_total - tc.first_group;
+        }
+        running += tc.tile_total;
+        __syncthreads();  // sh.planes is rewritten by the next sub-tile; sh.zp and sh.group are complete
+    }
+
+    const uint32_t T = running;
+
+    // ---- pads the data stores never touch (the last span of the segment)
+    if (b == blocks - 1) {
+        const uint64_t sm_end = kHeaderBytes + 8 * ((n + 7) / 8);
+        for (uint64_t i = sm_end + tid; i < L.off_p0; i += kThreads) out[i] = 0;
+        const uint64_t pl_end = 4 * ((n + 31) / 32);
+        for (uint64_t i = pl_end + tid; i < L.plane_bytes; i += kThreads) {
+            out[L.off_p0 + i] = 0;
+            out[L.off_p1 + i] = 0;
+            out[L.off_p2 + i] = 0;
+        }
+        for (uint64_t i = L.off_tab + 4 * (L.groups + 1) + tid; i < L.off_zp; i += kThreads) out[i] = 0;
+    }
+    if (direct) {
+        direct_place(args, s, b, T, sh);
+        return;
+    }
+
+    // ---- staged: the span's zero-point bytes -> its staging slot
+    {
+        uint8_t *const slot = scratch + S.staging + (uint64_t)b * kEncSpan;
+        for (uint32_t i = tid; 16 * i < T; i += kThreads) {
+            const uint4 v = reinterpret_cast<const uint4 *>(sh.zp)[i];
+            put_staged8(slot + 16 * i, v.x, v.y);
+            put_staged8(slot + 16 * i + 8, v.z, v.w);
+        }
+    }
+
+    // ---- publish: every store of every thread has completed (the staged
+    // bytes at the coherence point) before the span word is written
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+        put_word(scratch + S.span_words + (uint64_t)kWordBytes * b, Token{args.tok_lo, args.tok_hi},
+                 sh.group[0] | (sh.group[1] << 16));
+}
+
+// Finalize role: block r of a segment places the staged zero-point bytes of
+// run r, spans [kRun r, kRun r + count) of the segment.
+//   1. It waits for the run's span words, publishes the run word (the run's
+//      count) and lands the first batch of staged bytes in LDS.
+//   2. It sums the zero-points before the run: the earlier runs of its chunk
+//      (kChunkRuns runs) through their run words and the earlier chunks
+//      through their chunk words.  The last run of a chunk first sums its
+//      chunk's runs and publishes the chunk word, so that no chunk word waits
+//      for another one.
+//   3. It writes the run's table entries and its zero-point bytes, a landed
+//      batch at a time.
+//   4. The last run of a chunk waits until the chunk's other runs have passed
+//      their waits and publishes the chunk's done word; the segment's last run
+//      instead writes the header once every earlier chunk is done.
+__device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, uint32_t r, FinShared &sh) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const EncSeg &sg = args.seg[s];
+    const uint64_t n = sg.n;
+    const Layout L = layout_for(n);
+    const Scratch S = scratch_for(n);
+    const uint32_t nb = (uint32_t)enc_blocks(n);
+    const uint32_t nr = (uint32_t)ceil_div(nb, kRun);
+    const uint32_t first = r * kRun, count = min(kRun, nb - first);
+    const bool last_run = r + 1 == nr;
+    const uint32_t c = r / kChunkRuns, cfirst = c * kChunkRuns;
+    const bool chunk_last = r % kChunkRuns == kChunkRuns - 1 || last_run;
     const Token tok{args.tok_lo, args.tok_hi};
     uint8_t *const out = sg.out;
     uint8_t *const scratch = out + L.off_scratch;
     uint32_t *const tab = reinterpret_cast<uint32_t *>(out + L.off_tab);
-    static_assert(kFinRunMax <= 2 * kThreads, "two spans per thread");
-    static_assert(kFinMaxBlocks <= 4 * kThreads, "four earlier runs per thread");
 
-    // ---- span words of the window
-    bool ok;
-    {
-        uint32_t sp[4];
-        ok = poll_words<4>(scratch + S.span_words + (uint64_t)kWordBytes * ws, nsw, tok, sp);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if ((uint32_t)tid + kThreads * q < nsw) sh.span[tid + kThreads * q] = sp[q];
-    }
+    // ---- 1. the run's span words (threads 0 .. count-1, all in wave 0): the
+    // exclusive prefixes of zero-points and of landing units, the run's count
+    uint32_t sp[1];
+    bool ok = poll_words<1>(scratch + S.span_words + (uint64_t)kWordBytes * first, count, tok, sp);
     ok = __syncthreads_and(ok);
-
-    // ---- the run (thread tid: its spans 2 tid, 2 tid + 1): exclusive prefixes
-    // of zero-points and of landing units, the run total; the window's spans
-    // before the run: their sum
-    uint32_t g00 = 0, g01 = 0, g10 = 0, g11 = 0, ex = 0, A = 0, P = 0;
-    if (ok) {
-        if ((uint32_t)(2 * tid) < count) {
-            const uint32_t v = sh.span[before + 2 * tid];
-            g00 = v & 0xFFFFu;
-            g01 = v >> 16;
+    if (wave == 0) {
+        const uint32_t g0 = sp[0] & 0xFFFFu, T = g0 + (sp[0] >> 16), U = (T + 15) / 16;  // 0 past count
+        const uint32_t inc = wave_inclusive_scan(T), uinc = wave_inclusive_scan(U);
+        if ((uint32_t)lane < count) {
+            sh.pre[lane] = inc - T;
+            sh.land16[lane] = uinc - U;
+            sh.g0[lane] = g0;
         }
-        if ((uint32_t)(2 * tid + 1) < count) {
-            const uint32_t v = sh.span[before + 2 * tid + 1];
-            g10 = v & 0xFFFFu;
-            g11 = v >> 16;
-        }
-        uint32_t acc = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t i = (uint32_t)tid + kThreads * q;
-            if (i < before) acc += (sh.span[i] & 0xFFFFu) + (sh.span[i] >> 16);
-        }
-        const uint32_t T0 = g00 + g01, T1 = g10 + g11, pair = T0 + T1;
-        const uint32_t U0 = (T0 + 15) / 16, upair = U0 + (T1 + 15) / 16;
-        const uint32_t inc = wave_inclusive_scan(pair), uinc = wave_inclusive_scan(upair);
-        const uint32_t wacc = wave_sum(acc);
-        if (lane == kWave - 1) {
-            sh.red[0][wave] = inc;
-            sh.red[2][wave] = uinc;
-        }
-        if (lane == 0) sh.red[1][wave] = wacc;
-        __syncthreads();
-        uint32_t base = 0, ubase = 0, AU = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            base += w < wave ? sh.red[0][w] : 0u;
-            ubase += w < wave ? sh.red[2][w] : 0u;
-            A += sh.red[0][w];
-            AU += sh.red[2][w];
-            P += sh.red[1][w];
-        }
-        ex = base + inc - pair;
-        const uint32_t uex = ubase + uinc - upair;
-        if (tid == 0) put_word(scratch + S.run_words + (uint64_t)kWordBytes * jb, tok, A);
-        if ((uint32_t)(2 * tid) < count) {
-            sh.pre[2 * tid] = ex;
-            sh.land16[2 * tid] = uex;
-        }
-        if ((uint32_t)(2 * tid + 1) < count) {
-            sh.pre[2 * tid + 1] = ex + T0;
-            sh.land16[2 * tid + 1] = uex + U0;
-        }
-        if (tid == 0) {
-            sh.pre[count] = A;
-            sh.land16[count] = AU;
+        if ((uint32_t)lane + 1 == count) {
+            sh.pre[count] = inc;
+            sh.land16[count] = uinc;
         }
     }
-
-    __syncthreads();  // sh.pre, sh.land16 complete; sh.span is no longer read
+    __syncthreads();
+    const uint32_t A = sh.pre[count];
+    if (ok && tid == 0) put_word(scratch + S.run_words + (uint64_t)kWordBytes * r, tok, A);
 
     // ---- staged bytes -> the zero-point array, a batch of spans at a time:
     // spans [j0, j1) whose landing units fit the zone.  The first batch lands
-    // while the totals of older runs are still awaited (the landing needs only
-    // the run's own prefixes; the destination needs those totals).
+    // while the counts of earlier runs are still awaited (the landing needs only
+    // the run's own prefixes; the destination needs those counts).
     uint8_t *const zp = out + L.off_zp;
     const uint8_t *const slots = scratch + S.staging;
     auto batch_end = [&](uint32_t j0, uint32_t u0) {  // largest j1 with land16[j1] - u0 <= kLandBytes / 16
@@ -816,28 +921,43 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
         land_batch(0, j1, u0);
     }
 
-    // ---- totals of the runs older than the window (segments over kFinWindow spans)
-    if (ok && wr) {
-        uint32_t rp[4];
-        ok = poll_words<4>(scratch + S.run_words, wr, tok, rp);
-        const uint32_t wacc = wave_sum(rp[0] + rp[1] + rp[2] + rp[3]);
-        __syncthreads();  // sh.red is reused
-        if (lane == 0) sh.red[1][wave] = wacc;
-        ok = __syncthreads_and(ok);
-        P += sh.red[1][0] + sh.red[1][1] + sh.red[1][2] + sh.red[1][3];
+    // ---- 2. the zero-points before the run
+    uint32_t rsum = 0;  // the chunk's runs before r (the chunk's last run)
+    uint32_t P;
+    {
+        if (chunk_last) {
+            uint32_t rp[1] = {0};
+            if (ok) ok = poll_words<1>(scratch + S.run_words + (uint64_t)kWordBytes * cfirst, r - cfirst, tok, rp);
+            ok = __syncthreads_and(ok);
+            rsum = block_sum(rp[0], sh.red);
+            if (ok && tid == 0 && r % kChunkRuns == kChunkRuns - 1)
+                put_word(scratch + S.chunk_words + (uint64_t)kWordBytes * c, tok, rsum + A);
+        }
+        {
+            const uint32_t nrun = chunk_last ? 0u : r - cfirst;  // earlier runs of the chunk, then earlier chunks
+            uint32_t pp[3] = {0, 0, 0};
+            static_assert(kChunkRuns - 1 + ((kMaxElems + kEncSpan - 1) / kEncSpan + kChunkSpans - 1) / kChunkSpans <=
+                              3 * kThreads, "one round polls every word");
+            if (ok)
+                ok = poll_list<3>(
+                    nrun + c,
+                    [&](uint32_t i) {
+                        return i < nrun ? scratch + S.run_words + (uint64_t)kWordBytes * (cfirst + i)
+                                        : scratch + S.chunk_words + (uint64_t)kWordBytes * (i - nrun);
+                    },
+                    tok, pp);
+            ok = __syncthreads_and(ok);
+            P = rsum + block_sum(pp[0] + pp[1] + pp[2], sh.red);
+        }
     }
 
+    // ---- 3. table entries and zero-point bytes
     if (ok) {
-        // ---- table entries of the run's groups
-        const uint64_t g0 = ((uint64_t)first + 2u * (uint32_t)tid) * kEncGroups;
-        const uint32_t T0 = g00 + g01;
-        if ((uint32_t)(2 * tid) < count) {
-            if (g0 < L.groups) tab[g0] = P + ex;
-            if (g0 + 1 < L.groups) tab[g0 + 1] = P + ex + g00;
-        }
-        if ((uint32_t)(2 * tid + 1) < count) {
-            if (g0 + 2 < L.groups) tab[g0 + 2] = P + ex + T0;
-            if (g0 + 3 < L.groups) tab[g0 + 3] = P + ex + T0 + g10;
+        if ((uint32_t)tid < count) {
+            const uint64_t gi = (uint64_t)(first + tid) * kEncGroups;
+            const uint32_t p0 = P + sh.pre[tid];
+            if (gi < L.groups) tab[gi] = p0;
+            if (gi + 1 < L.groups) tab[gi + 1] = p0 + sh.g0[tid];
         }
         const uint32_t Pu = (uint32_t)__builtin_amdgcn_readfirstlane((int)P);
         for (;;) {
@@ -875,57 +995,42 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
     }
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no landing left in flight (a given-up call)
 
-    if (!last) {
-        if (ok && tid == 0) put_word(scratch + S.done_words + (uint64_t)kWordBytes * jb, tok, 1u);
+    // ---- 4. done words; the header of a segment without direct spans
+    if (!chunk_last) {
+        if (ok && tid == 0) put_word(scratch + S.run_done + (uint64_t)kWordBytes * r, tok, 1u);
         return;
     }
-    // ---- last block of the segment: every other block has passed its waits
-    if (ok) {
-        uint32_t dn[4];
-        ok = poll_words<4>(scratch + S.done_words, nf - 1, tok, dn);
+    {
+        uint32_t dn[1] = {0};
+        if (ok) ok = poll_words<1>(scratch + S.run_done + (uint64_t)kWordBytes * cfirst, r - cfirst, tok, dn);
         ok = __syncthreads_and(ok);
     }
-    const uint32_t E = P + A;
-    // raw fallback: when the plan allows it and coding has made the stream
-    // larger than the input, the header says raw and the raw pass (a second
-    // launch) copies the input behind it
-    const uint64_t raw_total = kHeaderBytes + 2 * n;
-    const bool raw = sg.raw_ok && L.off_zp + E > raw_total;
-    const uint64_t total = raw ? raw_total : L.off_zp + E;
-    if (ok && tid == 0) tab[L.groups] = E;
-    if (tid < 32) {
-        uint32_t w = 0;
-        switch (tid) {
-            case 0: w = ok ? kMagic : 0u; break;  // a given-up call leaves a stream every decoder rejects
-            case 1: w = (uint32_t)kVersion | (kHeaderBytes << 16); break;
-            case 2: w = (uint32_t)n; break;
-            case 3: w = (uint32_t)(n >> 32); break;
-            case 4: w = kGroup; break;
-            case 5: w = (uint32_t)L.groups; break;
-            case 6: w = sg.exps[0] | (sg.exps[1] << 8) | (sg.exps[2] << 16) | ((uint32_t)sg.exps[3] << 24); break;
-            case 7: w = sg.exps[4] | (sg.exps[5] << 8) | (sg.exps[6] << 16) | ((raw ? kModeRaw : kModeCoded) << 24); break;
-            case 8: w = E; break;
-            case 10: w = (uint32_t)total; break;
-            case 11: w = (uint32_t)(total >> 32); break;
-            default: break;
-        }
-        reinterpret_cast<uint32_t *>(out)[tid] = w;
+    if (!last_run) {
+        if (ok && tid == 0) put_word(scratch + S.chunk_done + (uint64_t)kWordBytes * c, tok, 1u);
+        return;
     }
-    if (tid == 0 && sg.out_bytes) *sg.out_bytes = ok ? total : 0ull;
+    {
+        uint32_t dn[2] = {0, 0};
+        if (ok) ok = poll_words<2>(scratch + S.chunk_done, c, tok, dn);
+        ok = __syncthreads_and(ok);
+    }
+    write_header(sg, L, (uint64_t)P + A, ok);
 }
 
 __global__ __launch_bounds__(kThreads) void compress_kernel(EncArgs args) {
     __shared__ CompressShared sh;
     const uint32_t flat = blockIdx.x;
     const uint32_t p = find_piece(args, flat);
-    const uint32_t info = args.piece_info[p], idx = flat - args.piece_start[p];
-    if (info & kPieceFinalize) {
+    const uint32_t w = args.piece[p];
+    const uint32_t kind = (w >> 24) & 3u, seg = w >> 26;
+    const uint32_t idx = args.first[p] + (flat - (w & kBlockMask));
+    if (kind == kPieceFinalize) {
         // A finalize block's waves issue ahead of the encoder waves sharing its
-        // CU: the last runs' landing and writing are the call's tail.
+        // CU: finalize work must keep up with the encoding it follows.
         __builtin_amdgcn_s_setprio(2);
-        finalize_run(args, info & 0x7Fu, idx, sh.f);
+        finalize_run(args, seg, idx, sh.f);
     } else {
-        encode_span(args, info, idx, sh.e);
+        encode_span(args, seg, idx, kind == kPieceDirect, sh.e);
     }
 }
 
@@ -1799,17 +1904,19 @@ extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void 
         e.out_bytes = reinterpret_cast<unsigned long long *>(g.out_bytes);
         e.n = (uint32_t)g.n;
         std::memcpy(e.exps, g.plan.exps, 7);
-        e.mode = (g.plan.exps[0] >= 1 && g.plan.exps[6] - g.plan.exps[0] == 6) ? kModeWindow : kModeTable;
-        e.raw_ok = (g.plan.flags & ZC_PLAN_RAW_FALLBACK) ? 1 : 0;
+        // exps = w+1 .. w+7 with w >= 0: codes by saturating arithmetic; any
+        // other ascending set: codes from a 256-byte LDS table
+        const bool window = g.plan.exps[0] >= 1 && g.plan.exps[6] - g.plan.exps[0] == 6;
+        e.flags = (uint8_t)((window ? 0 : kSegTable) | ((g.plan.flags & ZC_PLAN_RAW_FALLBACK) ? kSegRawOk : 0));
     }
     uint64_t ns[ZC_MAX_BATCH];
     for (uint32_t i = 0; i < k; ++i) ns[i] = segs[i].n;
     GridPlan grid;
     if (!plan_grid(ns, k, grid)) return ZC_ERR_INVALID_ARG;
-    std::memcpy(a.piece_start, grid.piece_start, sizeof(a.piece_start));
-    for (uint32_t i = 0; i < kMaxPieces; ++i) a.piece_info[i] = grid.piece_info[i];
+    std::memcpy(a.piece, grid.piece, sizeof(a.piece));
+    std::memcpy(a.first, grid.first, sizeof(a.first));
     const uint32_t np = grid.pieces;
-    const uint64_t pos = grid.piece_start[np];
+    const uint64_t pos = grid.piece[np];
     a.k = k;
     a.pieces = np;
     const uint64_t tok = next_token();
@@ -1817,8 +1924,8 @@ extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void 
     a.tok_hi = (uint32_t)(tok >> 32);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    // every finalize block follows the encoder blocks it waits for: workgroups
-    // are dispatched in index order, so each of those has been dispatched first
+    // every block follows the blocks it waits for (zc_grid.h): workgroups are
+    // dispatched in index order, so each of those has been dispatched first
     hipLaunchKernelGGL(compress_kernel, dim3((uint32_t)pos), dim3(kThreads), 0, st, a);
     if (hipGetLastError() != hipSuccess) return ZC_ERR_HIP;
     // the raw pass, for the segments whose plan allows the fallback

@@ -92,40 +92,56 @@ ZC_HD Layout layout_for(uint64_t n) {
     return L;
 }
 
-// Finalize blocks: each one completes a run of consecutive encoder spans.  A
-// run has at least kFinRunMin spans, more when a segment would otherwise need
-// over kFinMaxBlocks finalize blocks.
-constexpr uint32_t kFinRunMin = 16;
-constexpr uint32_t kFinMaxBlocks = 1024;
-ZC_HD uint32_t fin_run(uint64_t nb) {
-    const uint64_t r = (nb + kFinMaxBlocks - 1) / kFinMaxBlocks;
-    return (uint32_t)(r > kFinRunMin ? r : kFinRunMin);
-}
-ZC_HD uint64_t fin_blocks(uint64_t n) {
-    const uint64_t nb = enc_blocks(n);
-    const uint32_t r = fin_run(nb);
-    return (nb + r - 1) / r;
-}
-constexpr uint32_t kFinRunMax = (uint32_t)((((kMaxElems + kEncSpan - 1) / kEncSpan) + kFinMaxBlocks - 1) / kFinMaxBlocks);
+// Compress work split (not part of the format).  Encoder spans are coded in
+// one of two modes:
+//   * staged (a launch longer than the device holds at once): the block stages
+//     its zero-point bytes in scratch and leaves; a finalize block later places
+//     the bytes of a run of kRun consecutive spans;
+//   * direct (a launch of at most kDirectMax encoder blocks, all resident at
+//     once): the block finds its place in the zero-point array itself and
+//     writes its bytes there.
+// Prefix sums of zero-point counts come from a hierarchy of words that blocks
+// publish for each other: a span word per span; in staged mode a run word per
+// finalize run and a chunk word per kChunkRuns runs; in direct mode a group
+// word per kGroupSpans spans.
+constexpr uint32_t kRun = 16;
+constexpr uint32_t kChunkRuns = 64;
+constexpr uint32_t kChunkSpans = kRun * kChunkRuns;  // 1024
+constexpr uint32_t kGroupSpans = 64;
+constexpr uint32_t kDirectMax = 2048;  // about the number of blocks the device holds at once
+constexpr uint32_t kMaxDirectGroups = (kDirectMax + kGroupSpans - 1) / kGroupSpans;
 
-// Encoder scratch, at off_scratch (behind the largest possible stream):
-//   span words  16 B per encoder span: zero-point counts of its two groups
-//   run words   16 B per finalize block: zero-point total of its run
-//   done words  16 B per finalize block: the block has finished its waits
-//   staging     kEncSpan B per encoder span: its zero-point bytes, in order
+ZC_HD uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+// Encoder scratch, at off_scratch (behind the largest possible stream), sized
+// for either mode:
+//   span words    one per encoder span: zero-point counts of its two groups
+//   run words     one per run: zero-point count of the run
+//   chunk words   one per chunk: zero-point count of its runs
+//   chunk done    one per chunk: every finalize block of the chunk passed its waits
+//   group words   one per group of direct spans: their zero-point count
+//   run done      one per run: its finalize block passed its waits
+//   span done     one per direct span: its block passed its waits
+//   staging       kEncSpan B per encoder span: its zero-point bytes, in order
 // Every word carries the 64-bit token of the call that wrote it, so words
 // left by an earlier call (or any other old contents) never pass for fresh.
 constexpr uint32_t kWordBytes = 16;
 struct Scratch {
-    uint64_t span_words, run_words, done_words, staging, bytes;  // offsets from off_scratch, total size
+    uint64_t span_words, run_words, chunk_words, chunk_done, group_words, run_done, span_done, staging,
+        bytes;  // offsets from off_scratch, total size
 };
 ZC_HD Scratch scratch_for(uint64_t n) {
-    const uint64_t nb = enc_blocks(n), nf = fin_blocks(n);
+    const uint64_t nb = enc_blocks(n), nr = ceil_div(nb, kRun), nc = ceil_div(nr, kChunkRuns);
+    const uint64_t ng = ceil_div(nb, kGroupSpans);
     Scratch S;
     S.span_words = 0;
-    S.run_words = align128(kWordBytes * nb);
-    S.done_words = S.run_words + align128(kWordBytes * nf);
-    S.staging = S.done_words + align128(kWordBytes * nf);
+    S.run_words = S.span_words + align128(kWordBytes * nb);
+    S.chunk_words = S.run_words + align128(kWordBytes * nr);
+    S.chunk_done = S.chunk_words + align128(kWordBytes * nc);
+    S.group_words = S.chunk_done + align128(kWordBytes * nc);
+    S.run_done = S.group_words + align128(kWordBytes * ng);
+    S.span_done = S.run_done + align128(kWordBytes * nr);
+    S.staging = S.span_done + align128(kWordBytes * nb);
     S.bytes = S.staging + nb * (uint64_t)kEncSpan;
     return S;
 }

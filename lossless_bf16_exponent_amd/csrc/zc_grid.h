@@ -1,14 +1,24 @@
 // Layout of the compress grid (host side): which blocks of one launch encode
-// which spans, and where each segment's finalize blocks go.
+// which spans, in which mode, and where the finalize blocks go.
 //
-// The grid is a sequence of pieces: the encoder blocks of a segment, or its
-// finalize blocks.  Encoder pieces come in segment order.  A segment's
-// finalize piece goes right after the first encoder piece that ends kFinLag or
-// more encoder blocks past the end of its own encoder piece (by then its
-// blocks have most likely finished, and its finalize work overlaps the
-// encoding of later segments), else at the end of the grid.  Every finalize
-// block thus comes after every encoder block it waits for; workgroups are
-// dispatched in index order.
+// A launch of at most kDirectMax encoder blocks (all of them resident at
+// once) is coded in direct mode: every block finds its own place in the
+// zero-point array and writes its bytes there.  A longer launch is staged:
+// while the device is saturated, a round trip between blocks costs as much as
+// a data load under that load (measured: about 5 us), so no encoder block
+// waits; finalize blocks place the staged bytes instead.  Each segment's
+// spans are cut into chunks of `chunk` spans (a multiple of kChunkSpans; one
+// chunk for most segments, several for a long one, as the piece table
+// allows).  A chunk's finalize blocks (one per run of kRun spans) go right
+// after the first encoder chunk that ends kFinLag or more encoder blocks past
+// the end of their own chunk (by then its blocks have most likely finished,
+// and the finalize work overlaps later encoding), or at the end of the grid.
+//
+// Every block waits only for blocks placed before it: a finalize block for
+// the encoder blocks of its run and for the finalize blocks of earlier runs of
+// its segment; a direct block for earlier direct blocks of its segment.
+// Workgroups are dispatched in index order, so every block waited for has been
+// dispatched first.
 #pragma once
 
 #include <stdint.h>
@@ -18,43 +28,85 @@
 namespace zc {
 
 constexpr uint32_t kMaxSegments = 64;
+// Pieces: at most two per segment (a staged chunk and its finalize blocks)
+// once the chunk size has grown to hold each segment; one per segment in
+// direct mode.
 constexpr uint32_t kMaxPieces = 2 * kMaxSegments;
-constexpr uint8_t kPieceFinalize = 0x80;  // piece info: this bit (a finalize piece), plus the segment in bits 0..6
-constexpr uint64_t kFinLag = 2048;         // about the number of blocks the device keeps in flight
+constexpr uint32_t kPieceStaged = 0, kPieceDirect = 1, kPieceFinalize = 2;
+constexpr uint64_t kFinLag = 2048;          // about the number of blocks the device keeps in flight
+constexpr uint32_t kMaxGrid = 1u << 24;     // grid blocks; piece starts keep 24 bits
+constexpr uint32_t kBlockMask = kMaxGrid - 1;
+
+// piece word: bits 0..23 the piece's first grid block, bits 24..25 its kind,
+// bits 26..31 its segment.
+inline uint32_t piece_word(uint64_t start, uint32_t kind, uint32_t seg) {
+    return (uint32_t)start | (kind << 24) | (seg << 26);
+}
 
 struct GridPlan {
     uint32_t pieces;
-    uint32_t piece_start[kMaxPieces + 1];  // first grid block of each piece; the last entry is the grid size
-    uint8_t piece_info[kMaxPieces];
+    uint32_t piece[kMaxPieces + 1];  // piece words; entry [pieces] holds the grid size
+    uint32_t first[kMaxPieces];      // first span (encoder pieces) or first run (finalize pieces) in the segment
+    bool direct;                     // the launch is coded in direct mode
+    uint64_t chunk;                  // spans per staged chunk
 };
 
-// Returns false when k is out of range or the grid would exceed 2^32 - 1 blocks.
+// Returns false when k is out of range or the grid would reach kMaxGrid blocks.
 inline bool plan_grid(const uint64_t *n, uint32_t k, GridPlan &g) {
     if (k == 0 || k > kMaxSegments) return false;
-    uint64_t pos = 0, enc_done = 0;
-    uint64_t enc_end[kMaxSegments];
-    uint32_t next_fin = 0;
-    g.pieces = 0;
-    auto add_piece = [&](uint32_t info, uint64_t blocks) {
-        g.piece_start[g.pieces] = (uint32_t)pos;
-        g.piece_info[g.pieces] = (uint8_t)info;
-        ++g.pieces;
-        pos += blocks;
-    };
+    uint64_t nb[kMaxSegments], total = 0;
     for (uint32_t i = 0; i < k; ++i) {
-        const uint64_t nb = enc_blocks(n[i]);
-        add_piece(i, nb);
-        enc_done += nb;
-        enc_end[i] = enc_done;
-        while (next_fin < i && enc_done - enc_end[next_fin] >= kFinLag) {
-            add_piece(kPieceFinalize | next_fin, fin_blocks(n[next_fin]));
-            ++next_fin;
-        }
-        if (pos > 0xFFFFFFFFull) return false;
+        nb[i] = enc_blocks(n[i]);
+        total += nb[i];
     }
-    for (; next_fin < k; ++next_fin) add_piece(kPieceFinalize | next_fin, fin_blocks(n[next_fin]));
-    if (pos > 0xFFFFFFFFull) return false;
-    g.piece_start[g.pieces] = (uint32_t)pos;
+    uint64_t grid = 0;
+    g.pieces = 0;
+    auto add = [&](uint32_t kind, uint32_t seg, uint64_t first, uint64_t blocks) {
+        g.piece[g.pieces] = piece_word(grid, kind, seg);
+        g.first[g.pieces] = (uint32_t)first;
+        ++g.pieces;
+        grid += blocks;
+        return grid < kMaxGrid;
+    };
+    g.direct = total <= kDirectMax;
+    g.chunk = kChunkSpans;
+    if (g.direct) {
+        for (uint32_t i = 0; i < k; ++i)
+            if (!add(kPieceDirect, i, 0, nb[i])) return false;
+        g.piece[g.pieces] = (uint32_t)grid;
+        return true;
+    }
+    // chunk size: the smallest of 1024, 2048, ... spans that fits the piece table
+    auto pieces_for = [&](uint64_t c) {
+        uint64_t p = 0;
+        for (uint32_t i = 0; i < k; ++i) p += 2 * ceil_div(nb[i], c);
+        return p;
+    };
+    while (pieces_for(g.chunk) > kMaxPieces) g.chunk *= 2;
+
+    struct Pending {
+        uint32_t seg, first_run, runs;
+        uint64_t ready;  // encoder blocks emitted when it may go
+    };
+    Pending queue[kMaxPieces];
+    uint32_t qh = 0, qt = 0;
+    uint64_t enc_done = 0;
+    for (uint32_t i = 0; i < k; ++i) {
+        for (uint64_t f = 0; f < nb[i]; f += g.chunk) {
+            const uint64_t cnt = nb[i] - f < g.chunk ? nb[i] - f : g.chunk;
+            if (!add(kPieceStaged, i, f, cnt)) return false;
+            enc_done += cnt;
+            const uint64_t r0 = f / kRun, r1 = ceil_div(f + cnt, kRun);
+            queue[qt++] = Pending{i, (uint32_t)r0, (uint32_t)(r1 - r0), enc_done + kFinLag};
+            while (qh < qt && queue[qh].ready <= enc_done) {
+                if (!add(kPieceFinalize, queue[qh].seg, queue[qh].first_run, queue[qh].runs)) return false;
+                ++qh;
+            }
+        }
+    }
+    for (; qh < qt; ++qh)
+        if (!add(kPieceFinalize, queue[qh].seg, queue[qh].first_run, queue[qh].runs)) return false;
+    g.piece[g.pieces] = (uint32_t)grid;
     return true;
 }
 

@@ -1,9 +1,10 @@
-// Host check of the compress grid layout (zc_grid.h): for random
-// batches, every encoder span and every finalize block of every segment has
-// exactly one grid block, and every finalize block comes after every block it
-// waits for -- the encoder blocks of the spans up to the end of its run, the
-// finalize blocks of the segment's earlier runs, and (for a segment's last
-// finalize block) every other finalize block of the segment.  Built by
+// Host check of the compress grid layout (zc_grid.h): for random and
+// boundary batches, every encoder span and every finalize run of every
+// segment has exactly one grid block; a launch of at most kDirectMax
+// encoder blocks is all direct, a longer one all staged; every block comes
+// after every block it waits for -- a finalize block after the encoder blocks
+// of its run and the finalize blocks of the segment's earlier runs, a direct
+// block after the segment's earlier direct blocks.  Built by
 // tests/test_host.py; no GPU.
 #include <cstdio>
 #include <vector>
@@ -30,78 +31,114 @@ static int failures = 0;
 
 // The device's view of grid block `flat`: which segment, which role, which index.
 struct Role {
-    uint32_t seg;
-    bool fin;
+    uint32_t seg, kind;
     uint64_t index;
 };
 
 static Role role_of(const GridPlan &g, uint32_t flat) {
     uint32_t p = 0;
-    while (p + 1 < g.pieces && g.piece_start[p + 1] <= flat) ++p;  // linear: independent of the kernel's search
-    const uint32_t info = g.piece_info[p];
-    return Role{info & 0x7Fu, (info & kPieceFinalize) != 0, (uint64_t)(flat - g.piece_start[p])};
+    // linear: independent of the kernel's search
+    while (p + 1 < g.pieces && (g.piece[p + 1] & kBlockMask) <= flat) ++p;
+    const uint32_t w = g.piece[p];
+    return Role{w >> 26, (w >> 24) & 3u, (uint64_t)g.first[p] + (flat - (w & kBlockMask))};
 }
 
 static void check_batch(const std::vector<uint64_t> &n) {
     GridPlan g;
     CHECK(plan_grid(n.data(), (uint32_t)n.size(), g));
-    const uint32_t total = g.piece_start[g.pieces];
+    CHECK(g.pieces <= kMaxPieces);
+    const uint32_t total = g.piece[g.pieces];
+    CHECK(total < kMaxGrid);
     const size_t k = n.size();
     std::vector<std::vector<int64_t>> enc_pos(k), fin_pos(k);
+    std::vector<std::vector<int>> enc_kind(k);
+    uint64_t all_spans = 0;
     for (size_t s = 0; s < k; ++s) {
         enc_pos[s].assign(enc_blocks(n[s]), -1);
-        fin_pos[s].assign(fin_blocks(n[s]), -1);
+        enc_kind[s].assign(enc_blocks(n[s]), -1);
+        fin_pos[s].assign(g.direct ? 0 : ceil_div(enc_blocks(n[s]), kRun), -1);
+        all_spans += enc_blocks(n[s]);
     }
+    int64_t first_direct = -1;
     for (uint32_t flat = 0; flat < total; ++flat) {
         const Role r = role_of(g, flat);
-        CHECK(r.seg < k);
-        std::vector<int64_t> &v = r.fin ? fin_pos[r.seg] : enc_pos[r.seg];
-        CHECK(r.index < v.size());
-        if (r.index < v.size()) {
-            CHECK(v[r.index] == -1);  // each block once
-            v[r.index] = flat;
+        CHECK(r.seg < k && r.kind <= kPieceFinalize);
+        if (r.seg >= k) continue;
+        if (r.kind == kPieceFinalize) {
+            std::vector<int64_t> &v = fin_pos[r.seg];
+            CHECK(r.index < v.size());
+            if (r.index < v.size()) {
+                CHECK(v[r.index] == -1);  // each run once
+                v[r.index] = flat;
+            }
+        } else {
+            if (r.kind == kPieceDirect && first_direct < 0) first_direct = flat;
+            std::vector<int64_t> &v = enc_pos[r.seg];
+            CHECK(r.index < v.size());
+            if (r.index < v.size()) {
+                CHECK(v[r.index] == -1);  // each span once
+                v[r.index] = flat;
+                enc_kind[r.seg][r.index] = (int)r.kind;
+            }
+        }
+    }
+    // a launch that fits kDirectMax blocks is all direct, a longer one all staged
+    const bool direct = all_spans <= kDirectMax;
+    CHECK(direct == (first_direct >= 0) && direct == g.direct);
+    for (size_t s = 0; s < k; ++s) {
+        const uint64_t nb = enc_blocks(n[s]);
+        for (uint64_t b = 0; b < nb; ++b) {
+            CHECK(enc_pos[s][b] >= 0);
+            CHECK(enc_kind[s][b] == (direct ? (int)kPieceDirect : (int)kPieceStaged));
         }
     }
     for (size_t s = 0; s < k; ++s) {
-        const uint64_t nb = enc_blocks(n[s]), nf = fin_blocks(n[s]);
-        const uint32_t run = fin_run(nb);
-        for (uint64_t b = 0; b < nb; ++b) CHECK(enc_pos[s][b] >= 0);
-        int64_t max_fin = -1;
-        for (uint64_t j = 0; j < nf; ++j) {
-            const int64_t at = fin_pos[s][j];
-            CHECK(at >= 0);
-            const uint64_t end = (j + 1) * run < nb ? (j + 1) * run : nb;
-            for (uint64_t b = 0; b < end; ++b) CHECK(enc_pos[s][b] < at);  // spans up to the end of its run
-            for (uint64_t i = 0; i < j; ++i) CHECK(fin_pos[s][i] < at);    // earlier runs' words
-            if (j + 1 < nf) max_fin = at > max_fin ? at : max_fin;
+        const uint64_t nb = enc_blocks(n[s]);
+        if (g.direct) {
+            for (uint64_t b = 1; b < nb; ++b) CHECK(enc_pos[s][b] > enc_pos[s][b - 1]);  // earlier spans' words
+            continue;
         }
-        CHECK(fin_pos[s][nf - 1] > max_fin);  // the last block waits for every other one
+        const uint64_t nr = ceil_div(nb, kRun);
+        int64_t max_fin = -1;
+        for (uint64_t r = 0; r < nr; ++r) {
+            const int64_t at = fin_pos[s][r];
+            CHECK(at >= 0);
+            const uint64_t end = (r + 1) * kRun < nb ? (r + 1) * kRun : nb;
+            for (uint64_t b = r * kRun; b < end; ++b) CHECK(enc_pos[s][b] < at);  // the spans of its run
+            CHECK(at > max_fin);                                                  // earlier runs' words
+            max_fin = at;
+        }
     }
 }
 
 int main() {
-    // single segments around the interleaving thresholds, with ragged tails
+    // single segments around the tail and chunk thresholds, with ragged tails
     const uint64_t tile = kEncSpan;
-    const uint64_t singles[] = {0, 1, 8191, 8192, 8193, tile * 31, tile * 32 + 5, tile * 2047, tile * 2048,
-                                tile * 2049, tile * 4096 + 77, tile * 7168, tile * 40000 + 1};
+    const uint64_t singles[] = {0,           1,           8191,       8192,        8193,           tile * 31,
+                                tile * 32 + 5, tile * 2047, tile * 2048, tile * 2049, tile * 2065 + 3, tile * 4096 + 77,
+                                tile * 7168, tile * 40000 + 1, tile * 131072};
     for (uint64_t n : singles) check_batch({n});
-    // the gradient bucket shape and random batches (some empty segments)
+    // the gradient bucket and the all-to-all shapes, and random batches (some empty segments)
     check_batch(std::vector<uint64_t>(32, tile * 1024));
-    for (int it = 0; it < 300; ++it) {
+    check_batch(std::vector<uint64_t>(64, tile * 1024 * 64));  // every segment one chunk only after growing it
+    check_batch(std::vector<uint64_t>(64, tile * 32));         // exactly kDirectMax blocks: direct
+    check_batch(std::vector<uint64_t>(64, tile * 32 + 1));     // one block more per segment: staged
+    for (int it = 0; it < 400; ++it) {
         const size_t k = 1 + rnd() % kMaxSegments;
         std::vector<uint64_t> n(k);
         for (auto &x : n) {
             const uint64_t r = rnd() % 8;
-            x = r == 0 ? 0 : (r < 4 ? rnd() % (tile * 64) : rnd() % (tile * 3000));
+            x = r == 0 ? 0 : (r < 4 ? rnd() % (tile * 64) : rnd() % (tile * 6000));
         }
         check_batch(n);
     }
-    // the largest segment and a batch near the 2^32-block grid limit are planned
+    // the largest segment is planned
     {
         GridPlan g;
         const uint64_t big[] = {0xFFFFFFFFull};
         CHECK(plan_grid(big, 1, g));
-        CHECK(g.piece_start[g.pieces] == enc_blocks(big[0]) + fin_blocks(big[0]));
+        const uint64_t nb = enc_blocks(big[0]);
+        CHECK(g.piece[g.pieces] == nb + ceil_div(nb, kRun));
     }
     if (failures) {
         std::printf("%d failures\n", failures);

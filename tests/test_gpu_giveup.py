@@ -40,49 +40,73 @@ def gaussian(n, sigma, seed):
     return workloads.bf16_bits_from_f32((g.standard_normal(n) * sigma).astype(np.float32))
 
 
-def test_given_up_compress_reports_nothing_and_decoders_reject_it(zc, giveup):
-    ns = [300_007, 0, 8192 * 40 + 5, 1_000_003]
-    plans = [zc.zc_plan_from_sigma(s) for s in (0.02, 1.0, 1e-3, 0.16)]
-    plans[3] = zc.plan_with_raw_fallback(plans[3])
-    xs = [gaussian(n, s, i) for i, (n, s) in enumerate(zip(ns, (0.02, 1.0, 1e-3, 0.16)))]
+def given_up_batch(zc, giveup, ns, sigmas, waits, raw_at=None):
+    """Compress ns in one batched launch with the give-up build: segments that
+    wait (waits[i]) report size 0 and a zero magic, and the shipped decoder
+    rejects them without writing; the others equal the oracle's streams."""
+    import oracle
+    plans = [zc.zc_plan_from_sigma(s) for s in sigmas]
+    if raw_at is not None:
+        plans[raw_at] = zc.plan_with_raw_fallback(plans[raw_at])
+    xs = [gaussian(n, s, i) for i, (n, s) in enumerate(zip(ns, sigmas))]
     devs = [to_device(x) if x.size else None for x in xs]
     caps = [zc.zc_max_compressed_bytes(n) for n in ns]
     offs = np.concatenate([[0], np.cumsum([slot(c) for c in caps])]).astype(np.int64)
     buf = torch.full((int(offs[-1]),), 0x5A, dtype=torch.uint8, device="cuda")
     sizes = torch.full((len(ns),), 12345, dtype=torch.int64, device="cuda")
     stream = torch.cuda.current_stream()
-
-    # one call alone, then the four in one batched launch
-    p0 = zc._plan(plans[0])
-    rc = giveup.zc_compress(devs[0].data_ptr(), ns[0], ctypes.byref(p0), buf.data_ptr(), caps[0],
-                            sizes.data_ptr(), stream.cuda_stream)
-    assert rc == zc.ZC_OK
-    torch.cuda.synchronize()  # the kernels ended
-    assert int(sizes[0].item()) == 0
-    assert int.from_bytes(buf[0:4].cpu().numpy().tobytes(), "little") == 0
-
-    sizes.fill_(12345)
     arr, k = zc.make_enc_segs([(devs[i] if ns[i] else 0, ns[i], plans[i], buf.data_ptr() + int(offs[i]), caps[i],
                                 sizes.data_ptr() + 8 * i) for i in range(len(ns))])
     assert giveup.zc_compress_batch(arr, k, stream.cuda_stream) == zc.ZC_OK
-    torch.cuda.synchronize()
-    assert sizes.cpu().numpy().tolist() == [0] * len(ns)
+    torch.cuda.synchronize()  # the kernels ended
+    got = sizes.cpu().numpy().tolist()
     for i in range(len(ns)):
         o = int(offs[i])
-        assert int.from_bytes(buf[o:o + 4].cpu().numpy().tobytes(), "little") == 0, i
-
-    # the shipped decoder rejects every such stream and writes nothing
+        magic = int.from_bytes(buf[o:o + 4].cpu().numpy().tobytes(), "little")
+        if waits[i]:
+            assert got[i] == 0 and magic == 0, i
+        else:
+            ref = oracle.encode(xs[i], plans[i])
+            assert got[i] == ref.size and np.array_equal(buf[o:o + ref.size].cpu().numpy(), ref), i
     status = torch.full((len(ns),), -1, dtype=torch.int32, device="cuda")
     outs = [torch.full((max(n, 1),), 0x1357, dtype=torch.int16, device="cuda") for n in ns]
     zc.zc_decompress_batch([(buf.data_ptr() + int(offs[i]), caps[i], ns[i], outs[i], status.data_ptr() + 4 * i)
                             for i in range(len(ns))])
     torch.cuda.synchronize()
-    assert status.cpu().numpy().tolist() == [zc.ZC_ERR_CORRUPT] * len(ns)
-    for o in outs:
-        assert bool((o == 0x1357).all())
+    assert status.cpu().numpy().tolist() == [zc.ZC_ERR_CORRUPT if w else 0 for w in waits]
+    for o, w in zip(outs, waits):
+        if w:
+            assert bool((o == 0x1357).all())
+    return xs, plans, devs, buf, caps, sizes
 
-    # and the shipped library, in the same process, still compresses correctly
+
+def test_given_up_staged_launch(zc, giveup):
+    """A launch of more than 2048 spans is staged: every segment's finalize
+    blocks wait for its encoder blocks, so every segment gives up (the
+    one-span n = 0 segment too)."""
+    ns = [300_007, 20_000_003, 8192 * 40 + 5, 1_000_003, 0]
+    given_up_batch(zc, giveup, ns, (0.02, 1.0, 1e-3, 0.16, 1.0), [True] * len(ns), raw_at=3)
+
+
+def test_given_up_direct_launch_and_single_call(zc, giveup):
+    """A launch of at most 2048 spans is direct: a span waits for the spans
+    before it, so a segment of more than one span gives up; a one-span segment
+    waits for nothing and completes.  Then a single call, and the shipped
+    library in the same process still compresses correctly."""
     import oracle
+    ns = [300_007, 0, 8192 * 40 + 5, 1_000_003, 8000]
+    xs, plans, devs, buf, caps, sizes = given_up_batch(zc, giveup, ns, (0.02, 1.0, 1e-3, 0.16, 0.5),
+                                                      [n > 8192 for n in ns], raw_at=3)
+    stream = torch.cuda.current_stream()
+    sizes.fill_(12345)
+    p0 = zc._plan(plans[0])
+    rc = giveup.zc_compress(devs[0].data_ptr(), ns[0], ctypes.byref(p0), buf.data_ptr(), caps[0],
+                            sizes.data_ptr(), stream.cuda_stream)
+    assert rc == zc.ZC_OK
+    torch.cuda.synchronize()
+    assert int(sizes[0].item()) == 0
+    assert int.from_bytes(buf[0:4].cpu().numpy().tobytes(), "little") == 0
+
     zc.zc_compress(devs[0], ns[0], plans[0], buf, caps[0], sizes)
     torch.cuda.synchronize()
     ref = oracle.encode(xs[0], plans[0])
