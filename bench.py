@@ -6,12 +6,12 @@ decompress every stream in one batched launch (the whole hot path on the GPU).
 The exponent tables are computed once per sigma on the host before timing, as
 the pages precompute the table from sigma; their cost is reported as plan_us.
 
-Default workload: the 256 Mi-element gradient bucket (32 layer segments, per-
+Headline workload: the 256 Mi-element gradient bucket (32 layer segments, per-
 segment sigma log-uniform in [1e-5, 1e-2], 1 % exact zeros), the 256M-element
-buffer the throughput target is set on.  Inputs are resident in HBM before the
+buffer the throughput target is set on.  Inputs are resident in HBM before any
 timed region starts.
 
-Timing.  Region 1 (the headline): K steps back to back between two HIP events
+Timing of the headline.  Region 1: K steps back to back between two HIP events
 on the launch stream and a host clock, with a device synchronize on both
 sides; value = 2n bytes of uncompressed BF16 per step / the step time.
 Region 2 (per call): HIP events on the same stream around K back-to-back
@@ -21,14 +21,26 @@ figure against the 8 TB/s HBM peak.  No event sits between the two calls of a
 step in region 1: on this stack an event record between dependent kernels
 leaves the GPU idle for about 10 us.
 
-Printed: one JSON line with the metric, compress and decompress rates, the
-compression ratio, the roofline object (with the rocprofv3-counted HBM
-traffic when the committed counter summary matches the kernel sources) and
-the CPU oracle timed on the host on a bounded sample.
+Every workload of the pages' configurations (1, 2, 3, 4, 5a, 5b) also gets a
+record: compress, decompress and checked decompress (with status words, the
+form a collective uses) timed in R groups of C back-to-back calls, mean and
+p10 / p50 / p90 of the per-call time over the groups, HBM fraction, bits per
+value; the two cache-resident configurations (1, 2) also cold, rotating
+through enough buffer sets that the footprint exceeds the 256 MB MALL twice.
+Then the one-GPU parts of the collectives: the all-gather receive side
+(7 peer shards of 4096 x 14336 decoded in one batched launch into one
+gathered buffer), the all-to-all order (static segments in one launch, then
+the dynamic ones), the reduce-scatter receive side (decode + float32
+accumulate), the plan variants (histogram, sigma estimate) and the raw
+fallback; the practical ceilings of the codec's access shapes (a bench-only
+library); and the CPU oracle on the host cores (one thread, and all cores).
+
+Printed: one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -43,6 +55,13 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["lossless_bf16_exponent_amd/csrc/zc_codec.hip", "lossless_bf16_exponent_amd/csrc/zc_lane.h",
                   "lossless_bf16_exponent_amd/csrc/zc_format.h", "lossless_bf16_exponent_amd/csrc/zc_grid.h"]
 STATS_SOURCES = ["lossless_bf16_exponent_amd/csrc/zc_stats.hip"]
+MALL_BYTES = 256 << 20
+GROUPS = 10  # timing groups per call kind in the per-workload records
+BOX_CORES = 16  # the host cores of one GPU's share on the MI355X boxes
+
+
+def log(msg: str) -> None:
+    print("# " + msg, file=sys.stderr, flush=True)
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -75,36 +94,330 @@ def load_traffic(call: str, workload: str):
         return None
 
 
-def cpu_baseline(w, plans, max_segments: int, min_seconds: float = 10.0, max_passes: int = 5):
-    """The oracle as it stands (plain C, one thread) on the first segments,
-    repeated until about min_seconds of CPU work have been timed."""
+def pct(vals, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(vals, dtype=np.float64), q))
+
+
+def timed_groups(call, stream, groups: int, per: int) -> list:
+    """Per-call microseconds of `groups` groups of `per` back-to-back calls
+    (HIP events on the launch stream around each group)."""
+    import torch
+    out = []
+    for _ in range(groups):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(per):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3 / per)
+    return out
+
+
+def summary(us: list, alg_bytes: int, n: int) -> dict:
+    mean = sum(us) / len(us)
+    return {"us": round(mean, 2), "p10_us": round(pct(us, 10), 2), "p50_us": round(pct(us, 50), 2),
+            "p90_us": round(pct(us, 90), 2), "uncompressed_gbps": round(2.0 * n / (mean * 1e-6) / 1e9, 1),
+            "hbm_frac": round(alg_bytes / (mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+class Resident:
+    """One workload resident on the GPU: input, output slots (one per segment,
+    zc_max_compressed_bytes each), sizes, decode buffer and status words, with
+    the batched segment arrays for compress, decompress and checked
+    decompress."""
+
+    def __init__(self, zc, w, x=None):
+        import numpy as np
+        import torch
+        self.w = w
+        self.plans = [zc.zc_plan_from_sigma(seg.sigma) for seg in w.segments]
+        self.x = x if x is not None else torch.from_numpy(w.buffer.view(np.int16)).cuda()
+        self.ns = [seg.x.size for seg in w.segments]
+        offs = np.concatenate([[0], np.cumsum(self.ns)]).astype(np.int64)
+        caps = [zc.zc_max_compressed_bytes(n) for n in self.ns]
+        slots = [(c + 255) // 256 * 256 for c in caps]
+        soff = np.concatenate([[0], np.cumsum(slots)]).astype(np.int64)
+        self.out = torch.empty(int(soff[-1]), dtype=torch.uint8, device="cuda")
+        self.sizes = torch.zeros(len(self.ns), dtype=torch.int64, device="cuda")
+        self.dec = torch.empty_like(self.x)
+        self.status = torch.zeros(len(self.ns), dtype=torch.int32, device="cuda")
+        xb, ob, db = self.x.data_ptr(), self.out.data_ptr(), self.dec.data_ptr()
+        ns = self.ns
+        self.offs, self.soff, self.caps = offs, soff, caps
+        self.enc = zc.make_enc_segs([(xb + 2 * int(offs[i]) if ns[i] else 0, ns[i], self.plans[i],
+                                      ob + int(soff[i]), caps[i], self.sizes.data_ptr() + 8 * i)
+                                     for i in range(len(ns))])
+        self.dec_segs = zc.make_dec_segs([(ob + int(soff[i]), caps[i], ns[i], db + 2 * int(offs[i]) if ns[i] else 0, 0)
+                                          for i in range(len(ns))])
+        self.chk_segs = zc.make_dec_segs([(ob + int(soff[i]), caps[i], ns[i], db + 2 * int(offs[i]) if ns[i] else 0,
+                                           self.status.data_ptr() + 4 * i) for i in range(len(ns))])
+        self.footprint = self.x.numel() * 2 + self.out.numel() + self.dec.numel() * 2
+
+    def check(self, zc, stream) -> dict:
+        """One checked round trip; returns the stream facts."""
+        import torch
+        self.status.fill_(-1)
+        zc.zc_compress_batch(self.enc, stream)
+        zc.zc_decompress_batch(self.chk_segs, stream)
+        torch.cuda.synchronize()
+        if self.status.any() or not torch.equal(self.dec, self.x):
+            raise RuntimeError("GPU round trip is not lossless on %s" % self.w.name)
+        totals = [int(v) for v in self.sizes.cpu()]
+        zero_points, raw = 0, 0
+        for i in range(len(self.ns)):
+            o = int(self.soff[i])
+            hdr = self.out[o:o + 40].cpu().numpy().tobytes()
+            zero_points += int.from_bytes(hdr[32:40], "little")
+            raw += hdr[31] == 1
+        return {"stream_bytes": sum(totals), "zero_points": zero_points, "raw_segments": raw}
+
+
+def measure_workload(zc, w, steps: int, warmup: int, cold: bool = False) -> dict:
+    """The record of one workload: compress, decompress and checked decompress
+    in GROUPS groups of back-to-back calls; cold: also with buffer sets rotated
+    so that no call finds its input in the MALL."""
+    import torch
+    stream = torch.cuda.current_stream()
+    r = Resident(zc, w)
+    facts = r.check(zc, stream)
+    n = w.n
+    alg = 2 * n + facts["stream_bytes"]
+    per = max(1, steps // GROUPS)
+    rec = {"workload": w.name, "values": n, "segments": len(w.segments), "stream_bytes": facts["stream_bytes"],
+           "bits_per_value": round(8.0 * facts["stream_bytes"] / n, 4),
+           "compression_ratio": round(facts["stream_bytes"] / (2.0 * n), 5),
+           "zero_point_rate": round(facts["zero_points"] / n, 6), "algorithmic_bytes_per_call": int(alg),
+           "timing": "%d groups of %d back-to-back calls after %d warm-up calls; mean and percentiles of the "
+                     "per-call time over the groups" % (GROUPS, per, warmup)}
+    calls = {"compress": lambda: zc.zc_compress_batch(r.enc, stream),
+             "decompress": lambda: zc.zc_decompress_batch(r.dec_segs, stream),
+             "decompress_checked": lambda: zc.zc_decompress_batch(r.chk_segs, stream)}
+    for name, call in calls.items():
+        for _ in range(warmup):
+            call()
+        rec[name] = summary(timed_groups(call, stream, GROUPS, per), alg, n)
+    rec["decompress_checked"]["kernels"] = "zero_kernel (status words) + decode_kernel"
+    if not torch.equal(r.dec, r.x):
+        raise RuntimeError("decoded buffer differs after timing on %s" % w.name)
+    if cold:
+        sets = [r] + [Resident(zc, w, x=r.x.clone()) for _ in range(max(1, 2 * MALL_BYTES // r.footprint))]
+        for s in sets[1:]:
+            s.check(zc, stream)
+        k = len(sets)
+        rec["cache_resident"] = True
+        rec["cold"] = {"buffer_sets": k, "footprint_bytes": int(sum(s.footprint for s in sets))}
+        for name, attr in (("compress", "enc"), ("decompress", "dec_segs")):
+            fns = [(lambda s=s, a=attr: (zc.zc_compress_batch if a == "enc" else zc.zc_decompress_batch)(
+                getattr(s, a), stream)) for s in sets]
+            it = [0]
+
+            def rot():
+                fns[it[0] % k]()
+                it[0] += 1
+            for _ in range(k):
+                rot()
+            rec["cold"][name] = summary(timed_groups(rot, stream, GROUPS, max(per, k)), alg, n)
+        del sets
+    del r
+    torch.cuda.empty_cache()
+    return rec
+
+
+def allgather_receive(zc, steps: int, warmup: int) -> dict:
+    """The one-GPU part of a compressed all-gather of Llama3-8B shards over 8
+    ranks: this rank's 4096 x 14336 shard compressed once, and the 7 peers'
+    streams decoded in one batched launch into one gathered buffer.  Peer p's
+    shard is N(0, 0.02^2), drawn on the device from a seeded generator and
+    rounded to BF16 (nearest even), compressed untimed."""
+    import torch
+    stream = torch.cuda.current_stream()
+    shard, peers = 4096 * 14336, 7
+    plan = zc.zc_plan_from_sigma(0.02)
+    gathered = torch.empty(peers * shard, dtype=torch.int16, device="cuda")
+    src = torch.empty_like(gathered)
+    for p in range(peers):
+        g = torch.Generator(device="cuda").manual_seed(100 + p)
+        src[p * shard:(p + 1) * shard] = (torch.randn(shard, generator=g, device="cuda") * 0.02).to(
+            torch.bfloat16).view(torch.int16)
+    cap = zc.zc_max_compressed_bytes(shard)
+    slot = (cap + 255) // 256 * 256
+    bufs = torch.empty(peers * slot, dtype=torch.uint8, device="cuda")
+    sizes = torch.zeros(peers, dtype=torch.int64, device="cuda")
+    enc = zc.make_enc_segs([(src.data_ptr() + 2 * p * shard, shard, plan, bufs.data_ptr() + p * slot, cap,
+                             sizes.data_ptr() + 8 * p) for p in range(peers)])
+    zc.zc_compress_batch(enc, stream)
+    torch.cuda.synchronize()
+    totals = [int(v) for v in sizes.cpu()]
+    dec = zc.make_dec_segs([(bufs.data_ptr() + p * slot, totals[p], shard, gathered.data_ptr() + 2 * p * shard, 0)
+                            for p in range(peers)])
+    zc.zc_decompress_batch(dec, stream)
+    torch.cuda.synchronize()
+    if not torch.equal(gathered, src):
+        raise RuntimeError("all-gather receive side is not lossless")
+    per = max(1, steps // GROUPS)
+    alg = sum(totals) + 2 * peers * shard
+    call = lambda: zc.zc_decompress_batch(dec, stream)
+    for _ in range(warmup):
+        call()
+    rec = {"peers": peers, "shard_values": shard, "stream_bytes": sum(totals),
+           "decompress_gathered": summary(timed_groups(call, stream, GROUPS, per), alg, peers * shard)}
+    one = zc.make_enc_segs([(src.data_ptr(), shard, plan, bufs.data_ptr(), cap, sizes.data_ptr())])
+    call = lambda: zc.zc_compress_batch(one, stream)
+    for _ in range(warmup):
+        call()
+    rec["compress_own_shard"] = summary(timed_groups(call, stream, GROUPS, per), 2 * shard + totals[0], shard)
+    rec["kernels"] = {"decompress_gathered": "decode_kernel, 7 segments in one launch",
+                      "compress_own_shard": "compress_kernel"}
+    del gathered, src, bufs
+    torch.cuda.empty_cache()
+    return rec
+
+
+def alltoall_order(zc, w, steps: int, warmup: int) -> dict:
+    """The all-to-all segments of one rank (workload 4) in the two-phase order
+    the pages describe: the 8 static (fixed-size) segments compressed in one
+    launch, then the 8 dynamic ones in a second launch, back to back; against
+    all 16 in one launch."""
+    import torch
+    stream = torch.cuda.current_stream()
+    r = Resident(zc, w)
+    facts = r.check(zc, stream)
+    ns, plans = r.ns, r.plans
+    xb, ob = r.x.data_ptr(), r.out.data_ptr()
+
+    def segs(idx):
+        return zc.make_enc_segs([(xb + 2 * int(r.offs[i]) if ns[i] else 0, ns[i], plans[i], ob + int(r.soff[i]),
+                                  r.caps[i], r.sizes.data_ptr() + 8 * i) for i in idx])
+    static, dynamic = segs(range(8)), segs(range(8, 16))
+    per = max(1, steps // GROUPS)
+    alg = 2 * w.n + facts["stream_bytes"]
+    two = lambda: (zc.zc_compress_batch(static, stream), zc.zc_compress_batch(dynamic, stream))
+    one = lambda: zc.zc_compress_batch(r.enc, stream)
+    rec = {}
+    for name, call in (("static_then_dynamic", two), ("one_launch", one)):
+        for _ in range(warmup):
+            call()
+        rec[name] = summary(timed_groups(call, stream, GROUPS, per), alg, w.n)
+    rec["launches"] = {"static_then_dynamic": 2, "one_launch": 1}
+    del r
+    torch.cuda.empty_cache()
+    return rec
+
+
+def ceilings(n: int, steps: int) -> dict:
+    """Practical ceilings of the codec's access shapes for n values (a
+    bench-only library): a 128-bit copy of 2n bytes, the encoder's shape (read
+    2 B, write 1.375 B per value) and the decoder's (read 1.375 B, write 2 B)."""
+    import torch
+    from lossless_bf16_exponent_amd import _build
+    lib = ctypes.CDLL(_build.BENCH_LIB)
+    vp, u64 = ctypes.c_void_p, ctypes.c_uint64
+    lib.zcb_copy.argtypes = [vp, vp, u64, vp]
+    lib.zcb_encode_shape.argtypes = [vp, u64, vp, vp, vp]
+    lib.zcb_decode_shape.argtypes = [vp, vp, u64, vp, vp]
+    stream = torch.cuda.current_stream()
+    st = stream.cuda_stream
+    a = torch.empty(n, dtype=torch.int16, device="cuda")
+    b = torch.empty(n, dtype=torch.int16, device="cuda")
+    sm = torch.empty(n, dtype=torch.uint8, device="cuda")
+    pl = torch.empty(3 * n // 8, dtype=torch.uint8, device="cuda")
+    a.fill_(0x3C00)
+    calls = {"copy": (lambda: lib.zcb_copy(a.data_ptr(), b.data_ptr(), 2 * n, st), 4 * n),
+             "encode_shape": (lambda: lib.zcb_encode_shape(a.data_ptr(), n, sm.data_ptr(), pl.data_ptr(), st),
+                              2 * n + n + 3 * n // 8),
+             "decode_shape": (lambda: lib.zcb_decode_shape(sm.data_ptr(), pl.data_ptr(), n, b.data_ptr(), st),
+                              2 * n + n + 3 * n // 8)}
+    rec = {"values": n, "library": "libzc_bench.so (bench only)"}
+    for name, (call, nbytes) in calls.items():
+        for _ in range(3):
+            if call() != 0:
+                raise RuntimeError("ceiling kernel %s failed" % name)
+        us = timed_groups(call, stream, 5, max(1, steps // 5))
+        mean = sum(us) / len(us)
+        rec[name] = {"us": round(mean, 2), "bytes": int(nbytes), "gbps": round(nbytes / (mean * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    # torch's own device-to-device copy, for reference
+    for _ in range(3):
+        b.copy_(a)
+    us = timed_groups(lambda: b.copy_(a), stream, 5, max(1, steps // 5))
+    mean = sum(us) / len(us)
+    rec["torch_copy"] = {"us": round(mean, 2), "bytes": 4 * n, "gbps": round(4 * n / (mean * 1e-6) / 1e9, 1)}
+    del a, b, sm, pl
+    torch.cuda.empty_cache()
+    return rec
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, plans, one_thread_segments: int = 8, min_seconds: float = 5.0, max_passes: int = 6) -> dict:
+    """The oracle as it stands (plain C -O2, unchanged), timed on the host:
+    on one thread over the first segments, and on all the host cores this
+    GPU's share has (a thread pool over all segments; ctypes releases the GIL
+    during each call), each repeated to about min_seconds."""
     import numpy as np
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
 
-    segs = list(zip(w.segments, plans))[:max_segments]
-    n = sum(s.x.size for s, _ in segs)
+    segs = list(zip(w.segments, plans))
     outs = [np.empty(oracle.max_bytes(seg.x.size), dtype=np.uint8) for seg, _ in segs]
     decs = [np.empty(seg.x.size, dtype=np.uint16) for seg, _ in segs]
+
+    def one(i):
+        seg, plan = segs[i]
+        t0 = time.perf_counter()
+        total = oracle.encode_into(seg.x, plan, outs[i])
+        t1 = time.perf_counter()
+        rc = oracle.decode_into(outs[i][:total], seg.x.size, decs[i])
+        t2 = time.perf_counter()
+        if rc != 0 or not np.array_equal(decs[i], seg.x):
+            raise RuntimeError("oracle round trip failed on the CPU sample")
+        return t1 - t0, t2 - t1
+
+    # one thread
+    k1 = min(one_thread_segments, len(segs))
+    n1 = sum(segs[i][0].x.size for i in range(k1))
     t_enc = t_dec = 0.0
     passes = 0
     while passes < max_passes and (passes == 0 or t_enc + t_dec < min_seconds):
-        for (seg, plan), out, dec in zip(segs, outs, decs):
-            t0 = time.perf_counter()
-            total = oracle.encode_into(seg.x, plan, out)
-            t1 = time.perf_counter()
-            rc = oracle.decode_into(out[:total], seg.x.size, dec)
-            t2 = time.perf_counter()
-            if rc != 0 or not np.array_equal(dec, seg.x):
-                raise RuntimeError("oracle round trip failed on the CPU sample")
-            t_enc += t1 - t0
-            t_dec += t2 - t1
+        for i in range(k1):
+            a, b = one(i)
+            t_enc += a
+            t_dec += b
         passes += 1
+    gb1 = 2.0 * n1 * passes / 1e9
+    single = {"value": round(gb1 / (t_enc + t_dec), 4), "unit": "GB/s", "cores": 1,
+              "compress_gbps": round(gb1 / t_enc, 4), "decompress_gbps": round(gb1 / t_dec, 4),
+              "sample": "first %d of %d segments (%d BF16 values), compress + decompress, %d pass(es)"
+                        % (k1, len(segs), n1, passes)}
+    # all cores of the share
+    affinity = len(os.sched_getaffinity(0))
+    threads = max(1, min(affinity, BOX_CORES, len(segs)))
+    n = sum(seg.x.size for seg, _ in segs)
+    passes = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_seconds):
+            list(ex.map(one, range(len(segs))))
+            passes += 1
+    wall = time.perf_counter() - t0
     gb = 2.0 * n * passes / 1e9
-    return {"value": round(gb / (t_enc + t_dec), 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "first %d of %d segments (%d BF16 values), compress + decompress, %d pass(es), "
-                      "single-threaded plain C -O2" % (len(segs), len(w.segments), n, passes),
-            "compress_gbps": round(gb / t_enc, 4), "decompress_gbps": round(gb / t_dec, 4),
-            "seconds": round(t_enc + t_dec, 3)}
+    return {"value": round(gb / wall, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "all %d segments (%d BF16 values) of the workload, compress + decompress of each, %d pass(es), "
+                      "%d threads each running the unchanged plain C -O2 oracle on whole segments"
+                      % (len(segs), n, passes, threads),
+            "seconds": round(wall, 3), "affinity_cpus": affinity, "cpu_model": cpu_model(),
+            "single_thread": single}
 
 
 REDUCE_WARMUP_CALLS = 150
@@ -140,23 +453,20 @@ def reduce_measurement(zc, steps: int) -> dict:
     out = torch.empty(n, dtype=torch.int16, device="cuda")
     stream = torch.cuda.current_stream()
     ptrs = [b.data_ptr() for b in bufs]
+    call = lambda: zc.zc_decompress_reduce(ptrs, totals, n, xs[0], out, None, stream)
     for _ in range(REDUCE_WARMUP_CALLS):
-        zc.zc_decompress_reduce(ptrs, totals, n, xs[0], out, None, stream)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        call()
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps):
-        zc.zc_decompress_reduce(ptrs, totals, n, xs[0], out, None, stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
     alg = sum(totals) + 4 * n  # the peer streams and the local share read, the result written
-    achieved = alg / (ms * 1e-3) / 1e9
-    return {"shard_values": n, "peers": peers, "local": True, "warmup_calls": REDUCE_WARMUP_CALLS,
-            "us": round(ms * 1e3, 2),
-            "uncompressed_gbps": round(2.0 * n * (peers + 1) / (ms * 1e-3) / 1e9, 1),
-            "algorithmic_bytes": int(alg), "achieved_gbps": round(achieved, 1),
-            "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4), "kernel": "reduce_kernel"}
+    us = timed_groups(call, stream, GROUPS, max(1, steps // GROUPS))
+    rec = summary(us, alg, n)
+    rec.update({"shard_values": n, "peers": peers, "local": True, "warmup_calls": REDUCE_WARMUP_CALLS,
+                "uncompressed_gbps": round(2.0 * n * (peers + 1) / (rec["us"] * 1e-6) / 1e9, 1),
+                "algorithmic_bytes": int(alg), "achieved_gbps": round(alg / (rec["us"] * 1e-6) / 1e9, 1),
+                "kernel": "reduce_kernel"})
+    del xs, bufs, out
+    torch.cuda.empty_cache()
+    return rec
 
 
 def stats_measurement(zc, x, seg_ns, steps: int) -> dict:
@@ -183,14 +493,8 @@ def stats_measurement(zc, x, seg_ns, steps: int) -> dict:
     for name, call in (("histogram", hist_call), ("sigma", sig_call)):
         for _ in range(3):
             call()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(steps):
-            call()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
+        us = timed_groups(call, stream, 5, max(1, steps // 5))
+        ms = sum(us) / len(us) / 1e3
         gbps = 2.0 * n / (ms * 1e-3) / 1e9
         out[name] = {"us": round(ms * 1e3, 2), "achieved_gbps": round(gbps, 1),
                      "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": 2 * n}
@@ -202,6 +506,7 @@ def stats_measurement(zc, x, seg_ns, steps: int) -> dict:
     offs = np.concatenate([[0], np.cumsum(seg_ns)]).astype(np.int64)
     hs = torch.zeros((len(seg_ns), 256), dtype=torch.int64, device="cuda")
     wss = [torch.empty(zc.zc_stats_workspace_bytes(m), dtype=torch.uint8, device="cuda") for m in seg_ns]
+
     def route():
         for i, m in enumerate(seg_ns):
             zc.zc_exponent_histogram(xb + 2 * int(offs[i]), m, wss[i], wss[i].numel(), hs[i], stream)
@@ -222,9 +527,8 @@ def stats_measurement(zc, x, seg_ns, steps: int) -> dict:
 def fallback_measurement(zc, steps: int) -> dict:
     """The raw fallback on the stress workload that coding expands most
     (2^24 uniformly random non-NaN/Inf BF16 patterns under the sigma = 0.02
-    plan, 18.8 bits per value coded): compress with ZC_PLAN_RAW_FALLBACK (the
-    coded pass, then the raw pass that copies the input behind the raw header)
-    and decompress of the raw stream, HIP events around K calls each."""
+    plan, 18.8 bits per value coded): compress with ZC_PLAN_RAW_FALLBACK and
+    decompress of the raw stream, in groups of back-to-back calls."""
     import numpy as np
     import torch
 
@@ -248,19 +552,11 @@ def fallback_measurement(zc, steps: int) -> dict:
     if total != 128 + 2 * n or out[31].item() != 1 or not torch.equal(dec, x):
         raise RuntimeError("the fallback did not give a lossless raw stream")
     res = {"workload": w.name, "values": n, "stream_bytes": total, "raw": True}
+    alg = 2 * n + total
     for name, call in (("compress", enc_call), ("decompress", dec_call)):
         for _ in range(3):
             call()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(steps):
-            call()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
-        res[name + "_us"] = round(ms * 1e3, 2)
-        res[name + "_gbps"] = round(2.0 * n / (ms * 1e-3) / 1e9, 1)
+        res[name] = summary(timed_groups(call, stream, GROUPS, max(1, steps // GROUPS)), alg, n)
     res["kernels"] = {"compress": "compress_kernel + raw_pass_kernel", "decompress": "decode_kernel (raw branch)"}
     return res
 
@@ -268,14 +564,11 @@ def fallback_measurement(zc, steps: int) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="3", help="workload id (1, 2, 3, 4, 5a, 5b); default 3")
-    ap.add_argument("--cpu-segments", type=int, default=32, help="segments in the CPU oracle sample")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="3", help="headline workload id (1, 2, 3, 4, 5a, 5b); default 3")
+    ap.add_argument("--only-headline", action="store_true", help="skip every record besides the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-reduce", action="store_true", help="skip the reduce-scatter receive-side measurement")
-    ap.add_argument("--no-stats", action="store_true", help="skip the histogram / sigma-estimate measurement")
-    ap.add_argument("--no-fallback", action="store_true", help="skip the raw-fallback measurement")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -284,7 +577,6 @@ def main() -> int:
               "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     from lossless_bf16_exponent_amd import workloads, zc
@@ -297,50 +589,21 @@ def main() -> int:
 
     t_gen = time.perf_counter()
     w = workloads.get(args.workload)
-    print("# workload %s: %d values in %d segments, generated in %.1f s"
-          % (w.name, w.n, len(w.segments), time.perf_counter() - t_gen), file=sys.stderr, flush=True)
+    log("workload %s: %d values in %d segments, generated in %.1f s"
+        % (w.name, w.n, len(w.segments), time.perf_counter() - t_gen))
 
     t0 = time.perf_counter()
     plans = [zc.zc_plan_from_sigma(seg.sigma) for seg in w.segments]
     plan_us = (time.perf_counter() - t0) * 1e6 / len(plans)
 
-    x = torch.from_numpy(w.buffer.view(np.int16)).cuda()
-    ns = [seg.x.size for seg in w.segments]
-    offs = np.concatenate([[0], np.cumsum(ns)]).astype(np.int64)
-    caps = [zc.zc_max_compressed_bytes(n) for n in ns]
-    slots = [(c + 255) // 256 * 256 for c in caps]
-    soff = np.concatenate([[0], np.cumsum(slots)]).astype(np.int64)
-    out = torch.empty(int(soff[-1]), dtype=torch.uint8, device="cuda")
-    sizes = torch.zeros(len(ns), dtype=torch.int64, device="cuda")
-    dec = torch.empty_like(x)
-    status = torch.zeros(len(ns), dtype=torch.int32, device="cuda")
-    xb, ob, db = x.data_ptr(), out.data_ptr(), dec.data_ptr()
-    enc_segs = zc.make_enc_segs([(xb + 2 * int(offs[i]) if ns[i] else 0, ns[i], plans[i], ob + int(soff[i]),
-                                  caps[i], sizes.data_ptr() + 8 * i) for i in range(len(ns))])
-    dec_segs = zc.make_dec_segs([(ob + int(soff[i]), caps[i], ns[i], db + 2 * int(offs[i]) if ns[i] else 0, 0)
-                                 for i in range(len(ns))])
-    chk_segs = zc.make_dec_segs([(ob + int(soff[i]), caps[i], ns[i], db + 2 * int(offs[i]) if ns[i] else 0,
-                                  status.data_ptr() + 4 * i) for i in range(len(ns))])
+    r = Resident(zc, w)
     stream = torch.cuda.current_stream()
-
-    # correctness of what is timed: one checked round trip first
-    zc.zc_compress_batch(enc_segs, stream)
-    zc.zc_decompress_batch(chk_segs, stream)
-    torch.cuda.synchronize()
-    if status.any() or not torch.equal(dec, x):
-        print("bench.py: GPU round trip is not lossless", file=sys.stderr)
-        return 1
-    totals = sizes.cpu().numpy()
-    stream_bytes = int(totals.sum())
-    zero_points = 0
-    for i in range(len(ns)):
-        o = int(soff[i])
-        zero_points += int.from_bytes(out[o + 32:o + 40].cpu().numpy().tobytes(), "little")
-
+    facts = r.check(zc, stream)  # correctness of what is timed: one checked round trip first
+    stream_bytes = facts["stream_bytes"]
     n = w.n
     for _ in range(args.warmup):
-        zc.zc_compress_batch(enc_segs, stream)
-        zc.zc_decompress_batch(dec_segs, stream)
+        zc.zc_compress_batch(r.enc, stream)
+        zc.zc_decompress_batch(r.dec_segs, stream)
     torch.cuda.synchronize()
 
     # timed region 1, the whole hot path: K steps of one batched compress and
@@ -350,8 +613,8 @@ def main() -> int:
     t_start = time.perf_counter()
     g0.record(stream)
     for _ in range(args.steps):
-        zc.zc_compress_batch(enc_segs, stream)
-        zc.zc_decompress_batch(dec_segs, stream)
+        zc.zc_compress_batch(r.enc, stream)
+        zc.zc_decompress_batch(r.dec_segs, stream)
     g1.record(stream)
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
@@ -362,40 +625,28 @@ def main() -> int:
     e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     e[0].record(stream)
     for _ in range(args.steps):
-        zc.zc_compress_batch(enc_segs, stream)
+        zc.zc_compress_batch(r.enc, stream)
     e[1].record(stream)
     for _ in range(args.steps):
-        zc.zc_decompress_batch(dec_segs, stream)
+        zc.zc_decompress_batch(r.dec_segs, stream)
     e[2].record(stream)
     torch.cuda.synchronize()
     enc_ms = e[0].elapsed_time(e[1]) / args.steps
     dec_ms = e[1].elapsed_time(e[2]) / args.steps
-    if not torch.equal(dec, x):
+    if not torch.equal(r.dec, r.x):
         print("bench.py: decoded buffer differs after timing", file=sys.stderr)
         return 1
-
-    # practical ceiling: a device-to-device copy of the input
-    cp = torch.empty_like(x)
-    for _ in range(3):
-        cp.copy_(x)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(10):
-        cp.copy_(x)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_ms = c0.elapsed_time(c1) / 10
-    del cp
+    x_keep = r.x
+    del r
+    torch.cuda.empty_cache()
 
     ms_per_step = t_total * 1e3 / args.steps
     gb = 2.0 * n / 1e9
-    enc_alg = 2.0 * n + stream_bytes
-    dec_alg = stream_bytes + 2.0 * n
-    calls = {"compress": (enc_ms, enc_alg, "compress_kernel"),
-             "decompress": (dec_ms, dec_alg, "decode_kernel")}
+    alg = 2.0 * n + stream_bytes
+    calls = {"compress": (enc_ms, "compress_kernel"), "decompress": (dec_ms, "decode_kernel")}
     dom = max(calls, key=lambda k: calls[k][0])
-    dom_ms, dom_bytes, dom_kernels = calls[dom]
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    dom_ms, dom_kernels = calls[dom]
+    achieved = alg / (dom_ms * 1e-3) / 1e9
     traffic = load_traffic(dom, w.name)
 
     rec = {
@@ -411,40 +662,54 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "u16",
         "data": "synthetic",
-        "config": {"workload": w.name, "values": n, "segments": len(ns), "input": "bf16",
+        "config": {"workload": w.name, "values": n, "segments": len(w.segments), "input": "bf16",
                    "description": w.description, "launches_per_step": "1 batched compress + 1 batched decompress"},
         "compress_gbps": round(gb / (enc_ms * 1e-3), 2),
         "decompress_gbps": round(gb / (dec_ms * 1e-3), 2),
         "compress_us": round(enc_ms * 1e3, 2),
         "decompress_us": round(dec_ms * 1e3, 2),
-        "compress_hbm_frac": round(enc_alg / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "decompress_hbm_frac": round(dec_alg / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "compress_hbm_frac": round(alg / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "decompress_hbm_frac": round(alg / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "compression_ratio": round(stream_bytes / (2.0 * n), 5),
         "bits_per_value": round(8.0 * stream_bytes / n, 4),
-        "zero_point_rate": round(zero_points / n, 6),
-        "copy_ceiling_gbps": round(4.0 * n / (copy_ms * 1e-3) / 1e9, 1),
+        "zero_point_rate": round(facts["zero_points"] / n, 6),
         "plan_us": round(plan_us, 2),
         "device": dev_name,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "call": dom, "kernels": dom_kernels, "algorithmic_bytes": int(dom_bytes),
+                     "traffic": traffic, "call": dom, "kernels": dom_kernels, "algorithmic_bytes": int(alg),
                      "avg_launch_us": round(dom_ms * 1e3, 2)},
         "gpu_step_ms": round(gpu_step_ms, 4),
         "kernel_sha": kernel_source_hash(),
     }
-    if not args.no_stats:
-        rec["plan_variants"] = stats_measurement(zc, x, ns, args.steps)
-        rec["plan_variants"]["sigma_table_us_per_bucket"] = round(plan_us * len(ns), 2)
-    if not args.no_reduce or not args.no_fallback:
-        del out, dec
-        torch.cuda.empty_cache()
-    if not args.no_fallback:
+    if not args.only_headline:
+        rec["plan_variants"] = stats_measurement(zc, x_keep, [seg.x.size for seg in w.segments], args.steps)
+        rec["plan_variants"]["sigma_table_us_per_bucket"] = round(plan_us * len(w.segments), 2)
+        rec["ceilings"] = ceilings(n, args.steps)
+    del x_keep
+    torch.cuda.empty_cache()
+    if not args.only_headline:
+        recs = {}
+        for wid in ("1", "2", "3", "4", "5a", "5b"):
+            t0 = time.perf_counter()
+            wl = w if wid == args.workload else workloads.get(wid)
+            log("workload %s (%d values): generated in %.1f s" % (wid, wl.n, time.perf_counter() - t0))
+            recs[wid] = measure_workload(zc, wl, args.steps, args.warmup, cold=wid in ("1", "2"))
+            if wid == "4":
+                log("all-to-all order")
+                rec["alltoall_order"] = alltoall_order(zc, wl, args.steps, args.warmup)
+            if wl is not w:
+                del wl
+        rec["workloads"] = recs
+        log("all-gather receive side")
+        rec["allgather_receive"] = allgather_receive(zc, args.steps, args.warmup)
+        log("raw fallback")
         rec["raw_fallback"] = fallback_measurement(zc, args.steps)
-    if not args.no_reduce:
+        log("reduce-scatter receive side")
         rec["reduce_scatter_local"] = reduce_measurement(zc, args.steps)
     if not args.no_cpu_baseline:
-        print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(w, plans, args.cpu_segments)
+        log("timing the CPU oracle on the host")
+        rec["cpu_baseline"] = cpu_baseline(w, plans)
     print(json.dumps(rec), flush=True)
     return 0
 

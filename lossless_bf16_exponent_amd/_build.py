@@ -39,6 +39,23 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+BENCH_LIB = os.path.join(PKG, "libzc_bench.so")
+BENCH_SOURCE = os.path.join(CSRC, "zc_bench.hip")
+
+
+def build_bench(verbose: bool = False) -> str:
+    """The benchmark's practical-ceiling kernels (copy and the codec's two
+    access shapes), a library of their own that the codec never loads."""
+    tmp = BENCH_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared", *HIP_FLAGS,
+           BENCH_SOURCE, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, BENCH_LIB)
+    return BENCH_LIB
+
+
 GIVEUP_LIB = os.path.join(ROOT, "tests", "libzc_giveup.so")
 
 

@@ -25,11 +25,29 @@ framework applies when it casts float32 to bfloat16.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
 
 BLOCK = 1 << 24  # elements drawn per generator stream for the large buffers
+
+
+def _parallel(fn, items) -> None:
+    """fn(item) for every item, on a few threads.  Each item draws from its own
+    seeded generator into its own slice, so the result does not depend on the
+    order or the thread count (numpy's generators release the GIL while they
+    fill an array)."""
+    items = list(items)
+    workers = max(1, min(len(items), 8, len(os.sched_getaffinity(0))))
+    if workers == 1:
+        for it in items:
+            fn(it)
+        return
+    with ThreadPoolExecutor(workers) as ex:
+        for _ in ex.map(fn, items):
+            pass
 
 
 def bf16_bits_from_f32(f: np.ndarray) -> np.ndarray:
@@ -64,10 +82,14 @@ class Workload:
 def _normal_blocks(out: np.ndarray, key: int, sigma: float) -> None:
     """out[:] = bf16(N(0,1) * sigma) drawn block by block with seeds [key, b]."""
     s = np.float32(sigma)
-    for b, start in enumerate(range(0, out.size, BLOCK)):
+
+    def block(b):
+        start = b * BLOCK
         m = min(BLOCK, out.size - start)
         g = np.random.default_rng([key, b])
         out[start:start + m] = bf16_bits_from_f32(g.standard_normal(m, dtype=np.float32) * s)
+
+    _parallel(block, range((out.size + BLOCK - 1) // BLOCK))
 
 
 def config1() -> Workload:
@@ -99,14 +121,17 @@ def config3_sigmas() -> np.ndarray:
 def config3(segments: int = CONFIG3_SEGMENTS) -> Workload:
     sig = config3_sigmas()
     buf = np.empty(segments * CONFIG3_SEG_ELEMS, dtype=np.uint16)
-    segs = []
-    for s in range(segments):
+
+    def segment(s):
         g = np.random.default_rng([2, s])
         v = g.standard_normal(CONFIG3_SEG_ELEMS, dtype=np.float32) * np.float32(sig[s])
         view = buf[s * CONFIG3_SEG_ELEMS:(s + 1) * CONFIG3_SEG_ELEMS]
         view[:] = bf16_bits_from_f32(v)
         view[g.choice(CONFIG3_SEG_ELEMS, CONFIG3_ZEROS, replace=False)] = 0  # +0.0
-        segs.append(Segment("layer%02d" % s, view, float(sig[s])))
+
+    _parallel(segment, range(segments))
+    segs = [Segment("layer%02d" % s, buf[s * CONFIG3_SEG_ELEMS:(s + 1) * CONFIG3_SEG_ELEMS], float(sig[s]))
+            for s in range(segments)]
     return Workload("gradient-bucket-256M-32seg",
                     "256 Mi-element gradient bucket, 32 layer segments, sigma log-uniform "
                     "[1e-5, 1e-2], 1% zeros, per-segment plan", buf, segs)
@@ -138,17 +163,18 @@ def config4() -> Workload:
     static_tokens = int(loads.min())
     sizes = [static_tokens * MOE_HIDDEN] * MOE_DESTS + [int(l - static_tokens) * MOE_HIDDEN for l in loads]
     buf = np.empty(sum(sizes), dtype=np.uint16)
-    segs = []
     scale = np.float32(np.sqrt(0.6))  # Student-t(5) has variance 5/3
-    start = 0
-    for j, m in enumerate(sizes):
-        view = buf[start:start + m]
+    starts = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+
+    def segment(j):
+        m = sizes[j]
         if m:
             t = np.random.default_rng([3, j]).standard_t(5, m).astype(np.float32) * scale
-            view[:] = bf16_bits_from_f32(t)
-        kind = "static" if j < MOE_DESTS else "dynamic"
-        segs.append(Segment("%s-dest%d" % (kind, j % MOE_DESTS), view, 1.0))
-        start += m
+            buf[starts[j]:starts[j] + m] = bf16_bits_from_f32(t)
+
+    _parallel(segment, range(len(sizes)))
+    segs = [Segment("%s-dest%d" % ("static" if j < MOE_DESTS else "dynamic", j % MOE_DESTS),
+                    buf[starts[j]:starts[j] + sizes[j]], 1.0) for j in range(len(sizes))]
     return Workload("moe-a2a-8192tok-top8-h7168",
                     "MoE all-to-all payload, Student-t(5) at unit variance, 8 static + 8 dynamic "
                     "per-destination segments (one dynamic segment is empty)", buf, segs)
