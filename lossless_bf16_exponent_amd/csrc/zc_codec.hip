@@ -44,6 +44,7 @@
 
 #include "zc.h"
 #include "zc_format.h"
+#include "zc_host.h"
 #include "zc_grid.h"
 #include "zc_lane.h"
 
@@ -1846,12 +1847,6 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(RedArgs args) {
 
 using namespace zc;
 
-static bool plan_ok(const zc_plan &p) {
-    if (p.flags & ~(uint8_t)ZC_PLAN_RAW_FALLBACK) return false;
-    for (int k = 1; k < 7; ++k)
-        if (p.exps[k] <= p.exps[k - 1]) return false;
-    return true;
-}
 
 static zc_status launch_zero(ZeroArgs &z, hipStream_t st) {
     uint64_t words = 0;
@@ -1863,10 +1858,6 @@ static zc_status launch_zero(ZeroArgs &z, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
 }
 
-extern "C" uint64_t zc_max_compressed_bytes(uint64_t n) {
-    if (n > kMaxElems) return 0;
-    return layout_for(n).off_scratch + scratch_for(n).bytes;
-}
 
 // Per-call tokens: splitmix64 (Steele, Lea, Flood, "Fast splittable
 // pseudorandom number generators", 2014) of a process-wide counter whose
@@ -1894,7 +1885,7 @@ extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void 
     std::memset(&a, 0, sizeof(a));
     for (uint32_t i = 0; i < k; ++i) {
         const zc_enc_seg &g = segs[i];
-        if (!g.out || g.n > kMaxElems || (g.n && !g.in) || !plan_ok(g.plan)) return ZC_ERR_INVALID_ARG;
+        if (!g.out || g.n > kMaxElems || (g.n && !g.in) || !zc_plan_is_valid(&g.plan)) return ZC_ERR_INVALID_ARG;
         if (((uintptr_t)g.in & 15u) || ((uintptr_t)g.out & 127u) || ((uintptr_t)g.out_bytes & 7u))
             return ZC_ERR_MISALIGNED;
         if (g.out_capacity < zc_max_compressed_bytes(g.n)) return ZC_ERR_CAPACITY;
@@ -2062,55 +2053,4 @@ extern "C" zc_status zc_decompress_reduce(const void *const *d_streams, const ui
     const uint64_t blocks = tiles ? (tiles + kRedTilesPerBlock - 1) / kRedTilesPerBlock : 1;
     hipLaunchKernelGGL(reduce_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
-}
-
-static uint32_t rd32(const uint8_t *p) {
-    uint32_t v;
-    std::memcpy(&v, p, 4);
-    return v;
-}
-static uint64_t rd64(const uint8_t *p) {
-    uint64_t v;
-    std::memcpy(&v, p, 8);
-    return v;
-}
-
-extern "C" zc_status zc_read_header(const void *host_header, uint64_t len, zc_stream_info *out) {
-    if (!host_header || !out) return ZC_ERR_INVALID_ARG;
-    if (len < kHeaderBytes) return ZC_ERR_CORRUPT;
-    const uint8_t *h = static_cast<const uint8_t *>(host_header);
-    const uint64_t n = rd64(h + 8);
-    if (rd32(h) != kMagic || rd32(h + 4) != ((uint32_t)kVersion | (kHeaderBytes << 16)) || n > kMaxElems ||
-        rd32(h + 16) != kGroup)
-        return ZC_ERR_CORRUPT;
-    const Layout L = layout_for(n);
-    zc_plan p;
-    std::memcpy(p.exps, h + 24, 7);
-    p.flags = 0;
-    const uint32_t mode = h[31];
-    const uint64_t E = rd64(h + 32), total = rd64(h + 40);
-    if (mode != kModeCoded && mode != kModeRaw) return ZC_ERR_CORRUPT;
-    const uint64_t expect = mode == kModeRaw ? kHeaderBytes + 2 * n : L.off_zp + E;
-    if (rd32(h + 20) != L.groups || !plan_ok(p) || E > n || total != expect) return ZC_ERR_CORRUPT;
-    for (int i = 48; i < 128; ++i)
-        if (h[i]) return ZC_ERR_CORRUPT;
-    out->n = n;
-    out->zero_points = E;
-    out->total_bytes = total;
-    out->groups = (uint32_t)L.groups;
-    out->plan = p;
-    out->raw = mode == kModeRaw ? 1u : 0u;
-    return ZC_OK;
-}
-
-extern "C" const char *zc_status_string(zc_status s) {
-    switch (s) {
-        case ZC_OK: return "ok";
-        case ZC_ERR_INVALID_ARG: return "invalid argument";
-        case ZC_ERR_CAPACITY: return "output capacity below zc_max_compressed_bytes(n)";
-        case ZC_ERR_MISALIGNED: return "misaligned buffer";
-        case ZC_ERR_CORRUPT: return "corrupt stream";
-        case ZC_ERR_HIP: return "HIP launch failed";
-    }
-    return "unknown status";
 }

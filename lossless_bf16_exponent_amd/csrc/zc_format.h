@@ -13,6 +13,7 @@
 #include <stdint.h>
 
 #if defined(__HIPCC__)
+#include <hip/hip_runtime.h>
 #define ZC_HD __host__ __device__ __forceinline__
 #else
 #define ZC_HD static inline

@@ -6,6 +6,7 @@ import numpy as np
 import torch
 
 SLOT_ALIGN = 256
+GUARD = 4096  # bytes of sentinel before and after every device output of the helpers
 
 
 def require_gpu():
@@ -37,15 +38,24 @@ class Encoded:
         return self.buf[o:o + int(self.totals[i])].cpu().numpy()
 
 
+def check_untouched(t: torch.Tensor, fill: int, what: str) -> None:
+    """A sentinel region still holds its fill value everywhere."""
+    if t.numel() and not bool((t == fill).all()):
+        bad = torch.nonzero(t != fill).flatten()[:4].cpu().numpy()
+        raise AssertionError("%s: sentinel bytes overwritten (first at %s)" % (what, bad))
+
+
 def compress_batch(zc, xs_dev, ns, plans, batch: bool = True, fill: int = 0xA5) -> Encoded:
     """Compress segments (device tensors or views) into one buffer with one slot
-    per segment; batch=False issues one zc_compress per segment instead."""
+    per segment; batch=False issues one zc_compress per segment instead.  Every
+    slot has GUARD sentinel bytes before it and after its capacity, checked
+    untouched after the call."""
     caps = [zc.zc_max_compressed_bytes(n) for n in ns]
-    offsets, off = [], 0
+    offsets, off = [], GUARD
     for c in caps:
         offsets.append(off)
-        off += slot(c)
-    buf = torch.full((max(off, SLOT_ALIGN),), fill, dtype=torch.uint8, device="cuda")
+        off += slot(c) + GUARD
+    buf = torch.full((off,), fill, dtype=torch.uint8, device="cuda")
     sizes = torch.zeros(len(ns), dtype=torch.int64, device="cuda")
     base = buf.data_ptr()
     segs = [(x, n, p, base + o, c, sizes.data_ptr() + 8 * i)
@@ -56,12 +66,21 @@ def compress_batch(zc, xs_dev, ns, plans, batch: bool = True, fill: int = 0xA5) 
         for s in segs:
             zc.zc_compress(*s)
     torch.cuda.synchronize()
+    prev = 0
+    for i, (o, c) in enumerate(zip(offsets, caps)):
+        check_untouched(buf[prev:o], fill, "before the output of segment %d" % i)
+        prev = o + c
+    check_untouched(buf[prev:], fill, "after the last output")
     return Encoded(buf, offsets, sizes.cpu().numpy(), caps)
 
 
 def decompress_batch(zc, enc: Encoded, ns, batch: bool = True, fill: int = 0x5A5A, in_bytes=None):
-    outs = [torch.full((max(n, 1),), fill - 65536 if fill > 32767 else fill, dtype=torch.int16, device="cuda")
-            for n in ns]
+    """Decompress every stream of enc into its own output (a view with GUARD
+    sentinel bytes on both sides, checked untouched after the call)."""
+    g = GUARD // 2
+    v = fill - 65536 if fill > 32767 else fill
+    bufs = [torch.full((max(n, 1) + 2 * g,), v, dtype=torch.int16, device="cuda") for n in ns]
+    outs = [b[g:g + max(n, 1)] for b, n in zip(bufs, ns)]
     status = torch.full((len(ns),), -1, dtype=torch.int32, device="cuda")
     base = enc.buf.data_ptr()
     segs = []
@@ -74,4 +93,7 @@ def decompress_batch(zc, enc: Encoded, ns, batch: bool = True, fill: int = 0x5A5
         for s in segs:
             zc.zc_decompress(*s)
     torch.cuda.synchronize()
+    for i, (b, n) in enumerate(zip(bufs, ns)):
+        check_untouched(b[:g], v, "before the output of segment %d" % i)
+        check_untouched(b[g + n:], v, "after the %d values of segment %d" % (n, i))
     return outs, status.cpu().numpy()

@@ -7,6 +7,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -57,6 +58,65 @@ def test_compress_grid_layout_selftest(tmp_path):
                     os.path.join(ROOT, "tests", "grid_selftest.cpp"), "-o", exe], check=True)
     r = subprocess.run([exe], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+# ---------------------------------------------------------------------------
+# the host-side C and C++ code under the address and undefined-behaviour
+# sanitizers (host code only; no GPU code is built with them)
+# ---------------------------------------------------------------------------
+
+SANITIZE = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+
+
+def _clangxx() -> str:
+    """The ROCm clang++ (its vector extensions build zc_lane.h on the host)."""
+    cand = os.path.join(os.path.dirname(os.path.realpath(_build.hipcc())), "..", "llvm", "bin", "clang++")
+    for c in (cand, "/opt/rocm/llvm/bin/clang++"):
+        if os.path.exists(c):
+            return c
+    pytest.skip("the ROCm clang++ is not installed")
+
+
+def _run_sanitized(cmd_build, exe):
+    subprocess.run(cmd_build, check=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env)
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
+
+
+def test_host_abi_under_sanitizers(tmp_path):
+    """zc_host.cpp (plans, capacity, header parser, status names) and the
+    layout arithmetic, on edge and random inputs."""
+    exe = str(tmp_path / "host_selftest")
+    _run_sanitized(["g++", "-std=c++17", *SANITIZE, "-I", os.path.join(ROOT, "include"), "-I", _build.CSRC,
+                    os.path.join(ROOT, "tests", "host_selftest.cpp"), os.path.join(_build.CSRC, "zc_host.cpp"),
+                    "-o", exe], exe)
+
+
+def test_grid_layout_under_sanitizers(tmp_path):
+    exe = str(tmp_path / "grid_selftest_asan")
+    _run_sanitized(["g++", "-std=c++17", *SANITIZE, "-I", _build.CSRC,
+                    os.path.join(ROOT, "tests", "grid_selftest.cpp"), "-o", exe], exe)
+
+
+def test_lane_helpers_under_sanitizers(tmp_path):
+    exe = str(tmp_path / "lane_selftest_asan")
+    _run_sanitized([_clangxx(), "-std=c++17", *SANITIZE, "-x", "c++", "-I", _build.CSRC,
+                    os.path.join(ROOT, "tests", "lane_selftest.cpp"), "-o", exe], exe)
+
+
+def test_oracle_pins_under_sanitizers(tmp_path):
+    """Every oracle pin against a build of zc_oracle.c with the sanitizers, in a
+    subprocess that preloads the address sanitizer's runtime."""
+    lib = str(tmp_path / "liboracle_asan.so")
+    subprocess.run(["gcc", "-std=c11", "-fPIC", "-shared", *SANITIZE, "-o", lib, oracle.SOURCE, "-lm"], check=True)
+    libasan = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True,
+                             check=True).stdout.strip()
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1", LD_PRELOAD=libasan)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "oracle_sanitized.py"), lib],
+                       capture_output=True, text=True, env=env)
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
+    assert r.stdout.count("ok pin_") == len(oracle_pins.ALL_PINS)
 
 
 def _near_tie(sigma):
