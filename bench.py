@@ -557,7 +557,8 @@ def fallback_measurement(zc, steps: int) -> dict:
         for _ in range(3):
             call()
         res[name] = summary(timed_groups(call, stream, GROUPS, max(1, steps // GROUPS)), alg, n)
-    res["kernels"] = {"compress": "compress_kernel + raw_pass_kernel", "decompress": "decode_kernel (raw branch)"}
+    res["kernels"] = {"compress": "compress_kernel<true>, two launches (the guessing pass, the completing pass)",
+                      "decompress": "decode_kernel (raw branch)"}
     return res
 
 

@@ -113,8 +113,12 @@ uint64_t zc_max_compressed_bytes(uint64_t n);
  *   stream        hipStream_t
  * Errors: ZC_ERR_INVALID_ARG, ZC_ERR_MISALIGNED, ZC_ERR_CAPACITY, ZC_ERR_HIP.
  * The stream size is also in header bytes 40..47 once the work completes.
- * With ZC_PLAN_RAW_FALLBACK a second, small launch follows on the same stream
- * (it copies the input behind the header where the header says raw).
+ * With ZC_PLAN_RAW_FALLBACK the call makes two launches on the stream.  The
+ * first guesses, from a sample of the input, whether the stream will come out
+ * raw and writes the raw payload or the coded sections accordingly; the exact
+ * rule then decides, and the second launch completes a wrong guess (it copies
+ * the payload, or codes the stream).  The stream does not depend on the
+ * guess.  Until the second launch has run, the header may be invalid.
  * Given-up call: workgroups of the launch wait for words that earlier
  * workgroups of the same launch write, each wait bounded (about a second).
  * With workgroups dispatched in index order no wait runs out.  Should one run
@@ -243,9 +247,11 @@ typedef struct zc_dec_seg {
 
 /* Compress k (1..ZC_MAX_BATCH) independent tensors in one launch, each with its
  * own plan and output buffer (per-layer gradient segments, per-destination
- * all-to-all segments).  Each output equals what zc_compress gives for that
- * segment alone (the given-up outcome of zc_compress included, per segment).
- * segs is a host array read before the call returns. */
+ * all-to-all segments); a second launch follows, over the segments whose plan
+ * has ZC_PLAN_RAW_FALLBACK, when there are any.  Each output equals what
+ * zc_compress gives for that segment alone (the given-up outcome of
+ * zc_compress included, per segment).  segs is a host array read before the
+ * call returns. */
 zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void *stream);
 
 /* Decompress k (1..ZC_MAX_BATCH) streams in one launch. */

@@ -56,6 +56,17 @@ def build_bench(verbose: bool = False) -> str:
     return BENCH_LIB
 
 
+def build_variant(path: str, defines, verbose: bool = False) -> str:
+    """The library built with extra preprocessor definitions, at path."""
+    tmp = path + ".tmp%d" % os.getpid()
+    cmd = compile_command(tmp, extra=tuple("-D" + d for d in defines))
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, path)
+    return path
+
+
 GIVEUP_LIB = os.path.join(ROOT, "tests", "libzc_giveup.so")
 
 
@@ -65,13 +76,21 @@ def build_giveup(verbose: bool = False) -> str:
     once, from the host's point of view exactly as a dispatch that broke
     workgroup order would.  Test infrastructure only; never loaded by the
     package."""
-    tmp = GIVEUP_LIB + ".tmp%d" % os.getpid()
-    cmd = compile_command(tmp, extra=("-DZC_SPIN_LIMIT=0",))
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, GIVEUP_LIB)
-    return GIVEUP_LIB
+    return build_variant(GIVEUP_LIB, ["ZC_SPIN_LIMIT=0"], verbose)
+
+
+GUESS_LIBS = {"raw": os.path.join(ROOT, "tests", "libzc_guess_raw.so"),
+              "coded": os.path.join(ROOT, "tests", "libzc_guess_coded.so")}
+
+
+def build_guess(verbose: bool = False) -> dict:
+    """Two builds whose raw-fallback compress guesses the same way for every
+    flagged segment (raw, or coded) instead of sampling, so that tests reach
+    both outcomes of both guesses on small inputs.  The streams must not
+    depend on the guess.  Test infrastructure only."""
+    build_variant(GUESS_LIBS["raw"], ["ZC_GUESS=1"], verbose)
+    build_variant(GUESS_LIBS["coded"], ["ZC_GUESS=2"], verbose)
+    return GUESS_LIBS
 
 
 def assembly(out_path: str, source: str = SOURCES[0]) -> str:

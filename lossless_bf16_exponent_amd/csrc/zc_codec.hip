@@ -72,7 +72,10 @@ static_assert(kMaxSegments == ZC_MAX_BATCH, "one segment per batch entry");
 struct EncArgs {
     uint32_t k;
     uint32_t pieces;
-    uint32_t tok_lo, tok_hi;  // the call's token (scratch words of other calls never match it)
+    uint32_t tok_lo, tok_hi;  // the launch's token (scratch words of other launches never match it)
+    uint32_t pass;            // 0: the call's first launch; 1: the raw-fallback pass that completes it
+    uint32_t prev_lo, prev_hi;  // pass 1: the token of the call's first launch
+    uint32_t pad;
     EncSeg seg[ZC_MAX_BATCH];
     // Piece words (zc_grid.h: first grid block, kind, segment; the last entry
     // holds the grid size) and each piece's first span or run.  Words, not
@@ -539,24 +542,139 @@ __device__ __forceinline__ void write_span(uint8_t *zp, uint64_t dst_off, const 
 }
 
 
+// Raw fallback (ZC_PLAN_RAW_FALLBACK).  The stream is raw when coding makes it
+// larger: off_zp + E > 128 + 2n, which only the exact zero-point count E
+// decides.  The call's first launch guesses, for each flagged segment long
+// enough to sample: the block of span 0 counts the zero-points of a sample
+// spread over the segment and publishes its guess.  Encoder blocks then write
+// either the coded sections or the raw copy of their span, counting the
+// zero-points either way, and the segment's header writer applies the exact
+// rule.  The call's second launch (the same grid) completes what the first
+// left: it copies the payload of a segment that was coded but came out raw,
+// and codes a segment that was guessed raw but came out coded.  The stream
+// never depends on the guess; a wrong guess costs the second pass over that
+// segment.
+constexpr uint32_t kSpecMinSpans = 64;    // shorter flagged segments are coded first, never guessed raw
+constexpr uint32_t kSampleChunks = 1024;  // 8-value chunks the guess samples
+enum : uint32_t { kModeCodedPass = 0, kModeSpecRaw = 1, kModeCopyRaw = 2, kModeSkip = 3, kModeAbort = 4 };
+constexpr uint32_t kDecideRaw = 1, kDecideCoded = 2;
+constexpr uint32_t kStatusFinal = 1, kStatusNeedRaw = 2, kStatusNeedCoded = 3;
+#ifndef ZC_GUESS
+#define ZC_GUESS 0  // test builds: 1 guesses raw, 2 guesses coded, for every flagged segment
+#endif
+
+__device__ __forceinline__ bool guesses(const EncSeg &sg) {
+    return (sg.flags & kSegRawOk) &&
+           (ZC_GUESS != 0 ? sg.n > 0 : enc_blocks(sg.n) >= (uint64_t)kSpecMinSpans);
+}
+
+// Second launch: what the first left for this segment (read once: the first
+// launch has ended).  A segment without a status (not flagged, or given up)
+// needs nothing.
+__device__ __forceinline__ uint32_t second_pass_mode(const EncArgs &args, const uint8_t *scratch,
+                                                     const Scratch &S) {
+    uint32_t st = 0;
+    if (!get_word(scratch + S.status, Token{args.prev_lo, args.prev_hi}, st)) return kModeSkip;
+    return st == kStatusNeedRaw ? kModeCopyRaw : (st == kStatusNeedCoded ? kModeCodedPass : kModeSkip);
+}
+
+// First launch, a block of a guessing segment other than the sampler: the
+// guess (uniform), or kModeAbort when the wait for it gives up.
+__device__ __forceinline__ uint32_t await_guess(const EncArgs &args, const uint8_t *scratch, const Scratch &S,
+                                                uint32_t *red) {
+    uint32_t d[1] = {0};
+    bool ok = poll_words<1>(scratch + S.decision, 1, Token{args.tok_lo, args.tok_hi}, d);
+    ok = __syncthreads_and(ok);
+    const uint32_t g = block_sum(d[0], red);  // thread 0's payload, to every thread
+    return !ok ? kModeAbort : (g == kDecideRaw ? kModeSpecRaw : kModeCodedPass);
+}
+
+// Codes of the 8 values of one 16-byte chunk, as plane bytes (bits of values
+// at or past n cleared by vmask).
+__device__ __forceinline__ uint32_t chunk_planes(const uint32_t *d, uint32_t vmask, bool table, uint32_t base_hi,
+                                                 const uint8_t *code) {
+    const uint32_t t0 = exponent_high(d[0]), t1 = exponent_high(d[1]);
+    const uint32_t t2 = exponent_high(d[2]), t3 = exponent_high(d[3]);
+    uint32_t c_lo, c_hi;
+    if (!table) {
+        c_lo = window_codes4(t0, t1, base_hi);
+        c_hi = window_codes4(t2, t3, base_hi);
+    } else {
+        const uint32_t e0 = exponents4(t0, t1), e1 = exponents4(t2, t3);
+        c_lo = c_hi = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            c_lo |= (uint32_t)code[(e0 >> (8 * k)) & 0xFFu] << (8 * k);
+            c_hi |= (uint32_t)code[(e1 >> (8 * k)) & 0xFFu] << (8 * k);
+        }
+    }
+    return codes_to_planes(c_lo, c_hi) & (vmask * 0x010101u);
+}
+
+// The sampler (span 0 of a guessing segment, first launch): zero-points among
+// kSampleChunks chunks of 8 values spread evenly over the segment; the guess is
+// raw when their share exceeds the break-even share by 5 points (a sample of
+// 8192 values has a standard error under 0.6 points).
+__device__ __forceinline__ uint32_t sample_guess(const EncSeg &sg, const Layout &L, bool table, uint32_t base_hi,
+                                                 const uint8_t *code, uint32_t *red) {
+    if (ZC_GUESS == 1) return kDecideRaw;
+    if (ZC_GUESS == 2) return kDecideCoded;
+    const uint64_t n = sg.n, chunks = n / 8;  // n >= kSpecMinSpans * kEncSpan: every sampled chunk is whole
+    Step st[kSampleChunks / kThreads];
+#pragma unroll
+    for (uint32_t q = 0; q < kSampleChunks / kThreads; ++q) {
+        const uint64_t j = threadIdx.x + kThreads * q;
+        st[q] = load_step(sg.in, 8 * (j * chunks / kSampleChunks), n);
+    }
+    uint32_t z = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < kSampleChunks / kThreads; ++q)
+        z += __builtin_popcount(zero_point_mask(chunk_planes(st[q].d, st[q].vmask, table, base_hi, code)) &
+                                st[q].vmask);
+    const uint64_t zs = block_sum(z, red);
+    const uint64_t S = 8ull * kSampleChunks, T = kHeaderBytes + 2 * n - L.off_zp;  // raw iff E > T
+    return zs * n > S * T + S * n / 20 ? kDecideRaw : kDecideCoded;
+}
+
+// The n - span0 (at most kEncSpan) input values of a span behind the header
+// (the raw payload), 16 bytes per lane and step.
+__device__ __forceinline__ void copy_span_raw(const uint16_t *in, uint8_t *out, uint64_t span0, uint64_t n) {
+    uint16_t *dst = reinterpret_cast<uint16_t *>(out + kHeaderBytes);
+    const uint64_t v1 = min(span0 + kEncSpan, n), full = span0 + ((v1 - span0) & ~uint64_t(7));
+    for (uint64_t v = span0 + 8u * threadIdx.x; v < full; v += 8u * kThreads) {
+        const uint4 q = load_stream16(in + v);
+        store_stream16(dst + v, q.x, q.y, q.z, q.w);
+    }
+    for (uint64_t v = full + threadIdx.x; v < v1; v += kThreads) dst[v] = in[v];
+}
+
 // The header, the table's last entry and the stream size of a segment with E
 // zero-points.  ok = false (a wait given up somewhere in the segment) leaves a
 // zero magic, which every decoder rejects, and a stream size of 0.  Raw
 // fallback: when the plan allows it and coding has made the stream larger
 // than the input, the header says raw and the raw pass (a second launch)
 // copies the input behind it.
-__device__ __forceinline__ void write_header(const EncSeg &sg, const Layout &L, uint64_t E, bool ok) {
+template <bool kFb>
+__device__ __forceinline__ void write_header(const EncArgs &args, const EncSeg &sg, const Layout &L, uint64_t E,
+                                             bool ok, bool guessed_raw) {
     const int tid = threadIdx.x;
     const uint64_t n = sg.n;
     uint8_t *const out = sg.out;
     const uint64_t raw_total = kHeaderBytes + 2 * n;
-    const bool raw = (sg.flags & kSegRawOk) && L.off_zp + E > raw_total;
+    const bool raw = kFb && (sg.flags & kSegRawOk) && L.off_zp + E > raw_total;
+    // the stream is complete now (a coded pass that stays coded, a raw guess
+    // that comes out raw), complete once the second launch has copied the
+    // payload (coded pass, raw outcome), or left to the second launch entirely
+    // (raw guess, coded outcome: the header stays invalid until then)
+    const uint32_t status = !guessed_raw ? (raw ? kStatusNeedRaw : kStatusFinal)
+                                         : (raw ? kStatusFinal : kStatusNeedCoded);
+    const bool valid = ok && status != kStatusNeedCoded;
     const uint64_t total = raw ? raw_total : L.off_zp + E;
-    if (ok && tid == 0) reinterpret_cast<uint32_t *>(out + L.off_tab)[L.groups] = (uint32_t)E;
+    if (valid && !raw && tid == 0) reinterpret_cast<uint32_t *>(out + L.off_tab)[L.groups] = (uint32_t)E;
     if (tid < 32) {
         uint32_t w = 0;
         switch (tid) {
-            case 0: w = ok ? kMagic : 0u; break;
+            case 0: w = valid ? kMagic : 0u; break;
             case 1: w = (uint32_t)kVersion | (kHeaderBytes << 16); break;
             case 2: w = (uint32_t)n; break;
             case 3: w = (uint32_t)(n >> 32); break;
@@ -572,7 +690,9 @@ __device__ __forceinline__ void write_header(const EncSeg &sg, const Layout &L, 
         }
         reinterpret_cast<uint32_t *>(out)[tid] = w;
     }
-    if (tid == 0 && sg.out_bytes) *sg.out_bytes = ok ? total : 0ull;
+    if (tid == 0 && sg.out_bytes) *sg.out_bytes = valid ? total : 0ull;
+    if (kFb && ok && tid == 0 && args.pass == 0 && (sg.flags & kSegRawOk))
+        put_word(out + L.off_scratch + scratch_for(n).status, Token{args.tok_lo, args.tok_hi}, status);
 }
 
 // Direct role (every block of a launch that the device holds at once;
@@ -584,8 +704,9 @@ __device__ __forceinline__ void write_header(const EncSeg &sg, const Layout &L, 
 // its group's span words and publishes the group word, so that no group word
 // waits for another one.  The segment's last span writes the header once every
 // other block of the segment has passed its waits.
-__device__ __forceinline__ void direct_place(const EncArgs &args, uint32_t s, uint32_t b, uint32_t T,
-                                             EncShared &sh) {
+template <bool kFb>
+__device__ __forceinline__ void direct_place(const EncArgs &args, uint32_t s, uint32_t b, uint32_t T, uint32_t c0,
+                                             uint32_t c1, bool raw, EncShared &sh) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const EncSeg &sg = args.seg[s];
     const uint64_t n = sg.n;
@@ -599,7 +720,6 @@ __device__ __forceinline__ void direct_place(const EncArgs &args, uint32_t s, ui
     const uint8_t *const group_w = scratch + S.group_words;
     const uint32_t g = b / kGroupSpans, g0 = g * kGroupSpans;  // g0: the group's first span
     const bool group_last = b % kGroupSpans == kGroupSpans - 1 || b + 1 == nb;
-    const uint32_t c0 = sh.group[0], c1 = sh.group[1];
     // a count announces no data: no wait before it
     if (tid == 0) put_word(scratch + S.span_words + (uint64_t)kWordBytes * b, tok, c0 | (c1 << 16));
 
@@ -612,6 +732,8 @@ __device__ __forceinline__ void direct_place(const EncArgs &args, uint32_t s, ui
         sib = block_sum((sp[0] & 0xFFFFu) + (sp[0] >> 16), sh.red);
         if (ok && tid == 0) put_word(scratch + S.group_words + (uint64_t)kWordBytes * g, tok, sib + c0 + c1);
     }
+    // a raw guess places nothing: only the header writer needs its offset
+    if (raw && b + 1 < nb) return;
     // the group's earlier spans (unless summed above) and the earlier groups
     const uint32_t nsib = group_last ? 0u : b - g0;
     uint32_t pay[1] = {0};
@@ -627,7 +749,7 @@ __device__ __forceinline__ void direct_place(const EncArgs &args, uint32_t s, ui
     const uint32_t mine = (uint32_t)tid < nsib ? (pay[0] & 0xFFFFu) + (pay[0] >> 16) : pay[0];
     const uint32_t P = sib + block_sum(mine, sh.red);
 
-    if (ok) {
+    if (ok && !raw) {
         uint32_t *const tab = reinterpret_cast<uint32_t *>(out + L.off_tab);
         const uint64_t gi = (uint64_t)b * kEncGroups;
         if (tid == 0 && gi < L.groups) tab[gi] = P;
@@ -639,14 +761,58 @@ __device__ __forceinline__ void direct_place(const EncArgs &args, uint32_t s, ui
         if (ok && tid == 0) put_word(scratch + S.span_done + (uint64_t)kWordBytes * b, tok, 1u);
         return;
     }
-    // the segment's last span: every earlier span has passed its waits
-    if (ok) {
+    // the segment's last span: every earlier span has passed its waits (a raw
+    // guess: every span's count is in P, and spans write nothing else once
+    // they have counted)
+    if (ok && !raw) {
         uint32_t dn[8];
         static_assert(kDirectMax <= 8 * kThreads, "one round polls every done word");
         ok = poll_words<8>(scratch + S.span_done, b, tok, dn);
     }
     ok = __syncthreads_and(ok);
-    write_header(sg, L, (uint64_t)P + c0 + c1, ok);
+    write_header<kFb>(args, sg, L, (uint64_t)P + c0 + c1, ok, raw);
+}
+
+// Encoder role under a raw guess: the span's loaded values go behind the
+// header unchanged (the raw payload) and only their zero-points are counted,
+// for the exact rule: waves 0 and 1 hold the span's first 4096-value group,
+// waves 2 and 3 the second.
+__device__ __forceinline__ void raw_span(const EncArgs &args, uint32_t s, uint32_t b, bool direct,
+                                         const Step (&in)[kEncSubTiles][kSteps], bool table, uint32_t base_hi,
+                                         EncShared &sh) {
+    static_assert(kEncSubTiles == 1 && kWaves == 4, "a span is one tile, two waves per group");
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const EncSeg &sg = args.seg[s];
+    const uint64_t n = sg.n, span0 = (uint64_t)b * kEncSpan;
+    uint16_t *const dst = reinterpret_cast<uint16_t *>(sg.out + kHeaderBytes);
+    uint32_t z = 0;
+#pragma unroll
+    for (int u = 0; u < kSteps; ++u) {
+        const uint64_t base = span0 + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
+        const Step &st = in[0][u];
+        z += __builtin_popcount(zero_point_mask(chunk_planes(st.d, st.vmask, table, base_hi, sh.code)) & st.vmask);
+        if (st.vmask == 0xFFu) {
+            store_stream16(dst + base, st.d[0], st.d[1], st.d[2], st.d[3]);
+        } else {
+#pragma unroll
+            for (uint32_t i = 0; i < 8; ++i)  // constant indices keep st.d in registers
+                if (st.vmask >> i & 1u) dst[base + i] = (uint16_t)(st.d[i / 2] >> (16 * (i % 2)));
+        }
+    }
+    z = wave_sum(z);
+    if (lane == 0) sh.red[wave] = z;
+    __syncthreads();
+    const uint32_t c0 = sh.red[0] + sh.red[1], c1 = sh.red[2] + sh.red[3];
+    if (direct) {
+        direct_place<true>(args, s, b, 0, c0, c1, true, sh);
+        return;
+    }
+    // a count announces no data: no wait before the span word
+    if (tid == 0) {
+        const Scratch S = scratch_for(n);
+        put_word(sg.out + layout_for(n).off_scratch + S.span_words + (uint64_t)kWordBytes * b,
+                 Token{args.tok_lo, args.tok_hi}, c0 | (c1 << 16));
+    }
 }
 
 // Encoder role.  A block codes kEncSubTiles consecutive 8192-value sub-tiles
@@ -657,6 +823,7 @@ __device__ __forceinline__ void direct_place(const EncArgs &args, uint32_t s, ui
 // zero-point bytes to its staging slot, waits until every store of the block
 // has completed and publishes its span word for the finalize blocks; a direct
 // span places its bytes itself (direct_place).
+template <bool kFb>
 __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uint32_t b, bool direct,
                                             EncShared &sh) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -679,6 +846,24 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
     const uint32_t wbase = (uint32_t)sg.exps[0] - 1u;  // window mode only (exps[0] >= 1)
     const uint32_t base_hi = (wbase << 8) | (wbase << 24);
 
+    // ---- what this launch does with the span (raw fallback)
+    uint32_t mode = kModeCodedPass;
+    const bool guessing = kFb && args.pass == 0 && guesses(sg);
+    if (kFb && args.pass != 0) {
+        mode = second_pass_mode(args, scratch, S);
+        if (mode == kModeSkip) return;
+        if (mode == kModeCopyRaw) {
+            copy_span_raw(sg.in, out, span0, n);
+            return;
+        }
+    } else if (kFb && guessing && b == 0) {
+        // the sampler: its guess goes out before its own span is loaded
+        if (table) __syncthreads();  // sh.code ready
+        const uint32_t d = sample_guess(sg, L, table, base_hi, sh.code, sh.red);
+        if (tid == 0) put_word(scratch + S.decision, Token{args.tok_lo, args.tok_hi}, d);
+        mode = d == kDecideRaw ? kModeSpecRaw : kModeCodedPass;
+    }
+
     // ---- every load of the span in flight at once
     Step in[kEncSubTiles][kSteps];
 #pragma unroll
@@ -687,7 +872,21 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
         for (int u = 0; u < kSteps; ++u)
             in[sub][u] = load_step(sg.in, span0 + (uint64_t)sub * kTile + 512u * (uint32_t)(wave * kSteps + u) +
                                               8u * (uint32_t)lane, n);
-    if (table) __syncthreads();  // sh.code ready
+    if (kFb && guessing && b != 0) {
+        mode = await_guess(args, scratch, S, sh.red);  // its barriers also cover sh.code
+        if (mode == kModeAbort) {
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // a direct segment's last span writes the header: the invalid one
+            if (direct && b + 1 == blocks) write_header<kFb>(args, sg, L, 0, false, false);
+            return;
+        }
+    } else if (table) {
+        __syncthreads();  // sh.code ready
+    }
+    if (kFb && mode == kModeSpecRaw) {
+        raw_span(args, s, b, direct, in, table, base_hi, sh);
+        return;
+    }
 
     // ---- phase A: split, code, planes; count the span's zero-points
     uint32_t ex[kEncSubTiles][kSteps][2], pl[kEncSubTiles][kSteps], zm[kEncSubTiles][kSteps];
@@ -776,7 +975,7 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
         for (uint64_t i = L.off_tab + 4 * (L.groups + 1) + tid; i < L.off_zp; i += kThreads) out[i] = 0;
     }
     if (direct) {
-        direct_place(args, s, b, T, sh);
+        direct_place<kFb>(args, s, b, T, sh.group[0], sh.group[1], false, sh);
         return;
     }
 
@@ -813,6 +1012,7 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
 //   4. The last run of a chunk waits until the chunk's other runs have passed
 //      their waits and publishes the chunk's done word; the segment's last run
 //      instead writes the header once every earlier chunk is done.
+template <bool kFb>
 __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, uint32_t r, FinShared &sh) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const EncSeg &sg = args.seg[s];
@@ -830,10 +1030,21 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
     uint8_t *const scratch = out + L.off_scratch;
     uint32_t *const tab = reinterpret_cast<uint32_t *>(out + L.off_tab);
 
+    // ---- 0. the raw fallback: under a raw guess the run only counts (its
+    // spans staged nothing); a second launch codes only what the first left
+    bool raw = false, ok = true;
+    if (kFb && args.pass != 0) {
+        if (second_pass_mode(args, scratch, S) != kModeCodedPass) return;
+    } else if (kFb && guesses(sg)) {
+        const uint32_t m = await_guess(args, scratch, S, sh.red);
+        ok = m != kModeAbort;
+        raw = m == kModeSpecRaw;
+    }
+
     // ---- 1. the run's span words (threads 0 .. count-1, all in wave 0): the
     // exclusive prefixes of zero-points and of landing units, the run's count
-    uint32_t sp[1];
-    bool ok = poll_words<1>(scratch + S.span_words + (uint64_t)kWordBytes * first, count, tok, sp);
+    uint32_t sp[1] = {0};
+    if (ok) ok = poll_words<1>(scratch + S.span_words + (uint64_t)kWordBytes * first, count, tok, sp);
     ok = __syncthreads_and(ok);
     if (wave == 0) {
         const uint32_t g0 = sp[0] & 0xFFFFu, T = g0 + (sp[0] >> 16), U = (T + 15) / 16;  // 0 past count
@@ -916,7 +1127,7 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
         }
     };
     uint32_t j0 = 0, j1 = 0, u0 = 0;
-    if (ok) {
+    if (ok && !raw) {
         u0 = sh.land16[0];
         j1 = batch_end(0, u0);
         land_batch(0, j1, u0);
@@ -924,7 +1135,7 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
 
     // ---- 2. the zero-points before the run
     uint32_t rsum = 0;  // the chunk's runs before r (the chunk's last run)
-    uint32_t P;
+    uint32_t P = 0;
     {
         if (chunk_last) {
             uint32_t rp[1] = {0};
@@ -934,7 +1145,7 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
             if (ok && tid == 0 && r % kChunkRuns == kChunkRuns - 1)
                 put_word(scratch + S.chunk_words + (uint64_t)kWordBytes * c, tok, rsum + A);
         }
-        {
+        if (!raw || last_run) {  // a raw guess: only the header writer needs the offset
             const uint32_t nrun = chunk_last ? 0u : r - cfirst;  // earlier runs of the chunk, then earlier chunks
             uint32_t pp[3] = {0, 0, 0};
             static_assert(kChunkRuns - 1 + ((kMaxElems + kEncSpan - 1) / kEncSpan + kChunkSpans - 1) / kChunkSpans <=
@@ -953,7 +1164,7 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
     }
 
     // ---- 3. table entries and zero-point bytes
-    if (ok) {
+    if (ok && !raw) {
         if ((uint32_t)tid < count) {
             const uint64_t gi = (uint64_t)(first + tid) * kEncGroups;
             const uint32_t p0 = P + sh.pre[tid];
@@ -996,7 +1207,13 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
     }
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no landing left in flight (a given-up call)
 
-    // ---- 4. done words; the header of a segment without direct spans
+    // ---- 4. done words; the header of a segment without direct spans.  A raw
+    // guess wrote nothing a done word would cover: every span's count is in
+    // the header writer's offset.
+    if (kFb && raw) {
+        if (last_run) write_header<kFb>(args, sg, L, (uint64_t)P + A, ok, true);
+        return;
+    }
     if (!chunk_last) {
         if (ok && tid == 0) put_word(scratch + S.run_done + (uint64_t)kWordBytes * r, tok, 1u);
         return;
@@ -1015,11 +1232,13 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
         if (ok) ok = poll_words<2>(scratch + S.chunk_done, c, tok, dn);
         ok = __syncthreads_and(ok);
     }
-    write_header(sg, L, (uint64_t)P + A, ok);
+    write_header<kFb>(args, sg, L, (uint64_t)P + A, ok, false);
 }
 
-__global__ __launch_bounds__(kThreads) void compress_kernel(EncArgs args) {
-    __shared__ CompressShared sh;
+// One block of a compress launch.  kFb: the launch has segments under the
+// raw fallback (the first or the second launch of such a call).
+template <bool kFb>
+__device__ __forceinline__ void compress_block(const EncArgs &args, CompressShared &sh) {
     const uint32_t flat = blockIdx.x;
     const uint32_t p = find_piece(args, flat);
     const uint32_t w = args.piece[p];
@@ -1029,10 +1248,28 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(EncArgs args) {
         // A finalize block's waves issue ahead of the encoder waves sharing its
         // CU: finalize work must keep up with the encoding it follows.
         __builtin_amdgcn_s_setprio(2);
-        finalize_run(args, seg, idx, sh.f);
+        finalize_run<kFb>(args, seg, idx, sh.f);
     } else {
-        encode_span(args, seg, idx, kind == kPieceDirect, sh.e);
+        encode_span<kFb>(args, seg, idx, kind == kPieceDirect, sh.e);
     }
+}
+
+// Launches without the fallback.  Eight waves per SIMD: the register budget
+// for that (at most 64 VGPRs, and at most 80 SGPRs as the code object counts
+// them: measured on gfx950, 80 still gives eight 256-thread blocks per CU and
+// 81 gives seven) is requested explicitly, so that a few SGPRs more in the
+// code do not silently cost a block per CU; the compiler then keeps surplus
+// scalars in VGPR lanes.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void compress_kernel(
+    EncArgs args) {
+    __shared__ CompressShared sh;
+    compress_block<false>(args, sh);
+}
+
+// Launches with segments under the raw fallback.
+__global__ __launch_bounds__(kThreads) void compress_fallback_kernel(EncArgs args) {
+    __shared__ CompressShared sh;
+    compress_block<true>(args, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1310,47 +1547,6 @@ __global__ __launch_bounds__(kThreads) void decode_raw_kernel(DecArgs args) {
         return;
     }
     copy_raw(sg.in, sg.out, span0, min(span0 + kDecSpan, n));
-}
-
-// ---------------------------------------------------------------------------
-// raw pass of the compressor: for every segment whose plan allows the
-// fallback, the input goes behind the header when the header says raw.  A
-// fixed grid strides over the spans of all such segments, so that segments
-// that stayed coded cost one cached header read per span.
-// ---------------------------------------------------------------------------
-
-struct RawSeg {
-    const uint16_t *in;
-    uint8_t *out;
-    uint32_t n;
-    uint32_t span_begin;  // first span of this segment
-};
-
-struct RawArgs {
-    uint32_t k;
-    uint32_t spans;
-    RawSeg seg[ZC_MAX_BATCH];
-};
-
-constexpr uint32_t kRawBlocks = 2048;
-
-__global__ __launch_bounds__(kThreads) void raw_pass_kernel(RawArgs args) {
-    for (uint32_t c = blockIdx.x; c < args.spans; c += gridDim.x) {
-        uint32_t s = 0;
-        for (uint32_t i = 1; i < args.k; ++i)
-            if (args.seg[i].span_begin <= c) s = i;
-        const RawSeg &sg = args.seg[s];
-        if ((ld_u32(sg.out + 28) >> 24) != kModeRaw) continue;
-        const uint64_t v0 = (uint64_t)(c - sg.span_begin) * kDecSpan;
-        const uint64_t v1 = min(v0 + kDecSpan, (uint64_t)sg.n);
-        uint16_t *dst = reinterpret_cast<uint16_t *>(sg.out + kHeaderBytes);
-        const uint64_t full = v0 + ((v1 - v0) & ~uint64_t(7));
-        for (uint64_t v = v0 + 8u * threadIdx.x; v < full; v += 8u * kThreads) {
-            const uint4 q = load_stream16(sg.in + v);
-            store_stream16(dst + v, q.x, q.y, q.z, q.w);
-        }
-        for (uint64_t v = full + threadIdx.x; v < v1; v += kThreads) dst[v] = sg.in[v];
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1879,6 +2075,26 @@ static uint64_t next_token() {
     return splitmix64(counter.fetch_add(1, std::memory_order_relaxed));
 }
 
+// One compress launch over a.seg[0 .. a.k), its grid laid out here.
+static zc_status launch_compress(EncArgs &a, hipStream_t st) {
+    uint64_t ns[ZC_MAX_BATCH];
+    for (uint32_t i = 0; i < a.k; ++i) ns[i] = a.seg[i].n;
+    GridPlan grid;
+    if (!plan_grid(ns, a.k, grid)) return ZC_ERR_INVALID_ARG;
+    std::memcpy(a.piece, grid.piece, sizeof(a.piece));
+    std::memcpy(a.first, grid.first, sizeof(a.first));
+    a.pieces = grid.pieces;
+    // every block follows the blocks it waits for (zc_grid.h): workgroups are
+    // dispatched in index order, so each of those has been dispatched first
+    bool fb = false;
+    for (uint32_t i = 0; i < a.k; ++i) fb |= (a.seg[i].flags & kSegRawOk) != 0;
+    if (fb)
+        hipLaunchKernelGGL(compress_fallback_kernel, dim3(grid.piece[grid.pieces]), dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(compress_kernel, dim3(grid.piece[grid.pieces]), dim3(kThreads), 0, st, a);
+    return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
+}
+
 extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void *stream) {
     if (!segs || k == 0 || k > ZC_MAX_BATCH) return ZC_ERR_INVALID_ARG;
     EncArgs a;
@@ -1900,43 +2116,30 @@ extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void 
         const bool window = g.plan.exps[0] >= 1 && g.plan.exps[6] - g.plan.exps[0] == 6;
         e.flags = (uint8_t)((window ? 0 : kSegTable) | ((g.plan.flags & ZC_PLAN_RAW_FALLBACK) ? kSegRawOk : 0));
     }
-    uint64_t ns[ZC_MAX_BATCH];
-    for (uint32_t i = 0; i < k; ++i) ns[i] = segs[i].n;
-    GridPlan grid;
-    if (!plan_grid(ns, k, grid)) return ZC_ERR_INVALID_ARG;
-    std::memcpy(a.piece, grid.piece, sizeof(a.piece));
-    std::memcpy(a.first, grid.first, sizeof(a.first));
-    const uint32_t np = grid.pieces;
-    const uint64_t pos = grid.piece[np];
     a.k = k;
-    a.pieces = np;
     const uint64_t tok = next_token();
     a.tok_lo = (uint32_t)tok;
     a.tok_hi = (uint32_t)(tok >> 32);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    // every block follows the blocks it waits for (zc_grid.h): workgroups are
-    // dispatched in index order, so each of those has been dispatched first
-    hipLaunchKernelGGL(compress_kernel, dim3((uint32_t)pos), dim3(kThreads), 0, st, a);
-    if (hipGetLastError() != hipSuccess) return ZC_ERR_HIP;
-    // the raw pass, for the segments whose plan allows the fallback
-    RawArgs r;
-    std::memset(&r, 0, sizeof(r));
-    uint64_t spans = 0;
-    for (uint32_t i = 0; i < k; ++i) {
-        if (!(segs[i].plan.flags & ZC_PLAN_RAW_FALLBACK) || segs[i].n == 0) continue;
-        RawSeg &g = r.seg[r.k++];
-        g.in = a.seg[i].in;
-        g.out = a.seg[i].out;
-        g.n = a.seg[i].n;
-        g.span_begin = (uint32_t)spans;
-        spans += (segs[i].n + kDecSpan - 1) / kDecSpan;
-    }
-    if (!r.k) return ZC_OK;
-    r.spans = (uint32_t)spans;
-    const uint32_t blocks = spans < kRawBlocks ? (uint32_t)spans : kRawBlocks;
-    hipLaunchKernelGGL(raw_pass_kernel, dim3(blocks), dim3(kThreads), 0, st, r);
-    return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
+    zc_status rc = launch_compress(a, st);
+    if (rc != ZC_OK) return rc;
+    // The raw fallback's second launch, over the flagged segments only: it
+    // completes what the first left (the payload of a stream that came out
+    // raw, or the coded stream of a wrong raw guess).  The two launches are
+    // ordered on the stream, so it sees every word and byte of the first.
+    EncArgs b;
+    std::memset(&b, 0, sizeof(b));
+    for (uint32_t i = 0; i < k; ++i)
+        if (a.seg[i].flags & kSegRawOk) b.seg[b.k++] = a.seg[i];
+    if (!b.k) return ZC_OK;
+    const uint64_t tok2 = next_token();
+    b.tok_lo = (uint32_t)tok2;
+    b.tok_hi = (uint32_t)(tok2 >> 32);
+    b.pass = 1;
+    b.prev_lo = a.tok_lo;
+    b.prev_hi = a.tok_hi;
+    return launch_compress(b, st);
 }
 
 extern "C" zc_status zc_compress(const void *d_in, uint64_t n, const zc_plan *plan, void *d_out,

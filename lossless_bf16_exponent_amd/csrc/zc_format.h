@@ -116,6 +116,8 @@ ZC_HD uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
 // Encoder scratch, at off_scratch (behind the largest possible stream), sized
 // for either mode:
+//   decision      raw fallback: the first pass's guess, raw or coded
+//   status        raw fallback: what the second pass still has to do
 //   span words    one per encoder span: zero-point counts of its two groups
 //   run words     one per run: zero-point count of the run
 //   chunk words   one per chunk: zero-point count of its runs
@@ -128,14 +130,16 @@ ZC_HD uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 // left by an earlier call (or any other old contents) never pass for fresh.
 constexpr uint32_t kWordBytes = 16;
 struct Scratch {
-    uint64_t span_words, run_words, chunk_words, chunk_done, group_words, run_done, span_done, staging,
-        bytes;  // offsets from off_scratch, total size
+    uint64_t decision, status, span_words, run_words, chunk_words, chunk_done, group_words, run_done, span_done,
+        staging, bytes;  // offsets from off_scratch, total size
 };
 ZC_HD Scratch scratch_for(uint64_t n) {
     const uint64_t nb = enc_blocks(n), nr = ceil_div(nb, kRun), nc = ceil_div(nr, kChunkRuns);
     const uint64_t ng = ceil_div(nb, kGroupSpans);
     Scratch S;
-    S.span_words = 0;
+    S.decision = 0;
+    S.status = kWordBytes;
+    S.span_words = align128(2 * kWordBytes);
     S.run_words = S.span_words + align128(kWordBytes * nb);
     S.chunk_words = S.run_words + align128(kWordBytes * nr);
     S.chunk_done = S.chunk_words + align128(kWordBytes * nc);

@@ -38,6 +38,21 @@ class Encoded:
         return self.buf[o:o + int(self.totals[i])].cpu().numpy()
 
 
+def load_test_build(zc, path: str):
+    """A test build of the library (ctypes handle), loaded next to the shipped one."""
+    import ctypes
+    import os
+    if not os.path.exists(path):
+        raise RuntimeError("%s is not built (run __graft_entry__.build())" % path)
+    lib = ctypes.CDLL(path)
+    lib.zc_compress.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(zc.zc_plan), ctypes.c_void_p,
+                                ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.zc_compress.restype = ctypes.c_int
+    lib.zc_compress_batch.argtypes = [ctypes.POINTER(zc.zc_enc_seg), ctypes.c_uint32, ctypes.c_void_p]
+    lib.zc_compress_batch.restype = ctypes.c_int
+    return lib
+
+
 def check_untouched(t: torch.Tensor, fill: int, what: str) -> None:
     """A sentinel region still holds its fill value everywhere."""
     if t.numel() and not bool((t == fill).all()):
@@ -45,11 +60,12 @@ def check_untouched(t: torch.Tensor, fill: int, what: str) -> None:
         raise AssertionError("%s: sentinel bytes overwritten (first at %s)" % (what, bad))
 
 
-def compress_batch(zc, xs_dev, ns, plans, batch: bool = True, fill: int = 0xA5) -> Encoded:
+def compress_batch(zc, xs_dev, ns, plans, batch: bool = True, fill: int = 0xA5, lib=None) -> Encoded:
     """Compress segments (device tensors or views) into one buffer with one slot
-    per segment; batch=False issues one zc_compress per segment instead.  Every
-    slot has GUARD sentinel bytes before it and after its capacity, checked
-    untouched after the call."""
+    per segment; batch=False issues one zc_compress per segment instead; lib: a
+    test build of the library (ctypes handle) to call in place of the shipped
+    one (batched calls only).  Every slot has GUARD sentinel bytes before it and
+    after its capacity, checked untouched after the call."""
     caps = [zc.zc_max_compressed_bytes(n) for n in ns]
     offsets, off = [], GUARD
     for c in caps:
@@ -60,7 +76,11 @@ def compress_batch(zc, xs_dev, ns, plans, batch: bool = True, fill: int = 0xA5) 
     base = buf.data_ptr()
     segs = [(x, n, p, base + o, c, sizes.data_ptr() + 8 * i)
             for i, (x, n, p, o, c) in enumerate(zip(xs_dev, ns, plans, offsets, caps))]
-    if batch:
+    if lib is not None:
+        arr, k = zc.make_enc_segs(segs)
+        rc = lib.zc_compress_batch(arr, k, torch.cuda.current_stream().cuda_stream)
+        assert rc == zc.ZC_OK, rc
+    elif batch:
         zc.zc_compress_batch(segs)
     else:
         for s in segs:
