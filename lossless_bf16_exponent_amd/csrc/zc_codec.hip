@@ -73,9 +73,10 @@ struct EncArgs {
     uint32_t k;
     uint32_t pieces;
     uint32_t tok_lo, tok_hi;  // the launch's token (scratch words of other launches never match it)
-    uint32_t pass;            // 0: the call's first launch; 1: the raw-fallback pass that completes it
-    uint32_t prev_lo, prev_hi;  // pass 1: the token of the call's first launch
+    uint32_t prev_lo, prev_hi;  // the fallback's second launch: the token of the call's first launch
     uint32_t pad;
+    uint32_t mult;            // units (spans or runs) per block (zc_grid.h)
+    uint32_t chunk;           // spans per staged chunk
     EncSeg seg[ZC_MAX_BATCH];
     // Piece words (zc_grid.h: first grid block, kind, segment; the last entry
     // holds the grid size) and each piece's first span or run.  Words, not
@@ -545,15 +546,17 @@ __device__ __forceinline__ void write_span(uint8_t *zp, uint64_t dst_off, const 
 // Raw fallback (ZC_PLAN_RAW_FALLBACK).  The stream is raw when coding makes it
 // larger: off_zp + E > 128 + 2n, which only the exact zero-point count E
 // decides.  The call's first launch guesses, for each flagged segment long
-// enough to sample: the block of span 0 counts the zero-points of a sample
-// spread over the segment and publishes its guess.  Encoder blocks then write
+// enough to sample: a sampler block at the front of the grid counts the
+// zero-points of a sample spread over the segment and publishes its guess.
+// The segment's blocks issue their loads, then read the guess (long
+// published by then), and encoder blocks write
 // either the coded sections or the raw copy of their span, counting the
 // zero-points either way, and the segment's header writer applies the exact
-// rule.  The call's second launch (the same grid) completes what the first
-// left: it copies the payload of a segment that was coded but came out raw,
-// and codes a segment that was guessed raw but came out coded.  The stream
-// never depends on the guess; a wrong guess costs the second pass over that
-// segment.
+// rule and leaves a status word.  The call's second launch, over the flagged
+// segments only, completes what the first left: it copies the payload of a
+// segment that was coded but came out raw, and codes a segment that was
+// guessed raw but came out coded.  The stream never depends on the guess; a
+// wrong guess costs the second pass over that segment.
 constexpr uint32_t kSpecMinSpans = 64;    // shorter flagged segments are coded first, never guessed raw
 constexpr uint32_t kSampleChunks = 1024;  // 8-value chunks the guess samples
 enum : uint32_t { kModeCodedPass = 0, kModeSpecRaw = 1, kModeCopyRaw = 2, kModeSkip = 3, kModeAbort = 4 };
@@ -569,8 +572,8 @@ __device__ __forceinline__ bool guesses(const EncSeg &sg) {
 }
 
 // Second launch: what the first left for this segment (read once: the first
-// launch has ended).  A segment without a status (not flagged, or given up)
-// needs nothing.
+// launch has ended).  A segment without a status word of the first launch
+// (given up) needs nothing.
 __device__ __forceinline__ uint32_t second_pass_mode(const EncArgs &args, const uint8_t *scratch,
                                                      const Scratch &S) {
     uint32_t st = 0;
@@ -578,8 +581,8 @@ __device__ __forceinline__ uint32_t second_pass_mode(const EncArgs &args, const 
     return st == kStatusNeedRaw ? kModeCopyRaw : (st == kStatusNeedCoded ? kModeCodedPass : kModeSkip);
 }
 
-// First launch, a block of a guessing segment other than the sampler: the
-// guess (uniform), or kModeAbort when the wait for it gives up.
+// First launch, a block of a guessing segment: the guess (uniform), or
+// kModeAbort when the wait for it gives up.
 __device__ __forceinline__ uint32_t await_guess(const EncArgs &args, const uint8_t *scratch, const Scratch &S,
                                                 uint32_t *red) {
     uint32_t d[1] = {0};
@@ -611,10 +614,11 @@ __device__ __forceinline__ uint32_t chunk_planes(const uint32_t *d, uint32_t vma
     return codes_to_planes(c_lo, c_hi) & (vmask * 0x010101u);
 }
 
-// The sampler (span 0 of a guessing segment, first launch): zero-points among
-// kSampleChunks chunks of 8 values spread evenly over the segment; the guess is
-// raw when their share exceeds the break-even share by 5 points (a sample of
-// 8192 values has a standard error under 0.6 points).
+// The guess for a segment (first launch): zero-points among kSampleChunks
+// chunks of 8 values spread evenly over the segment; raw when their share
+// exceeds the break-even share (a sample of 8192 values has a standard error
+// under 0.6 points).  Both wrong guesses cost about the same (a raw copy and a
+// coded pass either way), so the estimate is taken as it is.
 __device__ __forceinline__ uint32_t sample_guess(const EncSeg &sg, const Layout &L, bool table, uint32_t base_hi,
                                                  const uint8_t *code, uint32_t *red) {
     if (ZC_GUESS == 1) return kDecideRaw;
@@ -633,13 +637,23 @@ __device__ __forceinline__ uint32_t sample_guess(const EncSeg &sg, const Layout 
                                 st[q].vmask);
     const uint64_t zs = block_sum(z, red);
     const uint64_t S = 8ull * kSampleChunks, T = kHeaderBytes + 2 * n - L.off_zp;  // raw iff E > T
-    return zs * n > S * T + S * n / 20 ? kDecideRaw : kDecideCoded;
+    return zs * n > S * T ? kDecideRaw : kDecideCoded;
 }
 
 // The n - span0 (at most kEncSpan) input values of a span behind the header
 // (the raw payload), 16 bytes per lane and step.
 __device__ __forceinline__ void copy_span_raw(const uint16_t *in, uint8_t *out, uint64_t span0, uint64_t n) {
     uint16_t *dst = reinterpret_cast<uint16_t *>(out + kHeaderBytes);
+    constexpr uint32_t kPer = kEncSpan / (8 * kThreads);  // 16-byte units per lane of a whole span
+    if (span0 + kEncSpan <= n) {  // every load in flight, then every store
+        uint4 q[kPer];
+#pragma unroll
+        for (uint32_t i = 0; i < kPer; ++i) q[i] = load_stream16(in + span0 + 8u * (threadIdx.x + kThreads * i));
+#pragma unroll
+        for (uint32_t i = 0; i < kPer; ++i)
+            store_stream16(dst + span0 + 8u * (threadIdx.x + kThreads * i), q[i].x, q[i].y, q[i].z, q[i].w);
+        return;
+    }
     const uint64_t v1 = min(span0 + kEncSpan, n), full = span0 + ((v1 - span0) & ~uint64_t(7));
     for (uint64_t v = span0 + 8u * threadIdx.x; v < full; v += 8u * kThreads) {
         const uint4 q = load_stream16(in + v);
@@ -691,7 +705,7 @@ __device__ __forceinline__ void write_header(const EncArgs &args, const EncSeg &
         reinterpret_cast<uint32_t *>(out)[tid] = w;
     }
     if (tid == 0 && sg.out_bytes) *sg.out_bytes = valid ? total : 0ull;
-    if (kFb && ok && tid == 0 && args.pass == 0 && (sg.flags & kSegRawOk))
+    if (kFb && ok && tid == 0 && (sg.flags & kSegRawOk))
         put_word(out + L.off_scratch + scratch_for(n).status, Token{args.tok_lo, args.tok_hi}, status);
 }
 
@@ -848,21 +862,7 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
 
     // ---- what this launch does with the span (raw fallback)
     uint32_t mode = kModeCodedPass;
-    const bool guessing = kFb && args.pass == 0 && guesses(sg);
-    if (kFb && args.pass != 0) {
-        mode = second_pass_mode(args, scratch, S);
-        if (mode == kModeSkip) return;
-        if (mode == kModeCopyRaw) {
-            copy_span_raw(sg.in, out, span0, n);
-            return;
-        }
-    } else if (kFb && guessing && b == 0) {
-        // the sampler: its guess goes out before its own span is loaded
-        if (table) __syncthreads();  // sh.code ready
-        const uint32_t d = sample_guess(sg, L, table, base_hi, sh.code, sh.red);
-        if (tid == 0) put_word(scratch + S.decision, Token{args.tok_lo, args.tok_hi}, d);
-        mode = d == kDecideRaw ? kModeSpecRaw : kModeCodedPass;
-    }
+    const bool guessing = kFb && guesses(sg);
 
     // ---- every load of the span in flight at once
     Step in[kEncSubTiles][kSteps];
@@ -872,7 +872,7 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
         for (int u = 0; u < kSteps; ++u)
             in[sub][u] = load_step(sg.in, span0 + (uint64_t)sub * kTile + 512u * (uint32_t)(wave * kSteps + u) +
                                               8u * (uint32_t)lane, n);
-    if (kFb && guessing && b != 0) {
+    if (kFb && guessing) {
         mode = await_guess(args, scratch, S, sh.red);  // its barriers also cover sh.code
         if (mode == kModeAbort) {
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1031,11 +1031,9 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
     uint32_t *const tab = reinterpret_cast<uint32_t *>(out + L.off_tab);
 
     // ---- 0. the raw fallback: under a raw guess the run only counts (its
-    // spans staged nothing); a second launch codes only what the first left
+    // spans staged nothing)
     bool raw = false, ok = true;
-    if (kFb && args.pass != 0) {
-        if (second_pass_mode(args, scratch, S) != kModeCodedPass) return;
-    } else if (kFb && guesses(sg)) {
+    if (kFb && guesses(sg)) {
         const uint32_t m = await_guess(args, scratch, S, sh.red);
         ok = m != kModeAbort;
         raw = m == kModeSpecRaw;
@@ -1235,22 +1233,53 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
     write_header<kFb>(args, sg, L, (uint64_t)P + A, ok, false);
 }
 
-// One block of a compress launch.  kFb: the launch has segments under the
-// raw fallback (the first or the second launch of such a call).
-template <bool kFb>
-__device__ __forceinline__ void compress_block(const EncArgs &args, CompressShared &sh) {
+// The role of block blockIdx.x: its piece's kind and segment, and its first
+// unit (span of an encoder piece, run of a finalize piece).
+struct BlockRole {
+    uint32_t kind, seg, unit, p;
+};
+__device__ __forceinline__ BlockRole block_role(const EncArgs &args, uint32_t mult) {
     const uint32_t flat = blockIdx.x;
     const uint32_t p = find_piece(args, flat);
     const uint32_t w = args.piece[p];
-    const uint32_t kind = (w >> 24) & 3u, seg = w >> 26;
-    const uint32_t idx = args.first[p] + (flat - (w & kBlockMask));
-    if (kind == kPieceFinalize) {
+    return BlockRole{(w >> 24) & 3u, w >> 26, args.first[p] + (flat - (w & kBlockMask)) * mult, p};
+}
+
+// Sampler role (the raw fallback's first launch): the guess for segment s,
+// published in its decision word.  The sampler blocks open the grid, so the
+// guesses are out before the segments' own blocks look for them.
+__device__ __forceinline__ void sample_segment(const EncArgs &args, uint32_t s, EncShared &sh) {
+    const EncSeg &sg = args.seg[s];
+    if (!guesses(sg)) return;
+    const bool table = (sg.flags & kSegTable) != 0;
+    if (table) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int k = 0; k < 7; ++k) c = (sg.exps[k] == (uint32_t)threadIdx.x) ? (uint32_t)(k + 1) : c;
+        sh.code[threadIdx.x] = (uint8_t)c;
+        __syncthreads();
+    }
+    const uint32_t wbase = (uint32_t)sg.exps[0] - 1u;  // window mode only (exps[0] >= 1)
+    const uint32_t base_hi = (wbase << 8) | (wbase << 24);
+    const Layout L = layout_for(sg.n);
+    const uint32_t d = sample_guess(sg, L, table, base_hi, sh.code, sh.red);
+    if (threadIdx.x == 0) put_word(sg.out + L.off_scratch + scratch_for(sg.n).decision, Token{args.tok_lo, args.tok_hi}, d);
+}
+
+// One block of a compress launch, one unit.  kFb: the launch has segments
+// under the raw fallback (the first launch of such a call).
+template <bool kFb>
+__device__ __forceinline__ void compress_block(const EncArgs &args, CompressShared &sh) {
+    const BlockRole r = block_role(args, 1);
+    if (kFb && r.kind == kPieceSample) {
+        sample_segment(args, r.unit, sh.e);
+    } else if (r.kind == kPieceFinalize) {
         // A finalize block's waves issue ahead of the encoder waves sharing its
         // CU: finalize work must keep up with the encoding it follows.
         __builtin_amdgcn_s_setprio(2);
-        finalize_run<kFb>(args, seg, idx, sh.f);
+        finalize_run<kFb>(args, r.seg, r.unit, sh.f);
     } else {
-        encode_span<kFb>(args, seg, idx, kind == kPieceDirect, sh.e);
+        encode_span<kFb>(args, r.seg, r.unit, r.kind == kPieceDirect, sh.e);
     }
 }
 
@@ -1266,10 +1295,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
     compress_block<false>(args, sh);
 }
 
-// Launches with segments under the raw fallback.
-__global__ __launch_bounds__(kThreads) void compress_fallback_kernel(EncArgs args) {
+// The first launch of a call with segments under the raw fallback.  Seven
+// waves per SIMD (at most 72 VGPRs, 94 SGPRs), asked for explicitly: eight
+// would spill registers to scratch, which measured slower than seven.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7, 8))) void compress_fallback_kernel(
+    EncArgs args) {
     __shared__ CompressShared sh;
     compress_block<true>(args, sh);
+}
+
+// The second launch of a call with segments under the raw fallback, over
+// those segments only, args.mult units per block (most blocks only read their
+// segment's status word, and a launch pays per block) on a staged grid.  A
+// segment that came out raw after a coded pass gets its payload copied; a
+// wrong raw guess gets a plain coded pass (the outcome is known to be coded),
+// unit by unit in each block's order.
+__global__ __launch_bounds__(kThreads) void compress_second_kernel(EncArgs args) {
+    __shared__ CompressShared sh;
+    const BlockRole r = block_role(args, args.mult);
+    const EncSeg &sg = args.seg[r.seg];
+    const uint32_t u1 = (uint32_t)min((uint64_t)r.unit + args.mult,
+                                      piece_end(r.kind, args.first[r.p], enc_blocks(sg.n), args.chunk));
+    const uint32_t mode = second_pass_mode(args, sg.out + layout_for(sg.n).off_scratch, scratch_for(sg.n));
+    if (mode == kModeSkip) return;
+    if (mode == kModeCopyRaw) {
+        if (r.kind != kPieceFinalize)
+            for (uint32_t u = r.unit; u < u1; ++u) copy_span_raw(sg.in, sg.out, (uint64_t)u * kEncSpan, sg.n);
+        return;
+    }
+    // one loop per role: a loop holding both roles needs twice the registers
+    if (r.kind == kPieceFinalize) {
+        __builtin_amdgcn_s_setprio(2);
+        for (uint32_t u = r.unit; u < u1; ++u) {
+            if (u != r.unit) __syncthreads();  // the previous unit is done with the LDS
+            finalize_run<false>(args, r.seg, u, sh.f);
+        }
+    } else {
+        for (uint32_t u = r.unit; u < u1; ++u) {
+            if (u != r.unit) __syncthreads();
+            encode_span<false>(args, r.seg, u, false, sh.e);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -2075,23 +2141,34 @@ static uint64_t next_token() {
     return splitmix64(counter.fetch_add(1, std::memory_order_relaxed));
 }
 
-// One compress launch over a.seg[0 .. a.k), its grid laid out here.
-static zc_status launch_compress(EncArgs &a, hipStream_t st) {
+// The raw fallback's second launch gives each block this many units: most of
+// its blocks only read a status word, and a launch pays per block.
+constexpr uint32_t kSecondPassMult = 16;
+
+// One compress launch over a.seg[0 .. a.k), its grid laid out here; second:
+// the fallback's second launch (a staged grid, several units per block).
+static zc_status launch_compress(EncArgs &a, hipStream_t st, bool second) {
+    const uint32_t mult = second ? kSecondPassMult : 1u;
     uint64_t ns[ZC_MAX_BATCH];
     for (uint32_t i = 0; i < a.k; ++i) ns[i] = a.seg[i].n;
     GridPlan grid;
-    if (!plan_grid(ns, a.k, grid)) return ZC_ERR_INVALID_ARG;
+    bool fb = false;
+    for (uint32_t i = 0; i < a.k; ++i) fb |= (a.seg[i].flags & kSegRawOk) != 0;
+    if (!plan_grid(ns, a.k, grid, mult, second, fb && !second)) return ZC_ERR_INVALID_ARG;
     std::memcpy(a.piece, grid.piece, sizeof(a.piece));
     std::memcpy(a.first, grid.first, sizeof(a.first));
     a.pieces = grid.pieces;
+    a.mult = mult;
+    a.chunk = (uint32_t)grid.chunk;
     // every block follows the blocks it waits for (zc_grid.h): workgroups are
     // dispatched in index order, so each of those has been dispatched first
-    bool fb = false;
-    for (uint32_t i = 0; i < a.k; ++i) fb |= (a.seg[i].flags & kSegRawOk) != 0;
-    if (fb)
-        hipLaunchKernelGGL(compress_fallback_kernel, dim3(grid.piece[grid.pieces]), dim3(kThreads), 0, st, a);
+    const dim3 blocks(grid.piece[grid.pieces]);
+    if (second)
+        hipLaunchKernelGGL(compress_second_kernel, blocks, dim3(kThreads), 0, st, a);
+    else if (fb)
+        hipLaunchKernelGGL(compress_fallback_kernel, blocks, dim3(kThreads), 0, st, a);
     else
-        hipLaunchKernelGGL(compress_kernel, dim3(grid.piece[grid.pieces]), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL(compress_kernel, blocks, dim3(kThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
 }
 
@@ -2122,7 +2199,7 @@ extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void 
     a.tok_hi = (uint32_t)(tok >> 32);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    zc_status rc = launch_compress(a, st);
+    zc_status rc = launch_compress(a, st, false);
     if (rc != ZC_OK) return rc;
     // The raw fallback's second launch, over the flagged segments only: it
     // completes what the first left (the payload of a stream that came out
@@ -2136,10 +2213,9 @@ extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void 
     const uint64_t tok2 = next_token();
     b.tok_lo = (uint32_t)tok2;
     b.tok_hi = (uint32_t)(tok2 >> 32);
-    b.pass = 1;
     b.prev_lo = a.tok_lo;
     b.prev_hi = a.tok_hi;
-    return launch_compress(b, st);
+    return launch_compress(b, st, true);
 }
 
 extern "C" zc_status zc_compress(const void *d_in, uint64_t n, const zc_plan *plan, void *d_out,

@@ -1,10 +1,11 @@
 // Host check of the compress grid layout (zc_grid.h): for random and
-// boundary batches, every encoder span and every finalize run of every
-// segment has exactly one grid block; a launch of at most kDirectMax
-// encoder blocks is all direct, a longer one all staged; every block comes
-// after every block it waits for -- a finalize block after the encoder blocks
-// of its run and the finalize blocks of the segment's earlier runs, a direct
-// block after the segment's earlier direct blocks.  Built by
+// boundary batches, one unit and several units per block, every encoder span
+// and every finalize run of every segment has exactly one place in the grid;
+// a launch of at most kDirectMax encoder blocks is all direct (unless staged
+// only is asked for), a longer one all staged; every unit comes after every
+// unit it waits for -- in a lower block, or earlier in its own block: a
+// finalize run after the encoder spans of its run and the segment's earlier
+// runs, a direct span after the segment's earlier spans.  Built by
 // tests/test_host.py; no GPU.
 #include <cstdio>
 #include <vector>
@@ -29,23 +30,30 @@ static int failures = 0;
         }                                                                                \
     } while (0)
 
-// The device's view of grid block `flat`: which segment, which role, which index.
+// The device's view of grid block `flat`: which segment, which role, which
+// units [index, end).
 struct Role {
     uint32_t seg, kind;
-    uint64_t index;
+    uint64_t index, end;
 };
 
-static Role role_of(const GridPlan &g, uint32_t flat) {
+static Role role_of(const GridPlan &g, uint32_t flat, const std::vector<uint64_t> &n) {
     uint32_t p = 0;
     // linear: independent of the kernel's search
     while (p + 1 < g.pieces && (g.piece[p + 1] & kBlockMask) <= flat) ++p;
     const uint32_t w = g.piece[p];
-    return Role{w >> 26, (w >> 24) & 3u, (uint64_t)g.first[p] + (flat - (w & kBlockMask))};
+    const uint32_t seg = w >> 26, kind = (w >> 24) & 3u;
+    const uint64_t u0 = (uint64_t)g.first[p] + (uint64_t)(flat - (w & kBlockMask)) * g.mult;
+    const uint64_t nb = seg < n.size() ? enc_blocks(n[seg]) : 0;
+    if (kind == kPieceSample) return Role{(uint32_t)u0, kind, u0, u0 + 1};  // sampler of segment u0
+    const uint64_t e = piece_end(kind, g.first[p], nb, g.chunk);
+    return Role{seg, kind, u0, u0 + g.mult < e ? u0 + g.mult : e};
 }
 
-static void check_batch(const std::vector<uint64_t> &n) {
+static void check_batch(const std::vector<uint64_t> &n, uint32_t mult = 1, bool staged_only = false,
+                        bool sample = false) {
     GridPlan g;
-    CHECK(plan_grid(n.data(), (uint32_t)n.size(), g));
+    CHECK(plan_grid(n.data(), (uint32_t)n.size(), g, mult, staged_only, sample));
     CHECK(g.pieces <= kMaxPieces);
     const uint32_t total = g.piece[g.pieces];
     CHECK(total < kMaxGrid);
@@ -59,31 +67,46 @@ static void check_batch(const std::vector<uint64_t> &n) {
         fin_pos[s].assign(g.direct ? 0 : ceil_div(enc_blocks(n[s]), kRun), -1);
         all_spans += enc_blocks(n[s]);
     }
+    // a unit's place: its block, then its turn in the block (the order of execution)
     int64_t first_direct = -1;
+    std::vector<int64_t> sampler(k, -1);
+    int64_t first_other = -1;
     for (uint32_t flat = 0; flat < total; ++flat) {
-        const Role r = role_of(g, flat);
-        CHECK(r.seg < k && r.kind <= kPieceFinalize);
+        const Role r = role_of(g, flat, n);
+        CHECK(r.seg < k && r.kind <= kPieceSample);
+        CHECK(r.index < r.end && r.end - r.index <= mult);  // no empty block
         if (r.seg >= k) continue;
-        if (r.kind == kPieceFinalize) {
-            std::vector<int64_t> &v = fin_pos[r.seg];
-            CHECK(r.index < v.size());
-            if (r.index < v.size()) {
-                CHECK(v[r.index] == -1);  // each run once
-                v[r.index] = flat;
-            }
-        } else {
-            if (r.kind == kPieceDirect && first_direct < 0) first_direct = flat;
-            std::vector<int64_t> &v = enc_pos[r.seg];
-            CHECK(r.index < v.size());
-            if (r.index < v.size()) {
-                CHECK(v[r.index] == -1);  // each span once
-                v[r.index] = flat;
-                enc_kind[r.seg][r.index] = (int)r.kind;
+        if (r.kind == kPieceSample) {
+            CHECK(sample && sampler[r.seg] == -1);  // one sampler per segment, only when asked for
+            sampler[r.seg] = flat;
+            continue;
+        }
+        if (first_other < 0) first_other = flat;
+        for (uint64_t u = r.index; u < r.end; ++u) {
+            const int64_t at = (int64_t)flat * 65536 + (int64_t)(u - r.index);
+            if (r.kind == kPieceFinalize) {
+                std::vector<int64_t> &v = fin_pos[r.seg];
+                CHECK(u < v.size());
+                if (u < v.size()) {
+                    CHECK(v[u] == -1);  // each run once
+                    v[u] = at;
+                }
+            } else {
+                if (r.kind == kPieceDirect && first_direct < 0) first_direct = flat;
+                std::vector<int64_t> &v = enc_pos[r.seg];
+                CHECK(u < v.size());
+                if (u < v.size()) {
+                    CHECK(v[u] == -1);  // each span once
+                    v[u] = at;
+                    enc_kind[r.seg][u] = (int)r.kind;
+                }
             }
         }
     }
+    // the samplers, when asked for, open the grid: every block of a segment waits for its sampler
+    for (size_t s = 0; s < k; ++s) CHECK(sample ? sampler[s] >= 0 && sampler[s] < first_other : sampler[s] < 0);
     // a launch that fits kDirectMax blocks is all direct, a longer one all staged
-    const bool direct = all_spans <= kDirectMax;
+    const bool direct = all_spans <= kDirectMax && !staged_only;
     CHECK(direct == (first_direct >= 0) && direct == g.direct);
     for (size_t s = 0; s < k; ++s) {
         const uint64_t nb = enc_blocks(n[s]);
@@ -117,12 +140,18 @@ int main() {
     const uint64_t singles[] = {0,           1,           8191,       8192,        8193,           tile * 31,
                                 tile * 32 + 5, tile * 2047, tile * 2048, tile * 2049, tile * 2065 + 3, tile * 4096 + 77,
                                 tile * 7168, tile * 40000 + 1, tile * 131072};
-    for (uint64_t n : singles) check_batch({n});
+    for (uint64_t n : singles) {
+        check_batch({n});
+        check_batch({n}, 1, false, true);  // the fallback's first launch
+        check_batch({n}, 16, true);        // the fallback's second launch
+        check_batch({n}, 3, false);
+    }
     // the gradient bucket and the all-to-all shapes, and random batches (some empty segments)
     check_batch(std::vector<uint64_t>(32, tile * 1024));
     check_batch(std::vector<uint64_t>(64, tile * 1024 * 64));  // every segment one chunk only after growing it
     check_batch(std::vector<uint64_t>(64, tile * 32));         // exactly kDirectMax blocks: direct
     check_batch(std::vector<uint64_t>(64, tile * 32 + 1));     // one block more per segment: staged
+    check_batch(std::vector<uint64_t>(64, tile * 1024 * 64), 1, false, true);  // the piece table full
     for (int it = 0; it < 400; ++it) {
         const size_t k = 1 + rnd() % kMaxSegments;
         std::vector<uint64_t> n(k);
@@ -131,6 +160,9 @@ int main() {
             x = r == 0 ? 0 : (r < 4 ? rnd() % (tile * 64) : rnd() % (tile * 6000));
         }
         check_batch(n);
+        check_batch(n, 1, false, true);
+        check_batch(n, 16, true);
+        check_batch(n, 1 + (uint32_t)(rnd() % 20), (rnd() & 1) != 0);
     }
     // the largest segment is planned
     {
