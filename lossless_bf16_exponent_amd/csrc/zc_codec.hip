@@ -142,6 +142,8 @@ struct ZeroArgs {
 // ---------------------------------------------------------------------------
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2a4 __attribute__((ext_vector_type(2), aligned(4)));  // 8 bytes, dword-aligned
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));  // 16 bytes, dword-aligned
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 load_stream16(const void *p) {
@@ -485,6 +487,17 @@ __device__ __forceinline__ void write_span_group(uint8_t *zp, uint64_t dst_off, 
         const uint4 a = *reinterpret_cast<const uint4 *>(w + k0), b = *reinterpret_cast<const uint4 *>(w + k0 + 4);
         src[1] = a.x; src[2] = a.y; src[3] = a.z; src[4] = a.w;
         src[5] = b.x; src[6] = b.y; src[7] = b.z; src[8] = b.w;
+        const int64_t bk = (int64_t)4 * k0 - r;  // source index of byte 0 of dword k0
+        if (k0 + 8 <= ndw && bk >= 0 && bk + 32 <= (int64_t)T) {
+            // all 8 dwords inside the span: two 16-byte stores, streamed out of the L2
+            uint32_t d[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) d[i] = r ? __builtin_amdgcn_alignbyte(src[i + 1], src[i], 4 - r) : src[i + 1];
+            __builtin_nontemporal_store(u32x4a4{d[0], d[1], d[2], d[3]}, reinterpret_cast<u32x4a4 *>(dst + 4u * k0));
+            __builtin_nontemporal_store(u32x4a4{d[4], d[5], d[6], d[7]},
+                                        reinterpret_cast<u32x4a4 *>(dst + 4u * k0 + 16u));
+            continue;
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const uint32_t m = k0 + (uint32_t)i;
@@ -533,6 +546,13 @@ __device__ __forceinline__ void write_span(uint8_t *zp, uint64_t dst_off, const 
         const uint32_t sm1 = k ? w[k - 1] : 0u, s0 = w[k], s1 = w[k + 1];
         const uint32_t d0 = r ? __builtin_amdgcn_alignbyte(s0, sm1, 4 - r) : s0;
         const uint32_t d1 = r ? __builtin_amdgcn_alignbyte(s1, s0, 4 - r) : s1;
+        const int64_t bk = (int64_t)4 * k - r;  // source index of byte 0 of dword k
+        if (k + 1 < ndw && bk >= 0 && bk + 8 <= (int64_t)T) {
+            // both dwords inside the span: one 8-byte store (a wave writes 512
+            // contiguous bytes), streamed out of the L2
+            __builtin_nontemporal_store(u32x2a4{d0, d1}, reinterpret_cast<u32x2a4 *>(dst + 4u * k));
+            continue;
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t m = k + h, d = h ? d1 : d0;
