@@ -737,17 +737,47 @@ __device__ __forceinline__ void write_header(const EncArgs &args, const EncSeg &
 }
 
 // Direct role (every block of a launch that the device holds at once;
-// zc_grid.h).  The block publishes its span word, then finds the zero-points
-// before its span: those of earlier groups of kGroupSpans spans through their
-// group words, and of the earlier spans of its own group through their span
-// words.  It then writes its table entries and its zero-point bytes (from
-// LDS) in place: nothing is staged.  The last span of each group first sums
-// its group's span words and publishes the group word, so that no group word
-// waits for another one.  The segment's last span writes the header once every
-// other block of the segment has passed its waits.
+// zc_grid.h), in two steps.  As soon as the span's counts are known (before
+// the zero-point bytes are collected) the block publishes its span word; the
+// last span of each group of kGroupSpans spans then sums its group's span
+// words and publishes the group word, so that no group word waits for another
+// one.  Once its bytes are collected, the block finds the zero-points before
+// its span: those of earlier groups through their group words and of the
+// earlier spans of its own group through their span words, and writes its
+// table entries and its zero-point bytes (from LDS) in place: nothing is
+// staged.  The segment's last span writes the header once every other block
+// of the segment has passed its waits.
+struct DirectState {
+    uint32_t sib;  // zero-points of the group's spans before b (the group's last span only)
+    bool ok;
+};
+__device__ __forceinline__ DirectState direct_publish(const EncArgs &args, uint32_t s, uint32_t b, uint32_t c0,
+                                                      uint32_t c1, EncShared &sh) {
+    const int tid = threadIdx.x;
+    const EncSeg &sg = args.seg[s];
+    const uint64_t n = sg.n;
+    const Scratch S = scratch_for(n);
+    const uint32_t nb = (uint32_t)enc_blocks(n);
+    const Token tok{args.tok_lo, args.tok_hi};
+    uint8_t *const scratch = sg.out + layout_for(n).off_scratch;
+    const uint32_t g = b / kGroupSpans, g0 = g * kGroupSpans;  // g0: the group's first span
+    const bool group_last = b % kGroupSpans == kGroupSpans - 1 || b + 1 == nb;
+    // a count announces no data: no wait before it
+    if (tid == 0) put_word(scratch + S.span_words + (uint64_t)kWordBytes * b, tok, c0 | (c1 << 16));
+    DirectState st{0u, true};
+    if (group_last) {
+        uint32_t sp[1];
+        st.ok = poll_words<1>(scratch + S.span_words + (uint64_t)kWordBytes * g0, b - g0, tok, sp);
+        st.ok = __syncthreads_and(st.ok);
+        st.sib = block_sum((sp[0] & 0xFFFFu) + (sp[0] >> 16), sh.red);
+        if (st.ok && tid == 0) put_word(scratch + S.group_words + (uint64_t)kWordBytes * g, tok, st.sib + c0 + c1);
+    }
+    return st;
+}
+
 template <bool kFb>
-__device__ __forceinline__ void direct_place(const EncArgs &args, uint32_t s, uint32_t b, uint32_t T, uint32_t c0,
-                                             uint32_t c1, bool raw, EncShared &sh) {
+__device__ __forceinline__ void direct_finish(const EncArgs &args, uint32_t s, uint32_t b, uint32_t T, uint32_t c0,
+                                              uint32_t c1, bool raw, DirectState st, EncShared &sh) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const EncSeg &sg = args.seg[s];
     const uint64_t n = sg.n;
@@ -759,20 +789,10 @@ __device__ __forceinline__ void direct_place(const EncArgs &args, uint32_t s, ui
     uint8_t *const scratch = out + L.off_scratch;
     const uint8_t *const span_w = scratch + S.span_words;
     const uint8_t *const group_w = scratch + S.group_words;
-    const uint32_t g = b / kGroupSpans, g0 = g * kGroupSpans;  // g0: the group's first span
+    const uint32_t g = b / kGroupSpans, g0 = g * kGroupSpans;
     const bool group_last = b % kGroupSpans == kGroupSpans - 1 || b + 1 == nb;
-    // a count announces no data: no wait before it
-    if (tid == 0) put_word(scratch + S.span_words + (uint64_t)kWordBytes * b, tok, c0 | (c1 << 16));
-
-    bool ok = true;
-    uint32_t sib = 0;  // zero-points of the group's spans before b (the group's last span only)
-    if (group_last) {
-        uint32_t sp[1];
-        ok = poll_words<1>(span_w + (uint64_t)kWordBytes * g0, b - g0, tok, sp);
-        ok = __syncthreads_and(ok);
-        sib = block_sum((sp[0] & 0xFFFFu) + (sp[0] >> 16), sh.red);
-        if (ok && tid == 0) put_word(scratch + S.group_words + (uint64_t)kWordBytes * g, tok, sib + c0 + c1);
-    }
+    bool ok = st.ok;
+    const uint32_t sib = st.sib;
     // a raw guess places nothing: only the header writer needs its offset
     if (raw && b + 1 < nb) return;
     // the group's earlier spans (unless summed above) and the earlier groups
@@ -845,7 +865,7 @@ __device__ __forceinline__ void raw_span(const EncArgs &args, uint32_t s, uint32
     __syncthreads();
     const uint32_t c0 = sh.red[0] + sh.red[1], c1 = sh.red[2] + sh.red[3];
     if (direct) {
-        direct_place<true>(args, s, b, 0, c0, c1, true, sh);
+        direct_finish<true>(args, s, b, 0, c0, c1, true, direct_publish(args, s, b, c0, c1, sh), sh);
         return;
     }
     // a count announces no data: no wait before the span word
@@ -949,6 +969,25 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
             if (vm) store_stream8(out + kHeaderBytes + base, sm0, sm1);
         }
     }
+    // ---- direct: the span's counts go out before phase B (waves 0 and 1 hold
+    // the first 4096-value group, waves 2 and 3 the second).  Not in a launch
+    // with the fallback: there the registers this takes would cost a wave per
+    // SIMD, which measured slower.
+    uint32_t c0 = 0, c1 = 0;
+    DirectState dst{0u, true};
+    if (!kFb && direct) {
+        static_assert(kEncSubTiles == 1 && kWaves == 4, "a span is one tile, two waves per group");
+        uint32_t z = 0;
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) z += __builtin_popcount(zm[0][u]);
+        z = wave_sum(z);
+        if (lane == 0) sh.red[wave] = z;
+        __syncthreads();
+        c0 = sh.red[0] + sh.red[1];
+        c1 = sh.red[2] + sh.red[3];
+        dst = direct_publish(args, s, b, c0, c1, sh);
+    }
+
     // ---- phase B: ranks, plane regrouping, zero-point staging
     uint32_t running = 0;  // zero-points of the span so far (uniform)
 #pragma unroll
@@ -1002,7 +1041,12 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
         for (uint64_t i = L.off_tab + 4 * (L.groups + 1) + tid; i < L.off_zp; i += kThreads) out[i] = 0;
     }
     if (direct) {
-        direct_place<kFb>(args, s, b, T, sh.group[0], sh.group[1], false, sh);
+        if (kFb) {
+            c0 = sh.group[0];
+            c1 = sh.group[1];
+            dst = direct_publish(args, s, b, c0, c1, sh);
+        }
+        direct_finish<kFb>(args, s, b, T, c0, c1, false, dst, sh);
         return;
     }
 
