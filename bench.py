@@ -124,8 +124,9 @@ def summary(us: list, alg_bytes: int, n: int) -> dict:
 
 class Resident:
     """One workload resident on the GPU: input, output slots (one per segment,
-    zc_max_compressed_bytes each), sizes, decode buffer and status words, with
-    the batched segment arrays for compress, decompress and checked
+    zc_max_compressed_bytes each: the stream bound), the encoder's workspace
+    (reused by every compress call), sizes, decode buffer and status words,
+    with the batched segment arrays for compress, decompress and checked
     decompress."""
 
     def __init__(self, zc, w, x=None):
@@ -153,13 +154,18 @@ class Resident:
                                           for i in range(len(ns))])
         self.chk_segs = zc.make_dec_segs([(ob + int(soff[i]), caps[i], ns[i], db + 2 * int(offs[i]) if ns[i] else 0,
                                            self.status.data_ptr() + 4 * i) for i in range(len(ns))])
-        self.footprint = self.x.numel() * 2 + self.out.numel() + self.dec.numel() * 2
+        self.ws = torch.empty(sum(zc.zc_compress_workspace_bytes(n) for n in ns), dtype=torch.uint8, device="cuda")
+        self.footprint = self.x.numel() * 2 + self.out.numel() + self.dec.numel() * 2 + self.ws.numel()
+
+    def compress(self, zc, stream, segs=None) -> None:
+        """One batched compress with the scratch in the workspace."""
+        zc.zc_compress_batch_ws(self.enc if segs is None else segs, self.ws, self.ws.numel(), stream)
 
     def check(self, zc, stream) -> dict:
         """One checked round trip; returns the stream facts."""
         import torch
         self.status.fill_(-1)
-        zc.zc_compress_batch(self.enc, stream)
+        self.compress(zc, stream)
         zc.zc_decompress_batch(self.chk_segs, stream)
         torch.cuda.synchronize()
         if self.status.any() or not torch.equal(self.dec, self.x):
@@ -191,7 +197,7 @@ def measure_workload(zc, w, steps: int, warmup: int, cold: bool = False) -> dict
            "zero_point_rate": round(facts["zero_points"] / n, 6), "algorithmic_bytes_per_call": int(alg),
            "timing": "%d groups of %d back-to-back calls after %d warm-up calls; mean and percentiles of the "
                      "per-call time over the groups" % (GROUPS, per, warmup)}
-    calls = {"compress": lambda: zc.zc_compress_batch(r.enc, stream),
+    calls = {"compress": lambda: r.compress(zc, stream),
              "decompress": lambda: zc.zc_decompress_batch(r.dec_segs, stream),
              "decompress_checked": lambda: zc.zc_decompress_batch(r.chk_segs, stream)}
     for name, call in calls.items():
@@ -209,7 +215,7 @@ def measure_workload(zc, w, steps: int, warmup: int, cold: bool = False) -> dict
         rec["cache_resident"] = True
         rec["cold"] = {"buffer_sets": k, "footprint_bytes": int(sum(s.footprint for s in sets))}
         for name, attr in (("compress", "enc"), ("decompress", "dec_segs")):
-            fns = [(lambda s=s, a=attr: (zc.zc_compress_batch if a == "enc" else zc.zc_decompress_batch)(
+            fns = [(lambda s=s, a=attr: s.compress(zc, stream) if a == "enc" else zc.zc_decompress_batch(
                 getattr(s, a), stream)) for s in sets]
             it = [0]
 
@@ -247,7 +253,8 @@ def allgather_receive(zc, steps: int, warmup: int) -> dict:
     sizes = torch.zeros(peers, dtype=torch.int64, device="cuda")
     enc = zc.make_enc_segs([(src.data_ptr() + 2 * p * shard, shard, plan, bufs.data_ptr() + p * slot, cap,
                              sizes.data_ptr() + 8 * p) for p in range(peers)])
-    zc.zc_compress_batch(enc, stream)
+    ws = torch.empty(peers * zc.zc_compress_workspace_bytes(shard), dtype=torch.uint8, device="cuda")
+    zc.zc_compress_batch_ws(enc, ws, ws.numel(), stream)
     torch.cuda.synchronize()
     totals = [int(v) for v in sizes.cpu()]
     dec = zc.make_dec_segs([(bufs.data_ptr() + p * slot, totals[p], shard, gathered.data_ptr() + 2 * p * shard, 0)
@@ -264,13 +271,13 @@ def allgather_receive(zc, steps: int, warmup: int) -> dict:
     rec = {"peers": peers, "shard_values": shard, "stream_bytes": sum(totals),
            "decompress_gathered": summary(timed_groups(call, stream, GROUPS, per), alg, peers * shard)}
     one = zc.make_enc_segs([(src.data_ptr(), shard, plan, bufs.data_ptr(), cap, sizes.data_ptr())])
-    call = lambda: zc.zc_compress_batch(one, stream)
+    call = lambda: zc.zc_compress_batch_ws(one, ws, ws.numel(), stream)
     for _ in range(warmup):
         call()
     rec["compress_own_shard"] = summary(timed_groups(call, stream, GROUPS, per), 2 * shard + totals[0], shard)
     rec["kernels"] = {"decompress_gathered": "decode_kernel, 7 segments in one launch",
                       "compress_own_shard": "compress_kernel"}
-    del gathered, src, bufs
+    del gathered, src, bufs, ws
     torch.cuda.empty_cache()
     return rec
 
@@ -293,8 +300,9 @@ def alltoall_order(zc, w, steps: int, warmup: int) -> dict:
     static, dynamic = segs(range(8)), segs(range(8, 16))
     per = max(1, steps // GROUPS)
     alg = 2 * w.n + facts["stream_bytes"]
-    two = lambda: (zc.zc_compress_batch(static, stream), zc.zc_compress_batch(dynamic, stream))
-    one = lambda: zc.zc_compress_batch(r.enc, stream)
+    # (one workspace for both launches: calls on one stream may share it)
+    two = lambda: (r.compress(zc, stream, static), r.compress(zc, stream, dynamic))
+    one = lambda: r.compress(zc, stream)
     rec = {}
     for name, call in (("static_then_dynamic", two), ("one_launch", one)):
         for _ in range(warmup):
@@ -443,7 +451,7 @@ def reduce_measurement(zc, steps: int) -> dict:
     g = np.random.default_rng(21)
     xs = [torch.from_numpy(workloads.bf16_bits_from_f32(g.standard_normal(n).astype(np.float32)
                                                           * np.float32(s)).view(np.int16)).cuda() for s in sig]
-    cap = zc.zc_max_compressed_bytes(n)
+    cap = zc.zc_compress_capacity(n)  # (untimed setup: the scratch behind each stream)
     bufs = [torch.empty(cap, dtype=torch.uint8, device="cuda") for _ in range(peers)]
     sizes = torch.zeros(peers, dtype=torch.int64, device="cuda")
     for p in range(peers):
@@ -543,7 +551,8 @@ def fallback_measurement(zc, steps: int) -> dict:
     size = torch.zeros(1, dtype=torch.int64, device="cuda")
     dec = torch.empty_like(x)
     stream = torch.cuda.current_stream()
-    enc_call = lambda: zc.zc_compress(x, n, plan, out, cap, size, stream)
+    ws = torch.empty(zc.zc_compress_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    enc_call = lambda: zc.zc_compress_ws(x, n, plan, out, cap, size, ws, ws.numel(), stream)
     dec_call = lambda: zc.zc_decompress(out, cap, n, dec, None, stream)
     enc_call()
     dec_call()
@@ -603,7 +612,7 @@ def main() -> int:
     stream_bytes = facts["stream_bytes"]
     n = w.n
     for _ in range(args.warmup):
-        zc.zc_compress_batch(r.enc, stream)
+        r.compress(zc, stream)
         zc.zc_decompress_batch(r.dec_segs, stream)
     torch.cuda.synchronize()
 
@@ -614,7 +623,7 @@ def main() -> int:
     t_start = time.perf_counter()
     g0.record(stream)
     for _ in range(args.steps):
-        zc.zc_compress_batch(r.enc, stream)
+        r.compress(zc, stream)
         zc.zc_decompress_batch(r.dec_segs, stream)
     g1.record(stream)
     torch.cuda.synchronize()
@@ -626,7 +635,7 @@ def main() -> int:
     e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     e[0].record(stream)
     for _ in range(args.steps):
-        zc.zc_compress_batch(r.enc, stream)
+        r.compress(zc, stream)
     e[1].record(stream)
     for _ in range(args.steps):
         zc.zc_decompress_batch(r.dec_segs, stream)

@@ -71,7 +71,7 @@ extern "C" {
 typedef enum zc_status {
     ZC_OK = 0,
     ZC_ERR_INVALID_ARG = 1, /* NULL pointer, bad plan, bad sigma, n > 2^32-1, k out of range */
-    ZC_ERR_CAPACITY = 2,    /* out_capacity below zc_max_compressed_bytes(n) */
+    ZC_ERR_CAPACITY = 2,    /* an output or workspace capacity below what the call needs */
     ZC_ERR_MISALIGNED = 3,  /* BF16 buffers need 16-byte, stream buffers 128-byte alignment */
     ZC_ERR_CORRUPT = 4,     /* a stream failed validation (device-side, via the status word) */
     ZC_ERR_HIP = 5          /* the HIP runtime refused a launch */
@@ -96,19 +96,31 @@ typedef struct zc_plan {
  * else ZC_ERR_INVALID_ARG. */
 zc_status zc_plan_from_sigma(double sigma, zc_plan *out);
 
-/* Capacity a compressed output buffer must have for n elements: the largest
- * stream (every element on the zero-point path, section 2.B) plus the scratch
- * the encoder keeps behind it.  Returns 0 for n > 2^32-1. */
+/* The largest stream of n elements (every element on the zero-point path,
+ * section 2.B; the raw fallback form is smaller), rounded up to 128 bytes:
+ * about 2.375 n + 512 bytes.  An output buffer of this capacity holds any
+ * stream when the encoder's scratch sits in a workspace (zc_compress_ws,
+ * zc_compress_batch_ws).  Returns 0 for n > 2^32-1. */
 uint64_t zc_max_compressed_bytes(uint64_t n);
+
+/* Encoder scratch for one tensor of n elements (a multiple of 256 bytes, a
+ * little over n bytes: a staging slot of 8192 bytes per 8192 elements for
+ * zero-point bytes, and the cross-workgroup words).  zc_compress and zc_compress_batch keep it in the output buffer
+ * behind the largest stream; the _ws calls take it from a workspace, which a
+ * caller can reuse from call to call (a send buffer then needs only
+ * zc_max_compressed_bytes(n)).  Returns 0 for n > 2^32-1. */
+uint64_t zc_compress_workspace_bytes(uint64_t n);
 
 /* Section 2.B, compress one BF16 tensor.
  *   d_in          device, n BF16 values (raw 16-bit patterns), 16-byte aligned
  *   n             element count, 0 .. 2^32-1
  *   plan          host pointer to the exponent table
  *   d_out         device, 128-byte aligned, out_capacity bytes; receives the
- *                 stream in [0, total_bytes); [total_bytes, out_capacity) is
- *                 encoder scratch with unspecified contents afterwards
- *   out_capacity  must be >= zc_max_compressed_bytes(n)
+ *                 stream in [0, total_bytes); [total_bytes, out_capacity) has
+ *                 unspecified contents afterwards (the encoder's scratch sits
+ *                 at zc_max_compressed_bytes(n))
+ *   out_capacity  must be >= zc_max_compressed_bytes(n) +
+ *                 zc_compress_workspace_bytes(n)
  *   d_out_bytes   device u64 (nullable): receives total_bytes
  *   stream        hipStream_t
  * Errors: ZC_ERR_INVALID_ARG, ZC_ERR_MISALIGNED, ZC_ERR_CAPACITY, ZC_ERR_HIP.
@@ -129,6 +141,19 @@ uint64_t zc_max_compressed_bytes(uint64_t n);
  * an invalid stream.  Neither outcome passes for a valid stream. */
 zc_status zc_compress(const void *d_in, uint64_t n, const zc_plan *plan, void *d_out,
                       uint64_t out_capacity, uint64_t *d_out_bytes, void *stream);
+
+/* zc_compress with the encoder's scratch in a workspace: out_capacity need
+ * only be >= zc_max_compressed_bytes(n), and nothing of d_out past the stream
+ * is written.
+ *   d_workspace      device, 256-byte aligned, workspace_bytes bytes, contents
+ *                    arbitrary before and unspecified after the call; it may
+ *                    be reused by any later call on the same stream (calls on
+ *                    other streams need their own)
+ *   workspace_bytes  must be >= zc_compress_workspace_bytes(n)
+ * Errors as zc_compress; ZC_ERR_INVALID_ARG also for a null workspace. */
+zc_status zc_compress_ws(const void *d_in, uint64_t n, const zc_plan *plan, void *d_out,
+                         uint64_t out_capacity, uint64_t *d_out_bytes, void *d_workspace,
+                         uint64_t workspace_bytes, void *stream);
 
 /* Inverse of zc_compress.
  *   d_in      device, 128-byte aligned, the stream, coded or raw (in_bytes
@@ -253,6 +278,14 @@ typedef struct zc_dec_seg {
  * zc_compress included, per segment).  segs is a host array read before the
  * call returns. */
 zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void *stream);
+
+/* zc_compress_batch with every segment's scratch in one workspace (segment
+ * i's at the sum of zc_compress_workspace_bytes over the segments before it):
+ * each out_capacity need only be >= zc_max_compressed_bytes(n), and
+ * workspace_bytes must be >= the sum over all segments.  Workspace rules as
+ * for zc_compress_ws. */
+zc_status zc_compress_batch_ws(const zc_enc_seg *segs, uint32_t k, void *d_workspace, uint64_t workspace_bytes,
+                               void *stream);
 
 /* Decompress k (1..ZC_MAX_BATCH) streams in one launch. */
 zc_status zc_decompress_batch(const zc_dec_seg *segs, uint32_t k, void *stream);

@@ -61,6 +61,7 @@ struct EncSeg {
     uint32_t n;
     uint8_t exps[7];
     uint8_t flags;     // kSegTable, kSegRawOk
+    uint32_t ws_off;   // with a workspace: the segment's scratch at ws + 256 * ws_off
 };
 static_assert(sizeof(EncSeg) == 40, "compact kernel arguments");
 constexpr uint8_t kSegTable = 1;  // codes from a 256-byte LDS table (else: the window's saturating arithmetic)
@@ -77,6 +78,7 @@ struct EncArgs {
     uint32_t pad;
     uint32_t mult;            // units (spans or runs) per block (zc_grid.h)
     uint32_t chunk;           // spans per staged chunk
+    uint8_t *ws;              // the call's workspace, or null: each segment's scratch behind its stream
     EncSeg seg[ZC_MAX_BATCH];
     // Piece words (zc_grid.h: first grid block, kind, segment; the last entry
     // holds the grid size) and each piece's first span or run.  Words, not
@@ -89,6 +91,12 @@ struct EncArgs {
 // Kept within the conventional 4 KiB kernel-argument budget, counting up to
 // 256 bytes of the runtime's hidden arguments.
 static_assert(sizeof(EncArgs) + 256 <= 4096, "compress arguments fit the kernarg segment");
+
+// A segment's encoder scratch: in the call's workspace, or behind the
+// largest stream in its own output buffer.
+__device__ __forceinline__ uint8_t *seg_scratch(const EncArgs &a, const EncSeg &sg) {
+    return a.ws ? a.ws + 256ull * sg.ws_off : sg.out + layout_for(sg.n).off_scratch;
+}
 
 struct DecSeg {
     const uint8_t *in;
@@ -733,7 +741,7 @@ __device__ __forceinline__ void write_header(const EncArgs &args, const EncSeg &
     }
     if (tid == 0 && sg.out_bytes) *sg.out_bytes = valid ? total : 0ull;
     if (kFb && ok && tid == 0 && (sg.flags & kSegRawOk))
-        put_word(out + L.off_scratch + scratch_for(n).status, Token{args.tok_lo, args.tok_hi}, status);
+        put_word(seg_scratch(args, sg) + scratch_for(n).status, Token{args.tok_lo, args.tok_hi}, status);
 }
 
 // Direct role (every block of a launch that the device holds at once;
@@ -759,7 +767,7 @@ __device__ __forceinline__ DirectState direct_publish(const EncArgs &args, uint3
     const Scratch S = scratch_for(n);
     const uint32_t nb = (uint32_t)enc_blocks(n);
     const Token tok{args.tok_lo, args.tok_hi};
-    uint8_t *const scratch = sg.out + layout_for(n).off_scratch;
+    uint8_t *const scratch = seg_scratch(args, sg);
     const uint32_t g = b / kGroupSpans, g0 = g * kGroupSpans;  // g0: the group's first span
     const bool group_last = b % kGroupSpans == kGroupSpans - 1 || b + 1 == nb;
     // a count announces no data: no wait before it
@@ -786,7 +794,7 @@ __device__ __forceinline__ void direct_finish(const EncArgs &args, uint32_t s, u
     const uint32_t nb = (uint32_t)enc_blocks(n);
     const Token tok{args.tok_lo, args.tok_hi};
     uint8_t *const out = sg.out;
-    uint8_t *const scratch = out + L.off_scratch;
+    uint8_t *const scratch = seg_scratch(args, sg);
     const uint8_t *const span_w = scratch + S.span_words;
     const uint8_t *const group_w = scratch + S.group_words;
     const uint32_t g = b / kGroupSpans, g0 = g * kGroupSpans;
@@ -871,7 +879,7 @@ __device__ __forceinline__ void raw_span(const EncArgs &args, uint32_t s, uint32
     // a count announces no data: no wait before the span word
     if (tid == 0) {
         const Scratch S = scratch_for(n);
-        put_word(sg.out + layout_for(n).off_scratch + S.span_words + (uint64_t)kWordBytes * b,
+        put_word(seg_scratch(args, sg) + S.span_words + (uint64_t)kWordBytes * b,
                  Token{args.tok_lo, args.tok_hi}, c0 | (c1 << 16));
     }
 }
@@ -895,7 +903,7 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
     const bool table = (sg.flags & kSegTable) != 0;
     const uint64_t span0 = (uint64_t)b * kEncSpan;
     uint8_t *const out = sg.out;
-    uint8_t *const scratch = out + L.off_scratch;
+    uint8_t *const scratch = seg_scratch(args, sg);
     const Scratch S = scratch_for(n);
 
     if (table) {
@@ -1096,7 +1104,7 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
     const bool chunk_last = r % kChunkRuns == kChunkRuns - 1 || last_run;
     const Token tok{args.tok_lo, args.tok_hi};
     uint8_t *const out = sg.out;
-    uint8_t *const scratch = out + L.off_scratch;
+    uint8_t *const scratch = seg_scratch(args, sg);
     uint32_t *const tab = reinterpret_cast<uint32_t *>(out + L.off_tab);
 
     // ---- 0. the raw fallback: under a raw guess the run only counts (its
@@ -1332,7 +1340,7 @@ __device__ __forceinline__ void sample_segment(const EncArgs &args, uint32_t s, 
     const uint32_t base_hi = (wbase << 8) | (wbase << 24);
     const Layout L = layout_for(sg.n);
     const uint32_t d = sample_guess(sg, L, table, base_hi, sh.code, sh.red);
-    if (threadIdx.x == 0) put_word(sg.out + L.off_scratch + scratch_for(sg.n).decision, Token{args.tok_lo, args.tok_hi}, d);
+    if (threadIdx.x == 0) put_word(seg_scratch(args, sg) + scratch_for(sg.n).decision, Token{args.tok_lo, args.tok_hi}, d);
 }
 
 // One block of a compress launch, one unit.  kFb: the launch has segments
@@ -1385,7 +1393,7 @@ __global__ __launch_bounds__(kThreads) void compress_second_kernel(EncArgs args)
     const EncSeg &sg = args.seg[r.seg];
     const uint32_t u1 = (uint32_t)min((uint64_t)r.unit + args.mult,
                                       piece_end(r.kind, args.first[r.p], enc_blocks(sg.n), args.chunk));
-    const uint32_t mode = second_pass_mode(args, sg.out + layout_for(sg.n).off_scratch, scratch_for(sg.n));
+    const uint32_t mode = second_pass_mode(args, seg_scratch(args, sg), scratch_for(sg.n));
     if (mode == kModeSkip) return;
     if (mode == kModeCopyRaw) {
         if (r.kind != kPieceFinalize)
@@ -2241,17 +2249,29 @@ static zc_status launch_compress(EncArgs &a, hipStream_t st, bool second) {
     return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
 }
 
-extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void *stream) {
+// Compress with the scratch in `ws` (ws_bytes, 256-byte aligned; segment i's
+// scratch at the sum of zc_compress_workspace_bytes over the segments before
+// it), or, ws null, behind each stream in its output buffer.
+static zc_status compress_impl(const zc_enc_seg *segs, uint32_t k, void *ws, uint64_t ws_bytes, void *stream) {
     if (!segs || k == 0 || k > ZC_MAX_BATCH) return ZC_ERR_INVALID_ARG;
+    if (ws && ((uintptr_t)ws & 255u)) return ZC_ERR_MISALIGNED;
     EncArgs a;
     std::memset(&a, 0, sizeof(a));
+    a.ws = static_cast<uint8_t *>(ws);
+    uint64_t ws_used = 0;
     for (uint32_t i = 0; i < k; ++i) {
         const zc_enc_seg &g = segs[i];
         if (!g.out || g.n > kMaxElems || (g.n && !g.in) || !zc_plan_is_valid(&g.plan)) return ZC_ERR_INVALID_ARG;
         if (((uintptr_t)g.in & 15u) || ((uintptr_t)g.out & 127u) || ((uintptr_t)g.out_bytes & 7u))
             return ZC_ERR_MISALIGNED;
-        if (g.out_capacity < zc_max_compressed_bytes(g.n)) return ZC_ERR_CAPACITY;
+        const uint64_t seg_ws = zc_compress_workspace_bytes(g.n);
+        if (g.out_capacity < zc_max_compressed_bytes(g.n) + (ws ? 0 : seg_ws)) return ZC_ERR_CAPACITY;
         EncSeg &e = a.seg[i];
+        if (ws) {
+            if (ws_used / 256 > 0xFFFFFFFFull) return ZC_ERR_INVALID_ARG;
+            e.ws_off = (uint32_t)(ws_used / 256);
+            ws_used += seg_ws;
+        }
         e.in = static_cast<const uint16_t *>(g.in);
         e.out = static_cast<uint8_t *>(g.out);
         e.out_bytes = reinterpret_cast<unsigned long long *>(g.out_bytes);
@@ -2262,6 +2282,7 @@ extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void 
         const bool window = g.plan.exps[0] >= 1 && g.plan.exps[6] - g.plan.exps[0] == 6;
         e.flags = (uint8_t)((window ? 0 : kSegTable) | ((g.plan.flags & ZC_PLAN_RAW_FALLBACK) ? kSegRawOk : 0));
     }
+    if (ws && ws_used > ws_bytes) return ZC_ERR_CAPACITY;
     a.k = k;
     const uint64_t tok = next_token();
     a.tok_lo = (uint32_t)tok;
@@ -2284,7 +2305,18 @@ extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void 
     b.tok_hi = (uint32_t)(tok2 >> 32);
     b.prev_lo = a.tok_lo;
     b.prev_hi = a.tok_hi;
+    b.ws = a.ws;
     return launch_compress(b, st, true);
+}
+
+extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void *stream) {
+    return compress_impl(segs, k, nullptr, 0, stream);
+}
+
+extern "C" zc_status zc_compress_batch_ws(const zc_enc_seg *segs, uint32_t k, void *d_workspace,
+                                          uint64_t workspace_bytes, void *stream) {
+    if (!d_workspace) return ZC_ERR_INVALID_ARG;
+    return compress_impl(segs, k, d_workspace, workspace_bytes, stream);
 }
 
 extern "C" zc_status zc_compress(const void *d_in, uint64_t n, const zc_plan *plan, void *d_out,
@@ -2298,6 +2330,20 @@ extern "C" zc_status zc_compress(const void *d_in, uint64_t n, const zc_plan *pl
     s.out_capacity = out_capacity;
     s.out_bytes = d_out_bytes;
     return zc_compress_batch(&s, 1, stream);
+}
+
+extern "C" zc_status zc_compress_ws(const void *d_in, uint64_t n, const zc_plan *plan, void *d_out,
+                                    uint64_t out_capacity, uint64_t *d_out_bytes, void *d_workspace,
+                                    uint64_t workspace_bytes, void *stream) {
+    if (!plan) return ZC_ERR_INVALID_ARG;
+    zc_enc_seg s;
+    s.in = d_in;
+    s.n = n;
+    s.plan = *plan;
+    s.out = d_out;
+    s.out_capacity = out_capacity;
+    s.out_bytes = d_out_bytes;
+    return zc_compress_batch_ws(&s, 1, d_workspace, workspace_bytes, stream);
 }
 
 extern "C" zc_status zc_decompress_batch(const zc_dec_seg *segs, uint32_t k, void *stream) {

@@ -71,7 +71,12 @@ bool zc_plan_is_valid(const zc_plan *p) {
 
 extern "C" uint64_t zc_max_compressed_bytes(uint64_t n) {
     if (n > kMaxElems) return 0;
-    return layout_for(n).off_scratch + scratch_for(n).bytes;
+    return layout_for(n).off_scratch;  // the largest stream, coded or raw, rounded up to 128
+}
+
+extern "C" uint64_t zc_compress_workspace_bytes(uint64_t n) {
+    if (n > kMaxElems) return 0;
+    return (scratch_for(n).bytes + 255u) & ~uint64_t(255u);
 }
 
 static uint32_t rd32(const uint8_t *p) {
@@ -117,7 +122,7 @@ extern "C" const char *zc_status_string(zc_status s) {
     switch (s) {
         case ZC_OK: return "ok";
         case ZC_ERR_INVALID_ARG: return "invalid argument";
-        case ZC_ERR_CAPACITY: return "output capacity below zc_max_compressed_bytes(n)";
+        case ZC_ERR_CAPACITY: return "output or workspace capacity below what the call needs";
         case ZC_ERR_MISALIGNED: return "misaligned buffer";
         case ZC_ERR_CORRUPT: return "corrupt stream";
         case ZC_ERR_HIP: return "HIP launch failed";

@@ -54,6 +54,14 @@ _lib.zc_max_compressed_bytes.restype = ctypes.c_uint64
 _lib.zc_compress.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(zc_plan), ctypes.c_void_p,
                              ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
 _lib.zc_compress.restype = ctypes.c_int
+_lib.zc_compress_workspace_bytes.argtypes = [ctypes.c_uint64]
+_lib.zc_compress_workspace_bytes.restype = ctypes.c_uint64
+_lib.zc_compress_ws.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(zc_plan), ctypes.c_void_p,
+                                ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+_lib.zc_compress_ws.restype = ctypes.c_int
+_lib.zc_compress_batch_ws.argtypes = [ctypes.POINTER(zc_enc_seg), ctypes.c_uint32, ctypes.c_void_p, ctypes.c_uint64,
+                                      ctypes.c_void_p]
+_lib.zc_compress_batch_ws.restype = ctypes.c_int
 _lib.zc_decompress.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p]
 _lib.zc_decompress.restype = ctypes.c_int
@@ -85,7 +93,8 @@ _lib.zc_status_string.restype = ctypes.c_char_p
 EXPORTED = ("zc_plan_from_sigma", "zc_max_compressed_bytes", "zc_compress", "zc_decompress",
             "zc_compress_batch", "zc_decompress_batch", "zc_decompress_reduce", "zc_read_header",
             "zc_status_string", "zc_stats_workspace_bytes", "zc_exponent_histogram", "zc_plan_from_histogram",
-            "zc_estimate_sigma", "zc_exponent_histogram_noalloc")
+            "zc_estimate_sigma", "zc_exponent_histogram_noalloc", "zc_compress_workspace_bytes", "zc_compress_ws",
+            "zc_compress_batch_ws")
 
 
 class ZcError(RuntimeError):
@@ -143,6 +152,24 @@ def zc_plan_from_sigma(sigma: float) -> tuple:
 
 def zc_max_compressed_bytes(n: int) -> int:
     return int(_lib.zc_max_compressed_bytes(int(n)))
+
+
+def zc_compress_workspace_bytes(n: int) -> int:
+    return int(_lib.zc_compress_workspace_bytes(int(n)))
+
+
+def zc_compress_capacity(n: int) -> int:
+    """Output capacity zc_compress / zc_compress_batch need for n values (the
+    stream bound and the encoder's scratch behind it)."""
+    return zc_max_compressed_bytes(n) + zc_compress_workspace_bytes(n)
+
+
+def zc_compress_ws(d_in, n, plan, d_out, out_capacity, d_out_bytes, d_workspace, workspace_bytes,
+                   stream=None) -> None:
+    p = _plan(plan)
+    _check(_lib.zc_compress_ws(_ptr(d_in), int(n), ctypes.byref(p), _ptr(d_out), int(out_capacity),
+                               _ptr(d_out_bytes), _ptr(d_workspace), int(workspace_bytes), _stream(stream)),
+           "zc_compress_ws")
 
 
 def zc_compress(d_in, n, plan, d_out, out_capacity, d_out_bytes=None, stream=None) -> None:
@@ -219,6 +246,14 @@ def zc_compress_batch(segs, stream=None) -> None:
     arr, k = segs if isinstance(segs, tuple) and len(segs) == 2 and isinstance(segs[0], ctypes.Array) \
         else make_enc_segs(segs)
     _check(_lib.zc_compress_batch(arr, k, _stream(stream)), "zc_compress_batch")
+
+
+def zc_compress_batch_ws(segs, d_workspace, workspace_bytes, stream=None) -> None:
+    """zc_compress_batch with every segment's scratch in one workspace."""
+    arr, k = segs if isinstance(segs, tuple) and len(segs) == 2 and isinstance(segs[0], ctypes.Array) \
+        else make_enc_segs(segs)
+    _check(_lib.zc_compress_batch_ws(arr, k, _ptr(d_workspace), int(workspace_bytes), _stream(stream)),
+           "zc_compress_batch_ws")
 
 
 def zc_decompress_batch(segs, stream=None) -> None:

@@ -50,6 +50,9 @@ def load_test_build(zc, path: str):
     lib.zc_compress.restype = ctypes.c_int
     lib.zc_compress_batch.argtypes = [ctypes.POINTER(zc.zc_enc_seg), ctypes.c_uint32, ctypes.c_void_p]
     lib.zc_compress_batch.restype = ctypes.c_int
+    lib.zc_compress_batch_ws.argtypes = [ctypes.POINTER(zc.zc_enc_seg), ctypes.c_uint32, ctypes.c_void_p,
+                                         ctypes.c_uint64, ctypes.c_void_p]
+    lib.zc_compress_batch_ws.restype = ctypes.c_int
     return lib
 
 
@@ -60,13 +63,16 @@ def check_untouched(t: torch.Tensor, fill: int, what: str) -> None:
         raise AssertionError("%s: sentinel bytes overwritten (first at %s)" % (what, bad))
 
 
-def compress_batch(zc, xs_dev, ns, plans, batch: bool = True, fill: int = 0xA5, lib=None) -> Encoded:
+def compress_batch(zc, xs_dev, ns, plans, batch: bool = True, fill: int = 0xA5, lib=None,
+                   workspace: bool = False) -> Encoded:
     """Compress segments (device tensors or views) into one buffer with one slot
     per segment; batch=False issues one zc_compress per segment instead; lib: a
     test build of the library (ctypes handle) to call in place of the shipped
-    one (batched calls only).  Every slot has GUARD sentinel bytes before it and
-    after its capacity, checked untouched after the call."""
-    caps = [zc.zc_max_compressed_bytes(n) for n in ns]
+    one (batched calls only); workspace: the _ws calls, with the encoder's
+    scratch in a separate workspace (filled with random bytes first) and slots
+    of zc_max_compressed_bytes(n) only.  Every slot has GUARD sentinel bytes
+    before it and after its capacity, checked untouched after the call."""
+    caps = [zc.zc_max_compressed_bytes(n) if workspace else zc.zc_compress_capacity(n) for n in ns]
     offsets, off = [], GUARD
     for c in caps:
         offsets.append(off)
@@ -76,7 +82,21 @@ def compress_batch(zc, xs_dev, ns, plans, batch: bool = True, fill: int = 0xA5, 
     base = buf.data_ptr()
     segs = [(x, n, p, base + o, c, sizes.data_ptr() + 8 * i)
             for i, (x, n, p, o, c) in enumerate(zip(xs_dev, ns, plans, offsets, caps))]
-    if lib is not None:
+    if workspace:
+        wsb = [zc.zc_compress_workspace_bytes(n) for n in ns]
+        ws = torch.randint(0, 256, (sum(wsb) if batch else max(wsb),), dtype=torch.uint8, device="cuda")
+        if batch:
+            arr, k = zc.make_enc_segs(segs)
+            if lib is not None:
+                rc = lib.zc_compress_batch_ws(arr, k, ws.data_ptr(), ws.numel(),
+                                              torch.cuda.current_stream().cuda_stream)
+                assert rc == zc.ZC_OK, rc
+            else:
+                zc.zc_compress_batch_ws((arr, k), ws, ws.numel())
+        else:
+            for s in segs:  # one workspace, reused call after call on the stream
+                zc.zc_compress_ws(*s, ws, ws.numel())
+    elif lib is not None:
         arr, k = zc.make_enc_segs(segs)
         rc = lib.zc_compress_batch(arr, k, torch.cuda.current_stream().cuda_stream)
         assert rc == zc.ZC_OK, rc

@@ -109,10 +109,14 @@ int main() {
         CHECK(L.off_scratch >= L.off_zp + n);                      // the largest stream fits before the scratch
         CHECK(L.off_scratch >= kHeaderBytes + 2 * n);              // so does the raw form
         CHECK(S.staging >= S.span_done && S.bytes == S.staging + enc_blocks(n) * (uint64_t)kEncSpan);
-        CHECK(cap == L.off_scratch + S.bytes);
+        CHECK(cap == L.off_scratch);                               // the stream bound
+        const uint64_t ws = zc_compress_workspace_bytes(n);
+        CHECK(ws % 256 == 0 && ws >= S.bytes && ws < S.bytes + 256);
+        CHECK(S.decision % kWordBytes == 0 && S.status % kWordBytes == 0 && S.span_words >= S.status + kWordBytes);
     }
     CHECK(zc_max_compressed_bytes(kMaxElems + 1) == 0);
     CHECK(zc_max_compressed_bytes(~0ull) == 0);
+    CHECK(zc_compress_workspace_bytes(kMaxElems + 1) == 0);
 
     // ---- the header parser: valid headers, every single-byte corruption, random bytes, short lengths
     {

@@ -50,7 +50,7 @@ def given_up_batch(zc, giveup, ns, sigmas, waits, raw_at=None):
         plans[raw_at] = zc.plan_with_raw_fallback(plans[raw_at])
     xs = [gaussian(n, s, i) for i, (n, s) in enumerate(zip(ns, sigmas))]
     devs = [to_device(x) if x.size else None for x in xs]
-    caps = [zc.zc_max_compressed_bytes(n) for n in ns]
+    caps = [zc.zc_compress_capacity(n) for n in ns]
     offs = np.concatenate([[0], np.cumsum([slot(c) for c in caps])]).astype(np.int64)
     buf = torch.full((int(offs[-1]),), 0x5A, dtype=torch.uint8, device="cuda")
     sizes = torch.full((len(ns),), 12345, dtype=torch.int64, device="cuda")

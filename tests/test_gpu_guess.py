@@ -103,7 +103,7 @@ def test_forced_guess_repeated_calls_same_buffers(zc, guess):
         x = oracle_pins.with_escapes(n, E, seed)
         ref = oracle.encode(x, WINDOW_PLAN, raw_fallback=True)
         if E == T + 1:
-            buf = torch.full((zc.zc_max_compressed_bytes(n),), 0x33, dtype=torch.uint8, device="cuda")
+            buf = torch.full((zc.zc_compress_capacity(n),), 0x33, dtype=torch.uint8, device="cuda")
             size = torch.zeros(1, dtype=torch.int64, device="cuda")
             d = to_device(x)
         else:

@@ -39,13 +39,16 @@ def test_maximum_size_round_trip(zc):
         m = min(chunk, n - s)
         x[s:s + m] = (torch.randn(m, generator=g, device="cuda") * 0.02).to(torch.bfloat16).view(torch.int16)
     plan = zc.zc_plan_from_sigma(0.02)
-    cap = zc.zc_max_compressed_bytes(n)
+    cap = zc.zc_max_compressed_bytes(n)  # the stream bound: the scratch goes to a workspace
     out = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    wsb = zc.zc_compress_workspace_bytes(n)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     size = torch.zeros(1, dtype=torch.int64, device="cuda")
-    say("max size: compress")
-    zc.zc_compress(x, n, plan, out, cap, size)
+    say("max size: compress (output %d bytes, workspace %d bytes)" % (cap, wsb))
+    zc.zc_compress_ws(x, n, plan, out, cap, size, ws, wsb)
     torch.cuda.synchronize()
     total = int(size.item())
+    del ws
 
     say("max size: decompress")
     dec = torch.empty_like(x)

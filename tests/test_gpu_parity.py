@@ -27,11 +27,11 @@ def zc():
     return require_gpu()
 
 
-def roundtrip_check(zc, xs, plans, batch=True):
+def roundtrip_check(zc, xs, plans, batch=True, workspace=False):
     """Compress + decompress a list of uint16 arrays; compare with the oracle."""
     ns = [x.size for x in xs]
     devs = [to_device(x) if x.size else None for x in xs]
-    enc = compress_batch(zc, devs, ns, plans, batch=batch)
+    enc = compress_batch(zc, devs, ns, plans, batch=batch, workspace=workspace)
     for i, (x, p) in enumerate(zip(xs, plans)):
         ref = oracle.encode(x, p)
         got = enc.stream(i)
@@ -127,13 +127,38 @@ def test_max_batch_of_64_segments(zc):
     roundtrip_check(zc, xs, plans)
 
 
+@pytest.mark.parametrize("batch", [True, False], ids=["batch", "single"])
+def test_workspace_calls(zc, batch):
+    """The _ws calls: output slots of the stream bound only (the sentinel bytes
+    right behind each slot stay untouched), the scratch in a workspace that
+    starts with random bytes; a direct launch, a staged one (more than 2048
+    spans) and one with raw-fallback segments, each equal to the oracle."""
+    small = [gaussian(n, sig, 40 + i) for i, (n, sig) in enumerate(((300_007, 0.02), (8192 * 40 + 5, 1e-3),
+                                                                     (0, 0.02), (100, 0.16), (1_000_003, 0.16)))]
+    plans = [WINDOW_PLAN, oracle.plan_from_sigma(1e-3), WINDOW_PLAN, WINDOW_PLAN, WINDOW_PLAN]
+    print("workspace: direct launch, batch=%s" % batch, flush=True)
+    roundtrip_check(zc, small, plans, batch=batch, workspace=True)
+    big = small + [gaussian(8192 * 2100 + 11, 0.02, 50)]
+    print("workspace: staged launch, batch=%s" % batch, flush=True)
+    roundtrip_check(zc, big, plans + [WINDOW_PLAN], batch=batch, workspace=True)
+    if batch:
+        print("workspace: raw fallback", flush=True)
+        xs = [oracle_pins.with_escapes(70_001, 70_001, 3), oracle_pins.with_escapes(8192 * 100 + 3, 100, 4),
+              oracle_pins.with_escapes(8192 * 100 + 3, 8192 * 100, 5)]
+        ns = [x.size for x in xs]
+        enc = compress_batch(zc, [to_device(x) for x in xs], ns, [zc.plan_with_raw_fallback(WINDOW_PLAN)] * 3,
+                             workspace=True)
+        for i, x in enumerate(xs):
+            assert np.array_equal(enc.stream(i), oracle.encode(x, WINDOW_PLAN, raw_fallback=True)), i
+
+
 def test_output_buffer_reuse_and_old_contents(zc):
     """Calls in a row into one output buffer that starts with random bytes: the
     scratch words left behind by earlier calls (or by anything else) must never
     be taken for the current call's.  Sizes give several finalize blocks."""
     from gpu_util import slot
     for n in (300_007, 1_000_003):
-        cap = zc.zc_max_compressed_bytes(n)
+        cap = zc.zc_compress_capacity(n)
         g = torch.Generator(device="cuda").manual_seed(n)
         buf = torch.randint(0, 256, (slot(cap),), dtype=torch.uint8, device="cuda", generator=g)
         size = torch.zeros(1, dtype=torch.int64, device="cuda")
@@ -159,6 +184,9 @@ def test_calls_in_flight_on_two_streams(zc):
     dev = [to_device(x) for x in xs]
     caps = [zc.zc_max_compressed_bytes(n) for n, _, _ in cases]
     bufs = [torch.empty(c, dtype=torch.uint8, device="cuda") for c in caps]
+    # one workspace per stream, reused by every call on it
+    wsb = max(zc.zc_compress_workspace_bytes(n) for n, _, _ in cases)
+    wss = [torch.empty(wsb, dtype=torch.uint8, device="cuda") for _ in range(2)]
     sizes = torch.zeros(len(cases), dtype=torch.int64, device="cuda")
     outs = [torch.empty_like(d) for d in dev]
     st = torch.full((len(cases),), -1, dtype=torch.int32, device="cuda")
@@ -166,7 +194,7 @@ def test_calls_in_flight_on_two_streams(zc):
     for rnd in range(3):
         for i, (n, _, plan) in enumerate(cases):
             s = sa if i % 2 == 0 else sb
-            zc.zc_compress(dev[i], n, plan, bufs[i], caps[i], sizes.data_ptr() + 8 * i, stream=s)
+            zc.zc_compress_ws(dev[i], n, plan, bufs[i], caps[i], sizes.data_ptr() + 8 * i, wss[i % 2], wsb, stream=s)
     for i, (n, _, _) in enumerate(cases):
         s = sa if i % 2 == 0 else sb
         zc.zc_decompress(bufs[i], caps[i], n, outs[i], st.data_ptr() + 4 * i, stream=s)

@@ -146,11 +146,18 @@ def test_plan_rejects_bad_sigma(zc):
 
 
 def test_max_compressed_bytes_covers_worst_stream(zc):
+    """The stream bound covers the oracle's largest stream and the raw form and
+    stays under 2.4 n for large n; the scratch is a little over n bytes."""
     for n in (0, 1, 63, 64, 4095, 4096, 4097, 8193, 1 << 20, 58_720_256, (1 << 30), (1 << 32) - 1):
         cap = zc.zc_max_compressed_bytes(n)
-        assert cap >= oracle.max_bytes(n) + 128 + 8, n
-        assert cap % 8 == 0
+        ws = zc.zc_compress_workspace_bytes(n)
+        assert cap >= oracle.max_bytes(n) and cap >= 128 + 2 * n, n
+        assert cap % 128 == 0 and ws % 256 == 0 and ws >= n
+        assert zc.zc_compress_capacity(n) == cap + ws
+        if n >= 1 << 20:
+            assert cap <= 2.4 * n and ws <= 1.01 * n + 16384, n
     assert zc.zc_max_compressed_bytes(1 << 32) == 0
+    assert zc.zc_compress_workspace_bytes(1 << 32) == 0
 
 
 FAKE_IN = 0x7F0000000000  # never dereferenced: every call below fails validation first
@@ -162,7 +169,7 @@ def _compress_status(zc, d_in=FAKE_IN, n=1000, plan=PLAN, flags=0, d_out=FAKE_OU
     p = zc._plan(plan)
     p.flags = flags
     if cap is None:
-        cap = zc.zc_max_compressed_bytes(n) - 1  # one byte short: every other check must fire first
+        cap = zc.zc_compress_capacity(n) - 1  # one byte short: every other check must fire first
     return zc.raw_status("zc_compress", d_in, n, ctypes.byref(p), d_out, cap, d_bytes, 0)
 
 
@@ -189,7 +196,7 @@ def test_batch_host_errors(zc):
     big, _ = zc.make_enc_segs([(FAKE_IN, 10, PLAN, FAKE_OUT, 1, 0)] * 65)
     assert zc.raw_status("zc_compress_batch", big, 65, 0) == zc.ZC_ERR_INVALID_ARG
     # one bad segment among good ones rejects the whole batch before any launch
-    cap = zc.zc_max_compressed_bytes(10)
+    cap = zc.zc_compress_capacity(10)
     arr, k = zc.make_enc_segs([(FAKE_IN, 10, PLAN, FAKE_OUT, cap, 0),
                                (FAKE_IN, 10, PLAN, FAKE_OUT + (1 << 20), cap - 8, 0)])
     assert zc.raw_status("zc_compress_batch", arr, k, 0) == zc.ZC_ERR_CAPACITY
@@ -197,6 +204,31 @@ def test_batch_host_errors(zc):
     assert zc.raw_status("zc_decompress_batch", darr, 0, 0) == zc.ZC_ERR_INVALID_ARG
     dbig, _ = zc.make_dec_segs([(FAKE_OUT, 1 << 20, 10, FAKE_IN, 0)] * 65)
     assert zc.raw_status("zc_decompress_batch", dbig, 65, 0) == zc.ZC_ERR_INVALID_ARG
+
+
+def test_workspace_host_errors(zc):
+    """The _ws calls: a null or misaligned workspace, one too small (by a byte,
+    or for a batch, short of the sum over its segments), and an output buffer
+    short of the stream bound are rejected before any launch; the stream bound
+    alone is enough output capacity."""
+    n = 1000
+    cap = zc.zc_max_compressed_bytes(n)
+    wsb = zc.zc_compress_workspace_bytes(n)
+    p = zc._plan(PLAN)
+    WS = 0x7F2000000000
+    st = lambda *a: zc.raw_status("zc_compress_ws", *a)
+    assert st(FAKE_IN, n, ctypes.byref(p), FAKE_OUT, cap, 0, 0, wsb, 0) == zc.ZC_ERR_INVALID_ARG
+    assert st(FAKE_IN, n, ctypes.byref(p), FAKE_OUT, cap, 0, WS + 128, wsb, 0) == zc.ZC_ERR_MISALIGNED
+    assert st(FAKE_IN, n, ctypes.byref(p), FAKE_OUT, cap, 0, WS, wsb - 1, 0) == zc.ZC_ERR_CAPACITY
+    assert st(FAKE_IN, n, ctypes.byref(p), FAKE_OUT, cap - 1, 0, WS, wsb, 0) == zc.ZC_ERR_CAPACITY
+    assert st(FAKE_IN + 2, n, ctypes.byref(p), FAKE_OUT, cap, 0, WS, wsb, 0) == zc.ZC_ERR_MISALIGNED
+    arr, k = zc.make_enc_segs([(FAKE_IN, n, PLAN, FAKE_OUT, cap, 0), (FAKE_IN, 5000, PLAN, FAKE_OUT + (1 << 20),
+                                                                      zc.zc_max_compressed_bytes(5000), 0)])
+    need = wsb + zc.zc_compress_workspace_bytes(5000)
+    assert zc.raw_status("zc_compress_batch_ws", arr, k, WS, need - 256, 0) == zc.ZC_ERR_CAPACITY
+    assert zc.raw_status("zc_compress_batch_ws", arr, k, 0, need, 0) == zc.ZC_ERR_INVALID_ARG
+    # without a workspace the same output buffers are too small (the scratch goes behind the stream)
+    assert zc.raw_status("zc_compress_batch", arr, k, 0) == zc.ZC_ERR_CAPACITY
 
 
 def test_decompress_host_errors(zc):
