@@ -52,9 +52,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["lossless_bf16_exponent_amd/csrc/zc_codec.hip", "lossless_bf16_exponent_amd/csrc/zc_lane.h",
-                  "lossless_bf16_exponent_amd/csrc/zc_format.h", "lossless_bf16_exponent_amd/csrc/zc_grid.h"]
-STATS_SOURCES = ["lossless_bf16_exponent_amd/csrc/zc_stats.hip"]
+_CSRC = "lossless_bf16_exponent_amd/csrc/"
+_COMMON = [_CSRC + f for f in ("zc_device.h", "zc_lane.h", "zc_format.h")]
+# the sources each call's kernels are built from: a counter summary of a call
+# is used only while these are unchanged
+CALL_SOURCES = {"compress": [_CSRC + "zc_compress.hip", _CSRC + "zc_grid.h"] + _COMMON,
+                "decompress": [_CSRC + "zc_decode.hip"] + _COMMON,
+                "reduce": [_CSRC + "zc_reduce.hip"] + _COMMON,
+                "stats": [_CSRC + "zc_stats.hip"] + _COMMON}
 MALL_BYTES = 256 << 20
 GROUPS = 10  # timing groups per call kind in the per-workload records
 BOX_CORES = 16  # the host cores of one GPU's share on the MI355X boxes
@@ -64,11 +69,11 @@ def log(msg: str) -> None:
     print("# " + msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(sources=None) -> str:
-    """Hash of the codec kernel sources (or of `sources`): a counter summary
-    is used only while the kernels it measured are unchanged."""
+def kernel_source_hash(call: str) -> str:
+    """Hash of the sources of one call's kernels (CALL_SOURCES): a counter
+    summary is used only while the kernels it measured are unchanged."""
     h = hashlib.sha256()
-    for rel in (KERNEL_SOURCES if sources is None else sources):
+    for rel in CALL_SOURCES[call]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -86,7 +91,7 @@ def load_traffic(call: str, workload: str):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_sha") != kernel_source_hash():
+    if vals.get("kernel_sha") != kernel_source_hash(call):
         return None
     try:
         return int(float(vals["fetch_bytes"]) + float(vals["write_bytes"]))
@@ -205,6 +210,10 @@ def measure_workload(zc, w, steps: int, warmup: int, cold: bool = False) -> dict
             call()
         rec[name] = summary(timed_groups(call, stream, GROUPS, per), alg, n)
     rec["decompress_checked"]["kernels"] = "zero_kernel (status words) + decode_kernel"
+    for name in ("compress", "decompress"):
+        t = load_traffic(name, w.name)  # counter bytes per call, when profiled for the current kernels
+        rec[name]["traffic"] = t
+        rec[name]["traffic_over_algorithmic"] = round(t / alg, 4) if t else None
     if not torch.equal(r.dec, r.x):
         raise RuntimeError("decoded buffer differs after timing on %s" % w.name)
     if cold:
@@ -468,6 +477,8 @@ def reduce_measurement(zc, steps: int) -> dict:
     alg = sum(totals) + 4 * n  # the peer streams and the local share read, the result written
     us = timed_groups(call, stream, GROUPS, max(1, steps // GROUPS))
     rec = summary(us, alg, n)
+    t = load_traffic("reduce", "shard-32M-7peers")
+    rec.update({"traffic": t, "traffic_over_algorithmic": round(t / alg, 4) if t else None})
     rec.update({"shard_values": n, "peers": peers, "local": True, "warmup_calls": REDUCE_WARMUP_CALLS,
                 "uncompressed_gbps": round(2.0 * n * (peers + 1) / (rec["us"] * 1e-6) / 1e9, 1),
                 "algorithmic_bytes": int(alg), "achieved_gbps": round(alg / (rec["us"] * 1e-6) / 1e9, 1),
@@ -690,7 +701,7 @@ def main() -> int:
                      "traffic": traffic, "call": dom, "kernels": dom_kernels, "algorithmic_bytes": int(alg),
                      "avg_launch_us": round(dom_ms * 1e3, 2)},
         "gpu_step_ms": round(gpu_step_ms, 4),
-        "kernel_sha": kernel_source_hash(),
+        "kernel_sha": {c: kernel_source_hash(c) for c in CALL_SOURCES},
     }
     if not args.only_headline:
         rec["plan_variants"] = stats_measurement(zc, x_keep, [seg.x.size for seg in w.segments], args.steps)

@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libzc.so")
-SOURCES = [os.path.join(CSRC, "zc_codec.hip"), os.path.join(CSRC, "zc_stats.hip"), os.path.join(CSRC, "zc_host.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("zc_compress.hip", "zc_decode.hip", "zc_reduce.hip", "zc_stats.hip",
+                                            "zc_host.cpp")]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions stay disabled for every HIP translation unit.

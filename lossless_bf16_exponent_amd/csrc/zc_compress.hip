@@ -1,4 +1,5 @@
-// HIP kernels and C ABI of the BF16 exponent-coding codec for MI355X (gfx950).
+// Compress kernels and their C ABI: the BF16 exponent-coding codec for MI355X
+// (gfx950).
 //
 // Method: the ZipCCL explainer pages ("ZipCCL: Efficient Lossless Data
 // Compression of Communication Collectives for Accelerating LLM Training"),
@@ -18,7 +19,8 @@
 //   * zero-point bytes are placed by an exclusive scan across the tensor.  In
 //     a launch longer than the device holds at once, encoder blocks never wait:
 //     each leaves its zero-point count (a span word) and its zero-point bytes
-//     staged in the output's scratch tail.  Finalize blocks of the same launch,
+//     staged in the segment's scratch (in the call's workspace, or behind the
+//     stream in the output buffer).  Finalize blocks of the same launch,
 //     placed about a device's worth of blocks behind the spans they complete,
 //     sum the counts through a hierarchy of run and chunk words, fill the
 //     table and move the staged bytes to their place.  A launch the device
@@ -31,21 +33,20 @@
 //     other block of the segment has passed its waits (zc_grid.h places the
 //     roles; the scratch words are described below, with the reasons the
 //     handshakes are device-scope accesses and not release/acquire pairs);
-//   * the decoder needs no scan across tiles: the table of zero-point counts
-//     per 4096-element group gives every tile its slice of the zero-point
-//     array, which is staged in LDS and gathered by rank.
+//   * under the raw fallback the first launch guesses each long segment's
+//     form from a sample and a second launch completes wrong guesses.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
 #include <chrono>
-#include <cmath>
 #include <cstring>
 #include <random>
 
 #include "zc.h"
+#include "zc_device.h"
 #include "zc_format.h"
-#include "zc_host.h"
 #include "zc_grid.h"
+#include "zc_host.h"
 #include "zc_lane.h"
 
 namespace zc {
@@ -98,193 +99,9 @@ __device__ __forceinline__ uint8_t *seg_scratch(const EncArgs &a, const EncSeg &
     return a.ws ? a.ws + 256ull * sg.ws_off : sg.out + layout_for(sg.n).off_scratch;
 }
 
-struct DecSeg {
-    const uint8_t *in;
-    uint16_t *out;
-    int32_t *status;
-    uint64_t in_bytes;
-    uint32_t n;
-    uint32_t tile_begin;  // first flat block of this segment
-};
-static_assert(sizeof(DecSeg) == 40, "compact kernel arguments");
-
-struct DecArgs {
-    uint32_t k;
-    uint32_t total_tiles;
-    DecSeg seg[ZC_MAX_BATCH];
-    uint32_t tile_begin[ZC_MAX_BATCH];  // seg[i].tile_begin, contiguous for the block -> segment lookup
-};
-static_assert(sizeof(DecArgs) + 256 <= 4096, "decompress arguments fit the kernarg segment");
-
-// Local reduction of the reduce-scatter path: k streams of the same n values.
-struct RedStream {
-    const uint8_t *in;
-    uint64_t in_bytes;
-};
-
-struct RedArgs {
-    uint32_t k;
-    uint32_t n;
-    const uint16_t *local;  // nullable
-    uint16_t *out;
-    int32_t *status;        // nullable
-    RedStream s[ZC_MAX_BATCH];
-};
-
-struct ZeroRegion {
-    uint32_t *ptr;
-    uint64_t words;
-};
-
-struct ZeroArgs {
-    uint32_t count;
-    ZeroRegion r[ZC_MAX_BATCH];
-};
-
-
-
-// ---------------------------------------------------------------------------
-// streaming memory access: every codec byte is read once and written once,
-// so loads and stores carry the non-temporal hint (measured on MI355X: a
-// 128-bit copy moves 13 % more bytes per second with it)
-// ---------------------------------------------------------------------------
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2a4 __attribute__((ext_vector_type(2), aligned(4)));  // 8 bytes, dword-aligned
-typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));  // 16 bytes, dword-aligned
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint4 load_stream16(const void *p) {
-    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    return make_uint4(t.x, t.y, t.z, t.w);
-}
-__device__ __forceinline__ uint2 load_stream8(const void *p) {
-    const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
-    return make_uint2(t.x, t.y);
-}
-__device__ __forceinline__ uint32_t load_stream4(const void *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
-}
-__device__ __forceinline__ void store_stream16(void *p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-    const u32x4 t = {a, b, c, d};
-    __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(p));
-}
-__device__ __forceinline__ void store_stream8(void *p, uint32_t a, uint32_t b) {
-    const u32x2 t = {a, b};
-    __builtin_nontemporal_store(t, reinterpret_cast<u32x2 *>(p));
-}
-__device__ __forceinline__ void store_stream4(void *p, uint32_t a) {
-    __builtin_nontemporal_store(a, reinterpret_cast<uint32_t *>(p));
-}
-
-// ---------------------------------------------------------------------------
-// wave helpers
-// ---------------------------------------------------------------------------
-
-// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS):
-// shifts of 1, 2, 4 and 8 lanes inside each 16-lane row, then the last lane
-// of row 0 / row 2 is broadcast into rows 1 / 3 and lane 31 into rows 2 and 3.
-// A lane whose source lies outside its row keeps the 0 passed as `old`.
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
-    return v;
-}
-
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(v), kWave - 1);
-}
-
-// How many of v[1 .. count) are at or below flat, for non-decreasing v: the
-// index of the last entry at or below it.  Lane i reads entries 1 + i,
-// 65 + i, ... with one vector load per 64 entries and a ballot counts the
-// hits, so the lookup costs one round trip whatever the count (a loop of
-// dependent reads, one per entry or per halving, cost a decoder block 32 of
-// them at its start, 7 % of the bucket's decompress time).  All lanes of the
-// wave must be active.
-template <uint32_t kEntries>
-__device__ __forceinline__ uint32_t count_at_or_below(const uint32_t *v, uint32_t count, uint32_t flat,
-                                                      uint32_t mask = ~0u) {
-    const uint32_t lane = __lane_id();
-    uint32_t total = 0;
-#pragma unroll
-    for (uint32_t c = 0; c < (kEntries - 1 + kWave - 1) / kWave; ++c) {
-        const uint32_t i = 1u + (uint32_t)kWave * c + lane;
-        const bool hit = i < count && (v[i] & mask) <= flat;  // (read only below count: inside the array)
-        total += (uint32_t)__builtin_popcountll(__ballot(hit));
-    }
-    return total;
-}
-
 // The piece holding grid block `flat` (piece words keep the block in their low 24 bits).
 __device__ __forceinline__ uint32_t find_piece(const EncArgs &a, uint32_t flat) {
     return count_at_or_below<kMaxPieces + 1>(a.piece, a.pieces, flat, kBlockMask);
-}
-
-// The decode segment holding grid block `flat`.
-__device__ __forceinline__ uint32_t find_segment_dec(const DecArgs &a, uint32_t flat) {
-    return count_at_or_below<ZC_MAX_BATCH>(a.tile_begin, a.k, flat);
-}
-
-// Zero-point counts of the four steps of a lane -> tile-local ranks of the
-// lane's first zero-point value in each step, plus the wave and tile totals.
-// Order inside a tile: wave-major, then step, then lane, then value.
-struct TileCounts {
-    uint32_t rank[kSteps];
-    uint32_t tile_total;
-    uint32_t first_group;  // zero-points among the tile's first 4096 values (waves 0, 1)
-};
-
-__device__ __forceinline__ TileCounts count_tile(const uint32_t (&zmask)[kSteps], int lane, int wave,
-                                                 uint32_t *s_wave_total) {
-    static_assert(kSteps == 4, "two packed 16-bit scans cover four steps");
-    uint32_t c[kSteps];
-#pragma unroll
-    for (int u = 0; u < kSteps; ++u) c[u] = __builtin_popcount(zmask[u]);
-    const uint32_t a = c[0] | (c[1] << 16), b = c[2] | (c[3] << 16);
-    const uint32_t ai = wave_inclusive_scan(a), bi = wave_inclusive_scan(b);
-    const uint32_t at = (uint32_t)__builtin_amdgcn_readlane((int)ai, kWave - 1);
-    const uint32_t bt = (uint32_t)__builtin_amdgcn_readlane((int)bi, kWave - 1);
-    const uint32_t ae = ai - a, be = bi - b;
-    const uint32_t tot[kSteps] = {at & 0xFFFFu, at >> 16, bt & 0xFFFFu, bt >> 16};
-    const uint32_t ex[kSteps] = {ae & 0xFFFFu, ae >> 16, be & 0xFFFFu, be >> 16};
-    if (lane == 0) s_wave_total[wave] = tot[0] + tot[1] + tot[2] + tot[3];
-    __syncthreads();
-    uint32_t wave_off = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        const uint32_t v = s_wave_total[w];
-        wave_off += (w < wave) ? v : 0u;
-        total += v;
-    }
-    TileCounts r;
-    uint32_t run = wave_off;
-#pragma unroll
-    for (int u = 0; u < kSteps; ++u) {
-        r.rank[u] = run + ex[u];
-        run += tot[u];
-    }
-    r.tile_total = total;
-    r.first_group = s_wave_total[0] + s_wave_total[1];
-    static_assert(kGroup == 2 * kWave * 8 * kSteps, "a group is the span of two waves");
-    return r;
-}
-
-// ---------------------------------------------------------------------------
-// small fill kernel: look-back scratch before an encode, status words before a decode
-// ---------------------------------------------------------------------------
-
-__global__ __launch_bounds__(256) void zero_kernel(ZeroArgs a) {
-    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    for (uint32_t i = 0; i < a.count; ++i) {
-        uint32_t *p = a.r[i].ptr;
-        const uint64_t words = a.r[i].words;
-        for (uint64_t w = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; w < words; w += stride) p[w] = 0;
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -522,8 +339,6 @@ __device__ __forceinline__ void write_span_group(uint8_t *zp, uint64_t dst_off, 
     }
 }
 
-typedef __attribute__((address_space(1))) void global_void;
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Chunks c0, c0 + stride, ... of kWave units each (the waves of a block share
 // a span's chunks, so one large span is not left to a single wave).
@@ -1415,788 +1230,13 @@ __global__ __launch_bounds__(kThreads) void compress_second_kernel(EncArgs args)
     }
 }
 
-// ---------------------------------------------------------------------------
-// decoder
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ uint32_t ld_u32(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
-
-// Header of a stream of n values, coded or raw: all 32 words load at once
-// (uniform, scalar loads) and every field is tested without short-circuiting,
-// so that no test waits for the one before it (a reduce block checks k headers
-// up front).  On success `raw` tells the mode; for a coded stream tbl_lo/tbl_hi
-// hold the code -> exponent table for v_perm (byte 0, code 000, is a
-// placeholder) and E the zero-point count.  A raw stream (the fallback) is the
-// header and the n values unchanged: total_bytes = 128 + 2n; its exps and E
-// describe the coded form that was not kept.
-typedef __attribute__((address_space(4))) const uint32_t const_u32;
-
-__device__ __forceinline__ bool header_ok(const uint8_t *in, uint64_t in_bytes, uint64_t n, const Layout &L,
-                                          uint32_t &tbl_lo, uint32_t &tbl_hi, uint64_t &E, bool &raw) {
-    // constant address space: scalar loads, which never wait behind the
-    // vector loads in flight
-    const_u32 *h = (const_u32 *)in;
-    uint32_t w[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) w[i] = h[i];
-    uint32_t pad = 0;
-#pragma unroll
-    for (int i = 12; i < 32; ++i) pad |= w[i];
-    E = w[8] | ((uint64_t)w[9] << 32);
-    const uint64_t total = w[10] | ((uint64_t)w[11] << 32);
-    const uint32_t h6 = w[6], h7 = w[7];
-    const uint32_t e[7] = {h6 & 0xFFu, (h6 >> 8) & 0xFFu, (h6 >> 16) & 0xFFu, h6 >> 24,
-                           h7 & 0xFFu, (h7 >> 8) & 0xFFu, (h7 >> 16) & 0xFFu};
-    const uint32_t mode = h7 >> 24;
-    raw = mode == kModeRaw;
-    const bool sized = ((mode == kModeCoded) & (total == L.off_zp + E)) | (raw & (total == kHeaderBytes + 2 * n));
-    bool ok = (w[0] == kMagic) & (w[1] == ((uint32_t)kVersion | (kHeaderBytes << 16))) & (w[2] == (uint32_t)n) &
-              (w[3] == (uint32_t)(n >> 32)) & (w[4] == kGroup) & (w[5] == (uint32_t)L.groups) & sized &
-              (E <= n) & (total <= in_bytes) & (pad == 0u);
-#pragma unroll
-    for (int k = 1; k < 7; ++k) ok = ok & (e[k] > e[k - 1]);
-    tbl_lo = h6 << 8;
-    tbl_hi = (h6 >> 24) | (h7 << 8);
-    return ok;
-}
-
-__device__ __forceinline__ bool raw_header_ok(const uint8_t *in, uint64_t in_bytes, uint64_t n, const Layout &L) {
-    uint32_t lo, hi;
-    uint64_t E;
-    bool raw;
-    return header_ok(in, in_bytes, n, L, lo, hi, E, raw) & raw;
-}
-
-// Values [v0, v1) of a raw stream to out (v0 a multiple of 8; the whole block).
-__device__ __forceinline__ void copy_raw(const uint8_t *in, uint16_t *out, uint64_t v0, uint64_t v1) {
-    const uint16_t *src = reinterpret_cast<const uint16_t *>(in + kHeaderBytes);
-    const uint64_t full = v0 + ((v1 - v0) & ~uint64_t(7));
-    for (uint64_t v = v0 + 8u * threadIdx.x; v < full; v += 8u * kThreads) {
-        const uint4 q = load_stream16(src + v);
-        store_stream16(out + v, q.x, q.y, q.z, q.w);
-    }
-    for (uint64_t v = full + threadIdx.x; v < v1; v += kThreads) out[v] = src[v];
-}
-
-// Gather of the zero-point bytes of an 8-value step without a loop: the
-// step's zero-points are the bytes [r, r + popcount(m)) of the slice, in
-// order.  sel[m] holds, for each of the 8 positions, the index among the set
-// bits of m (a v_perm selector into those bytes) or 0x0C (a zero byte) where
-// the bit is clear; the same selector applied to all-ones bytes gives the
-// byte mask of the positions to replace.
-__device__ __forceinline__ void zp_selectors(uint2 *sel) {  // 256 entries, filled by the block
-    for (uint32_t m = threadIdx.x; m < 256; m += kThreads) {
-        uint32_t lo = 0, hi = 0, idx = 0;
-        for (uint32_t p = 0; p < 8; ++p) {
-            const uint32_t b = (m >> p) & 1u ? idx++ : 0x0Cu;
-            if (p < 4)
-                lo |= b << (8 * p);
-            else
-                hi |= b << (8 * (p - 4));
-        }
-        sel[m] = make_uint2(lo, hi);
-    }
-}
-
-__device__ __forceinline__ void put_zero_points(uint32_t &e_lo, uint32_t &e_hi, uint32_t m, uint32_t r,
-                                                const uint32_t *zw, const uint2 *sel) {
-    const uint32_t d0 = zw[r / 4], d1 = zw[r / 4 + 1], d2 = zw[r / 4 + 2];
-    const uint32_t sh = r & 3u;
-    const uint32_t z_lo = __builtin_amdgcn_alignbyte(d1, d0, sh), z_hi = __builtin_amdgcn_alignbyte(d2, d1, sh);
-    const uint2 s = sel[m];
-    e_lo = bfi(perm(~0u, ~0u, s.x), perm(z_hi, z_lo, s.x), e_lo);
-    e_hi = bfi(perm(~0u, ~0u, s.y), perm(z_hi, z_lo, s.y), e_hi);
-}
-
-// A block decodes kDecSubTiles consecutive tiles (its span).  Every plane and
-// sign+mantissa load of the span, and the span's zero-point table entries,
-// are issued before the header is checked (all of them lie inside the n-value
-// layout, which the host has checked against in_bytes); the zero-point slice
-// is then staged in LDS with dword loads and gathered by rank.
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
-    __shared__ uint32_t s_planes[kTile / 8];
-    __shared__ uint32_t s_zp32[kDecSpan / 4 + 3];  // the span's zero-point bytes from a dword-aligned start
-    __shared__ uint32_t s_wave_total[2][kWaves];    // (+ slack for the 3-dword reads of the gather)
-    __shared__ uint2 s_sel[256];
-
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const uint32_t flat = blockIdx.x;
-    const uint32_t s = find_segment_dec(args, flat);
-    const DecSeg &sg = args.seg[s];
-    const uint32_t b = flat - sg.tile_begin;
-    const uint64_t n = sg.n;
-    const Layout L = layout_for(n);
-    const uint8_t *const in = sg.in;
-    const uint64_t span0 = (uint64_t)b * kDecSpan;
-
-    // ---- data loads of the whole span
-    uint32_t pw[kDecSubTiles][3];
-    uint32_t sm[kDecSubTiles][kSteps][2], vmask[kDecSubTiles][kSteps];
-#pragma unroll
-    for (int sub = 0; sub < kDecSubTiles; ++sub) {
-        const uint64_t tile0 = span0 + (uint64_t)sub * kTile;
-        pw[sub][0] = pw[sub][1] = pw[sub][2] = 0;
-        if (tile0 + 32u * (uint32_t)tid < n) {
-            const uint64_t off = tile0 / 8 + 4u * (uint32_t)tid;
-            pw[sub][0] = load_stream4(in + L.off_p0 + off);
-            pw[sub][1] = load_stream4(in + L.off_p1 + off);
-            pw[sub][2] = load_stream4(in + L.off_p2 + off);
-        }
-#pragma unroll
-        for (int u = 0; u < kSteps; ++u) {
-            const uint64_t base = tile0 + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
-            sm[sub][u][0] = sm[sub][u][1] = 0;
-            vmask[sub][u] = 0;
-            if (base < n) {
-                const uint2 v = load_stream8(in + kHeaderBytes + base);
-                sm[sub][u][0] = v.x;
-                sm[sub][u][1] = v.y;
-                vmask[sub][u] = base + 8 <= n ? 0xFFu : (1u << (uint32_t)(n - base)) - 1u;
-            }
-        }
-    }
-
-    // ---- the span's zero-point table entries
-    const uint32_t *tab = reinterpret_cast<const uint32_t *>(in + L.off_tab);
-    uint32_t z[kDecGroups + 1];
-#pragma unroll
-    for (int j = 0; j <= kDecGroups; ++j) {
-        const uint64_t g = (uint64_t)b * kDecGroups + j;
-        z[j] = tab[g <= L.groups ? g : L.groups];
-    }
-
-    // ---- header: every block checks it, so a bad header stops all of them.
-    // (Tested field by field: this keeps the table entries above on scalar
-    // loads issued with the data loads; the checks overlap those loads.)
-    const uint32_t h6 = ld_u32(in + 24), h7 = ld_u32(in + 28);
-    const uint64_t E = ld_u32(in + 32) | ((uint64_t)ld_u32(in + 36) << 32);
-    const uint64_t total = ld_u32(in + 40) | ((uint64_t)ld_u32(in + 44) << 32);
-    bool ok = ld_u32(in) == kMagic && ld_u32(in + 4) == ((uint32_t)kVersion | (kHeaderBytes << 16)) &&
-              ld_u32(in + 8) == (uint32_t)n && ld_u32(in + 12) == (uint32_t)(n >> 32) && ld_u32(in + 16) == kGroup &&
-              ld_u32(in + 20) == (uint32_t)L.groups && (h7 >> 24) == 0u && E <= n && total == L.off_zp + E &&
-              total <= sg.in_bytes;
-    {
-        const uint32_t e[7] = {h6 & 0xFFu, (h6 >> 8) & 0xFFu, (h6 >> 16) & 0xFFu, h6 >> 24,
-                               h7 & 0xFFu, (h7 >> 8) & 0xFFu, (h7 >> 16) & 0xFFu};
-#pragma unroll
-        for (int k = 1; k < 7; ++k) ok = ok && e[k] > e[k - 1];
-#pragma unroll
-        for (int w = 12; w < 32; ++w) ok = ok && ld_u32(in + 4 * w) == 0u;
-    }
-    if (!ok) {
-        // not a coded stream: the raw fallback form, or corrupt
-        if (raw_header_ok(in, sg.in_bytes, n, L)) {
-            copy_raw(in, sg.out, span0, min(span0 + kDecSpan, n));
-            return;
-        }
-        if (tid == 0 && sg.status) *sg.status = ZC_ERR_CORRUPT;
-        return;
-    }
-    // code -> exponent table for v_perm: byte 0 (code 000) is a placeholder
-    const uint32_t tbl_lo = h6 << 8, tbl_hi = (h6 >> 24) | (h7 << 8);
-
-    // ---- table consistency; clamp so that every read stays inside the stream
-    const bool last = (b == dec_blocks(n) - 1);
-    bool bad = (b == 0 && z[0] != 0) || (last && z[kDecGroups] != E);
-#pragma unroll
-    for (int j = 0; j <= kDecGroups; ++j) {
-        const uint32_t lo = j ? z[j - 1] : 0u;
-        if (z[j] < lo || z[j] > E) bad = true;
-        z[j] = z[j] < lo ? lo : (z[j] > E ? (uint32_t)E : z[j]);
-    }
-    if (z[kDecGroups] - z[0] > kDecSpan) {
-        bad = true;
-#pragma unroll
-        for (int j = 0; j <= kDecGroups; ++j) z[j] = z[j] - z[0] > kDecSpan ? z[0] + kDecSpan : z[j];
-    }
-
-    // ---- stage the span's zero-point bytes: stream bytes [A0, A1)
-    const uint64_t A0 = L.off_zp + z[0], A1 = L.off_zp + z[kDecGroups];
-    const uint64_t a0 = A0 & ~uint64_t(3), a1 = A1 & ~uint64_t(3);
-    const uint32_t shift = (uint32_t)(A0 & 3u);
-    const uint32_t ndw = (uint32_t)((a1 - a0) / 4);
-    for (uint32_t i = tid; i < ndw; i += kThreads) s_zp32[i] = ld_u32(in + a0 + 4u * i);
-    if (tid == 0 && A1 > a1) {
-        uint32_t w = 0;
-        for (uint32_t i = 0; i < (uint32_t)(A1 - a1); ++i) w |= (uint32_t)in[a1 + i] << (8 * i);
-        s_zp32[ndw] = w;
-    }
-    const uint32_t zspan = z[kDecGroups] - z[0];
-    zp_selectors(s_sel);  // visible after the first sub-tile's barrier
-
-#pragma unroll
-    for (int sub = 0; sub < kDecSubTiles; ++sub) {
-        const uint64_t tile0 = span0 + (uint64_t)sub * kTile;
-        {
-            const uint32_t p0 = pw[sub][0], p1 = pw[sub][1], p2 = pw[sub][2];
-            const uint32_t lo = perm(p1, p0, 0x05010400u), hi = perm(p1, p0, 0x07030602u);
-            uint4 q;
-            q.x = perm(p2, lo, 0x0C040100u);
-            q.y = perm(p2, lo, 0x0C050302u);
-            q.z = perm(p2, hi, 0x0C060100u);
-            q.w = perm(p2, hi, 0x0C070302u);
-            reinterpret_cast<uint4 *>(s_planes)[tid] = q;
-        }
-        __syncthreads();  // s_planes (and, for the first sub-tile, s_zp32)
-
-        uint32_t e[kSteps][2], zmask[kSteps];
-#pragma unroll
-        for (int u = 0; u < kSteps; ++u) {
-            const uint32_t planes = s_planes[(wave * kSteps + u) * kWave + lane] & 0x00FFFFFFu;
-            uint32_t c_lo, c_hi;
-            planes_to_codes(planes, c_lo, c_hi);
-            e[u][0] = perm(tbl_hi, tbl_lo, c_lo);
-            e[u][1] = perm(tbl_hi, tbl_lo, c_hi);
-            zmask[u] = zero_point_mask(planes) & vmask[sub][u];
-        }
-        const TileCounts tc = count_tile(zmask, lane, wave, s_wave_total[sub & 1]);
-        const uint32_t zb = z[2 * sub], zm = z[2 * sub + 1], ze = z[2 * sub + 2];
-        if (tc.tile_total != ze - zb || tc.first_group != zm - zb) bad = true;
-
-        const uint32_t rank0 = zb - z[0];
-#pragma unroll
-        for (int u = 0; u < kSteps; ++u) {
-            // slice byte j sits at byte shift + j of s_zp32; a rank past the
-            // slice (a corrupt table, already flagged) reads the slack instead
-            const uint32_t rk = rank0 + tc.rank[u];
-            put_zero_points(e[u][0], e[u][1], zmask[u], shift + (rk <= zspan ? rk : zspan), s_zp32, s_sel);
-            const uint64_t base = tile0 + 512u * (uint32_t)(wave * kSteps + u) + 8u * (uint32_t)lane;
-            uint32_t o0, o1, o2, o3;
-            rebuild4(sm[sub][u][0], e[u][0], o0, o1);
-            rebuild4(sm[sub][u][1], e[u][1], o2, o3);
-            if (vmask[sub][u] == 0xFFu) {
-                store_stream16(sg.out + base, o0, o1, o2, o3);
-            } else if (vmask[sub][u]) {
-                const uint32_t w4[4] = {o0, o1, o2, o3};
-                for (uint32_t i = 0; base + i < n; ++i) sg.out[base + i] = (uint16_t)(w4[i / 2] >> (16 * (i % 2)));
-            }
-        }
-        if (sub + 1 < kDecSubTiles) __syncthreads();  // s_planes is rewritten by the next sub-tile
-    }
-    if (bad && tid == 0 && sg.status) atomicMax(sg.status, (int32_t)ZC_ERR_CORRUPT);
-}
-
-// Segments whose buffer is shorter than the coded layout of n values can only
-// hold a raw stream: checked and copied without any read at a coded offset.
-__global__ __launch_bounds__(kThreads) void decode_raw_kernel(DecArgs args) {
-    const uint32_t flat = blockIdx.x;
-    const uint32_t s = find_segment_dec(args, flat);
-    const DecSeg &sg = args.seg[s];
-    const uint64_t n = sg.n;
-    const Layout L = layout_for(n);
-    const uint64_t span0 = (uint64_t)(flat - sg.tile_begin) * kDecSpan;
-    if (!raw_header_ok(sg.in, sg.in_bytes, n, L)) {
-        if (threadIdx.x == 0 && sg.status) *sg.status = ZC_ERR_CORRUPT;
-        return;
-    }
-    copy_raw(sg.in, sg.out, span0, min(span0 + kDecSpan, n));
-}
-
-// ---------------------------------------------------------------------------
-// local reduction of the reduce-scatter path (section 2.D): decode k streams
-// of the same n values and add them
-// ---------------------------------------------------------------------------
-
-// BF16 value pair of a dword -> two floats (exact).
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// Nearest BF16 to a float, ties to even (the bias 0x7FFF plus the lowest kept
-// bit carries into the kept half exactly when the dropped half is above one
-// half, or equal to it with an odd kept half); a NaN gives 0x7FC0.
-__device__ __forceinline__ uint32_t float_to_bf16(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (f != f) ? 0x7FC0u : ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
-// Work split.  A 4096-value tile (one zero-point group) is decoded by two
-// waves, one per 2048-value half, each lane owning 32 consecutive values; a
-// block holds two tiles.  The waves do not wait for each other while they
-// work: each keeps its lanes' sign+mantissa and plane words in registers (the
-// next stream's in flight while the current one is decoded) and stages its
-// own zero-point slice in LDS.  Half 0's zero-points start at the group's
-// table entry and half 1's end at the next group's, so neither needs the
-// other's count.  At the end the two halves of a tile compare, stream by
-// stream, where the first one's zero-points end and the second one's begin: a
-// table that disagrees with the planes sets the status.
-constexpr uint32_t kRedTile = 4096;
-static_assert(kRedTile == kGroup, "a tile is one zero-point group");
-constexpr uint32_t kRedHalf = kRedTile / 2;
-static_assert(kRedHalf / kWave == 32, "a lane's zero-point flags fill one dword");
-constexpr uint32_t kRedTilesPerBlock = kWaves / 2;
-// Zero-point bytes a wave stages per stream (a quarter of its tile's values).
-// A half with more zero-points than that reads them from memory one by one.
-constexpr uint32_t kRedSliceCap = 1024;
-// the staged bytes from a dword-aligned start (up to 3 bytes of lead-in), and
-// the gather's 3-dword reads at the last zero-point
-constexpr uint32_t kRedSliceWords = 260;
-static_assert(kRedSliceWords >= (kRedSliceCap + 3) / 4 + 3, "room for the gather's reads");
-
-// Per-stream facts of a checked header, kept in LDS: E (two words), the code
-// table (two words).  Bit 31 of E's high word marks a raw stream.
-struct RedHdr {
-    uint32_t e_lo, e_hi, tbl_lo, tbl_hi;
-};
-
-struct RedShared {
-    uint32_t slice[kWaves][2][kRedSliceWords];  // before the first stream: every header's 32 words
-    uint32_t edge[kWaves][ZC_MAX_BATCH];        // per stream: where half 0's zero-points end / half 1's begin
-    RedHdr hdr[ZC_MAX_BATCH];
-    uint2 sel[256];
-};
-static_assert(sizeof(RedShared::slice) >= 4u * 32u * ZC_MAX_BATCH, "room for every header");
-
-// Every stream's header at once: the 32 words of each go to LDS with one
-// vector load per thread and word (all in flight together), then thread s
-// checks stream s.  Returns the block-wide verdict; hdr[s] receives stream s's
-// facts.  `words` (k * 32 words) may alias memory that is not yet in use.
-__device__ __forceinline__ bool red_check_headers(const RedArgs &args, uint64_t n, const Layout &L, uint32_t *words,
-                                                  RedHdr *hdr) {
-    const uint32_t k = args.k, tid = threadIdx.x;
-    for (uint32_t i = tid; i < 32u * k; i += kThreads)
-        words[i] = *reinterpret_cast<const uint32_t *>(args.s[i / 32].in + 4u * (i % 32));
-    __syncthreads();
-    bool ok = true;
-    if (tid < k) {
-        const uint32_t *w = words + 32u * tid;
-        uint32_t pad = 0;
-        for (int i = 12; i < 32; ++i) pad |= w[i];
-        const uint64_t E = w[8] | ((uint64_t)w[9] << 32);
-        const uint64_t total = w[10] | ((uint64_t)w[11] << 32);
-        const uint32_t h6 = w[6], h7 = w[7];
-        const uint32_t mode = h7 >> 24;
-        const bool raw = mode == kModeRaw;
-        const bool sized = ((mode == kModeCoded) & (total == L.off_zp + E)) | (raw & (total == kHeaderBytes + 2 * n));
-        ok = (w[0] == kMagic) & (w[1] == ((uint32_t)kVersion | (kHeaderBytes << 16))) & (w[2] == (uint32_t)n) &
-             (w[3] == (uint32_t)(n >> 32)) & (w[4] == kGroup) & (w[5] == (uint32_t)L.groups) & sized & (E <= n) &
-             (total <= args.s[tid].in_bytes) & (pad == 0u);
-        const uint32_t e[7] = {h6 & 0xFFu, (h6 >> 8) & 0xFFu, (h6 >> 16) & 0xFFu, h6 >> 24,
-                               h7 & 0xFFu, (h7 >> 8) & 0xFFu, (h7 >> 16) & 0xFFu};
-        for (int j = 1; j < 7; ++j) ok = ok & (e[j] > e[j - 1]);
-        RedHdr r;
-        r.e_lo = (uint32_t)E;
-        r.e_hi = (uint32_t)(E >> 32) | (raw ? 0x80000000u : 0u);
-        r.tbl_lo = h6 << 8;
-        r.tbl_hi = (h6 >> 24) | (h7 << 8);
-        hdr[tid] = r;
-    }
-    return __syncthreads_and(ok);
-}
-
-// Uniform per-stream facts of a checked header.  E <= n < 2^32.
-struct RedMeta {
-    const uint8_t *in;
-    uint64_t in_bytes;
-    uint32_t E;
-    uint32_t tbl_lo, tbl_hi;  // exponent of code c in byte c of {tbl_hi:tbl_lo} (byte 0 unused)
-    bool raw;
-};
-
-__device__ __forceinline__ RedMeta red_meta(const RedArgs &args, uint32_t s, const RedHdr *hdr) {
-    RedMeta m;
-    m.in = args.s[s].in;
-    m.in_bytes = args.s[s].in_bytes;
-    const uint4 h = *reinterpret_cast<const uint4 *>(hdr + s);
-    m.E = (uint32_t)__builtin_amdgcn_readfirstlane((int)h.x);
-    m.raw = ((uint32_t)__builtin_amdgcn_readfirstlane((int)h.y) >> 31) != 0u;
-    m.tbl_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)h.z);
-    m.tbl_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)h.w);
-    return m;
-}
-
-// s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
-// lgkmcnt 11:8): vmcnt(0), the others unconstrained.
-constexpr int kWaitVm0 = 0x0F70;
-
-// Wait for every load of the wave, direct-to-LDS ones included, as a compiler
-// barrier as well (inline assembly with a memory clobber): no LDS read moves
-// above it.  Used where the reads of LDS that such loads wrote do not depend
-// on any later load.
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Lanes of one wave exchanging data through LDS: the wave's LDS accesses
-// complete in order, so waiting for its own is enough; the memory clobber
-// keeps the compiler from moving accesses across (per lane, the addresses
-// written and read look unrelated).
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// Direct-to-LDS dword load, written as inline assembly so that the compiler
-// adds no waits of its own for it; the kernel waits with an explicit count.
-// The LDS address is the wave-uniform base in M0 plus 4 bytes per lane.
-__device__ __forceinline__ uint32_t lds_base(const void *lds) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds);
-}
-__device__ __forceinline__ void lds_load4(const void *src, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off nt" ::"s"(m0), "v"(src)
-                 : "memory", "m0");
-}
-
-// The lane's values: [v0, v0 + nv) inside the stream, nv = 0..32.
-struct RedLane {
-    uint64_t v0;
-    uint32_t nv;
-    uint32_t vmask;   // bit i: value v0 + i exists
-    uint32_t sm_off;  // byte offsets of its sign+mantissa bytes and plane words (0 past the end: always readable)
-    uint32_t pl_off;
-};
-
-// The lane's sign+mantissa bytes (32) and plane words (one per plane).
-struct RedData {
-    uint4 sm0, sm1;
-    uint32_t p0, p1, p2;
-};
-
-__device__ __forceinline__ void red_load(RedData &d, const RedMeta &m, const Layout &L, const RedLane &ln) {
-    const uint8_t *sm = m.in + kHeaderBytes;
-    const uint8_t *pl = m.in + L.off_p0;
-    d.sm0 = load_stream16(sm + ln.sm_off);
-    d.sm1 = load_stream16(sm + ln.sm_off + 16u);
-    d.p0 = load_stream4(pl + ln.pl_off);
-    d.p1 = load_stream4(pl + L.plane_bytes + ln.pl_off);
-    d.p2 = load_stream4(pl + 2 * L.plane_bytes + ln.pl_off);
-}
-
-// Zero-points [lo, lo + len) of a stream into buf: whole dwords direct to
-// LDS (from the dword holding zero-point lo); a partial last dword is read
-// whole when the buffer holds all of it, else byte by byte.
-__device__ __forceinline__ void red_stage_range(const RedMeta &m, const Layout &L, uint32_t lo, uint32_t len,
-                                                uint32_t *buf, int lane) {
-    const uint64_t A0 = L.off_zp + lo, A1 = A0 + len;
-    const uint64_t a0 = A0 & ~uint64_t(3);
-    const uint64_t a1 = (A1 + 3 <= m.in_bytes) ? ((A1 + 3) & ~uint64_t(3)) : (A1 & ~uint64_t(3));
-    const uint32_t ndw = (uint32_t)((a1 - a0) / 4);
-    for (uint32_t i0 = 0; i0 < ndw; i0 += kWave)
-        if (i0 + (uint32_t)lane < ndw) lds_load4(m.in + a0 + 4u * (i0 + (uint32_t)lane), lds_base(buf + i0));
-    if (A1 > a1 && lane == 0) {  // a partial dword at the very end of the buffer
-        uint32_t w = 0;
-        for (uint32_t i = 0; i < (uint32_t)(A1 - a1); ++i) w |= (uint32_t)m.in[a1 + i] << (8 * i);
-        buf[ndw] = w;
-    }
-}
-
-// Table entries of tile t, checked and clamped to the stream (a mismatch sets
-// bad), and the zero-points [lo, lo + len) the wave stages in buf: the first
-// ones of the group for half 0, the last ones for half 1, at most
-// kRedSliceCap.
-__device__ __forceinline__ void red_stage(const RedMeta &m, const Layout &L, uint32_t t, bool last, uint32_t half,
-                                          uint32_t &z0, uint32_t &z1, uint32_t &lo, uint32_t &len, uint32_t *buf,
-                                          int lane, bool &bad) {
-    const_u32 *tab = (const_u32 *)(m.in + L.off_tab);
-    z0 = tab[t];
-    z1 = tab[t + 1];  // t + 1 <= groups: the table's last entry at most
-    if ((t == 0 && z0 != 0) || (last && z1 != m.E)) bad = true;
-    if (z0 > m.E) { bad = true; z0 = m.E; }
-    if (z1 < z0 || z1 > m.E) { bad = true; z1 = z1 < z0 ? z0 : m.E; }
-    if (z1 - z0 > kRedTile) { bad = true; z1 = z0 + kRedTile; }
-    len = min(z1 - z0, kRedSliceCap);
-    lo = half ? z1 - len : z0;
-    red_stage_range(m, L, lo, len, buf, lane);
-}
-
-// Plane bytes of the lane's 8-value unit u: [plane 0, plane 1, plane 2, 0].
-__device__ __forceinline__ uint32_t red_planes(const RedData &d, uint32_t u) {
-    const uint32_t w01 = perm(d.p1, d.p0, u | ((4u + u) << 8) | 0x0C0C0000u);
-    return perm(d.p2, w01, 0x0100u | ((4u + u) << 16) | 0x0C000000u);
-}
-
-// Adds 8 values (sign+mantissa dwords sm_lo / sm_hi, exponent bytes e_lo /
-// e_hi) to acc8.  The float of a BF16 value has the value's high byte (sign,
-// exponent >> 1) on top and its low byte (exponent & 1, mantissa) below it:
-// one byte select per value.
-__device__ __forceinline__ void red_add8(float *acc8, uint32_t sm_lo, uint32_t sm_hi, uint32_t e_lo, uint32_t e_hi) {
-    const uint32_t h0 = bfi(0x80808080u, sm_lo, e_lo >> 1), l0 = bfi(0x7F7F7F7Fu, sm_lo, e_lo << 7);
-    const uint32_t h1 = bfi(0x80808080u, sm_hi, e_hi >> 1), l1 = bfi(0x7F7F7F7Fu, sm_hi, e_hi << 7);
-#pragma unroll
-    for (uint32_t j = 0; j < 4; ++j) {
-        const uint32_t sel = 0x0C0Cu | (j << 16) | ((4u + j) << 24);
-        acc8[j] += __uint_as_float(perm(h0, l0, sel));
-        acc8[4 + j] += __uint_as_float(perm(h1, l1, sel));
-    }
-}
-
-// The wave's zero-point flags (bit i: value v0 + i of the lane) and their
-// exclusive prefix count over the lanes; returns the wave's count.
-__device__ __forceinline__ uint32_t red_flags(const RedData &d, const RedLane &ln, uint32_t &z32, uint32_t &excl) {
-    z32 = ~(d.p0 | d.p1 | d.p2) & ln.vmask;
-    const uint32_t cnt = (uint32_t)__builtin_popcount(z32);
-    const uint32_t incl = wave_inclusive_scan(cnt);
-    excl = incl - cnt;
-    return (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
-}
-
-// Where a raw stream's (or the local share's) values are read: the tile's
-// values wv (uniform; the tile's first value always exists), the lane's byte
-// offset from there, whether all 2048 values of the wave exist (uniform).
-// When not, the lane reads value by value from tail_off (its own offset, or 0
-// for a lane past the end), at most value tail_last (nv - 1, or 0) from there.
-struct RedRaw {
-    const uint8_t *wv;
-    uint32_t lane_off;
-    bool full;
-    uint32_t tail_off, tail_last;
-};
-
-// The 8 values of unit u of a raw stream as 4 BF16 pairs (missing values
-// repeat an existing one; their sums are never stored).
-__device__ __forceinline__ void red_raw_unit(const RedRaw &rw, uint32_t u, uint32_t (&w)[4]) {
-    if (rw.full) {
-        const uint4 v = load_stream16(rw.wv + (rw.lane_off + 16u * u));
-        w[0] = v.x;
-        w[1] = v.y;
-        w[2] = v.z;
-        w[3] = v.w;
-    } else {
-        // (an opaque copy: offsets computed from it are not hoisted out of the
-        // stream loop, where they would hold 32 registers)
-        uint32_t lastv = rw.tail_last, loff = rw.tail_off;
-        asm volatile("" : "+v"(lastv), "+v"(loff));
-#pragma unroll
-        for (uint32_t j = 0; j < 4; ++j) {
-            const uint32_t i = 8u * u + 2u * j;
-            const uint32_t lo = *reinterpret_cast<const uint16_t *>(rw.wv + (loff + 2u * min(i, lastv)));
-            const uint32_t hi = *reinterpret_cast<const uint16_t *>(rw.wv + (loff + 2u * min(i + 1u, lastv)));
-            w[j] = lo | (hi << 16);
-        }
-    }
-}
-
-// Decodes the lane's 32 values of a stream and adds them to acc.  Coded: the
-// lane's first zero-point is byte r0 of buf and each 8-value unit's are
-// contiguous there.  Raw: the values are read as they are and split like the
-// encoder splits them (sign+mantissa bytes, exponent bytes), so that every
-// stream's values enter the sums through the same instructions.
-__device__ __forceinline__ void red_decode(const RedMeta &m, const RedData &d, uint32_t z32, uint32_t r0,
-                                           const uint32_t *buf, const uint2 *sel, const RedRaw &rw,
-                                           float (&acc)[32]) {
-    const uint32_t smw[8] = {d.sm0.x, d.sm0.y, d.sm0.z, d.sm0.w, d.sm1.x, d.sm1.y, d.sm1.z, d.sm1.w};
-#pragma unroll
-    for (uint32_t u = 0; u < 4; ++u) {
-        uint32_t sm_lo, sm_hi, e_lo, e_hi;
-        if (m.raw) {
-            uint32_t w[4];
-            red_raw_unit(rw, u, w);
-            sm_lo = sign_mantissa4(w[0], w[1]);
-            sm_hi = sign_mantissa4(w[2], w[3]);
-            e_lo = exponents4(exponent_high(w[0]), exponent_high(w[1]));
-            e_hi = exponents4(exponent_high(w[2]), exponent_high(w[3]));
-        } else {
-            uint32_t c_lo, c_hi;
-            planes_to_codes(red_planes(d, u), c_lo, c_hi);
-            e_lo = perm(m.tbl_hi, m.tbl_lo, c_lo);
-            e_hi = perm(m.tbl_hi, m.tbl_lo, c_hi);
-            const uint32_t r = u ? r0 + (uint32_t)__builtin_popcount(z32 & ((1u << (8u * u)) - 1u)) : r0;
-            put_zero_points(e_lo, e_hi, (z32 >> (8u * u)) & 0xFFu, r, buf, sel);
-            sm_lo = smw[2u * u];
-            sm_hi = smw[2u * u + 1u];
-        }
-        red_add8(acc + 8u * u, sm_lo, sm_hi, e_lo, e_hi);
-        __builtin_amdgcn_sched_barrier(0);  // one unit's registers live at a time
-    }
-}
-
-// A block checks every stream's header first (a bad header anywhere leaves the
-// whole output untouched), then each wave decodes its half-tile of every
-// stream in order.  The float32 sums start from the local value, or from -0.0
-// (-0.0 + x is x for every x, so the first stream enters exactly).
-__global__ __launch_bounds__(kThreads) void reduce_kernel(RedArgs args) {
-    __shared__ RedShared sh;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: tile, half and addresses in SGPRs
-    const uint64_t n = args.n;
-    const Layout L = layout_for(n);
-    const uint32_t k = args.k;
-    const uint32_t half = (uint32_t)wave & 1u;
-    const uint32_t t = blockIdx.x * kRedTilesPerBlock + (uint32_t)wave / 2;
-    const bool active = t < L.groups;
-    const bool last = t + 1 == L.groups;
-
-    zp_selectors(sh.sel);  // visible after the barriers of the header check
-    if (!red_check_headers(args, n, L, &sh.slice[0][0][0], sh.hdr)) {
-        if (tid == 0 && args.status) *args.status = ZC_ERR_CORRUPT;
-        return;
-    }
-
-    RedLane ln;
-    ln.v0 = (uint64_t)t * kRedTile + kRedHalf * half + 32u * (uint32_t)lane;
-    ln.nv = ln.v0 < n ? (uint32_t)min(n - ln.v0, (uint64_t)32) : 0u;
-    ln.vmask = ln.nv == 32 ? ~0u : (1u << ln.nv) - 1u;
-    ln.sm_off = ln.nv ? (uint32_t)ln.v0 : 0u;
-    ln.pl_off = ln.nv ? (uint32_t)(ln.v0 / 8) : 0u;
-
-    // where the lane reads BF16 arrays (the local share, raw streams)
-    const uint64_t tile0 = (uint64_t)t * kRedTile;
-    RedRaw rw;
-    rw.lane_off = 2u * (kRedHalf * half + 32u * (uint32_t)lane);
-    rw.full = tile0 + kRedHalf * (half + 1u) <= n;
-    rw.tail_off = ln.nv ? rw.lane_off : 0u;
-    rw.tail_last = ln.nv ? ln.nv - 1u : 0u;
-
-    // A wave whose 2048 values all exist moves its local share in and its
-    // result out through its slice buffers (free at both times), in two
-    // rounds of 1024 values: each global access instruction then covers 1 KiB
-    // of consecutive bytes, where lanes of 32 consecutive values would touch
-    // every cache line in part (measured: a quarter of the kernel's time).
-    uint8_t *const xpose = reinterpret_cast<uint8_t *>(sh.slice[wave][0]);
-    static_assert(sizeof(RedShared::slice[0]) >= 2048, "a round of 1024 values fits a wave's slice buffers");
-    const uint64_t half0 = tile0 + kRedHalf * half;  // the wave's first value
-
-    float acc[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] = -0.0f;
-    if (args.local && active) {
-        if (rw.full) {
-#pragma unroll
-            for (uint32_t r = 0; r < 2; ++r) {
-                const uint8_t *src = reinterpret_cast<const uint8_t *>(args.local + half0 + 1024u * r);
-                const uint4 a = load_stream16(src + 16u * (uint32_t)lane);
-                const uint4 b = load_stream16(src + 1024u + 16u * (uint32_t)lane);
-                *reinterpret_cast<uint4 *>(xpose + 16u * (uint32_t)lane) = a;
-                *reinterpret_cast<uint4 *>(xpose + 1024u + 16u * (uint32_t)lane) = b;
-                wave_lds_sync();
-                if ((uint32_t)lane / 32u == r) {
-                    const uint8_t *mine = xpose + 64u * ((uint32_t)lane % 32u);
-#pragma unroll
-                    for (uint32_t q = 0; q < 4; ++q) {
-                        const uint4 v = *reinterpret_cast<const uint4 *>(mine + 16u * q);
-                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                        for (uint32_t j = 0; j < 4; ++j) {
-                            acc[8 * q + 2 * j] = bf16_lo(w[j]);
-                            acc[8 * q + 2 * j + 1] = bf16_hi(w[j]);
-                        }
-                    }
-                }
-                wave_lds_sync();  // (the next round rewrites the buffer: reads first)
-            }
-        } else {
-            rw.wv = reinterpret_cast<const uint8_t *>(args.local + tile0);
-#pragma unroll
-            for (uint32_t u = 0; u < 4; ++u) {
-                uint32_t w[4];
-                red_raw_unit(rw, u, w);
-#pragma unroll
-                for (uint32_t j = 0; j < 4; ++j) {
-                    acc[8 * u + 2 * j] = bf16_lo(w[j]);
-                    acc[8 * u + 2 * j + 1] = bf16_hi(w[j]);
-                }
-            }
-        }
-    }
-
-    bool bad = false;
-    if (active && k) {
-        RedMeta cur = red_meta(args, 0, sh.hdr);
-        RedData dc, dn;
-        uint32_t z0 = 0, z1 = 0, lo = 0, len = 0;
-        if (!cur.raw) {
-            red_stage(cur, L, t, last, half, z0, z1, lo, len, sh.slice[wave][0], lane, bad);
-            red_load(dc, cur, L, ln);
-        }
-        for (uint32_t s = 0; s < k; ++s) {
-            // Stream s's words and slice have landed.  (This wait orders no LDS
-            // read for the compiler; it does not need to: the slice's reads
-            // take their addresses from stream s's plane words, which the
-            // compiler waits for, and the slice was issued before them.)
-            __builtin_amdgcn_s_waitcnt(kWaitVm0);
-            RedMeta nxt = cur;
-            uint32_t nz0 = 0, nz1 = 0, nlo = 0, nlen = 0;
-            const bool staged = s + 1 < k && !(nxt = red_meta(args, s + 1, sh.hdr)).raw;
-            if (staged) {  // the next stream's slice and words go out now
-                red_stage(nxt, L, t, last, half, nz0, nz1, nlo, nlen, sh.slice[wave][(s + 1) & 1u], lane, bad);
-                red_load(dn, nxt, L, ln);
-            }
-            uint32_t edge = 0, z32 = 0, r0 = 0, x = s & 1u;
-            bool heavy = false;
-            rw.wv = cur.in + kHeaderBytes + 2 * tile0;
-            if (!cur.raw) {
-                uint32_t excl;
-                const uint32_t c = red_flags(dc, ln, z32, excl);
-                edge = half ? z1 - c : z0 + c;
-                // half 0's zero-points open the staged slice, half 1's close it
-                r0 = (lo & 3u) + (half ? len - c : 0u) + excl;
-                heavy = c > len;
-                if (heavy) {
-                    // More zero-points than staged (or than the table allows): the
-                    // half's own ones, at most 2048 bytes, go to both slice buffers
-                    // (back to back); the next stream's slice is staged again after.
-                    const uint32_t a = half ? (c <= z1 ? z1 - c : 0u) : z0;
-                    wait_loads();
-                    red_stage_range(cur, L, a, min(c, cur.E - a), sh.slice[wave][0], lane);
-                    wait_loads();
-                    r0 = (a & 3u) + excl;
-                    x = 0;
-                }
-            }
-            red_decode(cur, dc, z32, r0, sh.slice[wave][x], sh.sel, rw, acc);
-            if (heavy && staged) {
-                red_stage_range(nxt, L, nlo, nlen, sh.slice[wave][(s + 1) & 1u], lane);
-                wait_loads();  // (issued after the next stream's plane words: not covered by waiting for them)
-            }
-            if (lane == 0) sh.edge[wave][s] = edge;
-            cur = nxt;
-            dc = dn;
-            z0 = nz0;
-            z1 = nz1;
-            lo = nlo;
-            len = nlen;
-        }
-    }
-    __syncthreads();  // the edges of both halves
-    if (active && half == 0)
-        for (uint32_t s = (uint32_t)lane; s < k; s += kWave)
-            if (sh.edge[wave][s] != sh.edge[wave + 1][s]) bad = true;
-
-    if (active) {
-        uint32_t o[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[i] = float_to_bf16(acc[2 * i]) | (float_to_bf16(acc[2 * i + 1]) << 16);
-        if (rw.full) {
-#pragma unroll
-            for (uint32_t r = 0; r < 2; ++r) {
-                if ((uint32_t)lane / 32u == r) {
-                    uint8_t *mine = xpose + 64u * ((uint32_t)lane % 32u);
-#pragma unroll
-                    for (uint32_t q = 0; q < 4; ++q)
-                        *reinterpret_cast<uint4 *>(mine + 16u * q) =
-                            make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-                }
-                wave_lds_sync();
-                uint8_t *dst = reinterpret_cast<uint8_t *>(args.out + half0 + 1024u * r);
-                const uint4 a = *reinterpret_cast<const uint4 *>(xpose + 16u * (uint32_t)lane);
-                const uint4 b = *reinterpret_cast<const uint4 *>(xpose + 1024u + 16u * (uint32_t)lane);
-                store_stream16(dst + 16u * (uint32_t)lane, a.x, a.y, a.z, a.w);
-                store_stream16(dst + 1024u + 16u * (uint32_t)lane, b.x, b.y, b.z, b.w);
-                wave_lds_sync();  // (the next round rewrites the buffer: reads first)
-            }
-        } else if (ln.nv) {
-            uint16_t *dst = args.out + ln.v0;
-#pragma unroll
-            for (uint32_t i = 0; i < 32; ++i)
-                if (i < ln.nv) dst[i] = (uint16_t)(o[i / 2] >> (16 * (i % 2)));
-        }
-    }
-    if (bad && args.status) atomicMax(args.status, (int32_t)ZC_ERR_CORRUPT);
-}
-
 }  // namespace zc
-
 
 // ===========================================================================
 // C ABI
 // ===========================================================================
 
 using namespace zc;
-
-
-static zc_status launch_zero(ZeroArgs &z, hipStream_t st) {
-    uint64_t words = 0;
-    for (uint32_t i = 0; i < z.count; ++i) words += z.r[i].words;
-    if (!words) return ZC_OK;
-    uint64_t blocks = (words + 255) / 256;
-    if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL(zero_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, z);
-    return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
-}
-
 
 // Per-call tokens: splitmix64 (Steele, Lea, Flood, "Fast splittable
 // pseudorandom number generators", 2014) of a process-wide counter whose
@@ -2344,107 +1384,4 @@ extern "C" zc_status zc_compress_ws(const void *d_in, uint64_t n, const zc_plan 
     s.out_capacity = out_capacity;
     s.out_bytes = d_out_bytes;
     return zc_compress_batch_ws(&s, 1, d_workspace, workspace_bytes, stream);
-}
-
-extern "C" zc_status zc_decompress_batch(const zc_dec_seg *segs, uint32_t k, void *stream) {
-    if (!segs || k == 0 || k > ZC_MAX_BATCH) return ZC_ERR_INVALID_ARG;
-    // a[0]: decode_kernel; a[1]: decode_raw_kernel, for buffers shorter than
-    // the coded layout (only a raw stream fits there)
-    DecArgs a[2];
-    std::memset(a, 0, sizeof(a));
-    ZeroArgs z;
-    std::memset(&z, 0, sizeof(z));
-    uint64_t tiles[2] = {0, 0};
-    for (uint32_t i = 0; i < k; ++i) {
-        const zc_dec_seg &g = segs[i];
-        if (!g.in || g.n > kMaxElems || (g.n && !g.out)) return ZC_ERR_INVALID_ARG;
-        if (((uintptr_t)g.in & 127u) || ((uintptr_t)g.out & 15u) || ((uintptr_t)g.status & 3u))
-            return ZC_ERR_MISALIGNED;
-        const Layout L = layout_for(g.n);
-        // no stream of n values is shorter than both forms
-        if (g.in_bytes < L.off_zp && g.in_bytes < kHeaderBytes + 2 * g.n) return ZC_ERR_CORRUPT;
-        const int which = g.in_bytes < L.off_zp ? 1 : 0;
-        DecSeg &d = a[which].seg[a[which].k++];
-        d.in = static_cast<const uint8_t *>(g.in);
-        d.out = static_cast<uint16_t *>(g.out);
-        d.status = g.status;
-        d.in_bytes = g.in_bytes;
-        d.n = (uint32_t)g.n;
-        d.tile_begin = (uint32_t)tiles[which];
-        a[which].tile_begin[a[which].k - 1] = d.tile_begin;
-        tiles[which] += dec_blocks(g.n);
-        if (tiles[which] > 0xFFFFFFFFull) return ZC_ERR_INVALID_ARG;
-        if (g.status) {
-            z.r[z.count].ptr = reinterpret_cast<uint32_t *>(g.status);
-            z.r[z.count].words = 1;
-            ++z.count;
-        }
-    }
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    (void)hipGetLastError();
-    zc_status rc = launch_zero(z, st);
-    if (rc != ZC_OK) return rc;
-    for (int which = 0; which < 2; ++which) {
-        if (!a[which].k) continue;
-        a[which].total_tiles = (uint32_t)tiles[which];
-        if (which == 0)
-            hipLaunchKernelGGL(decode_kernel, dim3(a[0].total_tiles), dim3(kThreads), 0, st, a[0]);
-        else
-            hipLaunchKernelGGL(decode_raw_kernel, dim3(a[1].total_tiles), dim3(kThreads), 0, st, a[1]);
-        if (hipGetLastError() != hipSuccess) return ZC_ERR_HIP;
-    }
-    return ZC_OK;
-}
-
-extern "C" zc_status zc_decompress(const void *d_in, uint64_t in_bytes, uint64_t n, void *d_out, int32_t *d_status,
-                                   void *stream) {
-    zc_dec_seg s;
-    s.in = d_in;
-    s.in_bytes = in_bytes;
-    s.n = n;
-    s.out = d_out;
-    s.status = d_status;
-    return zc_decompress_batch(&s, 1, stream);
-}
-
-extern "C" zc_status zc_decompress_reduce(const void *const *d_streams, const uint64_t *in_bytes, uint32_t k,
-                                          uint64_t n, const void *d_local, void *d_out, int32_t *d_status,
-                                          void *stream) {
-    if (k > ZC_MAX_BATCH || (k && (!d_streams || !in_bytes)) || (k == 0 && !d_local) || n > kMaxElems ||
-        (n && !d_out))
-        return ZC_ERR_INVALID_ARG;
-    if (((uintptr_t)d_local & 15u) || ((uintptr_t)d_out & 15u) || ((uintptr_t)d_status & 3u))
-        return ZC_ERR_MISALIGNED;
-    RedArgs a;
-    std::memset(&a, 0, sizeof(a));
-    const Layout L = layout_for(n);
-    for (uint32_t i = 0; i < k; ++i) {
-        if (!d_streams[i]) return ZC_ERR_INVALID_ARG;
-        if ((uintptr_t)d_streams[i] & 127u) return ZC_ERR_MISALIGNED;
-        // no stream of n values is shorter than both forms
-        if (in_bytes[i] < L.off_zp && in_bytes[i] < kHeaderBytes + 2 * n) return ZC_ERR_CORRUPT;
-        a.s[i].in = static_cast<const uint8_t *>(d_streams[i]);
-        a.s[i].in_bytes = in_bytes[i];
-    }
-    a.k = k;
-    a.n = (uint32_t)n;
-    a.local = static_cast<const uint16_t *>(d_local);
-    a.out = static_cast<uint16_t *>(d_out);
-    a.status = d_status;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    (void)hipGetLastError();
-    if (d_status) {
-        ZeroArgs z;
-        std::memset(&z, 0, sizeof(z));
-        z.count = 1;
-        z.r[0].ptr = reinterpret_cast<uint32_t *>(d_status);
-        z.r[0].words = 1;
-        const zc_status rc = launch_zero(z, st);
-        if (rc != ZC_OK) return rc;
-    }
-    // n = 0 still runs one block: every header is checked, nothing is written
-    const uint64_t tiles = (n + kRedTile - 1) / kRedTile;
-    const uint64_t blocks = tiles ? (tiles + kRedTilesPerBlock - 1) / kRedTilesPerBlock : 1;
-    hipLaunchKernelGGL(reduce_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, st, a);
-    return hipGetLastError() == hipSuccess ? ZC_OK : ZC_ERR_HIP;
 }
