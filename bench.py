@@ -323,6 +323,43 @@ def alltoall_order(zc, w, steps: int, warmup: int) -> dict:
     return rec
 
 
+def profile_pass(zc, w, call: str, steps: int) -> dict:
+    """The command rocprofv3 counter passes run (--profile CALL): a copy of
+    known size with the bench library's copy kernel (the counters' scale: the
+    bytes the copy reads and writes over what the counters report), then
+    `steps` calls of CALL on workload w as the bench times them (compress and
+    decompress on the resident workload; reduce on the 32 Mi-value shard of 7
+    peers)."""
+    import torch
+    from lossless_bf16_exponent_amd import _build
+    lib = ctypes.CDLL(_build.BENCH_LIB)
+    vp, u64 = ctypes.c_void_p, ctypes.c_uint64
+    lib.zcb_copy.argtypes = [vp, vp, u64, vp]
+    stream = torch.cuda.current_stream()
+    copy_bytes = 1 << 30
+    a = torch.full((copy_bytes // 2,), 0x3C00, dtype=torch.int16, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        if lib.zcb_copy(a.data_ptr(), b.data_ptr(), copy_bytes, stream.cuda_stream) != 0:
+            raise RuntimeError("copy kernel failed")
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
+    rec = {"profile": call, "copy_kernel_bytes": copy_bytes, "steps": steps}
+    if call == "reduce":
+        rec["reduce"] = reduce_measurement(zc, steps)
+        return rec
+    r = Resident(zc, w)
+    facts = r.check(zc, stream)
+    fn = (lambda: r.compress(zc, stream)) if call == "compress" else (lambda: zc.zc_decompress_batch(r.dec_segs, stream))
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    rec.update({"workload": w.name, "values": w.n, "stream_bytes": facts["stream_bytes"],
+                "algorithmic_bytes_per_call": 2 * w.n + facts["stream_bytes"]})
+    return rec
+
+
 def ceilings(n: int, steps: int) -> dict:
     """Practical ceilings of the codec's access shapes for n values (a
     bench-only library): a 128-bit copy of 2n bytes, the encoder's shape (read
@@ -590,6 +627,9 @@ def main() -> int:
     ap.add_argument("--workload", default="3", help="headline workload id (1, 2, 3, 4, 5a, 5b); default 3")
     ap.add_argument("--only-headline", action="store_true", help="skip every record besides the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", choices=("compress", "decompress", "reduce"),
+                    help="run only what a rocprofv3 counter pass measures: a copy of known size, then --steps "
+                         "calls of this kind on --workload; prints that run's facts instead of the bench line")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -610,6 +650,9 @@ def main() -> int:
 
     t_gen = time.perf_counter()
     w = workloads.get(args.workload)
+    if args.profile:
+        print(json.dumps(profile_pass(zc, w, args.profile, args.steps)), flush=True)
+        return 0
     log("workload %s: %d values in %d segments, generated in %.1f s"
         % (w.name, w.n, len(w.segments), time.perf_counter() - t_gen))
 
