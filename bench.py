@@ -614,7 +614,7 @@ def fallback_measurement(zc, steps: int) -> dict:
         for _ in range(3):
             call()
         res[name] = summary(timed_groups(call, stream, GROUPS, max(1, steps // GROUPS)), alg, n)
-    res["kernels"] = {"compress": "compress_kernel<true>, two launches (the guessing pass, the completing pass)",
+    res["kernels"] = {"compress": "compress_fallback_kernel (the guessing launch) + compress_second_kernel",
                       "decompress": "decode_kernel (raw branch)"}
     return res
 
