@@ -76,7 +76,6 @@ struct EncArgs {
     uint32_t pieces;
     uint32_t tok_lo, tok_hi;  // the launch's token (scratch words of other launches never match it)
     uint32_t prev_lo, prev_hi;  // the fallback's second launch: the token of the call's first launch
-    uint32_t pad;
     uint32_t mult;            // units (spans or runs) per block (zc_grid.h)
     uint32_t chunk;           // spans per staged chunk
     uint8_t *ws;              // the call's workspace, or null: each segment's scratch behind its stream
@@ -117,8 +116,9 @@ __device__ __forceinline__ uint32_t find_piece(const EncArgs &a, uint32_t flat) 
 // XCDs, whose L2 caches are not coherent with each other.  Every access to
 // memory that one block writes and another block of the same launch reads (the
 // words and the staged zero-point bytes) is a device-scope (agent) access:
-// relaxed agent-scope atomics, which gfx950 issues with the sc1 cache policy,
-// and direct-to-LDS loads with that policy.  An sc1 store writes through the
+// relaxed agent-scope atomics for the words, which gfx950 issues with the sc1
+// cache policy, 16-byte buffer stores with that policy for the staged bytes
+// and direct-to-LDS loads with it to read them back.  An sc1 store writes through the
 // L2 to the device's coherence point and its vmcnt completion means it has
 // reached that point; an sc1 load is served from that point, never from a
 // stale line of the reader's L2.  So a writer that stores data with sc1, waits
@@ -515,9 +515,11 @@ __device__ __forceinline__ void copy_span_raw(const uint16_t *in, uint8_t *out, 
 // The header, the table's last entry and the stream size of a segment with E
 // zero-points.  ok = false (a wait given up somewhere in the segment) leaves a
 // zero magic, which every decoder rejects, and a stream size of 0.  Raw
-// fallback: when the plan allows it and coding has made the stream larger
-// than the input, the header says raw and the raw pass (a second launch)
-// copies the input behind it.
+// fallback (first launch, kFb): the exact rule decides the form, and the
+// segment's status word tells the second launch what is left: nothing, the
+// raw payload (a coded pass that came out raw: the header already says raw),
+// or the coded pass (a raw guess that came out coded: the header stays
+// invalid until then).
 template <bool kFb>
 __device__ __forceinline__ void write_header(const EncArgs &args, const EncSeg &sg, const Layout &L, uint64_t E,
                                              bool ok, bool guessed_raw) {
