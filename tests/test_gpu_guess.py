@@ -40,14 +40,14 @@ def break_even(n):
     return 128 + 2 * n - oracle.layout(n)["off_zp"]  # raw iff E > this
 
 
-def check_batch(zc, specs, lib=None, seed=0):
-    """specs: (n, E, flagged) per segment; compress in one call, compare every
-    stream with the oracle's and decode every one back."""
+def check_batch(zc, specs, lib=None, seed=0, workspace=False):
+    """specs: (n, E, flagged) per segment; compress in one call (workspace: the
+    _ws call), compare every stream with the oracle's and decode every one back."""
     xs = [oracle_pins.with_escapes(n, E, seed + 31 * i) for i, (n, E, _) in enumerate(specs)]
     ns = [n for (n, _, _) in specs]
     plans = [zc.plan_with_raw_fallback(WINDOW_PLAN) if f else WINDOW_PLAN for (_, _, f) in specs]
     devs = [to_device(x) if x.size else None for x in xs]
-    enc = compress_batch(zc, devs, ns, plans, lib=lib)
+    enc = compress_batch(zc, devs, ns, plans, lib=lib, workspace=workspace)
     for i, (x, (n, E, f)) in enumerate(zip(xs, specs)):
         ref = oracle.encode(x, WINDOW_PLAN, raw_fallback=f)
         got = enc.stream(i)
@@ -71,26 +71,31 @@ def direct_specs():
 
 def test_forced_guess_direct_launch(zc, guess):
     """Every break-even case of several sizes, flagged, in launches of at most
-    2048 spans (direct placement), both outcomes under the forced guess."""
+    2048 spans (direct placement), both outcomes under the forced guess; every
+    other batch through a workspace."""
     name, lib = guess
     specs = direct_specs()
     for lo in range(0, len(specs), 16):
         part = specs[lo:lo + 16]
         assert sum(-(-n // SPAN) for (n, _, _) in part) <= 2048
-        print("guess %s direct segments %d..%d" % (name, lo, lo + len(part)), flush=True)
-        check_batch(zc, part, lib=lib, seed=lo)
+        ws = (lo // 16) % 2 == 1
+        print("guess %s direct segments %d..%d workspace=%s" % (name, lo, lo + len(part), ws), flush=True)
+        check_batch(zc, part, lib=lib, seed=lo, workspace=ws)
 
 
-def test_forced_guess_staged_launch(zc, guess):
+@pytest.mark.parametrize("workspace", [False, True], ids=["in-buffer", "workspace"])
+def test_forced_guess_staged_launch(zc, guess, workspace):
     """A launch of more than 2048 spans (staged placement): a long flagged
-    segment on each side of break-even, short flagged and plain ones."""
+    segment on each side of break-even, short flagged and plain ones; the
+    scratch behind each stream, or in a workspace (both launches of the call
+    then use it)."""
     name, lib = guess
     n_big = 1200 * SPAN + 77
     T = break_even(n_big)
     specs = [(n_big, T + 1, True), (n_big, T, True), (70_001, 70_001, True), (70_001, 10, True), (100, 100, True),
              (9000, 9000, False), (0, 0, True)]
-    print("guess %s staged" % name, flush=True)
-    check_batch(zc, specs, lib=lib, seed=7)
+    print("guess %s staged workspace=%s" % (name, workspace), flush=True)
+    check_batch(zc, specs, lib=lib, seed=7, workspace=workspace)
 
 
 def test_forced_guess_repeated_calls_same_buffers(zc, guess):
