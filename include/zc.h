@@ -105,10 +105,11 @@ uint64_t zc_max_compressed_bytes(uint64_t n);
 
 /* Encoder scratch for one tensor of n elements (a multiple of 256 bytes, a
  * little over n bytes: a staging slot of 8192 bytes per 8192 elements for
- * zero-point bytes, and the cross-workgroup words).  zc_compress and zc_compress_batch keep it in the output buffer
- * behind the largest stream; the _ws calls take it from a workspace, which a
- * caller can reuse from call to call (a send buffer then needs only
- * zc_max_compressed_bytes(n)).  Returns 0 for n > 2^32-1. */
+ * zero-point bytes, and the cross-workgroup words).  zc_compress and
+ * zc_compress_batch keep it in the output buffer behind the largest stream;
+ * the _ws calls take it from a workspace, which a caller can reuse from call
+ * to call (a send buffer then needs only zc_max_compressed_bytes(n)).
+ * Returns 0 for n > 2^32-1. */
 uint64_t zc_compress_workspace_bytes(uint64_t n);
 
 /* Section 2.B, compress one BF16 tensor.
