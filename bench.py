@@ -474,7 +474,7 @@ def cpu_baseline(w, plans, one_thread_segments: int = 8, min_seconds: float = 5.
             "single_thread": single}
 
 
-REDUCE_WARMUP_CALLS = 150
+REDUCE_WARMUP_CALLS = 300
 
 
 def reduce_measurement(zc, steps: int) -> dict:
@@ -483,10 +483,11 @@ def reduce_measurement(zc, steps: int) -> dict:
     plus the local share, reduced by zc_decompress_reduce.  Peer p's values are
     N(0, sigma_p^2) with sigma_p the first eight layer sigmas of the gradient
     bucket, each compressed with its own plan.  HIP events around K calls,
-    after REDUCE_WARMUP_CALLS calls: per-call timings on MI355X show about 20
-    fast calls, then about 80 calls some 20 % slower, then a steady state (the
-    device settling after a burst of this kernel), which is what a training
-    job that reduces bucket after bucket sees."""
+    after REDUCE_WARMUP_CALLS calls: per-call timings of 1,000 calls in a row on
+    MI355X, in means over 50 calls, go 111, 99, 93, 89, 87, 86 us and then stay
+    at 85-86 us from about the 250th call on (the device settling after a burst
+    of this kernel), the steady state a training job that reduces bucket after
+    bucket sees."""
     import numpy as np
     import torch
 
