@@ -94,6 +94,16 @@ def build_guess(verbose: bool = False) -> dict:
     return GUESS_LIBS
 
 
+NARROW_LIB = os.path.join(ROOT, "tests", "libzc_dec_narrow.so")
+
+
+def build_narrow(verbose: bool = False) -> str:
+    """The library whose decoder takes one-tile spans for launches of any size
+    (the shipped one does so only from 2^27 values on), so that tests reach that
+    form on small and ragged inputs.  Test infrastructure only."""
+    return build_variant(NARROW_LIB, ["ZC_DEC_NARROW_MIN=0"], verbose)
+
+
 def assembly(out_path: str, source: str = SOURCES[0]) -> str:
     """Device assembly of the kernels (for inspection of the generated gfx950 code)."""
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC,

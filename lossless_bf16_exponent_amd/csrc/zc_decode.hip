@@ -113,14 +113,20 @@ __device__ __forceinline__ void copy_raw(const uint8_t *in, uint16_t *out, uint6
     for (uint64_t v = full + threadIdx.x; v < v1; v += kThreads) out[v] = src[v];
 }
 
-// A block decodes kDecSubTiles consecutive tiles (its span).  Every plane and
+// A block decodes kSub consecutive tiles (its span).  Every plane and
 // sign+mantissa load of the span, and the span's zero-point table entries,
 // are issued before the header is checked (all of them lie inside the n-value
 // layout, which the host has checked against in_bytes); the zero-point slice
-// is then staged in LDS with dword loads and gathered by rank.
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
+// is then staged in LDS with dword loads and gathered by rank.  The one-tile
+// form asks for eight waves per SIMD: it then keeps to 77 SGPRs (82 without
+// the budget, which leaves room for seven blocks per CU, not eight).
+template <int kSub>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSub == 1 ? 8 : 1, 8))) void decode_kernel(
+    DecArgs args) {
+    constexpr uint32_t kSpan = kTile * kSub;
+    constexpr int kSpanGroups = (int)(kSpan / kGroup);
     __shared__ uint32_t s_planes[kTile / 8];
-    __shared__ uint32_t s_zp32[kDecSpan / 4 + 3];  // the span's zero-point bytes from a dword-aligned start
+    __shared__ uint32_t s_zp32[kSpan / 4 + 3];  // the span's zero-point bytes from a dword-aligned start
     __shared__ uint32_t s_wave_total[2][kWaves];    // (+ slack for the 3-dword reads of the gather)
     __shared__ uint2 s_sel[256];
 
@@ -132,13 +138,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
     const uint64_t n = sg.n;
     const Layout L = layout_for(n);
     const uint8_t *const in = sg.in;
-    const uint64_t span0 = (uint64_t)b * kDecSpan;
+    const uint64_t span0 = (uint64_t)b * kSpan;
 
     // ---- data loads of the whole span
-    uint32_t pw[kDecSubTiles][3];
-    uint32_t sm[kDecSubTiles][kSteps][2], vmask[kDecSubTiles][kSteps];
+    uint32_t pw[kSub][3];
+    uint32_t sm[kSub][kSteps][2], vmask[kSub][kSteps];
 #pragma unroll
-    for (int sub = 0; sub < kDecSubTiles; ++sub) {
+    for (int sub = 0; sub < kSub; ++sub) {
         const uint64_t tile0 = span0 + (uint64_t)sub * kTile;
         pw[sub][0] = pw[sub][1] = pw[sub][2] = 0;
         if (tile0 + 32u * (uint32_t)tid < n) {
@@ -163,10 +169,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
 
     // ---- the span's zero-point table entries
     const uint32_t *tab = reinterpret_cast<const uint32_t *>(in + L.off_tab);
-    uint32_t z[kDecGroups + 1];
+    uint32_t z[kSpanGroups + 1];
 #pragma unroll
-    for (int j = 0; j <= kDecGroups; ++j) {
-        const uint64_t g = (uint64_t)b * kDecGroups + j;
+    for (int j = 0; j <= kSpanGroups; ++j) {
+        const uint64_t g = (uint64_t)b * kSpanGroups + j;
         z[j] = tab[g <= L.groups ? g : L.groups];
     }
 
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
     if (!ok) {
         // not a coded stream: the raw fallback form, or corrupt
         if (raw_header_ok(in, sg.in_bytes, n, L)) {
-            copy_raw(in, sg.out, span0, min(span0 + kDecSpan, n));
+            copy_raw(in, sg.out, span0, min(span0 + kSpan, n));
             return;
         }
         if (tid == 0 && sg.status) *sg.status = ZC_ERR_CORRUPT;
@@ -201,22 +207,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
     const uint32_t tbl_lo = h6 << 8, tbl_hi = (h6 >> 24) | (h7 << 8);
 
     // ---- table consistency; clamp so that every read stays inside the stream
-    const bool last = (b == dec_blocks(n) - 1);
-    bool bad = (b == 0 && z[0] != 0) || (last && z[kDecGroups] != E);
+    const bool last = (b == dec_blocks(n, kSpan) - 1);
+    bool bad = (b == 0 && z[0] != 0) || (last && z[kSpanGroups] != E);
 #pragma unroll
-    for (int j = 0; j <= kDecGroups; ++j) {
+    for (int j = 0; j <= kSpanGroups; ++j) {
         const uint32_t lo = j ? z[j - 1] : 0u;
         if (z[j] < lo || z[j] > E) bad = true;
         z[j] = z[j] < lo ? lo : (z[j] > E ? (uint32_t)E : z[j]);
     }
-    if (z[kDecGroups] - z[0] > kDecSpan) {
+    if (z[kSpanGroups] - z[0] > kSpan) {
         bad = true;
 #pragma unroll
-        for (int j = 0; j <= kDecGroups; ++j) z[j] = z[j] - z[0] > kDecSpan ? z[0] + kDecSpan : z[j];
+        for (int j = 0; j <= kSpanGroups; ++j) z[j] = z[j] - z[0] > kSpan ? z[0] + kSpan : z[j];
     }
 
     // ---- stage the span's zero-point bytes: stream bytes [A0, A1)
-    const uint64_t A0 = L.off_zp + z[0], A1 = L.off_zp + z[kDecGroups];
+    const uint64_t A0 = L.off_zp + z[0], A1 = L.off_zp + z[kSpanGroups];
     const uint64_t a0 = A0 & ~uint64_t(3), a1 = A1 & ~uint64_t(3);
     const uint32_t shift = (uint32_t)(A0 & 3u);
     const uint32_t ndw = (uint32_t)((a1 - a0) / 4);
@@ -226,11 +232,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
         for (uint32_t i = 0; i < (uint32_t)(A1 - a1); ++i) w |= (uint32_t)in[a1 + i] << (8 * i);
         s_zp32[ndw] = w;
     }
-    const uint32_t zspan = z[kDecGroups] - z[0];
+    const uint32_t zspan = z[kSpanGroups] - z[0];
     zp_selectors(s_sel);  // visible after the first sub-tile's barrier
 
 #pragma unroll
-    for (int sub = 0; sub < kDecSubTiles; ++sub) {
+    for (int sub = 0; sub < kSub; ++sub) {
         const uint64_t tile0 = span0 + (uint64_t)sub * kTile;
         {
             const uint32_t p0 = pw[sub][0], p1 = pw[sub][1], p2 = pw[sub][2];
@@ -276,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs args) {
                 for (uint32_t i = 0; base + i < n; ++i) sg.out[base + i] = (uint16_t)(w4[i / 2] >> (16 * (i % 2)));
             }
         }
-        if (sub + 1 < kDecSubTiles) __syncthreads();  // s_planes is rewritten by the next sub-tile
+        if (sub + 1 < kSub) __syncthreads();  // s_planes is rewritten by the next sub-tile
     }
     if (bad && tid == 0 && sg.status) atomicMax(sg.status, (int32_t)ZC_ERR_CORRUPT);
 }
@@ -289,12 +295,12 @@ __global__ __launch_bounds__(kThreads) void decode_raw_kernel(DecArgs args) {
     const DecSeg &sg = args.seg[s];
     const uint64_t n = sg.n;
     const Layout L = layout_for(n);
-    const uint64_t span0 = (uint64_t)(flat - sg.tile_begin) * kDecSpan;
+    const uint64_t span0 = (uint64_t)(flat - sg.tile_begin) * kDecRawSpan;
     if (!raw_header_ok(sg.in, sg.in_bytes, n, L)) {
         if (threadIdx.x == 0 && sg.status) *sg.status = ZC_ERR_CORRUPT;
         return;
     }
-    copy_raw(sg.in, sg.out, span0, min(span0 + kDecSpan, n));
+    copy_raw(sg.in, sg.out, span0, min(span0 + kDecRawSpan, n));
 }
 
 }  // namespace zc
@@ -324,6 +330,9 @@ extern "C" zc_status zc_decompress_batch(const zc_dec_seg *segs, uint32_t k, voi
     ZeroArgs z;
     std::memset(&z, 0, sizeof(z));
     uint64_t tiles[2] = {0, 0};
+    // the decode_kernel launch's span: one tile for a launch of at least
+    // kDecNarrowMin values, else two (decode_raw_kernel keeps two)
+    uint64_t coded_values = 0;
     for (uint32_t i = 0; i < k; ++i) {
         const zc_dec_seg &g = segs[i];
         if (!g.in || g.n > kMaxElems || (g.n && !g.out)) return ZC_ERR_INVALID_ARG;
@@ -332,6 +341,13 @@ extern "C" zc_status zc_decompress_batch(const zc_dec_seg *segs, uint32_t k, voi
         const Layout L = layout_for(g.n);
         // no stream of n values is shorter than both forms
         if (g.in_bytes < L.off_zp && g.in_bytes < kHeaderBytes + 2 * g.n) return ZC_ERR_CORRUPT;
+        if (g.in_bytes >= L.off_zp) coded_values += g.n;
+    }
+    const bool narrow = coded_values >= kDecNarrowMin;
+    const uint32_t span[2] = {narrow ? kTile : kTile * kDecWideTiles, kDecRawSpan};
+    for (uint32_t i = 0; i < k; ++i) {
+        const zc_dec_seg &g = segs[i];
+        const Layout L = layout_for(g.n);
         const int which = g.in_bytes < L.off_zp ? 1 : 0;
         DecSeg &d = a[which].seg[a[which].k++];
         d.in = static_cast<const uint8_t *>(g.in);
@@ -341,7 +357,7 @@ extern "C" zc_status zc_decompress_batch(const zc_dec_seg *segs, uint32_t k, voi
         d.n = (uint32_t)g.n;
         d.tile_begin = (uint32_t)tiles[which];
         a[which].tile_begin[a[which].k - 1] = d.tile_begin;
-        tiles[which] += dec_blocks(g.n);
+        tiles[which] += dec_blocks(g.n, span[which]);
         if (tiles[which] > 0xFFFFFFFFull) return ZC_ERR_INVALID_ARG;
         if (g.status) {
             z.r[z.count].ptr = reinterpret_cast<uint32_t *>(g.status);
@@ -356,8 +372,10 @@ extern "C" zc_status zc_decompress_batch(const zc_dec_seg *segs, uint32_t k, voi
     for (int which = 0; which < 2; ++which) {
         if (!a[which].k) continue;
         a[which].total_tiles = (uint32_t)tiles[which];
-        if (which == 0)
-            hipLaunchKernelGGL(decode_kernel, dim3(a[0].total_tiles), dim3(kThreads), 0, st, a[0]);
+        if (which == 0 && narrow)
+            hipLaunchKernelGGL(decode_kernel<1>, dim3(a[0].total_tiles), dim3(kThreads), 0, st, a[0]);
+        else if (which == 0)
+            hipLaunchKernelGGL(decode_kernel<kDecWideTiles>, dim3(a[0].total_tiles), dim3(kThreads), 0, st, a[0]);
         else
             hipLaunchKernelGGL(decode_raw_kernel, dim3(a[1].total_tiles), dim3(kThreads), 0, st, a[1]);
         if (hipGetLastError() != hipSuccess) return ZC_ERR_HIP;

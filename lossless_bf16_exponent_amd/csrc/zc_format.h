@@ -53,16 +53,22 @@ ZC_HD uint64_t enc_blocks(uint64_t n) {
     return b ? b : 1;
 }
 
-// The decoder gives each block a span of kDecSubTiles consecutive tiles.
-#ifndef ZC_DEC_SUBTILES
-#define ZC_DEC_SUBTILES 2
+// The decoder gives each block a span of one or two consecutive tiles, the
+// same for every segment of a launch: one tile when the launch decodes at
+// least kDecNarrowMin values, two otherwise.  (Measured on MI355X: one-tile
+// spans decode long launches 3-4 % faster once the device has settled, and
+// short ones up to 15 % slower.)  A test build lowers the threshold to 0.
+#ifndef ZC_DEC_NARROW_MIN
+#define ZC_DEC_NARROW_MIN (1ull << 27)
 #endif
-constexpr int kDecSubTiles = ZC_DEC_SUBTILES;
-constexpr uint32_t kDecSpan = kTile * kDecSubTiles;
-constexpr int kDecGroups = (int)(kDecSpan / kGroup);
+constexpr uint64_t kDecNarrowMin = ZC_DEC_NARROW_MIN;
+constexpr int kDecWideTiles = 2;
+constexpr uint32_t kDecRawSpan = kTile * kDecWideTiles;  // values per block of the raw-only decoder
 
-ZC_HD uint64_t dec_blocks(uint64_t n) {
-    const uint64_t b = (n + kDecSpan - 1) / kDecSpan;
+// Blocks for n values in spans of `span` values (at least one, so that n = 0
+// still checks its header).
+ZC_HD uint64_t dec_blocks(uint64_t n, uint32_t span) {
+    const uint64_t b = (n + span - 1) / span;
     return b ? b : 1;
 }
 

@@ -53,6 +53,8 @@ def load_test_build(zc, path: str):
     lib.zc_compress_batch_ws.argtypes = [ctypes.POINTER(zc.zc_enc_seg), ctypes.c_uint32, ctypes.c_void_p,
                                          ctypes.c_uint64, ctypes.c_void_p]
     lib.zc_compress_batch_ws.restype = ctypes.c_int
+    lib.zc_decompress_batch.argtypes = [ctypes.POINTER(zc.zc_dec_seg), ctypes.c_uint32, ctypes.c_void_p]
+    lib.zc_decompress_batch.restype = ctypes.c_int
     return lib
 
 
