@@ -94,14 +94,18 @@ def build_guess(verbose: bool = False) -> dict:
     return GUESS_LIBS
 
 
-NARROW_LIB = os.path.join(ROOT, "tests", "libzc_dec_narrow.so")
+SPAN_LIBS = {"one-tile": os.path.join(ROOT, "tests", "libzc_dec_narrow.so"),
+             "two-tile": os.path.join(ROOT, "tests", "libzc_dec_wide.so")}
 
 
-def build_narrow(verbose: bool = False) -> str:
-    """The library whose decoder takes one-tile spans for launches of any size
-    (the shipped one does so only from 2^27 values on), so that tests reach that
-    form on small and ragged inputs.  Test infrastructure only."""
-    return build_variant(NARROW_LIB, ["ZC_DEC_NARROW_MIN=0"], verbose)
+def build_spans(verbose: bool = False) -> dict:
+    """Two builds whose decoder takes one span form for launches of every size
+    (one tile, or two), where the shipped one picks by the launch's size, so
+    that tests reach both forms on small and ragged inputs.  Test
+    infrastructure only."""
+    build_variant(SPAN_LIBS["one-tile"], ["ZC_DEC_NARROW_MIN=0"], verbose)
+    build_variant(SPAN_LIBS["two-tile"], ["ZC_DEC_NARROW_MIN=0xFFFFFFFFFFFFFFFFull", "ZC_DEC_NARROW_MAX=0"], verbose)
+    return SPAN_LIBS
 
 
 def assembly(out_path: str, source: str = SOURCES[0]) -> str:

@@ -331,7 +331,8 @@ extern "C" zc_status zc_decompress_batch(const zc_dec_seg *segs, uint32_t k, voi
     std::memset(&z, 0, sizeof(z));
     uint64_t tiles[2] = {0, 0};
     // the decode_kernel launch's span: one tile for a launch of at least
-    // kDecNarrowMin values, else two (decode_raw_kernel keeps two)
+    // kDecNarrowMin values or at most kDecNarrowMax, else two
+    // (decode_raw_kernel keeps two)
     uint64_t coded_values = 0;
     for (uint32_t i = 0; i < k; ++i) {
         const zc_dec_seg &g = segs[i];
@@ -343,7 +344,7 @@ extern "C" zc_status zc_decompress_batch(const zc_dec_seg *segs, uint32_t k, voi
         if (g.in_bytes < L.off_zp && g.in_bytes < kHeaderBytes + 2 * g.n) return ZC_ERR_CORRUPT;
         if (g.in_bytes >= L.off_zp) coded_values += g.n;
     }
-    const bool narrow = coded_values >= kDecNarrowMin;
+    const bool narrow = coded_values >= kDecNarrowMin || coded_values <= kDecNarrowMax;
     const uint32_t span[2] = {narrow ? kTile : kTile * kDecWideTiles, kDecRawSpan};
     for (uint32_t i = 0; i < k; ++i) {
         const zc_dec_seg &g = segs[i];

@@ -55,13 +55,19 @@ ZC_HD uint64_t enc_blocks(uint64_t n) {
 
 // The decoder gives each block a span of one or two consecutive tiles, the
 // same for every segment of a launch: one tile when the launch decodes at
-// least kDecNarrowMin values, two otherwise.  (Measured on MI355X: one-tile
-// spans decode long launches 3-4 % faster once the device has settled, and
-// short ones up to 15 % slower.)  A test build lowers the threshold to 0.
+// least kDecNarrowMin values or at most kDecNarrowMax, two in between.
+// (Measured on MI355X: one-tile spans decode long launches 3-4 % faster once
+// the device has settled, and launches too small to fill the device up to
+// 20 % faster; in between, 58.7 Mi values for one, they were 3 % slower.)
+// Test builds move the thresholds so that either form takes every launch.
 #ifndef ZC_DEC_NARROW_MIN
 #define ZC_DEC_NARROW_MIN (1ull << 27)
 #endif
+#ifndef ZC_DEC_NARROW_MAX
+#define ZC_DEC_NARROW_MAX (1ull << 23)
+#endif
 constexpr uint64_t kDecNarrowMin = ZC_DEC_NARROW_MIN;
+constexpr uint64_t kDecNarrowMax = ZC_DEC_NARROW_MAX;
 constexpr int kDecWideTiles = 2;
 constexpr uint32_t kDecRawSpan = kTile * kDecWideTiles;  // values per block of the raw-only decoder
 

@@ -1,12 +1,12 @@
-"""The decoder's one-tile form on small and ragged inputs.  The shipped library
-decodes a launch of at least 2^27 values with one-tile spans and shorter ones
-with two-tile spans; a test build (tests/libzc_dec_narrow.so, threshold 0)
-takes the one-tile form for every launch, so the cases of the parity tests
-reach it: edge sizes, every bit pattern under several tables, zero-point
-densities from none to all, batches of many segments (block ranges of one
-tile), raw streams through the coded decoder's raw branch and through the
-raw-only decoder, header and table corruption, guard bytes.  Streams come from
-the oracle.  Integer and byte work: the bar is equality."""
+"""Both span forms of the decoder on small and ragged inputs.  The shipped
+library picks one-tile or two-tile spans by the size of the launch; two test
+builds (tests/libzc_dec_narrow.so, tests/libzc_dec_wide.so) take one form for
+every launch, so that the cases of the parity tests reach each form: edge
+sizes, every bit pattern under several tables, zero-point densities from none
+to all, batches of many segments (block ranges of one or two tiles), raw
+streams through the coded decoder's raw branch and through the raw-only
+decoder, header and table corruption, guard bytes.  Streams come from the
+oracle.  Integer and byte work: the bar is equality."""
 import numpy as np
 import pytest
 import torch
@@ -27,9 +27,9 @@ def zc():
     return require_gpu()
 
 
-@pytest.fixture(scope="module")
-def lib(zc):
-    return load_test_build(zc, _build.NARROW_LIB)
+@pytest.fixture(scope="module", params=sorted(_build.SPAN_LIBS))
+def lib(zc, request):
+    return load_test_build(zc, _build.SPAN_LIBS[request.param])
 
 
 def decode(zc, lib, streams, ns):
@@ -95,7 +95,7 @@ def test_zero_point_densities_in_one_batch(zc, lib):
 
 
 def test_batch_of_many_segments_with_raw_streams(zc, lib):
-    """Many segments in one launch (block ranges of one tile each), empty and
+    """Many segments in one launch (block ranges of one or two tiles), empty and
     one-value ones, and raw streams: long ones, whose exact size reaches the
     coded layout (the coded decoder's raw branch), and short ones, whose exact
     size does not (the raw-only decoder)."""
