@@ -323,6 +323,88 @@ def alltoall_order(zc, w, steps: int, warmup: int) -> dict:
     return rec
 
 
+TIMELINE_WORDS = 5  # per block in the instrumented build: four clock stamps and the role
+TIMELINE_TICK_US = 0.01  # the real-time clock runs at 100 MHz
+
+
+def timeline(zc, w, warmup: int) -> dict:
+    """Per-block timeline of one batched compress of workload w (no raw
+    fallback), from the instrumented build (libzc_timeline.so, ZC_TIMELINE):
+    after `warmup` calls, one call between HIP events with every block's four
+    clock stamps and role recorded (stamp meanings in zc_compress.hip).  The
+    record gives, per role, the median time between stamps, and the launch's
+    tail: what ends after the last encoder block."""
+    import ctypes
+    import numpy as np
+    import torch
+    from lossless_bf16_exponent_amd import _build
+    lib = ctypes.CDLL(_build.TIMELINE_LIB)
+    lib.zc_compress_batch_ws.argtypes = [ctypes.POINTER(zc.zc_enc_seg), ctypes.c_uint32, ctypes.c_void_p,
+                                         ctypes.c_uint64, ctypes.c_void_p]
+    lib.zc_compress_batch_ws.restype = ctypes.c_int
+    lib.zc_timeline_clear.restype = ctypes.c_int
+    lib.zc_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64]
+    lib.zc_timeline_read.restype = ctypes.c_int
+    stream = torch.cuda.current_stream()
+    r = Resident(zc, w)
+    arr, k = r.enc
+
+    def call():
+        rc = lib.zc_compress_batch_ws(arr, k, r.ws.data_ptr(), r.ws.numel(), stream.cuda_stream)
+        if rc != zc.ZC_OK:
+            raise RuntimeError("instrumented compress failed: %d" % rc)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    if lib.zc_timeline_clear() != 0:
+        raise RuntimeError("zc_timeline_clear failed")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    buf = np.zeros(TIMELINE_WORDS << 20, dtype=np.uint64)
+    if lib.zc_timeline_read(buf.ctypes.data, buf.nbytes) != 0:
+        raise RuntimeError("zc_timeline_read failed")
+    t = buf.reshape(-1, TIMELINE_WORDS)
+    ran = np.flatnonzero(t[:, 0])
+    blocks = int(ran.max()) + 1
+    t = t[:blocks]
+    stamps = t[:, :4].astype(np.int64)
+    stamps = (stamps - stamps[:, 0].min()) * TIMELINE_TICK_US
+    role = t[:, 4].astype(np.int64)
+    kind, seg = role & 3, (role >> 2) & 63
+    names = {0: "encoder_staged", 1: "encoder_direct", 2: "finalize"}
+
+    def med(a):
+        return round(float(np.median(a)), 2) if a.size else None
+    rec = {"workload": w.name, "values": w.n, "event_us": round(e0.elapsed_time(e1) * 1e3, 2), "blocks": blocks,
+           "span_us": round(float(stamps[:, 3].max()), 2), "stamps": "0 start, 1 first pass or span words, "
+           "2 bytes staged or offset known, 3 end (zc_compress.hip)", "roles": {}}
+    for kd, name in names.items():
+        m = kind == kd
+        if not m.any():
+            continue
+        S = stamps[m]
+        rec["roles"][name] = {"blocks": int(m.sum()), "lifetime_median_us": med(S[:, 3] - S[:, 0]),
+                              "stamp_0_1_median_us": med(S[:, 1] - S[:, 0]),
+                              "stamp_1_2_median_us": med(S[:, 2] - S[:, 1]),
+                              "stamp_2_3_median_us": med(S[:, 3] - S[:, 2]),
+                              "last_start_us": round(float(S[:, 0].max()), 2),
+                              "last_end_us": round(float(S[:, 3].max()), 2)}
+    enc = kind < 2
+    last_enc = float(stamps[enc, 3].max())
+    late = stamps[:, 3] > last_enc
+    rec["tail"] = {"last_encoder_end_us": round(last_enc, 2), "blocks_ending_later": int(late.sum()),
+                   "segments": sorted(set(int(v) for v in seg[late])), "last_end_us": round(float(stamps[:, 3].max()), 2)}
+    last = int(np.argmax(stamps[:, 3]))
+    rec["tail"]["last_block"] = {"role": names.get(int(kind[last]), str(int(kind[last]))), "segment": int(seg[last]),
+                                 "stamps_us": [round(float(v), 2) for v in stamps[last]]}
+    del r
+    torch.cuda.empty_cache()
+    return rec
+
+
 def profile_pass(zc, w, call: str, steps: int) -> dict:
     """The command rocprofv3 counter passes run (--profile CALL): a copy of
     known size with the bench library's copy kernel (the counters' scale: the
@@ -634,6 +716,9 @@ def main() -> int:
     ap.add_argument("--workload", default="3", help="headline workload id (1, 2, 3, 4, 5a, 5b); default 3")
     ap.add_argument("--only-headline", action="store_true", help="skip every record besides the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--timeline", action="store_true",
+                    help="print the per-block timeline of one compress call of --workload, from the instrumented "
+                         "build (libzc_timeline.so), instead of the bench line")
     ap.add_argument("--profile", choices=("compress", "decompress", "reduce"),
                     help="run only what a rocprofv3 counter pass measures: a copy of known size, then --steps "
                          "calls of this kind on --workload; prints that run's facts instead of the bench line")
@@ -659,6 +744,9 @@ def main() -> int:
     w = workloads.get(args.workload)
     if args.profile:
         print(json.dumps(profile_pass(zc, w, args.profile, args.steps)), flush=True)
+        return 0
+    if args.timeline:
+        print(json.dumps(timeline(zc, w, args.warmup)), flush=True)
         return 0
     log("workload %s: %d values in %d segments, generated in %.1f s"
         % (w.name, w.n, len(w.segments), time.perf_counter() - t_gen))

@@ -57,6 +57,15 @@ def build_bench(verbose: bool = False) -> str:
     return BENCH_LIB
 
 
+TIMELINE_LIB = os.path.join(PKG, "libzc_timeline.so")
+
+
+def build_timeline(verbose: bool = False) -> str:
+    """The codec built with the compress kernels' per-block timeline
+    (ZC_TIMELINE), for bench.py --timeline only; the codec never loads it."""
+    return build_variant(TIMELINE_LIB, ["ZC_TIMELINE"], verbose)
+
+
 def build_variant(path: str, defines, verbose: bool = False) -> str:
     """The library built with extra preprocessor definitions, at path."""
     tmp = path + ".tmp%d" % os.getpid()

@@ -51,6 +51,31 @@
 
 namespace zc {
 
+// Timeline of a compress launch, in an instrumented build only (ZC_TIMELINE,
+// the bench's libzc_timeline.so; the codec library compiles none of it):
+// thread 0 of each block records the real-time clock (100 MHz) at four points
+// of its role, and the role itself.  Stamp 0: the block starts; 1: an encoder
+// block's first pass is done (loads, codes, counts), a finalize block has its
+// run's span words; 2: a staged encoder block has stored its zero-point bytes
+// and seen them acknowledged, a direct one knows its offset, a finalize block
+// has landed its run's bytes and knows their offset; 3: the block ends.
+#ifdef ZC_TIMELINE
+constexpr uint32_t kTimelineBlocks = 1u << 20;
+constexpr uint32_t kTimelineWords = 5;  // four stamps and the role
+__device__ unsigned long long zc_timeline[kTimelineBlocks * kTimelineWords];
+__device__ __forceinline__ void stamp(uint32_t point) {
+    if (threadIdx.x == 0 && blockIdx.x < kTimelineBlocks)
+        zc_timeline[blockIdx.x * kTimelineWords + point] = __builtin_amdgcn_s_memrealtime();
+}
+__device__ __forceinline__ void stamp_role(uint32_t kind, uint32_t seg, uint32_t unit) {
+    if (threadIdx.x == 0 && blockIdx.x < kTimelineBlocks)
+        zc_timeline[blockIdx.x * kTimelineWords + 4] = kind | (seg << 2) | ((unsigned long long)unit << 8);
+}
+#else
+__device__ __forceinline__ void stamp(uint32_t) {}
+__device__ __forceinline__ void stamp_role(uint32_t, uint32_t, uint32_t) {}
+#endif
+
 // ---------------------------------------------------------------------------
 // kernel arguments (passed by value; at most ZC_MAX_BATCH segments)
 // ---------------------------------------------------------------------------
@@ -634,6 +659,7 @@ __device__ __forceinline__ void direct_finish(const EncArgs &args, uint32_t s, u
     ok = __syncthreads_and(ok);
     const uint32_t mine = (uint32_t)tid < nsib ? (pay[0] & 0xFFFFu) + (pay[0] >> 16) : pay[0];
     const uint32_t P = sib + block_sum(mine, sh.red);
+    stamp(2);
 
     if (ok && !raw) {
         uint32_t *const tab = reinterpret_cast<uint32_t *>(out + L.off_tab);
@@ -813,6 +839,7 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
         dst = direct_publish(args, s, b, c0, c1, sh);
     }
 
+    stamp(1);
     // ---- phase B: ranks, plane regrouping, zero-point staging
     uint32_t running = 0;  // zero-points of the span so far (uniform)
 #pragma unroll
@@ -887,6 +914,7 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
     // bytes at the coherence point) before the span word is written
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    stamp(2);
     if (tid == 0)
         put_word(scratch + S.span_words + (uint64_t)kWordBytes * b, Token{args.tok_lo, args.tok_hi},
                  sh.group[0] | (sh.group[1] << 16));
@@ -953,6 +981,7 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
     }
     __syncthreads();
     const uint32_t A = sh.pre[count];
+    stamp(1);
     if (ok && tid == 0) put_word(scratch + S.run_words + (uint64_t)kWordBytes * r, tok, A);
 
     // ---- staged bytes -> the zero-point array, a batch of spans at a time:
@@ -1055,6 +1084,7 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
         }
     }
 
+    stamp(2);
     // ---- 3. table entries and zero-point bytes
     if (ok && !raw) {
         if ((uint32_t)tid < count) {
@@ -1165,6 +1195,8 @@ __device__ __forceinline__ void sample_segment(const EncArgs &args, uint32_t s, 
 template <bool kFb>
 __device__ __forceinline__ void compress_block(const EncArgs &args, CompressShared &sh) {
     const BlockRole r = block_role(args, 1);
+    stamp(0);
+    stamp_role(r.kind, r.seg, r.unit);
     if (kFb && r.kind == kPieceSample) {
         sample_segment(args, r.unit, sh.e);
     } else if (r.kind == kPieceFinalize) {
@@ -1175,6 +1207,7 @@ __device__ __forceinline__ void compress_block(const EncArgs &args, CompressShar
     } else {
         encode_span<kFb>(args, r.seg, r.unit, r.kind == kPieceDirect, sh.e);
     }
+    stamp(3);
 }
 
 // Launches without the fallback.  Eight waves per SIMD: the register budget
@@ -1350,6 +1383,22 @@ static zc_status compress_impl(const zc_enc_seg *segs, uint32_t k, void *ws, uin
     b.ws = a.ws;
     return launch_compress(b, st, true);
 }
+
+#ifdef ZC_TIMELINE
+// The instrumented build's timeline: clear it before a launch, read it after
+// (both synchronous; 0 on success).
+extern "C" int zc_timeline_clear() {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(zc::zc_timeline)) != hipSuccess) return 1;
+    if (hipMemset(p, 0, sizeof(zc::zc_timeline)) != hipSuccess) return 1;
+    return hipDeviceSynchronize() == hipSuccess ? 0 : 1;
+}
+extern "C" int zc_timeline_read(void *dst, uint64_t bytes) {
+    if (bytes > sizeof(zc::zc_timeline)) bytes = sizeof(zc::zc_timeline);
+    return hipMemcpyFromSymbol(dst, HIP_SYMBOL(zc::zc_timeline), bytes, 0, hipMemcpyDeviceToHost) == hipSuccess ? 0
+                                                                                                       : 1;
+}
+#endif
 
 extern "C" zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void *stream) {
     return compress_impl(segs, k, nullptr, 0, stream);
