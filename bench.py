@@ -570,6 +570,31 @@ def reduce_measurement(zc, steps: int) -> dict:
     at 85-86 us from about the 250th call on (the device settling after a burst
     of this kernel), the steady state a training job that reduces bucket after
     bucket sees."""
+    import torch
+
+    call, state = reduce_setup(zc)
+    n, peers, totals = state["n"], state["peers"], state["totals"]
+    stream = torch.cuda.current_stream()
+    for _ in range(REDUCE_WARMUP_CALLS):
+        call()
+    torch.cuda.synchronize()
+    alg = sum(totals) + 4 * n  # the peer streams and the local share read, the result written
+    us = timed_groups(call, stream, GROUPS, max(1, steps // GROUPS))
+    rec = summary(us, alg, n)
+    t = load_traffic("reduce", "shard-32M-7peers")
+    rec.update({"traffic": t, "traffic_over_algorithmic": round(t / alg, 4) if t else None})
+    rec.update({"shard_values": n, "peers": peers, "local": True, "warmup_calls": REDUCE_WARMUP_CALLS,
+                "uncompressed_gbps": round(2.0 * n * (peers + 1) / (rec["us"] * 1e-6) / 1e9, 1),
+                "algorithmic_bytes": int(alg), "achieved_gbps": round(alg / (rec["us"] * 1e-6) / 1e9, 1),
+                "kernel": "reduce_kernel"})
+    del state
+    torch.cuda.empty_cache()
+    return rec
+
+
+def reduce_setup(zc):
+    """The shard of reduce_measurement, its 7 peers compressed: returns one
+    zc_decompress_reduce call (a function) and the buffers it uses."""
     import numpy as np
     import torch
 
@@ -590,21 +615,40 @@ def reduce_measurement(zc, steps: int) -> dict:
     out = torch.empty(n, dtype=torch.int16, device="cuda")
     stream = torch.cuda.current_stream()
     ptrs = [b.data_ptr() for b in bufs]
-    call = lambda: zc.zc_decompress_reduce(ptrs, totals, n, xs[0], out, None, stream)
-    for _ in range(REDUCE_WARMUP_CALLS):
-        call()
+    state = {"n": n, "peers": peers, "totals": totals, "xs": xs, "bufs": bufs, "out": out}
+    return (lambda: zc.zc_decompress_reduce(ptrs, totals, n, xs[0], out, None, stream)), state
+
+
+def percall(zc, w, call: str, calls: int) -> dict:
+    """HIP-event time of every one of `calls` back-to-back calls of one kind
+    (compress or decompress of workload w, or the reduce of
+    reduce_measurement), from the first call of the run on: the device's
+    start-of-burst transient that the warm-up counts are set from.  Means over
+    blocks of 50 calls."""
+    import numpy as np
+    import torch
+    stream = torch.cuda.current_stream()
+    keep = None
+    if call == "reduce":
+        fn, keep = reduce_setup(zc)
+    else:
+        keep = Resident(zc, w)
+        keep.check(zc, stream)
+        fn = (lambda: keep.compress(zc, stream)) if call == "compress" else (
+            lambda: zc.zc_decompress_batch(keep.dec_segs, stream))
     torch.cuda.synchronize()
-    alg = sum(totals) + 4 * n  # the peer streams and the local share read, the result written
-    us = timed_groups(call, stream, GROUPS, max(1, steps // GROUPS))
-    rec = summary(us, alg, n)
-    t = load_traffic("reduce", "shard-32M-7peers")
-    rec.update({"traffic": t, "traffic_over_algorithmic": round(t / alg, 4) if t else None})
-    rec.update({"shard_values": n, "peers": peers, "local": True, "warmup_calls": REDUCE_WARMUP_CALLS,
-                "uncompressed_gbps": round(2.0 * n * (peers + 1) / (rec["us"] * 1e-6) / 1e9, 1),
-                "algorithmic_bytes": int(alg), "achieved_gbps": round(alg / (rec["us"] * 1e-6) / 1e9, 1),
-                "kernel": "reduce_kernel"})
-    del xs, bufs, out
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(calls + 1)]
+    ev[0].record(stream)
+    for i in range(calls):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(calls)])
+    del keep
     torch.cuda.empty_cache()
+    return {"call": call, "workload": "shard-32M-7peers" if call == "reduce" else w.name, "calls": calls,
+            "note": "an event recorded between two kernels adds to each call; compare the blocks with each other",
+            "mean_us_per_50_calls": [round(float(t[i:i + 50].mean()), 1) for i in range(0, calls - 49, 50)]}
     return rec
 
 
@@ -719,6 +763,10 @@ def main() -> int:
     ap.add_argument("--timeline", action="store_true",
                     help="print the per-block timeline of one compress call of --workload, from the instrumented "
                          "build (libzc_timeline.so), instead of the bench line")
+    ap.add_argument("--percall", choices=("compress", "decompress", "reduce"),
+                    help="print the HIP-event time of every one of --calls back-to-back calls of this kind (means "
+                         "over 50), from the run's first call on, instead of the bench line")
+    ap.add_argument("--calls", type=int, default=400, help="calls for --percall (default 400)")
     ap.add_argument("--profile", choices=("compress", "decompress", "reduce"),
                     help="run only what a rocprofv3 counter pass measures: a copy of known size, then --steps "
                          "calls of this kind on --workload; prints that run's facts instead of the bench line")
@@ -747,6 +795,9 @@ def main() -> int:
         return 0
     if args.timeline:
         print(json.dumps(timeline(zc, w, args.warmup)), flush=True)
+        return 0
+    if args.percall:
+        print(json.dumps(percall(zc, w, args.percall, args.calls)), flush=True)
         return 0
     log("workload %s: %d values in %d segments, generated in %.1f s"
         % (w.name, w.n, len(w.segments), time.perf_counter() - t_gen))
