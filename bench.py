@@ -23,7 +23,8 @@ leaves the GPU idle for about 10 us.
 
 Every workload of the pages' configurations (1, 2, 3, 4, 5a, 5b) also gets a
 record: compress, decompress and checked decompress (with status words, the
-form a collective uses) timed in R groups of C back-to-back calls, mean and
+form a collective uses) timed in R groups of back-to-back calls (each group
+at least 1 ms of calls, behind an untimed lead call), mean and
 p10 / p50 / p90 of the per-call time over the groups, HBM fraction, bits per
 value; the two cache-resident configurations (1, 2) also cold, rotating
 through enough buffer sets that the footprint exceeds the 256 MB MALL twice.
@@ -104,20 +105,32 @@ def pct(vals, q):
     return float(np.percentile(np.asarray(vals, dtype=np.float64), q))
 
 
+MIN_GROUP_US = 1000.0  # GPU time a timing group spans at least
+
+
 def timed_groups(call, stream, groups: int, per: int) -> list:
-    """Per-call microseconds of `groups` groups of `per` back-to-back calls
-    (HIP events on the launch stream around each group)."""
+    """Per-call microseconds of `groups` groups of back-to-back calls (HIP
+    events on the launch stream around each group).  A group holds `per`
+    calls, or more where that spans less than MIN_GROUP_US (the count is
+    taken from a first, untimed group).  Each group starts behind one untimed
+    lead call, so the device is busy when the start event is recorded: the
+    host's launch time after the previous synchronize falls outside the timed
+    region, as it does for calls queued behind other work."""
+    import math
     import torch
-    out = []
-    for _ in range(groups):
+
+    def group(k: int) -> float:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        call()
         e0.record(stream)
-        for _ in range(per):
+        for _ in range(k):
             call()
         e1.record(stream)
         torch.cuda.synchronize()
-        out.append(e0.elapsed_time(e1) * 1e3 / per)
-    return out
+        return e0.elapsed_time(e1) * 1e3 / k
+
+    per = max(per, int(math.ceil(MIN_GROUP_US / max(group(per), 1e-3))))
+    return [group(per) for _ in range(groups)]
 
 
 def summary(us: list, alg_bytes: int, n: int) -> dict:
@@ -200,8 +213,9 @@ def measure_workload(zc, w, steps: int, warmup: int, cold: bool = False) -> dict
            "bits_per_value": round(8.0 * facts["stream_bytes"] / n, 4),
            "compression_ratio": round(facts["stream_bytes"] / (2.0 * n), 5),
            "zero_point_rate": round(facts["zero_points"] / n, 6), "algorithmic_bytes_per_call": int(alg),
-           "timing": "%d groups of %d back-to-back calls after %d warm-up calls; mean and percentiles of the "
-                     "per-call time over the groups" % (GROUPS, per, warmup)}
+           "timing": "%d groups of back-to-back calls (at least %d and at least %g us of calls per group, each "
+                     "behind an untimed lead call) after %d warm-up calls; mean and percentiles of the per-call "
+                     "time over the groups" % (GROUPS, per, MIN_GROUP_US, warmup)}
     calls = {"compress": lambda: r.compress(zc, stream),
              "decompress": lambda: zc.zc_decompress_batch(r.dec_segs, stream),
              "decompress_checked": lambda: zc.zc_decompress_batch(r.chk_segs, stream)}
@@ -442,10 +456,11 @@ def profile_pass(zc, w, call: str, steps: int) -> dict:
     return rec
 
 
-def ceilings(n: int, steps: int) -> dict:
+def ceilings(n: int, steps: int, warmup: int) -> dict:
     """Practical ceilings of the codec's access shapes for n values (a
     bench-only library): a 128-bit copy of 2n bytes, the encoder's shape (read
-    2 B, write 1.375 B per value) and the decoder's (read 1.375 B, write 2 B)."""
+    2 B, write 1.375 B per value) and the decoder's (read 1.375 B, write 2 B),
+    each timed after `warmup` calls like the codec's own calls."""
     import torch
     from lossless_bf16_exponent_amd import _build
     lib = ctypes.CDLL(_build.BENCH_LIB)
@@ -467,7 +482,7 @@ def ceilings(n: int, steps: int) -> dict:
                               2 * n + n + 3 * n // 8)}
     rec = {"values": n, "library": "libzc_bench.so (bench only)"}
     for name, (call, nbytes) in calls.items():
-        for _ in range(3):
+        for _ in range(warmup):
             if call() != 0:
                 raise RuntimeError("ceiling kernel %s failed" % name)
         us = timed_groups(call, stream, 5, max(1, steps // 5))
@@ -475,7 +490,7 @@ def ceilings(n: int, steps: int) -> dict:
         rec[name] = {"us": round(mean, 2), "bytes": int(nbytes), "gbps": round(nbytes / (mean * 1e-6) / 1e9, 1),
                      "hbm_frac": round(nbytes / (mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
     # torch's own device-to-device copy, for reference
-    for _ in range(3):
+    for _ in range(warmup):
         b.copy_(a)
     us = timed_groups(lambda: b.copy_(a), stream, 5, max(1, steps // 5))
     mean = sum(us) / len(us)
@@ -652,11 +667,11 @@ def percall(zc, w, call: str, calls: int) -> dict:
     return rec
 
 
-def stats_measurement(zc, x, seg_ns, steps: int) -> dict:
+def stats_measurement(zc, x, seg_ns, steps: int, warmup: int) -> dict:
     """The online statistics that section 2.A replaces by its sigma-derived
     table, on the resident gradient bucket: the exponent histogram and the
-    sigma estimate of the whole buffer (HIP events around K back-to-back
-    calls; algorithmic bytes = the 2n input bytes read), and the wall time of
+    sigma estimate of the whole buffer (HIP events around groups of back-to-back
+    calls after `warmup` calls; algorithmic bytes = the 2n input bytes read), and the wall time of
     the histogram route to a table for every segment (one histogram per
     segment, one copy of the counts to the host, host top-7), against the
     closed-form route (host table from the known sigma)."""
@@ -674,7 +689,7 @@ def stats_measurement(zc, x, seg_ns, steps: int) -> dict:
     out = {"values": n, "kernels": {"histogram": "hist_kernel + hist_sum_kernel",
                                     "sigma": "sigma_kernel + sigma_final_kernel"}}
     for name, call in (("histogram", hist_call), ("sigma", sig_call)):
-        for _ in range(3):
+        for _ in range(warmup):
             call()
         us = timed_groups(call, stream, 5, max(1, steps // 5))
         ms = sum(us) / len(us) / 1e3
@@ -707,11 +722,12 @@ def stats_measurement(zc, x, seg_ns, steps: int) -> dict:
     return out
 
 
-def fallback_measurement(zc, steps: int) -> dict:
+def fallback_measurement(zc, steps: int, warmup: int) -> dict:
     """The raw fallback on the stress workload that coding expands most
     (2^24 uniformly random non-NaN/Inf BF16 patterns under the sigma = 0.02
     plan, 18.8 bits per value coded): compress with ZC_PLAN_RAW_FALLBACK and
-    decompress of the raw stream, in groups of back-to-back calls."""
+    decompress of the raw stream, in groups of back-to-back calls after
+    `warmup` calls of each."""
     import numpy as np
     import torch
 
@@ -738,7 +754,7 @@ def fallback_measurement(zc, steps: int) -> dict:
     res = {"workload": w.name, "values": n, "stream_bytes": total, "raw": True}
     alg = 2 * n + total
     for name, call in (("compress", enc_call), ("decompress", dec_call)):
-        for _ in range(3):
+        for _ in range(warmup):
             call()
         res[name] = summary(timed_groups(call, stream, GROUPS, max(1, steps // GROUPS)), alg, n)
     res["kernels"] = {"compress": "compress_fallback_kernel (the guessing launch) + compress_second_kernel",
@@ -895,9 +911,10 @@ def main() -> int:
         "kernel_sha": {c: kernel_source_hash(c) for c in CALL_SOURCES},
     }
     if not args.only_headline:
-        rec["plan_variants"] = stats_measurement(zc, x_keep, [seg.x.size for seg in w.segments], args.steps)
+        rec["plan_variants"] = stats_measurement(zc, x_keep, [seg.x.size for seg in w.segments], args.steps,
+                                                 args.warmup)
         rec["plan_variants"]["sigma_table_us_per_bucket"] = round(plan_us * len(w.segments), 2)
-        rec["ceilings"] = ceilings(n, args.steps)
+        rec["ceilings"] = ceilings(n, args.steps, args.warmup)
     del x_keep
     torch.cuda.empty_cache()
     if not args.only_headline:
@@ -916,7 +933,7 @@ def main() -> int:
         log("all-gather receive side")
         rec["allgather_receive"] = allgather_receive(zc, args.steps, args.warmup)
         log("raw fallback")
-        rec["raw_fallback"] = fallback_measurement(zc, args.steps)
+        rec["raw_fallback"] = fallback_measurement(zc, args.steps, args.warmup)
         log("reduce-scatter receive side")
         rec["reduce_scatter_local"] = reduce_measurement(zc, args.steps)
     if not args.no_cpu_baseline:
