@@ -139,7 +139,15 @@ uint64_t zc_compress_workspace_bytes(uint64_t n);
  * stream's header has a zero magic (every decoder rejects it with
  * ZC_ERR_CORRUPT) and *d_out_bytes reads 0: a caller that sends
  * *d_out_bytes bytes sends nothing, and a caller that reads the header sees
- * an invalid stream.  Neither outcome passes for a valid stream. */
+ * an invalid stream.  Neither outcome passes for a valid stream.
+ * HIP graphs: the call may be captured into a graph and the graph replayed
+ * with new inputs in the same buffers; every replay produces the stream of
+ * its input.  (The workgroups' words carry a token that mixes the call's
+ * token with an 8-byte counter in the scratch, which every call advances, so
+ * a replay, whose arguments repeat the captured ones, never takes the words
+ * of an earlier replay for its own.)  After a given-up call, zero the scratch
+ * (the workspace, or d_out past zc_max_compressed_bytes(n)) before a graph
+ * that uses it is replayed. */
 zc_status zc_compress(const void *d_in, uint64_t n, const zc_plan *plan, void *d_out,
                       uint64_t out_capacity, uint64_t *d_out_bytes, void *stream);
 
@@ -276,8 +284,8 @@ typedef struct zc_dec_seg {
  * all-to-all segments); a second launch follows, over the segments whose plan
  * has ZC_PLAN_RAW_FALLBACK, when there are any.  Each output equals what
  * zc_compress gives for that segment alone (the given-up outcome of
- * zc_compress included, per segment).  segs is a host array read before the
- * call returns. */
+ * zc_compress included, per segment; graph capture as for zc_compress).  segs
+ * is a host array read before the call returns. */
 zc_status zc_compress_batch(const zc_enc_seg *segs, uint32_t k, void *stream);
 
 /* zc_compress_batch with every segment's scratch in one workspace (segment

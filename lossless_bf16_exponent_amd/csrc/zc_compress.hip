@@ -101,6 +101,7 @@ struct EncArgs {
     uint32_t pieces;
     uint32_t tok_lo, tok_hi;  // the launch's token (scratch words of other launches never match it)
     uint32_t prev_lo, prev_hi;  // the fallback's second launch: the token of the call's first launch
+    uint32_t advance;           // 1: each segment's header writer advances the segment's epoch
     uint32_t mult;            // units (spans or runs) per block (zc_grid.h)
     uint32_t chunk;           // spans per staged chunk
     uint8_t *ws;              // the call's workspace, or null: each segment's scratch behind its stream
@@ -167,12 +168,47 @@ __device__ __forceinline__ void put_word(uint8_t *w, Token t, uint32_t payload) 
     __hip_atomic_store(p + 1, ((uint64_t)t.hi << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ bool get_word(const uint8_t *w, Token t, uint32_t &payload) {
-    uint64_t *p = reinterpret_cast<uint64_t *>(const_cast<uint8_t *>(w));
-    const uint64_t a = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t b = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// A word's two halves as loaded, checked against token t.
+__device__ __forceinline__ bool word_valid(uint64_t a, uint64_t b, Token t, uint32_t &payload) {
     payload = (uint32_t)a;
     return (uint32_t)(a >> 32) == t.lo && (uint32_t)(b >> 32) == t.hi && (uint32_t)a == (uint32_t)b;
+}
+__device__ __forceinline__ void load_word(const uint8_t *w, uint64_t &a, uint64_t &b) {
+    uint64_t *p = reinterpret_cast<uint64_t *>(const_cast<uint8_t *>(w));
+    a = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    b = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool get_word(const uint8_t *w, Token t, uint32_t &payload) {
+    uint64_t a, b;
+    load_word(w, a, b);
+    return word_valid(a, b, t, payload);
+}
+
+// The segment's epoch word, read by every block of a launch before
+// it publishes or polls anything.  The segment's header writer advances it at
+// the end of a call's first launch, once every other block of the segment has
+// passed its waits: by then each of them has read it.  So within a launch the
+// word does not change while anyone reads it, and a load that may hit the L2
+// serves: the value a reader needs was written by an earlier launch on the
+// stream, which the kernel boundary makes visible.  (A device-scope load from
+// every block of the launch, all to one line, cost 2-4 us per call.)  It is a
+// vector load (a workgroup-scope atomic, which the compiler never turns into a
+// scalar load): a scalar load would be waited for with every later wait for
+// scalar or LDS results, which complete out of order.
+__device__ __forceinline__ uint64_t *epoch_word(const EncArgs &args, const EncSeg &sg) {
+    return reinterpret_cast<uint64_t *>(seg_scratch(args, sg) + scratch_for(sg.n).epoch);
+}
+__device__ __forceinline__ uint64_t read_epoch(const EncArgs &args, const EncSeg &sg) {
+    return __hip_atomic_load(epoch_word(args, sg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// A launch's token for a segment: the call's token from the host mixed with
+// the segment's epoch.  A replay of a captured graph repeats the host's token
+// but not the epoch, so its words never pass for the previous replay's.
+__device__ __forceinline__ Token mix_token(uint32_t lo, uint32_t hi, uint64_t epoch) {
+    return Token{lo ^ (uint32_t)epoch, hi ^ (uint32_t)(epoch >> 32)};
+}
+__device__ __forceinline__ Token launch_token(const EncArgs &args, const EncSeg &sg) {
+    return mix_token(args.tok_lo, args.tok_hi, read_epoch(args, sg));
 }
 
 // Staged zero-point bytes move between blocks with the same cache policy as
@@ -203,15 +239,17 @@ constexpr uint32_t kSpinLimit = ZC_SPIN_LIMIT;
 
 // Thread tid polls words addr(i), i = tid + kThreads q (q < Q, i < count),
 // until every one carries the token.  Payloads of valid words land in pay[q]
-// (0 for indices at or past count).  Returns false on timeout.
+// (0 for indices at or past count).  done: bit q set when the caller has
+// already found word q valid, its payload in pay[q].  Returns false on timeout.
 template <int Q, typename Addr>
-__device__ __forceinline__ bool poll_list(uint32_t count, Addr addr, Token t, uint32_t (&pay)[Q]) {
+__device__ __forceinline__ bool poll_list(uint32_t count, Addr addr, Token t, uint32_t (&pay)[Q],
+                                          uint32_t done = 0) {
     const uint32_t i0 = threadIdx.x;
     uint32_t pend = 0;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-        pay[q] = 0;
-        if (i0 + kThreads * q < count) pend |= 1u << q;
+        if (!(done >> q & 1u)) pay[q] = 0;
+        if (i0 + kThreads * q < count && !(done >> q & 1u)) pend |= 1u << q;
     }
     for (uint32_t it = 0; pend; ++it) {
         if (it == kSpinLimit) return false;
@@ -232,8 +270,9 @@ __device__ __forceinline__ bool poll_list(uint32_t count, Addr addr, Token t, ui
 
 // The same over words base[0 .. count).
 template <int Q>
-__device__ __forceinline__ bool poll_words(const uint8_t *base, uint32_t count, Token t, uint32_t (&pay)[Q]) {
-    return poll_list<Q>(count, [base](uint32_t i) { return base + (uint64_t)kWordBytes * i; }, t, pay);
+__device__ __forceinline__ bool poll_words(const uint8_t *base, uint32_t count, Token t, uint32_t (&pay)[Q],
+                                           uint32_t done = 0) {
+    return poll_list<Q>(count, [base](uint32_t i) { return base + (uint64_t)kWordBytes * i; }, t, pay, done);
 }
 
 // Sum of v over the block (every thread gets it); red: kWaves words of LDS.
@@ -449,19 +488,23 @@ __device__ __forceinline__ bool guesses(const EncSeg &sg) {
 // Second launch: what the first left for this segment (read once: the first
 // launch has ended).  A segment without a status word of the first launch
 // (given up) needs nothing.
-__device__ __forceinline__ uint32_t second_pass_mode(const EncArgs &args, const uint8_t *scratch,
-                                                     const Scratch &S) {
+__device__ __forceinline__ uint32_t second_pass_mode(const EncArgs &args, const EncSeg &sg) {
+    const uint64_t e = read_epoch(args, sg);
+    uint64_t a, b;
+    load_word(seg_scratch(args, sg) + scratch_for(sg.n).status, a, b);  // in flight with the epoch
+    // the first launch advanced the epoch once: its token used the one before
+    const Token prev = mix_token(args.prev_lo, args.prev_hi, e - 1u);
     uint32_t st = 0;
-    if (!get_word(scratch + S.status, Token{args.prev_lo, args.prev_hi}, st)) return kModeSkip;
+    if (!word_valid(a, b, prev, st)) return kModeSkip;
     return st == kStatusNeedRaw ? kModeCopyRaw : (st == kStatusNeedCoded ? kModeCodedPass : kModeSkip);
 }
 
 // First launch, a block of a guessing segment: the guess (uniform), or
 // kModeAbort when the wait for it gives up.
-__device__ __forceinline__ uint32_t await_guess(const EncArgs &args, const uint8_t *scratch, const Scratch &S,
+__device__ __forceinline__ uint32_t await_guess(const uint8_t *scratch, const Scratch &S, Token tok,
                                                 uint32_t *red) {
     uint32_t d[1] = {0};
-    bool ok = poll_words<1>(scratch + S.decision, 1, Token{args.tok_lo, args.tok_hi}, d);
+    bool ok = poll_words<1>(scratch + S.decision, 1, tok, d);
     ok = __syncthreads_and(ok);
     const uint32_t g = block_sum(d[0], red);  // thread 0's payload, to every thread
     return !ok ? kModeAbort : (g == kDecideRaw ? kModeSpecRaw : kModeCodedPass);
@@ -547,7 +590,7 @@ __device__ __forceinline__ void copy_span_raw(const uint16_t *in, uint8_t *out, 
 // invalid until then).
 template <bool kFb>
 __device__ __forceinline__ void write_header(const EncArgs &args, const EncSeg &sg, const Layout &L, uint64_t E,
-                                             bool ok, bool guessed_raw) {
+                                             bool ok, bool guessed_raw, Token tok) {
     const int tid = threadIdx.x;
     const uint64_t n = sg.n;
     uint8_t *const out = sg.out;
@@ -583,7 +626,12 @@ __device__ __forceinline__ void write_header(const EncArgs &args, const EncSeg &
     }
     if (tid == 0 && sg.out_bytes) *sg.out_bytes = valid ? total : 0ull;
     if (kFb && ok && tid == 0 && (sg.flags & kSegRawOk))
-        put_word(seg_scratch(args, sg) + scratch_for(n).status, Token{args.tok_lo, args.tok_hi}, status);
+        put_word(seg_scratch(args, sg) + scratch_for(n).status, tok, status);
+    // the epoch this launch read (its token without the host's part), plus one
+    if (args.advance && tid == 0)
+        __hip_atomic_store(epoch_word(args, sg),
+                           (((uint64_t)(tok.hi ^ args.tok_hi) << 32) | (tok.lo ^ args.tok_lo)) + 1u,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Direct role (every block of a launch that the device holds at once;
@@ -602,13 +650,12 @@ struct DirectState {
     bool ok;
 };
 __device__ __forceinline__ DirectState direct_publish(const EncArgs &args, uint32_t s, uint32_t b, uint32_t c0,
-                                                      uint32_t c1, EncShared &sh) {
+                                                      uint32_t c1, Token tok, EncShared &sh) {
     const int tid = threadIdx.x;
     const EncSeg &sg = args.seg[s];
     const uint64_t n = sg.n;
     const Scratch S = scratch_for(n);
     const uint32_t nb = (uint32_t)enc_blocks(n);
-    const Token tok{args.tok_lo, args.tok_hi};
     uint8_t *const scratch = seg_scratch(args, sg);
     const uint32_t g = b / kGroupSpans, g0 = g * kGroupSpans;  // g0: the group's first span
     const bool group_last = b % kGroupSpans == kGroupSpans - 1 || b + 1 == nb;
@@ -627,14 +674,13 @@ __device__ __forceinline__ DirectState direct_publish(const EncArgs &args, uint3
 
 template <bool kFb>
 __device__ __forceinline__ void direct_finish(const EncArgs &args, uint32_t s, uint32_t b, uint32_t T, uint32_t c0,
-                                              uint32_t c1, bool raw, DirectState st, EncShared &sh) {
+                                              uint32_t c1, bool raw, DirectState st, Token tok, EncShared &sh) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const EncSeg &sg = args.seg[s];
     const uint64_t n = sg.n;
     const Layout L = layout_for(n);
     const Scratch S = scratch_for(n);
     const uint32_t nb = (uint32_t)enc_blocks(n);
-    const Token tok{args.tok_lo, args.tok_hi};
     uint8_t *const out = sg.out;
     uint8_t *const scratch = seg_scratch(args, sg);
     const uint8_t *const span_w = scratch + S.span_words;
@@ -682,7 +728,7 @@ __device__ __forceinline__ void direct_finish(const EncArgs &args, uint32_t s, u
         ok = poll_words<8>(scratch + S.span_done, b, tok, dn);
     }
     ok = __syncthreads_and(ok);
-    write_header<kFb>(args, sg, L, (uint64_t)P + c0 + c1, ok, raw);
+    write_header<kFb>(args, sg, L, (uint64_t)P + c0 + c1, ok, raw, tok);
 }
 
 // Encoder role under a raw guess: the span's loaded values go behind the
@@ -691,7 +737,7 @@ __device__ __forceinline__ void direct_finish(const EncArgs &args, uint32_t s, u
 // waves 2 and 3 the second.
 __device__ __forceinline__ void raw_span(const EncArgs &args, uint32_t s, uint32_t b, bool direct,
                                          const Step (&in)[kEncSubTiles][kSteps], bool table, uint32_t base_hi,
-                                         EncShared &sh) {
+                                         Token tok, EncShared &sh) {
     static_assert(kEncSubTiles == 1 && kWaves == 4, "a span is one tile, two waves per group");
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const EncSeg &sg = args.seg[s];
@@ -716,14 +762,13 @@ __device__ __forceinline__ void raw_span(const EncArgs &args, uint32_t s, uint32
     __syncthreads();
     const uint32_t c0 = sh.red[0] + sh.red[1], c1 = sh.red[2] + sh.red[3];
     if (direct) {
-        direct_finish<true>(args, s, b, 0, c0, c1, true, direct_publish(args, s, b, c0, c1, sh), sh);
+        direct_finish<true>(args, s, b, 0, c0, c1, true, direct_publish(args, s, b, c0, c1, tok, sh), tok, sh);
         return;
     }
     // a count announces no data: no wait before the span word
     if (tid == 0) {
         const Scratch S = scratch_for(n);
-        put_word(seg_scratch(args, sg) + S.span_words + (uint64_t)kWordBytes * b,
-                 Token{args.tok_lo, args.tok_hi}, c0 | (c1 << 16));
+        put_word(seg_scratch(args, sg) + S.span_words + (uint64_t)kWordBytes * b, tok, c0 | (c1 << 16));
     }
 }
 
@@ -762,6 +807,10 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
     uint32_t mode = kModeCodedPass;
     const bool guessing = kFb && guesses(sg);
 
+    // the token: right ahead of the span's loads, which complete in order, so
+    // that waiting for the first of them covers it
+    const Token tok = launch_token(args, sg);
+
     // ---- every load of the span in flight at once
     Step in[kEncSubTiles][kSteps];
 #pragma unroll
@@ -771,18 +820,18 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
             in[sub][u] = load_step(sg.in, span0 + (uint64_t)sub * kTile + 512u * (uint32_t)(wave * kSteps + u) +
                                               8u * (uint32_t)lane, n);
     if (kFb && guessing) {
-        mode = await_guess(args, scratch, S, sh.red);  // its barriers also cover sh.code
+        mode = await_guess(scratch, S, tok, sh.red);  // its barriers also cover sh.code
         if (mode == kModeAbort) {
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
             // a direct segment's last span writes the header: the invalid one
-            if (direct && b + 1 == blocks) write_header<kFb>(args, sg, L, 0, false, false);
+            if (direct && b + 1 == blocks) write_header<kFb>(args, sg, L, 0, false, false, tok);
             return;
         }
     } else if (table) {
         __syncthreads();  // sh.code ready
     }
     if (kFb && mode == kModeSpecRaw) {
-        raw_span(args, s, b, direct, in, table, base_hi, sh);
+        raw_span(args, s, b, direct, in, table, base_hi, tok, sh);
         return;
     }
 
@@ -836,7 +885,7 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
         __syncthreads();
         c0 = sh.red[0] + sh.red[1];
         c1 = sh.red[2] + sh.red[3];
-        dst = direct_publish(args, s, b, c0, c1, sh);
+        dst = direct_publish(args, s, b, c0, c1, tok, sh);
     }
 
     stamp(1);
@@ -896,9 +945,9 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
         if (kFb) {
             c0 = sh.group[0];
             c1 = sh.group[1];
-            dst = direct_publish(args, s, b, c0, c1, sh);
+            dst = direct_publish(args, s, b, c0, c1, tok, sh);
         }
-        direct_finish<kFb>(args, s, b, T, c0, c1, false, dst, sh);
+        direct_finish<kFb>(args, s, b, T, c0, c1, false, dst, tok, sh);
         return;
     }
 
@@ -916,7 +965,7 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
     __syncthreads();
     stamp(2);
     if (tid == 0)
-        put_word(scratch + S.span_words + (uint64_t)kWordBytes * b, Token{args.tok_lo, args.tok_hi},
+        put_word(scratch + S.span_words + (uint64_t)kWordBytes * b, tok,
                  sh.group[0] | (sh.group[1] << 16));
 }
 
@@ -947,7 +996,7 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
     const bool last_run = r + 1 == nr;
     const uint32_t c = r / kChunkRuns, cfirst = c * kChunkRuns;
     const bool chunk_last = r % kChunkRuns == kChunkRuns - 1 || last_run;
-    const Token tok{args.tok_lo, args.tok_hi};
+    const uint64_t epoch = read_epoch(args, sg);
     uint8_t *const out = sg.out;
     uint8_t *const scratch = seg_scratch(args, sg);
     uint32_t *const tab = reinterpret_cast<uint32_t *>(out + L.off_tab);
@@ -956,15 +1005,22 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
     // spans staged nothing)
     bool raw = false, ok = true;
     if (kFb && guesses(sg)) {
-        const uint32_t m = await_guess(args, scratch, S, sh.red);
+        const uint32_t m = await_guess(scratch, S, mix_token(args.tok_lo, args.tok_hi, epoch), sh.red);
         ok = m != kModeAbort;
         raw = m == kModeSpecRaw;
     }
 
     // ---- 1. the run's span words (threads 0 .. count-1, all in wave 0): the
-    // exclusive prefixes of zero-points and of landing units, the run's count
+    // exclusive prefixes of zero-points and of landing units, the run's count.
+    // The first round of loads goes out before the token is formed, so that
+    // it is in flight with the epoch's load.
+    const uint8_t *const sw = scratch + S.span_words + (uint64_t)kWordBytes * first;
+    uint64_t w0 = 0, w1 = 0;
+    if (ok && (uint32_t)tid < count) load_word(sw + (uint64_t)kWordBytes * tid, w0, w1);
+    const Token tok = mix_token(args.tok_lo, args.tok_hi, epoch);
     uint32_t sp[1] = {0};
-    if (ok) ok = poll_words<1>(scratch + S.span_words + (uint64_t)kWordBytes * first, count, tok, sp);
+    const uint32_t done = (uint32_t)tid < count && word_valid(w0, w1, tok, sp[0]) ? 1u : 0u;
+    if (ok) ok = poll_words<1>(sw, count, tok, sp, done);
     ok = __syncthreads_and(ok);
     if (wave == 0) {
         const uint32_t g0 = sp[0] & 0xFFFFu, T = g0 + (sp[0] >> 16), U = (T + 15) / 16;  // 0 past count
@@ -1133,7 +1189,7 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
     // guess wrote nothing a done word would cover: every span's count is in
     // the header writer's offset.
     if (kFb && raw) {
-        if (last_run) write_header<kFb>(args, sg, L, (uint64_t)P + A, ok, true);
+        if (last_run) write_header<kFb>(args, sg, L, (uint64_t)P + A, ok, true, tok);
         return;
     }
     if (!chunk_last) {
@@ -1154,7 +1210,7 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
         if (ok) ok = poll_words<2>(scratch + S.chunk_done, c, tok, dn);
         ok = __syncthreads_and(ok);
     }
-    write_header<kFb>(args, sg, L, (uint64_t)P + A, ok, false);
+    write_header<kFb>(args, sg, L, (uint64_t)P + A, ok, false, tok);
 }
 
 // The role of block blockIdx.x: its piece's kind and segment, and its first
@@ -1175,6 +1231,7 @@ __device__ __forceinline__ BlockRole block_role(const EncArgs &args, uint32_t mu
 __device__ __forceinline__ void sample_segment(const EncArgs &args, uint32_t s, EncShared &sh) {
     const EncSeg &sg = args.seg[s];
     if (!guesses(sg)) return;
+    const Token tok = launch_token(args, sg);
     const bool table = (sg.flags & kSegTable) != 0;
     if (table) {
         uint32_t c = 0;
@@ -1187,7 +1244,7 @@ __device__ __forceinline__ void sample_segment(const EncArgs &args, uint32_t s, 
     const uint32_t base_hi = (wbase << 8) | (wbase << 24);
     const Layout L = layout_for(sg.n);
     const uint32_t d = sample_guess(sg, L, table, base_hi, sh.code, sh.red);
-    if (threadIdx.x == 0) put_word(seg_scratch(args, sg) + scratch_for(sg.n).decision, Token{args.tok_lo, args.tok_hi}, d);
+    if (threadIdx.x == 0) put_word(seg_scratch(args, sg) + scratch_for(sg.n).decision, tok, d);
 }
 
 // One block of a compress launch, one unit.  kFb: the launch has segments
@@ -1243,7 +1300,7 @@ __global__ __launch_bounds__(kThreads) void compress_second_kernel(EncArgs args)
     const EncSeg &sg = args.seg[r.seg];
     const uint32_t u1 = (uint32_t)min((uint64_t)r.unit + args.mult,
                                       piece_end(r.kind, args.first[r.p], enc_blocks(sg.n), args.chunk));
-    const uint32_t mode = second_pass_mode(args, seg_scratch(args, sg), scratch_for(sg.n));
+    const uint32_t mode = second_pass_mode(args, sg);
     if (mode == kModeSkip) return;
     if (mode == kModeCopyRaw) {
         if (r.kind != kPieceFinalize)
@@ -1362,6 +1419,7 @@ static zc_status compress_impl(const zc_enc_seg *segs, uint32_t k, void *ws, uin
     const uint64_t tok = next_token();
     a.tok_lo = (uint32_t)tok;
     a.tok_hi = (uint32_t)(tok >> 32);
+    a.advance = 1;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     zc_status rc = launch_compress(a, st, false);

@@ -130,6 +130,8 @@ ZC_HD uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 // for either mode:
 //   decision      raw fallback: the first pass's guess, raw or coded
 //   status        raw fallback: what the second pass still has to do
+//   epoch         8 bytes, no token: a counter the segment's header writer
+//                 advances at the end of each call's first launch
 //   span words    one per encoder span: zero-point counts of its two groups
 //   run words     one per run: zero-point count of the run
 //   chunk words   one per chunk: zero-point count of its runs
@@ -138,12 +140,15 @@ ZC_HD uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 //   run done      one per run: its finalize block passed its waits
 //   span done     one per direct span: its block passed its waits
 //   staging       kEncSpan B per encoder span: its zero-point bytes, in order
-// Every word carries the 64-bit token of the call that wrote it, so words
-// left by an earlier call (or any other old contents) never pass for fresh.
+// Every word carries the 64-bit token of the launch that wrote it, so words
+// left by an earlier launch (or any other old contents) never pass for fresh.
+// A launch's token is the call's token from the host mixed with the epoch, so
+// that it also changes between replays of a captured graph, which repeat the
+// host's arguments.
 constexpr uint32_t kWordBytes = 16;
 struct Scratch {
-    uint64_t decision, status, span_words, run_words, chunk_words, chunk_done, group_words, run_done, span_done,
-        staging, bytes;  // offsets from off_scratch, total size
+    uint64_t decision, status, epoch, span_words, run_words, chunk_words, chunk_done, group_words, run_done,
+        span_done, staging, bytes;  // offsets from off_scratch, total size
 };
 ZC_HD Scratch scratch_for(uint64_t n) {
     const uint64_t nb = enc_blocks(n), nr = ceil_div(nb, kRun), nc = ceil_div(nr, kChunkRuns);
@@ -151,7 +156,8 @@ ZC_HD Scratch scratch_for(uint64_t n) {
     Scratch S;
     S.decision = 0;
     S.status = kWordBytes;
-    S.span_words = align128(2 * kWordBytes);
+    S.epoch = 2 * kWordBytes;
+    S.span_words = align128(2 * kWordBytes + 8);
     S.run_words = S.span_words + align128(kWordBytes * nb);
     S.chunk_words = S.run_words + align128(kWordBytes * nr);
     S.chunk_done = S.chunk_words + align128(kWordBytes * nc);

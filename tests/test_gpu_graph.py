@@ -1,0 +1,165 @@
+"""Compress and decompress captured in a HIP graph (torch.cuda.CUDAGraph) and
+replayed with new inputs: after every replay each stream equals the oracle's
+for that replay's input, byte for byte, and decodes back to it.
+
+The blocks of a compress launch hand counts and offsets to each other through
+words in the segment's scratch, each word marked with the launch's token, so
+that words left by earlier calls never pass for current ones.  A replay runs
+with the arguments that were captured; the token must still change from one
+replay to the next.  Cases: a staged batch (more spans than the device holds
+at once), a direct launch, and segments under the raw fallback whose outcome
+flips between coded and raw from one replay to the next (two launches per
+call); the scratch in a workspace or behind each stream; an eager call on the
+same buffers between two replays."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import require_gpu, slot, to_host_u16
+from lossless_bf16_exponent_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+SPAN = 8192
+
+
+@pytest.fixture(scope="module")
+def zc():
+    return require_gpu()
+
+
+def gaussian(g, n: int, sigma: float) -> np.ndarray:
+    return workloads.bf16_bits_from_f32(g.standard_normal(n).astype(np.float32) * np.float32(sigma))
+
+
+def uniform_patterns(g, n: int) -> np.ndarray:
+    """Any BF16 pattern but NaN/Inf: coding expands these (raw under the fallback)."""
+    x = g.integers(0, 1 << 16, n).astype(np.uint16)
+    return np.where((x & 0x7F80) == 0x7F80, x & 0x807F, x).astype(np.uint16)
+
+
+class Captured:
+    """Buffers of one batch (inputs, outputs with their sizes, workspace,
+    decode outputs) and a graph holding one compress and one decompress call."""
+
+    def __init__(self, zc, ns, sigmas, flags, workspace: bool):
+        self.ns, self.sigmas, self.flags = ns, sigmas, flags
+        plans = [zc.zc_plan_from_sigma(s) for s in sigmas]
+        self.exps = [tuple(p) for p in plans]
+        plans = [zc.plan_with_raw_fallback(p) if f else p for p, f in zip(plans, flags)]
+        self.caps = [zc.zc_max_compressed_bytes(n) if workspace else zc.zc_compress_capacity(n) for n in ns]
+        offs = np.concatenate([[0], np.cumsum([slot(c) for c in self.caps])]).astype(np.int64)
+        self.offs = offs
+        self.x = [torch.zeros(max(n, 1), dtype=torch.int16, device="cuda") for n in ns]
+        self.out = torch.zeros(int(offs[-1]), dtype=torch.uint8, device="cuda")
+        self.sizes = torch.zeros(len(ns), dtype=torch.int64, device="cuda")
+        self.dec = [torch.zeros(max(n, 1), dtype=torch.int16, device="cuda") for n in ns]
+        self.status = torch.zeros(len(ns), dtype=torch.int32, device="cuda")
+        ob = self.out.data_ptr()
+        self.enc = zc.make_enc_segs([(self.x[i], n, plans[i], ob + int(offs[i]), self.caps[i],
+                                      self.sizes.data_ptr() + 8 * i) for i, n in enumerate(ns)])
+        self.decs = zc.make_dec_segs([(ob + int(offs[i]), self.caps[i], n, self.dec[i],
+                                       self.status.data_ptr() + 4 * i) for i, n in enumerate(ns)])
+        wsb = sum(zc.zc_compress_workspace_bytes(n) for n in ns)
+        self.ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda") if workspace else None
+        self.zc = zc
+
+    def compress(self):
+        if self.ws is not None:
+            self.zc.zc_compress_batch_ws(self.enc, self.ws, self.ws.numel())
+        else:
+            self.zc.zc_compress_batch(self.enc)
+
+    def both(self):
+        self.compress()
+        self.zc.zc_decompress_batch(self.decs)
+
+    def capture(self) -> torch.cuda.CUDAGraph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.both()  # eager once before the capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.both()
+        torch.cuda.synchronize()
+        return graph
+
+    def load(self, xs):
+        for t, x in zip(self.x, xs):
+            if x.size:
+                t[:x.size].copy_(torch.from_numpy(x.view(np.int16)))
+        for i, n in enumerate(self.ns):  # the stream areas only: scratch behind them keeps its words
+            o = int(self.offs[i])
+            self.out[o:o + self.zc.zc_max_compressed_bytes(n)].fill_(0xA5)
+        self.status.fill_(-1)
+        for d in self.dec:
+            d.fill_(0x1357)
+        torch.cuda.synchronize()
+
+    def check(self, xs, what: str):
+        sizes = self.sizes.cpu().numpy()
+        assert not self.status.cpu().numpy().any(), what
+        for i, (x, e, f) in enumerate(zip(xs, self.exps, self.flags)):
+            ref = oracle.encode(x, e, raw_fallback=f)
+            o = int(self.offs[i])
+            got = self.out[o:o + int(sizes[i])].cpu().numpy()
+            assert got.size == ref.size and np.array_equal(got, ref), (what, i, int(sizes[i]), ref.size)
+            assert np.array_equal(to_host_u16(self.dec[i][:x.size]), x), (what, i)
+
+
+def replays(zc, ns, sigmas, flags, workspace, make, rounds=4):
+    c = Captured(zc, ns, sigmas, flags, workspace)
+    g = np.random.default_rng(4242 + sum(ns))
+    c.load(make(g, 0))
+    graph = c.capture()
+    for r in range(rounds):
+        xs = make(g, r + 1)
+        c.load(xs)
+        print("replay %d: n=%s workspace=%s" % (r, ns, workspace), flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        c.check(xs, "replay %d" % r)
+        if r == 1:  # an eager call on the same buffers between two replays
+            xs = make(g, 100)
+            c.load(xs)
+            c.both()
+            torch.cuda.synchronize()
+            c.check(xs, "eager call between replays")
+
+
+@pytest.mark.parametrize("workspace", [True, False])
+def test_graph_staged_batch(zc, workspace):
+    """Three segments, 2,703 spans: a staged launch (finalize blocks)."""
+    ns = [1100 * SPAN + 37, 900 * SPAN, 703 * SPAN - 5]
+    sigmas = [0.02, 0.003, 0.0005]
+    # every replay: new values, and sigmas off the plans' by a replay-dependent
+    # factor, so that the zero-point counts (and every offset) change
+    replays(zc, ns, sigmas, [False] * 3, workspace,
+            lambda g, r: [gaussian(g, n, s * (1.0 + 0.6 * (r % 3))) for n, s in zip(ns, sigmas)])
+
+
+@pytest.mark.parametrize("workspace", [True, False])
+def test_graph_direct(zc, workspace):
+    """Two segments, 600 spans: a direct launch."""
+    ns = [300 * SPAN + 11, 300 * SPAN]
+    sigmas = [0.01, 0.05]
+    replays(zc, ns, sigmas, [False, False], workspace,
+            lambda g, r: [gaussian(g, n, s * (1.0 + 0.5 * (r % 2))) for n, s in zip(ns, sigmas)])
+
+
+@pytest.mark.parametrize("ns", [[200 * SPAN, 50 * SPAN + 3], [2100 * SPAN, 40 * SPAN]],
+                         ids=["direct", "staged"])
+def test_graph_raw_fallback(zc, ns):
+    """A flagged segment whose outcome flips between coded and raw from one
+    replay to the next (the second launch then copies the payload or codes
+    it), next to an unflagged one."""
+    sigmas = [0.02, 0.02]
+
+    def make(g, r):
+        first = uniform_patterns(g, ns[0]) if r % 2 else gaussian(g, ns[0], sigmas[0])
+        return [first, gaussian(g, ns[1], sigmas[1])]
+    replays(zc, ns, sigmas, [True, False], True, make)
