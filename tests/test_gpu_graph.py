@@ -10,7 +10,9 @@ replay to the next.  Cases: a staged batch (more spans than the device holds
 at once), a direct launch, and segments under the raw fallback whose outcome
 flips between coded and raw from one replay to the next (two launches per
 call); the scratch in a workspace or behind each stream; an eager call on the
-same buffers between two replays."""
+same buffers between two replays.  The other entry points (the local
+reduction, the histograms, the sigma estimate) pass no words between
+workgroups; one case replays them too."""
 import numpy as np
 import pytest
 import torch
@@ -163,3 +165,81 @@ def test_graph_raw_fallback(zc, ns):
         first = uniform_patterns(g, ns[0]) if r % 2 else gaussian(g, ns[0], sigmas[0])
         return [first, gaussian(g, ns[1], sigmas[1])]
     replays(zc, ns, sigmas, [True, False], True, make)
+
+
+def test_graph_reduce_and_statistics(zc):
+    """The local reduction of peer streams, the exponent histogram (with a
+    workspace, and the no-allocation form) and the sigma estimate captured in
+    one graph and replayed with new inputs; the peer streams are compressed
+    eagerly before each replay.  The reduction and both histograms equal the
+    oracle's; the sigma estimate equals that of an eager call on the same
+    input, bit for bit (its grid is fixed)."""
+    n, sigmas = 1_500_003, (0.01, 0.02, 0.005)
+    k = len(sigmas)
+    exps = [tuple(zc.zc_plan_from_sigma(s)) for s in sigmas]
+    cap = zc.zc_max_compressed_bytes(n)
+    streams = torch.zeros((k, slot(cap)), dtype=torch.uint8, device="cuda")
+    sizes = torch.zeros(k, dtype=torch.int64, device="cuda")
+    enc_ws = torch.zeros(zc.zc_compress_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    peers = [torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(k)]
+    local = torch.zeros(n, dtype=torch.int16, device="cuda")
+    out = torch.zeros(n, dtype=torch.int16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(zc.zc_stats_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    hist = torch.zeros(256, dtype=torch.int64, device="cuda")
+    hist_na = torch.zeros(256, dtype=torch.int64, device="cuda")
+    sig = torch.zeros(2, dtype=torch.int64, device="cuda")  # sigma bits, finite count
+    ptrs = [streams[i].data_ptr() for i in range(k)]
+
+    def body():
+        zc.zc_decompress_reduce(ptrs, [cap] * k, n, local, out, status)
+        zc.zc_exponent_histogram(local, n, ws, ws.numel(), hist)
+        zc.zc_exponent_histogram_noalloc(local, n, hist_na)
+        zc.zc_estimate_sigma(local, n, ws, ws.numel(), sig.data_ptr(), sig.data_ptr() + 8)
+
+    g = np.random.default_rng(77)
+
+    def load(r):
+        xs = [gaussian(g, n, s * (1.0 + 0.5 * (r % 3))) for s in sigmas]
+        x_local = gaussian(g, n, 0.01 * (1 + r))
+        for t, x in zip(peers, xs):
+            t.copy_(torch.from_numpy(x.view(np.int16)))
+        local.copy_(torch.from_numpy(x_local.view(np.int16)))
+        for i in range(k):  # eager work between replays
+            zc.zc_compress_ws(peers[i], n, exps[i], streams[i], cap, sizes.data_ptr() + 8 * i, enc_ws,
+                              enc_ws.numel())
+        out.fill_(0x1357)
+        status.fill_(-1)
+        torch.cuda.synchronize()
+        return xs, x_local
+
+    load(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        body()
+    torch.cuda.synchronize()
+    for r in range(4):
+        xs, x_local = load(r + 1)
+        print("replay %d: reduce of %d peers and statistics, n=%d" % (r, k, n), flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        refs = [oracle.encode(x, e) for x, e in zip(xs, exps)]
+        sz = sizes.cpu().numpy()
+        for i in range(k):
+            assert np.array_equal(streams[i][:int(sz[i])].cpu().numpy(), refs[i]), (r, i)
+        rc, want = oracle.decode_reduce(refs, n, x_local)
+        assert rc == 0 and int(status.item()) == 0, r
+        assert np.array_equal(to_host_u16(out), want), r
+        h = oracle.exponent_histogram(x_local)
+        assert np.array_equal(hist.cpu().numpy(), h) and np.array_equal(hist_na.cpu().numpy(), h), r
+        got = sig.cpu().numpy().copy()
+        sig.fill_(-1)
+        zc.zc_estimate_sigma(local, n, ws, ws.numel(), sig.data_ptr(), sig.data_ptr() + 8)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, sig.cpu().numpy()) and int(got[1]) == n, r
