@@ -57,7 +57,10 @@
  *   - "device" pointers are HIP device memory of the current device;
  *   - inputs and outputs must not overlap;
  *   - host-detectable errors return a status before anything is enqueued and
- *     nothing is written; ZC_ERR_HIP reports a failed launch.
+ *     nothing is written; ZC_ERR_HIP reports a failed launch;
+ *   - device work is kernel launches only (no memset, copy or allocation), so
+ *     every call may be captured into a HIP graph and the graph replayed with
+ *     new data in the same buffers (see zc_compress for its scratch).
  */
 #ifndef ZC_H
 #define ZC_H
