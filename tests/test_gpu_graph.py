@@ -45,9 +45,9 @@ class Captured:
     """Buffers of one batch (inputs, outputs with their sizes, workspace,
     decode outputs) and a graph holding one compress and one decompress call."""
 
-    def __init__(self, zc, ns, sigmas, flags, workspace: bool):
+    def __init__(self, zc, ns, sigmas, flags, workspace: bool, tables=None):
         self.ns, self.sigmas, self.flags = ns, sigmas, flags
-        plans = [zc.zc_plan_from_sigma(s) for s in sigmas]
+        plans = tables if tables is not None else [zc.zc_plan_from_sigma(s) for s in sigmas]
         self.exps = [tuple(p) for p in plans]
         plans = [zc.plan_with_raw_fallback(p) if f else p for p, f in zip(plans, flags)]
         self.caps = [zc.zc_max_compressed_bytes(n) if workspace else zc.zc_compress_capacity(n) for n in ns]
@@ -113,9 +113,9 @@ class Captured:
             assert np.array_equal(to_host_u16(self.dec[i][:x.size]), x), (what, i)
 
 
-def replays(zc, ns, sigmas, flags, workspace, make, rounds=4):
-    c = Captured(zc, ns, sigmas, flags, workspace)
-    g = np.random.default_rng(4242 + sum(ns))
+def replays(zc, ns, sigmas, flags, workspace, make, rounds=4, tables=None, seed=None):
+    c = Captured(zc, ns, sigmas, flags, workspace, tables)
+    g = np.random.default_rng(4242 + sum(ns) if seed is None else seed)
     c.load(make(g, 0))
     graph = c.capture()
     for r in range(rounds):
@@ -165,6 +165,26 @@ def test_graph_raw_fallback(zc, ns):
         first = uniform_patterns(g, ns[0]) if r % 2 else gaussian(g, ns[0], sigmas[0])
         return [first, gaussian(g, ns[1], sigmas[1])]
     replays(zc, ns, sigmas, [True, False], True, make)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_graph_random_batches(zc, case):
+    """Seeded random batches: 1-5 segments with sizes at the tiling's edges or
+    random (one case in two with a segment over 2,048 spans), random tables,
+    the raw-fallback flag and the workspace drawn per case; every replay draws
+    new values with a new zero-point share per segment."""
+    from test_gpu_random import random_plan, random_size, random_values
+    g = np.random.default_rng(5100 + case)
+    k = int(g.integers(1, 6))
+    ns = [random_size(g, case % 2 == 1 and i == 0) for i in range(k)]
+    tables = [random_plan(g) for _ in range(k)]
+    flags = [bool(g.random() < 0.35) for _ in range(k)]
+    workspace = bool(g.random() < 0.5)
+    print("graph random case %d: n=%s raw-fallback=%s workspace=%s" % (case, ns, flags, workspace), flush=True)
+
+    def make(gr, r):
+        return [random_values(gr, n, t, float(gr.choice([0.0, 0.01, 0.3, 1.0]))) for n, t in zip(ns, tables)]
+    replays(zc, ns, [None] * k, flags, workspace, make, rounds=3, tables=tables, seed=6100 + case)
 
 
 def test_graph_reduce_and_statistics(zc):
