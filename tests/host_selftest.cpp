@@ -113,6 +113,17 @@ int main() {
         const uint64_t ws = zc_compress_workspace_bytes(n);
         CHECK(ws % 256 == 0 && ws >= S.bytes && ws < S.bytes + 256);
         CHECK(S.decision % kWordBytes == 0 && S.status % kWordBytes == 0 && S.span_words >= S.status + kWordBytes);
+        // every region in order, none overlapping the next: the 8-byte epoch
+        // between the status word and the span words, each word array sized
+        // for its units
+        const uint64_t nb = enc_blocks(n), nr = ceil_div(nb, kRun), nc = ceil_div(nr, kChunkRuns);
+        const uint64_t ng = ceil_div(nb, kGroupSpans);
+        CHECK(S.status >= S.decision + kWordBytes && S.epoch >= S.status + kWordBytes && S.epoch % 8 == 0);
+        CHECK(S.span_words >= S.epoch + 8 && S.run_words >= S.span_words + kWordBytes * nb);
+        CHECK(S.chunk_words >= S.run_words + kWordBytes * nr && S.chunk_done >= S.chunk_words + kWordBytes * nc);
+        CHECK(S.group_words >= S.chunk_done + kWordBytes * nc && S.run_done >= S.group_words + kWordBytes * ng);
+        CHECK(S.span_done >= S.run_done + kWordBytes * nr && S.staging >= S.span_done + kWordBytes * nb);
+        CHECK(S.span_words % 128 == 0 && S.staging % 128 == 0);
     }
     CHECK(zc_max_compressed_bytes(kMaxElems + 1) == 0);
     CHECK(zc_max_compressed_bytes(~0ull) == 0);
