@@ -341,13 +341,16 @@ TIMELINE_WORDS = 5  # per block in the instrumented build: four clock stamps and
 TIMELINE_TICK_US = 0.01  # the real-time clock runs at 100 MHz
 
 
-def timeline(zc, w, warmup: int) -> dict:
+def timeline(zc, w, warmup: int, burst: int = 1) -> dict:
     """Per-block timeline of one batched compress of workload w (no raw
     fallback), from the instrumented build (libzc_timeline.so, ZC_TIMELINE):
-    after `warmup` calls, one call between HIP events with every block's four
-    clock stamps and role recorded (stamp meanings in zc_compress.hip).  The
-    record gives, per role, the median time between stamps, and the launch's
-    tail: what ends after the last encoder block."""
+    after `warmup` calls, `burst` back-to-back calls (HIP events between them)
+    with every block's four clock stamps and role recorded (stamp meanings in
+    zc_compress.hip); the stamps are the last call's, each call overwriting
+    the previous one's.  burst = 1: one call right after a synchronize; a
+    longer burst gives the steady state of back-to-back calls.  The record
+    gives, per role, the median time between stamps, and the launch's tail:
+    what ends after the last encoder block."""
     import ctypes
     import numpy as np
     import torch
@@ -372,11 +375,13 @@ def timeline(zc, w, warmup: int) -> dict:
     torch.cuda.synchronize()
     if lib.zc_timeline_clear() != 0:
         raise RuntimeError("zc_timeline_clear failed")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    call()
-    e1.record(stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(max(1, burst) + 1)]
+    ev[0].record(stream)
+    for i in range(max(1, burst)):
+        call()
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
+    e0, e1 = ev[-2], ev[-1]
     buf = np.zeros(TIMELINE_WORDS << 20, dtype=np.uint64)
     if lib.zc_timeline_read(buf.ctypes.data, buf.nbytes) != 0:
         raise RuntimeError("zc_timeline_read failed")
@@ -392,7 +397,8 @@ def timeline(zc, w, warmup: int) -> dict:
 
     def med(a):
         return round(float(np.median(a)), 2) if a.size else None
-    rec = {"workload": w.name, "values": w.n, "event_us": round(e0.elapsed_time(e1) * 1e3, 2), "blocks": blocks,
+    rec = {"workload": w.name, "values": w.n, "burst": max(1, burst),
+           "event_us": round(e0.elapsed_time(e1) * 1e3, 2), "blocks": blocks,
            "span_us": round(float(stamps[:, 3].max()), 2), "stamps": "0 start, 1 first pass or span words, "
            "2 bytes staged or offset known, 3 end (zc_compress.hip)", "roles": {}}
     for kd, name in names.items():
@@ -783,6 +789,9 @@ def main() -> int:
                     help="print the HIP-event time of every one of --calls back-to-back calls of this kind (means "
                          "over 50), from the run's first call on, instead of the bench line")
     ap.add_argument("--calls", type=int, default=400, help="calls for --percall (default 400)")
+    ap.add_argument("--burst", type=int, default=1,
+                    help="--timeline: the stamps of the last of this many back-to-back calls (the steady state "
+                         "of a burst; default 1, one call after a synchronize)")
     ap.add_argument("--profile", choices=("compress", "decompress", "reduce"),
                     help="run only what a rocprofv3 counter pass measures: a copy of known size, then --steps "
                          "calls of this kind on --workload; prints that run's facts instead of the bench line")
@@ -810,7 +819,7 @@ def main() -> int:
         print(json.dumps(profile_pass(zc, w, args.profile, args.steps)), flush=True)
         return 0
     if args.timeline:
-        print(json.dumps(timeline(zc, w, args.warmup)), flush=True)
+        print(json.dumps(timeline(zc, w, args.warmup, args.burst)), flush=True)
         return 0
     if args.percall:
         print(json.dumps(percall(zc, w, args.percall, args.calls)), flush=True)
