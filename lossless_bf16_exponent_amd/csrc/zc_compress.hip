@@ -29,10 +29,15 @@
 //     blocks of the same launch with lower indices, which workgroup dispatch
 //     in index order has started first; every wait is bounded, and a call
 //     whose wait runs out still ends, with a zero magic in its header and a
-//     stream size of 0.  The segment's last block writes the header once every
-//     other block of the segment has passed its waits (zc_grid.h places the
-//     roles; the scratch words are described below, with the reasons the
-//     handshakes are device-scope accesses and not release/acquire pairs);
+//     stream size of 0: a block whose wait runs out marks its segment as
+//     failed, and the segment's last block, which writes the header, reads
+//     the mark once its own waits have passed.  Those waits depend, directly
+//     or through other words, on a word from every other block of the
+//     segment, so by then every word that any block of the segment waits for
+//     has been published and a wait still pending ends at its next poll
+//     (zc_grid.h places the roles; the scratch words are described below,
+//     with the reasons the handshakes are device-scope accesses and not
+//     release/acquire pairs);
 //   * under the raw fallback the first launch guesses each long segment's
 //     form from a sample and a second launch completes wrong guesses.
 #include <hip/hip_runtime.h>
@@ -186,8 +191,9 @@ __device__ __forceinline__ bool get_word(const uint8_t *w, Token t, uint32_t &pa
 
 // The segment's epoch word, read by every block of a launch before
 // it publishes or polls anything.  The segment's header writer advances it at
-// the end of a call's first launch, once every other block of the segment has
-// passed its waits: by then each of them has read it.  So within a launch the
+// the end of a call's first launch, once its own waits have passed: those
+// depend on a word from every other block of the segment, each published after
+// its block read the epoch.  So within a launch the
 // word does not change while anyone reads it, and a load that may hit the L2
 // serves: the value a reader needs was written by an earlier launch on the
 // stream, which the kernel boundary makes visible.  (A device-scope load from
@@ -266,6 +272,13 @@ __device__ __forceinline__ bool poll_list(uint32_t count, Addr addr, Token t, ui
             }
     }
     return true;
+}
+
+// A block whose wait ran out marks its segment's launch as failed (thread 0;
+// ok is block-uniform).  The header writer reads the mark before it writes the
+// header: a given-up wait of any block of the segment invalidates the stream.
+__device__ __forceinline__ void mark_failed(uint8_t *scratch, const Scratch &S, Token tok, bool ok) {
+    if (!ok && threadIdx.x == 0) put_word(scratch + S.failed, tok, 1u);
 }
 
 // The same over words base[0 .. count).
@@ -643,8 +656,10 @@ __device__ __forceinline__ void write_header(const EncArgs &args, const EncSeg &
 // its span: those of earlier groups through their group words and of the
 // earlier spans of its own group through their span words, and writes its
 // table entries and its zero-point bytes (from LDS) in place: nothing is
-// staged.  The segment's last span writes the header once every other block
-// of the segment has passed its waits.
+// staged.  The segment's last span then writes the header, unless the
+// segment's failure mark is set: the group words it has read exist only once
+// every span word of their groups does, so every other span's waits are for
+// words already published.
 struct DirectState {
     uint32_t sib;  // zero-points of the group's spans before b (the group's last span only)
     bool ok;
@@ -690,7 +705,10 @@ __device__ __forceinline__ void direct_finish(const EncArgs &args, uint32_t s, u
     bool ok = st.ok;
     const uint32_t sib = st.sib;
     // a raw guess places nothing: only the header writer needs its offset
-    if (raw && b + 1 < nb) return;
+    if (raw && b + 1 < nb) {
+        mark_failed(scratch, S, tok, ok);
+        return;
+    }
     // the group's earlier spans (unless summed above) and the earlier groups
     const uint32_t nsib = group_last ? 0u : b - g0;
     uint32_t pay[1] = {0};
@@ -703,6 +721,11 @@ __device__ __forceinline__ void direct_finish(const EncArgs &args, uint32_t s, u
             },
             tok, pay);
     ok = __syncthreads_and(ok);
+    mark_failed(scratch, S, tok, ok);
+    // the header writer: the failure mark, read once its own waits have passed
+    // (in flight while it places its bytes)
+    uint64_t fa = 0, fb = 0;
+    if (b + 1 == nb) load_word(scratch + S.failed, fa, fb);
     const uint32_t mine = (uint32_t)tid < nsib ? (pay[0] & 0xFFFFu) + (pay[0] >> 16) : pay[0];
     const uint32_t P = sib + block_sum(mine, sh.red);
     stamp(2);
@@ -714,19 +737,9 @@ __device__ __forceinline__ void direct_finish(const EncArgs &args, uint32_t s, u
         if (tid == 1 && gi + 1 < L.groups) tab[gi + 1] = P + c0;
         write_span(out + L.off_zp, P, sh.zp, T, lane, (uint32_t)wave, kWaves);
     }
-    // data needs no wait before a done word: nothing in this launch reads it
-    if (b + 1 < nb) {
-        if (ok && tid == 0) put_word(scratch + S.span_done + (uint64_t)kWordBytes * b, tok, 1u);
-        return;
-    }
-    // the segment's last span: every earlier span has passed its waits (a raw
-    // guess: every span's count is in P, and spans write nothing else once
-    // they have counted)
-    if (ok && !raw) {
-        uint32_t dn[8];
-        static_assert(kDirectMax <= 8 * kThreads, "one round polls every done word");
-        ok = poll_words<8>(scratch + S.span_done, b, tok, dn);
-    }
+    if (b + 1 < nb) return;
+    uint32_t f;
+    if (word_valid(fa, fb, tok, f)) ok = false;
     ok = __syncthreads_and(ok);
     write_header<kFb>(args, sg, L, (uint64_t)P + c0 + c1, ok, raw, tok);
 }
@@ -822,6 +835,7 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
     if (kFb && guessing) {
         mode = await_guess(scratch, S, tok, sh.red);  // its barriers also cover sh.code
         if (mode == kModeAbort) {
+            mark_failed(scratch, S, tok, false);
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
             // a direct segment's last span writes the header: the invalid one
             if (direct && b + 1 == blocks) write_header<kFb>(args, sg, L, 0, false, false, tok);
@@ -980,9 +994,11 @@ __device__ __forceinline__ void encode_span(const EncArgs &args, uint32_t s, uin
 //      for another one.
 //   3. It writes the run's table entries and its zero-point bytes, a landed
 //      batch at a time.
-//   4. The last run of a chunk waits until the chunk's other runs have passed
-//      their waits and publishes the chunk's done word; the segment's last run
-//      instead writes the header once every earlier chunk is done.
+//   4. The segment's last run writes the header, unless the segment's
+//      failure mark is set.  Its offset needed every earlier chunk word (each
+//      published after all run words of its chunk) and its own chunk's run
+//      words, so every word that any finalize block of the segment waits for
+//      has been published.
 template <bool kFb>
 __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, uint32_t r, FinShared &sh) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -1139,6 +1155,11 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
             P = rsum + block_sum(pp[0] + pp[1] + pp[2], sh.red);
         }
     }
+    mark_failed(scratch, S, tok, ok);
+    // the header writer: the failure mark, read once its own waits have passed
+    // (in flight while it writes the run's bytes)
+    uint64_t fa = 0, fb = 0;
+    if (last_run) load_word(scratch + S.failed, fa, fb);
 
     stamp(2);
     // ---- 3. table entries and zero-point bytes
@@ -1185,32 +1206,13 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
     }
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no landing left in flight (a given-up call)
 
-    // ---- 4. done words; the header of a segment without direct spans.  A raw
-    // guess wrote nothing a done word would cover: every span's count is in
-    // the header writer's offset.
-    if (kFb && raw) {
-        if (last_run) write_header<kFb>(args, sg, L, (uint64_t)P + A, ok, true, tok);
-        return;
-    }
-    if (!chunk_last) {
-        if (ok && tid == 0) put_word(scratch + S.run_done + (uint64_t)kWordBytes * r, tok, 1u);
-        return;
-    }
-    {
-        uint32_t dn[1] = {0};
-        if (ok) ok = poll_words<1>(scratch + S.run_done + (uint64_t)kWordBytes * cfirst, r - cfirst, tok, dn);
+    // ---- 4. the header of a segment without direct spans
+    if (last_run) {
+        uint32_t f;
+        if (word_valid(fa, fb, tok, f)) ok = false;
         ok = __syncthreads_and(ok);
+        write_header<kFb>(args, sg, L, (uint64_t)P + A, ok, kFb && raw, tok);
     }
-    if (!last_run) {
-        if (ok && tid == 0) put_word(scratch + S.chunk_done + (uint64_t)kWordBytes * c, tok, 1u);
-        return;
-    }
-    {
-        uint32_t dn[2] = {0, 0};
-        if (ok) ok = poll_words<2>(scratch + S.chunk_done, c, tok, dn);
-        ok = __syncthreads_and(ok);
-    }
-    write_header<kFb>(args, sg, L, (uint64_t)P + A, ok, false, tok);
 }
 
 // The role of block blockIdx.x: its piece's kind and segment, and its first

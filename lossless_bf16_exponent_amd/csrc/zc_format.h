@@ -132,13 +132,11 @@ ZC_HD uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 //   status        raw fallback: what the second pass still has to do
 //   epoch         8 bytes, no token: a counter the segment's header writer
 //                 advances at the end of each call's first launch
+//   failed        set by a block of the segment whose wait ran out
 //   span words    one per encoder span: zero-point counts of its two groups
 //   run words     one per run: zero-point count of the run
 //   chunk words   one per chunk: zero-point count of its runs
-//   chunk done    one per chunk: every finalize block of the chunk passed its waits
 //   group words   one per group of direct spans: their zero-point count
-//   run done      one per run: its finalize block passed its waits
-//   span done     one per direct span: its block passed its waits
 //   staging       kEncSpan B per encoder span: its zero-point bytes, in order
 // Every word carries the 64-bit token of the launch that wrote it, so words
 // left by an earlier launch (or any other old contents) never pass for fresh.
@@ -147,8 +145,8 @@ ZC_HD uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 // host's arguments.
 constexpr uint32_t kWordBytes = 16;
 struct Scratch {
-    uint64_t decision, status, epoch, span_words, run_words, chunk_words, chunk_done, group_words, run_done,
-        span_done, staging, bytes;  // offsets from off_scratch, total size
+    uint64_t decision, status, epoch, failed, span_words, run_words, chunk_words, group_words, staging,
+        bytes;  // offsets from off_scratch, total size
 };
 ZC_HD Scratch scratch_for(uint64_t n) {
     const uint64_t nb = enc_blocks(n), nr = ceil_div(nb, kRun), nc = ceil_div(nr, kChunkRuns);
@@ -157,14 +155,12 @@ ZC_HD Scratch scratch_for(uint64_t n) {
     S.decision = 0;
     S.status = kWordBytes;
     S.epoch = 2 * kWordBytes;
-    S.span_words = align128(2 * kWordBytes + 8);
+    S.failed = 3 * kWordBytes;
+    S.span_words = align128(4 * kWordBytes);
     S.run_words = S.span_words + align128(kWordBytes * nb);
     S.chunk_words = S.run_words + align128(kWordBytes * nr);
-    S.chunk_done = S.chunk_words + align128(kWordBytes * nc);
-    S.group_words = S.chunk_done + align128(kWordBytes * nc);
-    S.run_done = S.group_words + align128(kWordBytes * ng);
-    S.span_done = S.run_done + align128(kWordBytes * nr);
-    S.staging = S.span_done + align128(kWordBytes * nb);
+    S.group_words = S.chunk_words + align128(kWordBytes * nc);
+    S.staging = S.group_words + align128(kWordBytes * ng);
     S.bytes = S.staging + nb * (uint64_t)kEncSpan;
     return S;
 }

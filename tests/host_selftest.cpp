@@ -108,7 +108,7 @@ int main() {
         CHECK(L.off_zp >= L.off_tab + 4 * (L.groups + 1));
         CHECK(L.off_scratch >= L.off_zp + n);                      // the largest stream fits before the scratch
         CHECK(L.off_scratch >= kHeaderBytes + 2 * n);              // so does the raw form
-        CHECK(S.staging >= S.span_done && S.bytes == S.staging + enc_blocks(n) * (uint64_t)kEncSpan);
+        CHECK(S.staging >= S.group_words && S.bytes == S.staging + enc_blocks(n) * (uint64_t)kEncSpan);
         CHECK(cap == L.off_scratch);                               // the stream bound
         const uint64_t ws = zc_compress_workspace_bytes(n);
         CHECK(ws % 256 == 0 && ws >= S.bytes && ws < S.bytes + 256);
@@ -120,9 +120,8 @@ int main() {
         const uint64_t ng = ceil_div(nb, kGroupSpans);
         CHECK(S.status >= S.decision + kWordBytes && S.epoch >= S.status + kWordBytes && S.epoch % 8 == 0);
         CHECK(S.span_words >= S.epoch + 8 && S.run_words >= S.span_words + kWordBytes * nb);
-        CHECK(S.chunk_words >= S.run_words + kWordBytes * nr && S.chunk_done >= S.chunk_words + kWordBytes * nc);
-        CHECK(S.group_words >= S.chunk_done + kWordBytes * nc && S.run_done >= S.group_words + kWordBytes * ng);
-        CHECK(S.span_done >= S.run_done + kWordBytes * nr && S.staging >= S.span_done + kWordBytes * nb);
+        CHECK(S.chunk_words >= S.run_words + kWordBytes * nr && S.group_words >= S.chunk_words + kWordBytes * nc);
+        CHECK(S.staging >= S.group_words + kWordBytes * ng);
         CHECK(S.span_words % 128 == 0 && S.staging % 128 == 0);
     }
     CHECK(zc_max_compressed_bytes(kMaxElems + 1) == 0);
