@@ -89,6 +89,17 @@ def build_giveup(verbose: bool = False) -> str:
     return build_variant(GIVEUP_LIB, ["ZC_SPIN_LIMIT=0"], verbose)
 
 
+FAIL_OTHERS_LIB = os.path.join(ROOT, "tests", "libzc_failothers.so")
+
+
+def build_failothers(verbose: bool = False) -> str:
+    """The library in which every compress workgroup other than a segment's
+    header writer acts as if a wait had run out, while the header writer's
+    own waits pass: the test that the failure mark alone invalidates the
+    stream.  Test infrastructure only; never loaded by the package."""
+    return build_variant(FAIL_OTHERS_LIB, ["ZC_FAIL_OTHERS=1"], verbose)
+
+
 GUESS_LIBS = {"raw": os.path.join(ROOT, "tests", "libzc_guess_raw.so"),
               "coded": os.path.join(ROOT, "tests", "libzc_guess_coded.so")}
 

@@ -242,6 +242,13 @@ __device__ __forceinline__ void put_staged16(__amdgpu_buffer_rsrc_t slot, uint32
 #define ZC_SPIN_LIMIT (1u << 20)
 #endif
 constexpr uint32_t kSpinLimit = ZC_SPIN_LIMIT;
+// A test build sets ZC_FAIL_OTHERS to 1: every finalize block and direct span
+// other than a segment's header writer then acts as if one of its waits had
+// run out, while the header writer's own waits pass, so that the failure mark
+// alone must keep the stream from being marked valid.
+#ifndef ZC_FAIL_OTHERS
+#define ZC_FAIL_OTHERS 0
+#endif
 
 // Thread tid polls words addr(i), i = tid + kThreads q (q < Q, i < count),
 // until every one carries the token.  Payloads of valid words land in pay[q]
@@ -702,7 +709,7 @@ __device__ __forceinline__ void direct_finish(const EncArgs &args, uint32_t s, u
     const uint8_t *const group_w = scratch + S.group_words;
     const uint32_t g = b / kGroupSpans, g0 = g * kGroupSpans;
     const bool group_last = b % kGroupSpans == kGroupSpans - 1 || b + 1 == nb;
-    bool ok = st.ok;
+    bool ok = st.ok && !(ZC_FAIL_OTHERS && b + 1 < nb);
     const uint32_t sib = st.sib;
     // a raw guess places nothing: only the header writer needs its offset
     if (raw && b + 1 < nb) {
@@ -1035,7 +1042,8 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
     if (ok && (uint32_t)tid < count) load_word(sw + (uint64_t)kWordBytes * tid, w0, w1);
     const Token tok = mix_token(args.tok_lo, args.tok_hi, epoch);
     uint32_t sp[1] = {0};
-    const uint32_t done = (uint32_t)tid < count && word_valid(w0, w1, tok, sp[0]) ? 1u : 0u;
+    // (that round is the wait's first poll: a spin limit of 0 allows none)
+    const uint32_t done = kSpinLimit > 0 && (uint32_t)tid < count && word_valid(w0, w1, tok, sp[0]) ? 1u : 0u;
     if (ok) ok = poll_words<1>(sw, count, tok, sp, done);
     ok = __syncthreads_and(ok);
     if (wave == 0) {
@@ -1155,6 +1163,7 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
             P = rsum + block_sum(pp[0] + pp[1] + pp[2], sh.red);
         }
     }
+    if (ZC_FAIL_OTHERS && !last_run) ok = false;
     mark_failed(scratch, S, tok, ok);
     // the header writer: the failure mark, read once its own waits have passed
     // (in flight while it writes the run's bytes)

@@ -2,8 +2,11 @@
 other workgroups of the same launch; every wait is bounded, and a call whose
 wait runs out must still end, leave a stream that every decoder rejects and
 report a stream size of 0.  With workgroups dispatched in index order no wait
-can run out, so the test uses a build of the library whose spin limit is 0
-(every wait gives up at once), loaded next to the shipped library."""
+can run out, so the tests use builds of the library loaded next to the
+shipped one: one whose spin limit is 0 (every wait gives up at once), and one
+in which only the workgroups other than each segment's header writer act as
+if a wait had run out (the header writer then learns of it only through the
+segment's failure mark)."""
 import ctypes
 import os
 
@@ -22,11 +25,10 @@ def zc():
     return require_gpu()
 
 
-@pytest.fixture(scope="module")
-def giveup(zc):
-    if not os.path.exists(_build.GIVEUP_LIB):
-        raise RuntimeError("%s is not built (run __graft_entry__.build())" % _build.GIVEUP_LIB)
-    lib = ctypes.CDLL(_build.GIVEUP_LIB)
+def load(zc, path):
+    if not os.path.exists(path):
+        raise RuntimeError("%s is not built (run __graft_entry__.build())" % path)
+    lib = ctypes.CDLL(path)
     lib.zc_compress.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.POINTER(zc.zc_plan), ctypes.c_void_p,
                                 ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
     lib.zc_compress.restype = ctypes.c_int
@@ -35,15 +37,26 @@ def giveup(zc):
     return lib
 
 
+@pytest.fixture(scope="module")
+def giveup(zc):
+    return load(zc, _build.GIVEUP_LIB)
+
+
+@pytest.fixture(scope="module")
+def failothers(zc):
+    return load(zc, _build.FAIL_OTHERS_LIB)
+
+
 def gaussian(n, sigma, seed):
     g = np.random.default_rng(seed)
     return workloads.bf16_bits_from_f32((g.standard_normal(n) * sigma).astype(np.float32))
 
 
 def given_up_batch(zc, giveup, ns, sigmas, waits, raw_at=None):
-    """Compress ns in one batched launch with the give-up build: segments that
-    wait (waits[i]) report size 0 and a zero magic, and the shipped decoder
-    rejects them without writing; the others equal the oracle's streams."""
+    """Compress ns in one batched launch with a test build (giveup): segments
+    that give up (waits[i]) report size 0 and a zero magic, and the shipped
+    decoder rejects them without writing; the others equal the oracle's
+    streams."""
     import oracle
     plans = [zc.zc_plan_from_sigma(s) for s in sigmas]
     if raw_at is not None:
@@ -112,3 +125,18 @@ def test_given_up_direct_launch_and_single_call(zc, giveup):
     ref = oracle.encode(xs[0], plans[0])
     assert int(sizes[0].item()) == ref.size
     assert np.array_equal(buf[:ref.size].cpu().numpy(), ref)
+
+
+def test_failure_mark_alone_invalidates(zc, failothers):
+    """A build in which every finalize block and direct span other than a
+    segment's header writer acts as if a wait had run out, while the header
+    writer's own waits pass: the header writer finds only the failure mark,
+    and must still leave an invalid stream.  A segment whose header writer is
+    its only waiting block (one run of finalize work, or one direct span)
+    completes and equals the oracle's stream."""
+    # staged: 20,000,003 values are 2,442 spans (153 runs); 81,920 values 10 spans (one run)
+    ns = [20_000_003, 8192 * 10, 300_007, 0]
+    given_up_batch(zc, failothers, ns, (1.0, 0.02, 1e-3, 1.0), [True, False, True, False], raw_at=2)
+    # direct: spans after the first wait for earlier ones; a one-span segment has no other block
+    ns = [300_007, 0, 8000, 8192 * 40 + 5]
+    given_up_batch(zc, failothers, ns, (0.02, 1.0, 0.5, 1e-3), [True, False, False, True])
