@@ -245,7 +245,10 @@ constexpr uint32_t kSpinLimit = ZC_SPIN_LIMIT;
 // A test build sets ZC_FAIL_OTHERS to 1: every finalize block and direct span
 // other than a segment's header writer then acts as if one of its waits had
 // run out, while the header writer's own waits pass, so that the failure mark
-// alone must keep the stream from being marked valid.
+// alone must keep the stream from being marked valid.  Such a block sets the
+// mark, and waits for it to be acknowledged, before it publishes any word, as
+// a block that gave up would have done before the words the header writer
+// waits for appeared.
 #ifndef ZC_FAIL_OTHERS
 #define ZC_FAIL_OTHERS 0
 #endif
@@ -681,6 +684,10 @@ __device__ __forceinline__ DirectState direct_publish(const EncArgs &args, uint3
     uint8_t *const scratch = seg_scratch(args, sg);
     const uint32_t g = b / kGroupSpans, g0 = g * kGroupSpans;  // g0: the group's first span
     const bool group_last = b % kGroupSpans == kGroupSpans - 1 || b + 1 == nb;
+    if (ZC_FAIL_OTHERS && b + 1 < nb) {
+        mark_failed(scratch, S, tok, false);
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     // a count announces no data: no wait before it
     if (tid == 0) put_word(scratch + S.span_words + (uint64_t)kWordBytes * b, tok, c0 | (c1 << 16));
     DirectState st{0u, true};
@@ -1041,6 +1048,10 @@ __device__ __forceinline__ void finalize_run(const EncArgs &args, uint32_t s, ui
     uint64_t w0 = 0, w1 = 0;
     if (ok && (uint32_t)tid < count) load_word(sw + (uint64_t)kWordBytes * tid, w0, w1);
     const Token tok = mix_token(args.tok_lo, args.tok_hi, epoch);
+    if (ZC_FAIL_OTHERS && !last_run) {
+        mark_failed(scratch, S, tok, false);
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     uint32_t sp[1] = {0};
     // (that round is the wait's first poll: a spin limit of 0 allows none)
     const uint32_t done = kSpinLimit > 0 && (uint32_t)tid < count && word_valid(w0, w1, tok, sp[0]) ? 1u : 0u;
