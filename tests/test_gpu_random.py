@@ -56,7 +56,7 @@ def random_size(g, big: bool) -> int:
     return int(g.integers(1, 400_000))
 
 
-@pytest.mark.parametrize("case", range(96))
+@pytest.mark.parametrize("case", range(192))
 def test_random_batches(zc, case):
     g = np.random.default_rng(9000 + case)
     big = case % 6 == 5
@@ -83,7 +83,7 @@ def test_random_batches(zc, case):
         assert np.array_equal(to_host_u16(o[:n]), x)
 
 
-@pytest.mark.parametrize("case", range(32))
+@pytest.mark.parametrize("case", range(64))
 def test_random_reductions(zc, case):
     g = np.random.default_rng(7000 + case)
     k = int(g.integers(0, 9))
