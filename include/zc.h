@@ -138,8 +138,10 @@ uint64_t zc_compress_workspace_bytes(uint64_t n);
  * Given-up call: workgroups of the launch wait for words that earlier
  * workgroups of the same launch write, each wait bounded (about a second).
  * With workgroups dispatched in index order no wait runs out.  Should one run
- * out anyway, the call still ends and ZC_OK has already been returned, but the
- * stream's header has a zero magic (every decoder rejects it with
+ * out anyway, its workgroup marks the segment in the scratch, the workgroup
+ * that writes the header reads the mark once its own waits have passed, and
+ * the call still ends; ZC_OK has already been returned, but the stream's
+ * header has a zero magic (every decoder rejects it with
  * ZC_ERR_CORRUPT) and *d_out_bytes reads 0: a caller that sends
  * *d_out_bytes bytes sends nothing, and a caller that reads the header sees
  * an invalid stream.  Neither outcome passes for a valid stream.
